@@ -1,0 +1,271 @@
+"""Merge-round throughput of the DiLoCo outer-step merge on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload KEY] [--no-cpu-baseline]
+
+A step is one whole merge round of the workload (every fold of every
+fragment, then every fragment's close), issued through the C ABI on inputs
+already resident in HBM.  W untimed rounds, then K timed rounds between two
+device synchronisations; every launch is bracketed by HIP events on the
+stream it runs on, giving each kernel's average duration.  Prints one JSON
+line: effective HBM GB/s (algorithmic bytes per round / round time), merged
+params/s, the fraction of the 8 TB/s HBM peak, the roofline of the dominant
+kernel, and the CPU oracle timed on a bounded sample of the same workload.
+
+Default workload: DiffuRefill-1B (1,075,980,288 fp32 params) in 4 fragments,
+5 fp32 workers, token-weighted delta mean + outer Nesterov (lr 0.7, momentum
+0.9) + EMA (beta 0.9) fused per fragment.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_WORKLOAD = "diffurefill1b_frag_nesterov_ema"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per launch of `kind` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kind)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def cpu_baseline(w, torch, max_seconds: float = 12.0):
+    """The oracle (unchanged) on a bounded sample of the workload: the first
+    `per_frag` elements of every fragment, full round structure (every fold
+    in arrival order, then the close).  Inputs are generated on the GPU by the
+    seeded generator and copied to host memory before timing."""
+    import numpy as np
+    import oracle
+    from checkpoint_averaging_amd import synth
+
+    cores = len(os.sched_getaffinity(0))
+    orc = oracle.load()
+    orc.set_threads(cores)
+    per_frag = min(1 << 24, min(w.frag_offsets[f + 1] - w.frag_offsets[f]
+                                for f in range(w.n_frags)))
+    n_s = per_frag * w.n_frags
+    dev = torch.device("cuda")
+    frags = []
+    for f in range(w.n_frags):
+        s = w.frag_offsets[f]
+        th0 = synth.global0(w.seed, per_frag, device=dev, start=s)
+        cks = []
+        for i in range(w.workers):
+            c = synth.worker_checkpoint(w.seed, 0, i, th0, start=s, dtype=w.ckpt_dtype)
+            c = c.cpu()
+            cks.append(c.view(torch.int16).numpy().view(np.uint16).copy()
+                       if w.ckpt_dtype == "bf16" else c.numpy().copy())
+        th = th0.cpu().numpy().copy()
+        frags.append({"theta": th, "m": np.zeros_like(th), "e": th.copy() if w.ema else None,
+                      "cks": cks})
+    orders = [synth.arrival_order(w, 0, f) for f in range(w.n_frags)]
+    tok = synth.token_counts(w, 0)
+    from checkpoint_averaging_amd.workload import algorithmic_bytes
+    bytes_per_round = algorithmic_bytes(w)["per_param"] * n_s
+    rounds = 0
+    t0 = time.perf_counter()
+    while True:
+        for f, F in enumerate(frags):
+            order = orders[f]
+            if w.mode == "mean":
+                F["theta"] = orc.mean_round([F["cks"][i] for i in order], ema=F["e"],
+                                            beta=w.beta)
+            else:
+                orc.nesterov_fragment_round(F["theta"], F["m"], [F["cks"][i] for i in order],
+                                            [tok[i] for i in order], w.lr, w.mu, F["e"],
+                                            w.beta)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= max_seconds:
+            break
+    sec = el / rounds
+    return {
+        "value": round(bytes_per_round / sec / 1e9, 3), "unit": "GB/s",
+        "params_per_s": round(n_s / sec, 1),
+        "cores": orc.threads(), "kind": "oracle",
+        "sample": (f"first {per_frag:,} elements of each of the {w.n_frags} fragment(s) "
+                   f"({n_s:,} params, {w.workers} {w.ckpt_dtype} workers), full round "
+                   f"structure, {rounds} rounds in {el:.1f} s"),
+        "cpu": cpu_model(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB "
+                         "(for scaling hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the merge shards with no exchange step; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from checkpoint_averaging_amd import synth
+    from checkpoint_averaging_amd.workload import GpuWorkload, algorithmic_bytes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    ab = algorithmic_bytes(w)
+    log(f"[bench] {w.key}: {w.n_params:,} params, {w.workers} {w.ckpt_dtype} workers, "
+        f"{w.n_frags} fragment(s), {ab['per_param']} B/param")
+    gw = GpuWorkload(w)
+    gw.generate_checkpoints(0)
+    torch.cuda.synchronize()
+    log("[bench] inputs resident")
+
+    if args.copy_calibration_mib:
+        nb = args.copy_calibration_mib << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {nb} bytes read, {nb} bytes written")
+        del src, dst
+
+    def plain(kind, n, call):
+        call()
+
+    for r in range(args.warmup):
+        gw.run_round(0, tag=r + 1, timer=plain)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup rounds done")
+
+    records = []
+
+    def timed(kind, n, call):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        records.append((kind, n, e0, e1))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        gw.run_round(0, tag=1000 + r, timer=timed)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f"[bench] {args.steps} timed rounds: {ms:.3f} ms/round")
+
+    kinds = {}
+    for kind, n, e0, e1 in records:
+        d = kinds.setdefault(kind, {"launches": 0, "ms": 0.0, "bytes": 0})
+        d["launches"] += 1
+        d["ms"] += e0.elapsed_time(e1)
+        d["bytes"] += ab["per_elem"][kind] * n
+    kern = {}
+    for kind, d in kinds.items():
+        kern[kind] = {"launches_per_round": d["launches"] // args.steps,
+                      "avg_ms": round(d["ms"] / d["launches"], 4),
+                      "GB_per_s": round(d["bytes"] / (d["ms"] / 1e3) / 1e9, 1),
+                      "share_of_kernel_time": None}
+    total_kernel_ms = sum(d["ms"] for d in kinds.values())
+    for kind, d in kinds.items():
+        kern[kind]["share_of_kernel_time"] = round(d["ms"] / total_kernel_ms, 3)
+    dom = max(kinds, key=lambda k: kinds[k]["ms"])
+    dd = kinds[dom]
+    achieved = dd["bytes"] / (dd["ms"] / 1e3) / 1e9
+    traffic = measured_traffic(w.key, dom)
+
+    value = ab["per_round"] / (ms / 1e3) / 1e9
+    out = {
+        "metric": "merge-round throughput: effective HBM GB/s and merged params/s; % of HBM peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox; shapes of the pages' models)",
+        "config": {
+            "workload": w.key,
+            "description": w.description,
+            "n_params": w.n_params,
+            "workers": w.workers,
+            "checkpoint_dtype": w.ckpt_dtype,
+            "fragments": w.n_frags,
+            "algorithmic_bytes_per_param": ab["per_param"],
+            "algorithmic_bytes_per_round": ab["per_round"],
+        },
+        "merged_params_per_s": round(w.n_params / (ms / 1e3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_time_ms_per_step": round(total_kernel_ms / args.steps, 4),
+        "kernels": kern,
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dd["bytes"] // dd["launches"],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del gw
+        torch.cuda.empty_cache()
+        log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(w, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,319 @@
+// C ABI of the merge (declared in include/dlmerge.h): the round state machine
+// and argument validation on the host, then one kernel launch per call.
+//
+// Round rules follow the pages: checkpoints must carry the current round's
+// tag (DiffuRefill-1B technical report, "Training system", failure rule iii),
+// a round closes once its quorum of checkpoints is in (Table 2, row "Merger";
+// GradientMail post, "Getting updates through the bucket": quorum 3 per
+// fragment, four fragments), quorum 1 drains the leftovers of dead workers
+// (Table 2, row "Recovery"), arrivals are folded in the order they come (model
+// card, "How it is trained", Merging bullet), and two rounds may be open at
+// once (GradientMail post, same section).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "dlmerge.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxFrags = 4096;
+constexpr int kMaxWorkers = 65536;
+
+struct Fragment {
+    bool closed = false;
+    std::vector<int> arrivals;       // worker ids in arrival order
+    int64_t tokens = 0;              // exact sum (DL_DELTA_NESTEROV)
+    const float* global = nullptr;   // global the deltas were taken against
+};
+
+struct Span {
+    uintptr_t lo, hi;                // [lo, hi)
+    bool overlaps(const Span& o) const { return lo < o.hi && o.lo < hi; }
+    bool same(const Span& o) const { return lo == o.lo && hi == o.hi; }
+};
+
+Span span_of(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Span{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+// The span must lie inside one device allocation known to the HIP runtime.
+// A host pointer or a span running past its allocation is rejected here
+// instead of faulting the GPU.
+int check_device_span(const void* p, int64_t bytes) {
+    if (p == nullptr) return DL_E_INVAL;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();     // do not leave the failure as a sticky error
+        return DL_E_INVAL;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (a < b || bytes < 0 || static_cast<uint64_t>(bytes) > size - (a - b)) return DL_E_INVAL;
+    return DL_OK;
+}
+
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// 1 - beta, one binary32 subtraction (exact for beta in [0.5, 1]).
+float one_minus(float beta) { return 1.0f - beta; }
+
+}  // namespace
+
+struct dl_round {
+    uint64_t tag = 0;
+    int mode = DL_MEAN;
+    int64_t n_params = 0;
+    std::vector<int64_t> offsets;
+    int quorum = 1;
+    int max_workers = 1;
+    float* acc = nullptr;
+    hipStream_t stream = nullptr;
+    bool failed = false;
+    std::vector<Fragment> frags;
+
+    int64_t off(int f) const { return offsets[f]; }
+    int64_t len(int f) const { return offsets[f + 1] - offsets[f]; }
+    int n_frags() const { return static_cast<int>(frags.size()); }
+};
+
+extern "C" {
+
+int dl_round_begin(dl_round** out, uint64_t round_tag, int mode, int64_t n_params, int n_frags,
+                   const int64_t* frag_offsets, int quorum, int max_workers, float* acc,
+                   void* stream) {
+    if (out == nullptr) return DL_E_INVAL;
+    *out = nullptr;
+    if (mode != DL_MEAN && mode != DL_DELTA_NESTEROV) return DL_E_INVAL;
+    if (n_params < 1 || n_frags < 1 || n_frags > kMaxFrags || frag_offsets == nullptr)
+        return DL_E_INVAL;
+    if (max_workers < 1 || max_workers > kMaxWorkers || quorum < 1 || quorum > max_workers)
+        return DL_E_INVAL;
+    if (acc == nullptr) return DL_E_INVAL;
+    if (!aligned_to(acc, alignof(float))) return DL_E_ALIGN;
+    if (frag_offsets[0] != 0 || frag_offsets[n_frags] != n_params) return DL_E_INVAL;
+    for (int f = 0; f < n_frags; ++f)
+        if (frag_offsets[f + 1] <= frag_offsets[f]) return DL_E_INVAL;
+    if (n_params > INT64_MAX / static_cast<int64_t>(sizeof(float))) return DL_E_INVAL;
+
+    dl_round* r = new (std::nothrow) dl_round;
+    if (r == nullptr) return DL_E_INVAL;
+    r->tag = round_tag;
+    r->mode = mode;
+    r->n_params = n_params;
+    r->offsets.assign(frag_offsets, frag_offsets + n_frags + 1);
+    r->quorum = quorum;
+    r->max_workers = max_workers;
+    r->acc = acc;
+    r->stream = static_cast<hipStream_t>(stream);
+    r->frags.resize(static_cast<size_t>(n_frags));
+    *out = r;
+    return DL_OK;
+}
+
+int dl_fold_checkpoint(dl_round* r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                       const void* ckpt, int dtype, const float* global, int64_t tokens) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->failed) return DL_E_STATE;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    Fragment& F = r->frags[frag];
+    if (F.closed) return DL_E_STATE;
+    if (worker_id < 0 || worker_id >= r->max_workers) return DL_E_INVAL;
+    if (dtype != DL_F32 && dtype != DL_BF16) return DL_E_INVAL;
+    if (ckpt_round_tag != r->tag) return DL_E_STALE;
+    if (std::find(F.arrivals.begin(), F.arrivals.end(), worker_id) != F.arrivals.end())
+        return DL_E_DUP;
+    if (r->mode == DL_MEAN) {
+        if (global != nullptr) return DL_E_INVAL;
+    } else {
+        if (global == nullptr || tokens <= 0) return DL_E_INVAL;
+        if (F.tokens > INT64_MAX - tokens) return DL_E_INVAL;
+        if (F.global != nullptr && F.global != global) return DL_E_INVAL;
+    }
+    if (ckpt == nullptr) return DL_E_INVAL;
+    const int64_t esize = dtype == DL_BF16 ? 2 : 4;
+    if (!aligned_to(ckpt, static_cast<uintptr_t>(esize))) return DL_E_ALIGN;
+    if (global != nullptr && !aligned_to(global, alignof(float))) return DL_E_ALIGN;
+
+    const int64_t off = r->off(frag), n = r->len(frag);
+    float* acc = r->acc + off;
+    const Span acc_s = span_of(acc, n * 4), ck_s = span_of(ckpt, n * esize);
+    if (acc_s.overlaps(ck_s)) return DL_E_INVAL;
+    const float* theta = nullptr;
+    if (global != nullptr) {
+        theta = global + off;
+        const Span th_s = span_of(theta, n * 4);
+        if (th_s.overlaps(acc_s) || th_s.overlaps(ck_s)) return DL_E_INVAL;
+        if (int e = check_device_span(theta, n * 4)) return e;
+    }
+    if (int e = check_device_span(acc, n * 4)) return e;
+    if (int e = check_device_span(ckpt, n * esize)) return e;
+
+    const bool first = F.arrivals.empty();
+    (void)hipGetLastError();          // launch status below is this call's own
+    hipError_t err;
+    if (r->mode == DL_MEAN) {
+        err = dlk::launch_fold_sum(acc, ckpt, dtype == DL_BF16, n, first, r->stream);
+    } else {
+        const float w = static_cast<float>(tokens);   // nearest-even
+        err = dlk::launch_fold_delta(acc, theta, ckpt, dtype == DL_BF16, w, n, first, r->stream);
+    }
+    if (err != hipSuccess) {
+        r->failed = true;
+        return DL_E_HIP;
+    }
+    F.arrivals.push_back(worker_id);
+    if (r->mode == DL_DELTA_NESTEROV) {
+        F.tokens += tokens;
+        F.global = global;
+    }
+    return DL_OK;
+}
+
+int dl_finalize_mean(dl_round* r, int frag, float* out_global, float* ema, float beta) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->failed || r->mode != DL_MEAN) return DL_E_STATE;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    Fragment& F = r->frags[frag];
+    if (F.closed) return DL_E_STATE;
+    if (static_cast<int>(F.arrivals.size()) < r->quorum) return DL_E_QUORUM;
+    if (out_global == nullptr) return DL_E_INVAL;
+    if (!aligned_to(out_global, alignof(float)) || (ema && !aligned_to(ema, alignof(float))))
+        return DL_E_ALIGN;
+
+    const int64_t off = r->off(frag), n = r->len(frag);
+    float* acc = r->acc + off;
+    float* out = out_global + off;
+    const Span acc_s = span_of(acc, n * 4), out_s = span_of(out, n * 4);
+    if (!out_s.same(acc_s) && out_s.overlaps(acc_s)) return DL_E_INVAL;
+    float* e = nullptr;
+    if (ema != nullptr) {
+        e = ema + off;
+        const Span e_s = span_of(e, n * 4);
+        if (e_s.overlaps(acc_s) || e_s.overlaps(out_s)) return DL_E_INVAL;
+        if (int st = check_device_span(e, n * 4)) return st;
+    }
+    if (int st = check_device_span(acc, n * 4)) return st;
+    if (int st = check_device_span(out, n * 4)) return st;
+
+    const float count = static_cast<float>(F.arrivals.size());
+    (void)hipGetLastError();
+    const hipError_t err =
+        dlk::launch_finalize_mean(out, acc, count, e, beta, one_minus(beta), n, r->stream);
+    if (err != hipSuccess) {
+        r->failed = true;
+        return DL_E_HIP;
+    }
+    F.closed = true;
+    return DL_OK;
+}
+
+int dl_outer_nesterov(dl_round* r, int frag, float* global, float* momentum, float lr, float mu,
+                      float* ema, float beta) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->failed || r->mode != DL_DELTA_NESTEROV) return DL_E_STATE;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    Fragment& F = r->frags[frag];
+    if (F.closed) return DL_E_STATE;
+    if (static_cast<int>(F.arrivals.size()) < r->quorum) return DL_E_QUORUM;
+    if (global == nullptr || momentum == nullptr || global != F.global) return DL_E_INVAL;
+    if (!aligned_to(momentum, alignof(float)) || (ema && !aligned_to(ema, alignof(float))))
+        return DL_E_ALIGN;
+
+    const int64_t off = r->off(frag), n = r->len(frag);
+    float* acc = r->acc + off;
+    float* theta = global + off;
+    float* m = momentum + off;
+    const Span acc_s = span_of(acc, n * 4), th_s = span_of(theta, n * 4), m_s = span_of(m, n * 4);
+    if (m_s.overlaps(acc_s) || m_s.overlaps(th_s)) return DL_E_INVAL;
+    float* e = nullptr;
+    if (ema != nullptr) {
+        e = ema + off;
+        const Span e_s = span_of(e, n * 4);
+        if (e_s.overlaps(acc_s) || e_s.overlaps(th_s) || e_s.overlaps(m_s)) return DL_E_INVAL;
+        if (int st = check_device_span(e, n * 4)) return st;
+    }
+    if (int st = check_device_span(acc, n * 4)) return st;
+    if (int st = check_device_span(theta, n * 4)) return st;
+    if (int st = check_device_span(m, n * 4)) return st;
+
+    const float total = static_cast<float>(F.tokens);    // exact int64 sum, rounded once
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_nesterov(theta, m, acc, total, lr, mu, e, beta,
+                                                one_minus(beta), n, r->stream);
+    if (err != hipSuccess) {
+        r->failed = true;
+        return DL_E_HIP;
+    }
+    F.closed = true;
+    return DL_OK;
+}
+
+int dl_ema_update(float* ema, const float* global, int64_t n, float beta, void* stream) {
+    if (n < 0) return DL_E_INVAL;
+    if (n == 0) return DL_OK;
+    if (ema == nullptr || global == nullptr) return DL_E_INVAL;
+    if (n > INT64_MAX / 4) return DL_E_INVAL;
+    if (!aligned_to(ema, alignof(float)) || !aligned_to(global, alignof(float))) return DL_E_ALIGN;
+    if (span_of(ema, n * 4).overlaps(span_of(global, n * 4))) return DL_E_INVAL;
+    if (int st = check_device_span(ema, n * 4)) return st;
+    if (int st = check_device_span(global, n * 4)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_ema(ema, global, beta, one_minus(beta), n,
+                                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_frag_range(const dl_round* r, int frag, int64_t* offset, int64_t* length) {
+    if (r == nullptr || offset == nullptr || length == nullptr) return DL_E_INVAL;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    *offset = r->off(frag);
+    *length = r->len(frag);
+    return DL_OK;
+}
+
+int dl_round_participants(const dl_round* r, int frag, int* count, int* workers, int capacity) {
+    if (r == nullptr || count == nullptr) return DL_E_INVAL;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    const std::vector<int>& a = r->frags[frag].arrivals;
+    *count = static_cast<int>(a.size());
+    if (workers == nullptr) return DL_OK;
+    if (capacity < *count) return DL_E_CAPACITY;
+    std::copy(a.begin(), a.end(), workers);
+    return DL_OK;
+}
+
+int dl_round_tokens(const dl_round* r, int frag, int64_t* total_tokens) {
+    if (r == nullptr || total_tokens == nullptr) return DL_E_INVAL;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    *total_tokens = r->frags[frag].tokens;
+    return DL_OK;
+}
+
+int dl_round_end(dl_round* r) {
+    delete r;
+    return DL_OK;
+}
+
+const char* dl_strerror(int status) {
+    switch (status) {
+        case DL_OK: return "ok";
+        case DL_E_INVAL: return "invalid argument";
+        case DL_E_STALE: return "checkpoint carries another round's tag";
+        case DL_E_DUP: return "worker already folded into this fragment";
+        case DL_E_QUORUM: return "fewer arrivals than the quorum";
+        case DL_E_STATE: return "call not allowed in this state";
+        case DL_E_ALIGN: return "pointer not aligned to its element type";
+        case DL_E_HIP: return "HIP launch failed; the round is failed";
+        case DL_E_CAPACITY: return "output array too small";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

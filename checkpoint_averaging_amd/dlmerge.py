@@ -1,0 +1,218 @@
+"""ctypes binding of libdlmerge.so (C ABI in include/dlmerge.h).
+
+Argument marshalling only: torch tensors become (device pointer, dtype), the
+stream defaults to torch's current stream, and a negative status becomes a
+DLError.  Every step of the merge runs in the library's HIP kernels; there is
+no fallback, and importing this module raises if the library is not built.
+
+Function names and arguments mirror the C functions.  An array argument is a
+torch tensor on the GPU or, for tests that need exact pointers, a plain
+integer device address (then ``dtype`` must be given where it matters).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple, Union
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdlmerge.so")
+
+DL_MEAN = 0
+DL_DELTA_NESTEROV = 1
+DL_F32 = 0
+DL_BF16 = 1
+
+DL_OK = 0
+DL_E_INVAL = -1
+DL_E_STALE = -2
+DL_E_DUP = -3
+DL_E_QUORUM = -4
+DL_E_STATE = -5
+DL_E_ALIGN = -6
+DL_E_HIP = -7
+DL_E_CAPACITY = -8
+
+SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
+           "dl_ema_update", "dl_frag_range", "dl_round_participants", "dl_round_tokens",
+           "dl_round_end", "dl_strerror")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m checkpoint_averaging_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i32, _i64, _u64, _f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
+                              ctypes.c_float)
+_lib.dl_round_begin.argtypes = [ctypes.POINTER(_p), _u64, _i32, _i64, _i32,
+                                ctypes.POINTER(_i64), _i32, _i32, _p, _p]
+_lib.dl_fold_checkpoint.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _p, _i64]
+_lib.dl_finalize_mean.argtypes = [_p, _i32, _p, _p, _f32]
+_lib.dl_outer_nesterov.argtypes = [_p, _i32, _p, _p, _f32, _f32, _p, _f32]
+_lib.dl_ema_update.argtypes = [_p, _p, _i64, _f32, _p]
+_lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+_lib.dl_round_participants.argtypes = [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32]
+_lib.dl_round_tokens.argtypes = [_p, _i32, ctypes.POINTER(_i64)]
+_lib.dl_round_end.argtypes = [_p]
+_lib.dl_strerror.argtypes = [_i32]
+_lib.dl_strerror.restype = ctypes.c_char_p
+for _name in SYMBOLS[:-1]:
+    getattr(_lib, _name).restype = _i32
+
+
+class DLError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {dl_strerror(status)} ({status})")
+
+
+def _check(status: int, call: str) -> None:
+    if status != DL_OK:
+        raise DLError(status, call)
+
+
+Array = Union[torch.Tensor, int, None]
+
+
+def _addr(a: Array) -> Optional[int]:
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        if not a.is_cuda:
+            raise TypeError("device tensor required")
+        if not a.is_contiguous():
+            raise TypeError("contiguous tensor required")
+        return a.data_ptr()
+    return int(a)
+
+
+def _f32_addr(a: Array, name: str) -> Optional[int]:
+    if isinstance(a, torch.Tensor) and a.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _addr(a)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def dl_strerror(status: int) -> str:
+    return _lib.dl_strerror(int(status)).decode()
+
+
+class Round:
+    """Handle of an open round (wraps the C dl_round pointer)."""
+
+    def __init__(self, handle: ctypes.c_void_p, n_frags: int):
+        self._h = handle
+        self.n_frags = n_frags
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("round already ended")
+        return self._h
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        dl_round_end(self)
+
+
+def dl_round_begin(round_tag: int, mode: int, n_params: int, frag_offsets: Sequence[int],
+                   quorum: int, max_workers: int, acc: Array, stream=None) -> Round:
+    offs = (_i64 * len(frag_offsets))(*[int(o) for o in frag_offsets])
+    h = _p()
+    _check(_lib.dl_round_begin(ctypes.byref(h), int(round_tag), int(mode), int(n_params),
+                               len(frag_offsets) - 1, offs, int(quorum), int(max_workers),
+                               _f32_addr(acc, "acc"), _stream(stream)),
+           "dl_round_begin")
+    return Round(h, len(frag_offsets) - 1)
+
+
+def dl_fold_checkpoint(r: Round, frag: int, worker_id: int, ckpt_round_tag: int, ckpt: Array,
+                       global_: Array = None, tokens: int = 0,
+                       dtype: Optional[int] = None) -> None:
+    if dtype is None:
+        if not isinstance(ckpt, torch.Tensor):
+            raise TypeError("dtype is required for a raw checkpoint address")
+        if ckpt.dtype == torch.float32:
+            dtype = DL_F32
+        elif ckpt.dtype == torch.bfloat16:
+            dtype = DL_BF16
+        else:
+            raise TypeError("checkpoint must be float32 or bfloat16")
+    _check(_lib.dl_fold_checkpoint(r.handle, int(frag), int(worker_id), int(ckpt_round_tag),
+                                   _addr(ckpt), int(dtype), _f32_addr(global_, "global"),
+                                   int(tokens)),
+           "dl_fold_checkpoint")
+
+
+def dl_finalize_mean(r: Round, frag: int, out_global: Array, ema: Array = None,
+                     beta: float = 0.9) -> None:
+    _check(_lib.dl_finalize_mean(r.handle, int(frag), _f32_addr(out_global, "out_global"),
+                                 _f32_addr(ema, "ema"), float(beta)),
+           "dl_finalize_mean")
+
+
+def dl_outer_nesterov(r: Round, frag: int, global_: Array, momentum: Array, lr: float = 0.7,
+                      mu: float = 0.9, ema: Array = None, beta: float = 0.9) -> None:
+    _check(_lib.dl_outer_nesterov(r.handle, int(frag), _f32_addr(global_, "global"),
+                                  _f32_addr(momentum, "momentum"), float(lr), float(mu),
+                                  _f32_addr(ema, "ema"), float(beta)),
+           "dl_outer_nesterov")
+
+
+def dl_ema_update(ema: Array, global_: Array, beta: float = 0.9, n: Optional[int] = None,
+                  stream=None) -> None:
+    if n is None:
+        if not isinstance(ema, torch.Tensor):
+            raise TypeError("n is required for raw addresses")
+        n = ema.numel()
+        if isinstance(global_, torch.Tensor) and global_.numel() != n:
+            raise ValueError("ema and global differ in size")
+    _check(_lib.dl_ema_update(_f32_addr(ema, "ema"), _f32_addr(global_, "global"), int(n),
+                              float(beta), _stream(stream)),
+           "dl_ema_update")
+
+
+def dl_frag_range(r: Round, frag: int) -> Tuple[int, int]:
+    off, length = _i64(), _i64()
+    _check(_lib.dl_frag_range(r.handle, int(frag), ctypes.byref(off), ctypes.byref(length)),
+           "dl_frag_range")
+    return off.value, length.value
+
+
+def dl_round_participants(r: Round, frag: int) -> List[int]:
+    count = _i32()
+    _check(_lib.dl_round_participants(r.handle, int(frag), ctypes.byref(count), None, 0),
+           "dl_round_participants")
+    buf = (_i32 * max(1, count.value))()
+    _check(_lib.dl_round_participants(r.handle, int(frag), ctypes.byref(count), buf,
+                                      count.value),
+           "dl_round_participants")
+    return list(buf[:count.value])
+
+
+def dl_round_tokens(r: Round, frag: int) -> int:
+    t = _i64()
+    _check(_lib.dl_round_tokens(r.handle, int(frag), ctypes.byref(t)), "dl_round_tokens")
+    return t.value
+
+
+def dl_round_end(r: Round) -> None:
+    if r._h is not None:
+        _check(_lib.dl_round_end(r._h), "dl_round_end")
+        r._h = None
+
+
+def raw_lib() -> ctypes.CDLL:
+    """The loaded library (status-code level access for tests)."""
+    return _lib

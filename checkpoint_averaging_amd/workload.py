@@ -1,0 +1,127 @@
+"""A merge workload resident on the GPU, and one merge round of it issued
+through the C ABI.
+
+The benchmark times `GpuWorkload.run_round`; the full-size parity tests run
+the very same calls.  Inputs come from the seeded generator
+(checkpoint_averaging_amd.synth): the initial global, and for round r the
+worker checkpoints c_i = global0 + drift(r, i), generated on the GPU before the
+round starts (never inside a timed region).
+
+Round structure (all on torch's current stream):
+* plain mean:      for each fragment, fold every worker in its seeded arrival
+                   order, then close the fragment with the mean (+ EMA)
+* delta Nesterov:  for each fragment, fold every worker's token-weighted delta
+                   in arrival order, then close with the outer Nesterov step
+                   (+ EMA)
+"""
+from __future__ import annotations
+
+from typing import Callable, Dict, List, Optional
+
+import torch
+
+from . import dlmerge as dl
+from . import synth
+
+_GEN_CHUNK = 1 << 25
+
+
+class GpuWorkload:
+    def __init__(self, w: synth.Workload, device="cuda"):
+        self.w = w
+        self.dev = torch.device(device)
+        n = w.n_params
+        self.delta = w.mode == "delta_nesterov"
+        self.theta = synth.global0(w.seed, n, device=self.dev)
+        self.m = torch.zeros(n, dtype=torch.float32, device=self.dev) if self.delta else None
+        self.e = self.theta.clone() if w.ema else None
+        self.acc = torch.empty(n, dtype=torch.float32, device=self.dev)
+        cdt = torch.bfloat16 if w.ckpt_dtype == "bf16" else torch.float32
+        self.ckpts: List[torch.Tensor] = [torch.empty(n, dtype=cdt, device=self.dev)
+                                          for _ in range(w.workers)]
+        self.ckpt_round = None
+
+    def generate_checkpoints(self, rnd: int) -> None:
+        """Worker checkpoints of round rnd: global0 + seeded drift (chunked so
+        the generator's temporaries stay small)."""
+        w, n = self.w, self.w.n_params
+        for s in range(0, n, _GEN_CHUNK):
+            c = min(_GEN_CHUNK, n - s)
+            th0 = synth.global0(w.seed, c, device=self.dev, start=s)
+            for i in range(w.workers):
+                synth.worker_checkpoint(w.seed, rnd, i, th0, start=s, dtype=w.ckpt_dtype,
+                                        out=self.ckpts[i][s:s + c])
+            del th0
+        self.ckpt_round = rnd
+
+    def orders(self, rnd: int) -> List[List[int]]:
+        return [synth.arrival_order(self.w, rnd, f) for f in range(self.w.n_frags)]
+
+    def tokens(self, rnd: int) -> List[int]:
+        return synth.token_counts(self.w, rnd)
+
+    def run_round(self, rnd: int, tag: int,
+                  timer: Optional[Callable[[str, int, Callable[[], None]], None]] = None) -> None:
+        """Issue one merge round.  `timer(kind, elements, call)` (if given)
+        wraps every kernel-launching call, e.g. to record events around it."""
+        w = self.w
+        offs = list(w.frag_offsets)
+        orders = self.orders(rnd)
+        run = timer if timer is not None else (lambda kind, n, call: call())
+        if not self.delta:
+            r = dl.dl_round_begin(tag, dl.DL_MEAN, w.n_params, offs, w.quorum, w.workers,
+                                  self.acc)
+            try:
+                for f in range(w.n_frags):
+                    o0, o1 = offs[f], offs[f + 1]
+                    for k, i in enumerate(orders[f]):
+                        kind = "fold_first" if k == 0 else "fold"
+                        ck = self.ckpts[i][o0:o1]
+                        run(kind, o1 - o0, lambda f=f, i=i, ck=ck:
+                            dl.dl_fold_checkpoint(r, f, i, tag, ck))
+                    run("finalize_mean_ema" if self.e is not None else "finalize_mean", o1 - o0,
+                        lambda f=f: dl.dl_finalize_mean(r, f, self.theta, self.e, w.beta))
+            finally:
+                dl.dl_round_end(r)
+        else:
+            tok = self.tokens(rnd)
+            r = dl.dl_round_begin(tag, dl.DL_DELTA_NESTEROV, w.n_params, offs, w.quorum,
+                                  w.workers, self.acc)
+            try:
+                for f in range(w.n_frags):
+                    o0, o1 = offs[f], offs[f + 1]
+                    for k, i in enumerate(orders[f]):
+                        kind = "fold_delta_first" if k == 0 else "fold_delta"
+                        ck = self.ckpts[i][o0:o1]
+                        run(kind, o1 - o0, lambda f=f, i=i, ck=ck:
+                            dl.dl_fold_checkpoint(r, f, i, tag, ck, self.theta, tok[i]))
+                    run("nesterov_ema" if self.e is not None else "nesterov", o1 - o0,
+                        lambda f=f: dl.dl_outer_nesterov(r, f, self.theta, self.m, w.lr, w.mu,
+                                                         self.e, w.beta))
+            finally:
+                dl.dl_round_end(r)
+
+
+def algorithmic_bytes(w: synth.Workload) -> Dict[str, int]:
+    """Bytes each kernel kind must move per element, and per round in total.
+
+    Each arriving checkpoint is read once; the accumulator is read and written
+    per arrival except the first, which only writes it; the delta fold also
+    reads the global; the close reads and writes each state buffer once, with
+    the EMA fused in."""
+    cb = 2 if w.ckpt_dtype == "bf16" else 4
+    per_elem = {
+        "fold_first": cb + 4, "fold": cb + 8,
+        "fold_delta_first": cb + 8, "fold_delta": cb + 12,
+        "finalize_mean": 8, "finalize_mean_ema": 16,
+        "nesterov": 20, "nesterov_ema": 28,
+    }
+    if w.mode == "mean":
+        close = "finalize_mean_ema" if w.ema else "finalize_mean"
+        per_param = per_elem["fold_first"] + (w.workers - 1) * per_elem["fold"] + per_elem[close]
+    else:
+        close = "nesterov_ema" if w.ema else "nesterov"
+        per_param = (per_elem["fold_delta_first"] + (w.workers - 1) * per_elem["fold_delta"]
+                     + per_elem[close])
+    return {"per_elem": per_elem, "per_param": per_param,
+            "per_round": per_param * w.n_params}

@@ -1,0 +1,237 @@
+/*
+ * dlmerge.h -- C ABI of the MI355X (gfx950) DiLoCo outer-step merge.
+ *
+ * A merge round turns the worker checkpoints pushed after H local steps into
+ * the next global model and its EMA.  Two variants are provided:
+ *
+ *  DL_MEAN            plain replacement averaging: every arriving checkpoint
+ *                     is folded into a running fp32 sum in arrival order; the
+ *                     new global is that sum divided by the number of
+ *                     checkpoints (DiffuRefill-1B technical report, section
+ *                     "Training system", Table 2, rows "Merger" and "Outer
+ *                     step"; DiffuRefill-1B model card, "How it is trained",
+ *                     Merging bullet).
+ *  DL_DELTA_NESTEROV  fragment merge: per parameter fragment, a token-weighted
+ *                     mean of the participants' deltas feeds an outer
+ *                     Nesterov optimizer (GradientMail post "Pythia-14M on
+ *                     four rented GPUs and a bucket", section "Getting
+ *                     updates through the bucket").
+ *
+ * Both can advance an EMA of globals in the same pass (technical report,
+ * Table 2, row "Side averages"; model card, EMA bullet).
+ *
+ * Arithmetic.  Every step is IEEE-754 binary32, one rounding per operation,
+ * round-to-nearest-even, no fused multiply-add, IEEE division, subnormals
+ * kept, NaN and infinity propagated (no value is rejected).  For element j of
+ * a fragment, with arrivals k = 1..N in arrival order:
+ *
+ *   DL_MEAN:   S = c_1 ;  S = S + c_k (k > 1) ;  g = S / N
+ *   DELTA:     d = theta - c_k ; p = w_k * d ; A = p (k = 1) or A + p
+ *              dbar = A / W ; m' = mu*m + dbar ; u = dbar + mu*m' ;
+ *              theta' = theta - lr*u
+ *   EMA:       e' = beta*e + (1 - beta)*x, x the new global (g or theta'),
+ *              with (1 - beta) formed once in binary32
+ *
+ * where bf16 checkpoints are widened exactly to fp32, w_k is the worker's
+ * int64 token count rounded once to binary32, and W is the exact int64 sum of
+ * the fragment's token counts rounded once to binary32.
+ *
+ * Memory.  Every array argument is a DEVICE pointer to memory the caller owns
+ * (e.g. a torch tensor's data_ptr()).  The library never allocates, frees or
+ * copies device memory, never synchronises, and launches every kernel of a
+ * round on the round's stream; the caller keeps buffers alive until that
+ * stream's work is done and synchronises through the stream.  Parameters are
+ * flat, contiguous vectors of n_params elements; fragment f covers elements
+ * [frag_offsets[f], frag_offsets[f+1]).  Full-length buffers (acc, global,
+ * momentum, ema) are indexed by those offsets; a checkpoint buffer holds only
+ * its fragment's elements.  Pointers must be aligned to their element type;
+ * when every pointer a kernel touches is 16-byte aligned the 128-bit path
+ * runs, otherwise a scalar path gives the same bits.  Each span
+ * [ptr, ptr + bytes) must lie inside one device allocation, which the library
+ * checks with the HIP runtime before launching.
+ *
+ * Errors.  Every call returns DL_OK (0) or a negative status.  All checks
+ * except DL_E_HIP happen on the host before any launch; a call that fails
+ * them launches nothing and leaves the handle unchanged.  Device buffers
+ * holding the global, momentum and EMA are written only by the closing calls
+ * (dl_finalize_mean, dl_outer_nesterov, dl_ema_update), so an abandoned round
+ * changes none of them.
+ *
+ * Threads.  A handle is used by one host thread at a time.  Several handles
+ * may be open at once (two rounds in flight, GradientMail post, "Getting
+ * updates through the bucket") if their accumulator ranges do not overlap and
+ * the caller orders rounds that write the same global, momentum or EMA range.
+ */
+#ifndef DLMERGE_H
+#define DLMERGE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dl_round dl_round;   /* opaque; host memory owned by the library */
+
+enum dl_mode {
+    DL_MEAN = 0,             /* plain replacement averaging                    */
+    DL_DELTA_NESTEROV = 1    /* token-weighted delta mean + outer Nesterov     */
+};
+
+enum dl_dtype {
+    DL_F32 = 0,              /* IEEE binary32                                  */
+    DL_BF16 = 1              /* bfloat16, widened exactly to binary32          */
+};
+
+enum dl_status {
+    DL_OK = 0,
+    DL_E_INVAL = -1,     /* bad argument: NULL/unknown value, range, overlap,
+                            pointer outside its allocation, token overflow    */
+    DL_E_STALE = -2,     /* checkpoint carries another round's tag             */
+    DL_E_DUP = -3,       /* worker already folded into this fragment           */
+    DL_E_QUORUM = -4,    /* closing a fragment with fewer arrivals than quorum */
+    DL_E_STATE = -5,     /* call not allowed in the fragment's/round's state   */
+    DL_E_ALIGN = -6,     /* pointer not aligned to its element type            */
+    DL_E_HIP = -7,       /* HIP runtime error at launch; round is now failed   */
+    DL_E_CAPACITY = -8   /* output array too small                             */
+};
+
+/*
+ * Open a merge round.  No device work.
+ *
+ * The merger closes a round once N or more checkpoints tagged with the
+ * current round are in (technical report, Table 2, row "Merger": N is 2, or 1
+ * with a single worker left or when a restarted merger first merges the
+ * leftovers of dead workers, row "Recovery"); in the GradientMail run three
+ * participants close a fragment's round ("Getting updates through the
+ * bucket").  Quorum is a minimum: every arrival folded before the close
+ * counts.
+ *
+ *   out           receives the handle (set to NULL on error).
+ *   round_tag     the round's tag; checkpoints carrying another tag are
+ *                 rejected (a rollback is published under a new round number,
+ *                 technical report, "Training system", failure rule iii).
+ *   mode          DL_MEAN or DL_DELTA_NESTEROV.
+ *   n_params      flat parameter count, >= 1.
+ *   n_frags       number of fragments, 1 <= n_frags <= 4096.
+ *   frag_offsets  host array of n_frags + 1 int64: 0 = o_0 < o_1 < ... <
+ *                 o_n = n_params.  Copied; the caller keeps ownership.
+ *   quorum        minimum arrivals per fragment, 1 <= quorum <= max_workers.
+ *   max_workers   worker ids are 0 .. max_workers-1, 1 <= max_workers <= 65536.
+ *   acc           device, n_params fp32: the running sum / weighted-delta
+ *                 accumulator.  Scratch owned by the caller; its contents on
+ *                 entry do not matter (the first fold of a fragment
+ *                 overwrites it).  Must not overlap the acc of another open
+ *                 round over the same fragments.
+ *   stream        hipStream_t on which every kernel of the round is launched
+ *                 (NULL: the null stream).
+ *
+ * Errors: DL_E_INVAL (bad value or offsets), DL_E_ALIGN (acc not 4-byte
+ * aligned).
+ */
+int dl_round_begin(dl_round **out, uint64_t round_tag, int mode, int64_t n_params,
+                   int n_frags, const int64_t *frag_offsets, int quorum, int max_workers,
+                   float *acc, void *stream);
+
+/*
+ * Fold one arriving checkpoint (or fragment snapshot) into the round's
+ * accumulator for fragment frag.  One kernel launch on the round's stream;
+ * arrivals are folded in call order, which is the arrival order.
+ *
+ *   frag            fragment index, 0 <= frag < n_frags.
+ *   worker_id       0 <= worker_id < max_workers; a worker is folded at
+ *                   most once per fragment per round.
+ *   ckpt_round_tag  must equal the round's tag.
+ *   ckpt            device, fragment-length array of dtype.
+ *   dtype           DL_F32 or DL_BF16.
+ *   global          DL_DELTA_NESTEROV: device, full-length fp32 global the
+ *                   participant trained from (deltas are theta - c); every
+ *                   fold of a fragment and its close must pass the same
+ *                   pointer.  DL_MEAN: must be NULL.
+ *   tokens          DL_DELTA_NESTEROV: the participant's token count, > 0;
+ *                   the fragment's total must stay below 2^63.  DL_MEAN:
+ *                   ignored.
+ *
+ * Errors (all before launch): DL_E_STATE (round failed, or fragment already
+ * closed), DL_E_INVAL, DL_E_STALE, DL_E_DUP, DL_E_ALIGN; DL_E_HIP after a
+ * launch failure (the round is then failed: only dl_round_end is allowed).
+ */
+int dl_fold_checkpoint(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                       const void *ckpt, int dtype, const float *global, int64_t tokens);
+
+/*
+ * Close fragment frag of a DL_MEAN round: write the mean of its arrivals
+ * into out_global[frag range] and, if ema is not NULL, advance the EMA of
+ * globals in the same pass.  One kernel launch.
+ *
+ *   out_global  device, full-length fp32; may be the round's acc (in place),
+ *               otherwise must not overlap it.
+ *   ema         device, full-length fp32 in/out, or NULL; must not overlap
+ *               acc or out_global.
+ *   beta        EMA weight of the old EMA (0.9 on the pages).
+ *
+ * Errors: DL_E_STATE (wrong mode, already closed, round failed),
+ * DL_E_QUORUM (fewer arrivals than quorum), DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_finalize_mean(dl_round *r, int frag, float *out_global, float *ema, float beta);
+
+/*
+ * Close fragment frag of a DL_DELTA_NESTEROV round: token-weighted mean delta
+ * from the accumulator, outer Nesterov step on global and momentum, and, if
+ * ema is not NULL, the EMA of the new global, all in one pass.  Momentum 0
+ * and learning rate 1 give plain parameter averaging (GradientMail post,
+ * "What might explain the loss difference", second follow-up run).
+ *
+ *   global    device, full-length fp32 in/out; the pointer the folds used.
+ *   momentum  device, full-length fp32 in/out (zero before the first round);
+ *             must not overlap acc, global or ema.
+ *   lr, mu    outer learning rate and momentum (0.7 and 0.9 on the pages).
+ *   ema, beta as in dl_finalize_mean.
+ *
+ * Errors: DL_E_STATE, DL_E_QUORUM, DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_outer_nesterov(dl_round *r, int frag, float *global, float *momentum, float lr,
+                      float mu, float *ema, float beta);
+
+/*
+ * Stand-alone EMA of globals: ema[j] = beta*ema[j] + (1-beta)*global[j] for
+ * j < n, on stream (technical report, Table 2, row "Side averages").
+ * n = 0 is a no-op.  ema and global must not overlap.
+ *
+ * Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_ema_update(float *ema, const float *global, int64_t n, float beta, void *stream);
+
+/* Element range [offset, offset + length) of fragment frag.  DL_E_INVAL. */
+int dl_frag_range(const dl_round *r, int frag, int64_t *offset, int64_t *length);
+
+/*
+ * Workers folded into fragment frag so far, in arrival order (round logs
+ * identify participants, GradientMail post, "Getting updates through the
+ * bucket").  *count receives the number; if workers is not NULL it receives
+ * the ids and must hold capacity >= *count entries, else DL_E_CAPACITY.
+ */
+int dl_round_participants(const dl_round *r, int frag, int *count, int *workers,
+                          int capacity);
+
+/* Exact int64 sum of the token counts folded into fragment frag. DL_E_INVAL. */
+int dl_round_tokens(const dl_round *r, int frag, int64_t *total_tokens);
+
+/*
+ * Release the handle (NULL is allowed).  Touches no device buffer and does
+ * not wait for the stream: work already launched still completes.  A failed
+ * round is recovered by a new round that re-folds the same arrivals in the
+ * same order, which gives identical bits (the GradientMail post rebuilds a
+ * failed round from its mailbox and then retries it, "Getting updates through
+ * the bucket").
+ */
+int dl_round_end(dl_round *r);
+
+/* Static description of a status code; never NULL. */
+const char *dl_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLMERGE_H */

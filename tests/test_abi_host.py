@@ -1,0 +1,188 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and its host-side round rules reject bad calls before any device
+work (these paths make no HIP call, so they run without a GPU).  Also checks
+the gfx950 assembly of the kernels for the arithmetic the merge requires."""
+import collections
+import os
+import re
+
+import pytest
+
+from checkpoint_averaging_amd import build as cabuild
+from checkpoint_averaging_amd import dlmerge as dl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "dlmerge.h")
+FAKE = 0x7F0000000000        # never dereferenced: every call below fails before use
+OFFS1 = [0, 1000]
+OFFS4 = [0, 96, 200, 208, 1000]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const\s+)?\w+\s*\*?\s*(dl_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert len(declared) == 10
+    assert sorted(dl.SYMBOLS) == declared
+    lib = dl.raw_lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name in ("DL_OK", "DL_E_INVAL", "DL_E_STALE", "DL_E_DUP", "DL_E_QUORUM", "DL_E_STATE",
+                 "DL_E_ALIGN", "DL_E_HIP", "DL_E_CAPACITY", "DL_MEAN", "DL_DELTA_NESTEROV",
+                 "DL_F32", "DL_BF16"):
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+        assert m and int(m.group(1)) == getattr(dl, name), name
+    for s in range(-8, 1):
+        assert dl.dl_strerror(s) != "unknown status"
+    assert dl.dl_strerror(-99) == "unknown status"
+
+
+def _expect(status, fn, *a, **k):
+    with pytest.raises(dl.DLError) as ei:
+        fn(*a, **k)
+    assert ei.value.status == status, (ei.value.status, status)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=2), dl.DL_E_INVAL),
+    (dict(n_params=0, frag_offsets=[0, 0]), dl.DL_E_INVAL),
+    (dict(frag_offsets=[0, 500]), dl.DL_E_INVAL),           # does not end at n_params
+    (dict(frag_offsets=[1, 1000]), dl.DL_E_INVAL),          # does not start at 0
+    (dict(frag_offsets=[0, 500, 500, 1000]), dl.DL_E_INVAL),  # empty fragment
+    (dict(frag_offsets=[0, 600, 400, 1000]), dl.DL_E_INVAL),  # decreasing
+    (dict(quorum=0), dl.DL_E_INVAL),
+    (dict(quorum=9, max_workers=8), dl.DL_E_INVAL),
+    (dict(max_workers=0, quorum=0), dl.DL_E_INVAL),
+    (dict(max_workers=70000), dl.DL_E_INVAL),
+    (dict(acc=0), dl.DL_E_INVAL),
+    (dict(acc=FAKE + 2), dl.DL_E_ALIGN),
+])
+def test_round_begin_rejects(kw, status):
+    args = dict(round_tag=5, mode=dl.DL_MEAN, n_params=1000, frag_offsets=OFFS1, quorum=2,
+                max_workers=8, acc=FAKE, stream=0)
+    args.update(kw)
+    _expect(status, dl.dl_round_begin, **args)
+
+
+def test_host_round_rules_without_device_work():
+    r = dl.dl_round_begin(7, dl.DL_MEAN, 1000, OFFS4, 3, 4, FAKE, stream=0)
+    try:
+        assert dl.dl_frag_range(r, 0) == (0, 96)
+        assert dl.dl_frag_range(r, 3) == (208, 792)
+        _expect(dl.DL_E_INVAL, dl.dl_frag_range, r, 4)
+        assert dl.dl_round_participants(r, 1) == []
+        assert dl.dl_round_tokens(r, 2) == 0
+        # checks that come before any device access
+        _expect(dl.DL_E_STALE, dl.dl_fold_checkpoint, r, 0, 1, 6, FAKE, dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 4, 1, 7, FAKE, dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, -1, 1, 7, FAKE, dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 4, 7, FAKE, dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, -1, 7, FAKE, dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 1, 7, FAKE, dtype=5)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 1, 7, FAKE, global_=FAKE,
+                dtype=dl.DL_F32)                              # global in MEAN mode
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 1, 7, 0, dtype=dl.DL_F32)
+        _expect(dl.DL_E_ALIGN, dl.dl_fold_checkpoint, r, 0, 1, 7, FAKE + 2, dtype=dl.DL_F32)
+        _expect(dl.DL_E_ALIGN, dl.dl_fold_checkpoint, r, 0, 1, 7, FAKE + 1, dtype=dl.DL_BF16)
+        # checkpoint overlapping the accumulator's fragment range
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 1, 1, 7, FAKE + 4 * 100,
+                dtype=dl.DL_F32)
+        # closing
+        _expect(dl.DL_E_QUORUM, dl.dl_finalize_mean, r, 0, FAKE + (1 << 20))
+        _expect(dl.DL_E_STATE, dl.dl_outer_nesterov, r, 0, FAKE, FAKE + 4096)
+        _expect(dl.DL_E_INVAL, dl.dl_finalize_mean, r, 9, FAKE)
+        # nothing was folded
+        assert dl.dl_round_participants(r, 0) == []
+    finally:
+        dl.dl_round_end(r)
+
+
+def test_host_rules_delta_mode():
+    r = dl.dl_round_begin(1, dl.DL_DELTA_NESTEROV, 1000, OFFS4, 1, 4, FAKE, stream=0)
+    try:
+        g = FAKE + (1 << 24)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 0, 1, FAKE + (1 << 22),
+                dtype=dl.DL_F32, global_=None, tokens=5)          # no global
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 0, 1, FAKE + (1 << 22),
+                dtype=dl.DL_F32, global_=g, tokens=0)             # no tokens
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 0, 1, FAKE + (1 << 22),
+                dtype=dl.DL_F32, global_=g, tokens=-3)
+        _expect(dl.DL_E_ALIGN, dl.dl_fold_checkpoint, r, 0, 0, 1, FAKE + (1 << 22),
+                dtype=dl.DL_F32, global_=g + 1, tokens=3)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoint, r, 0, 0, 1, g + 8,
+                dtype=dl.DL_F32, global_=g, tokens=3)             # ckpt overlaps global
+        _expect(dl.DL_E_STALE, dl.dl_fold_checkpoint, r, 0, 0, 2, FAKE + (1 << 22),
+                dtype=dl.DL_F32, global_=g, tokens=3)
+        _expect(dl.DL_E_QUORUM, dl.dl_outer_nesterov, r, 0, g, FAKE + (1 << 26))
+        _expect(dl.DL_E_STATE, dl.dl_finalize_mean, r, 0, g)
+    finally:
+        dl.dl_round_end(r)
+
+
+def test_ema_update_host_rules():
+    dl.dl_ema_update(FAKE, FAKE + 4096, n=0, stream=0)                    # empty: no-op
+    _expect(dl.DL_E_INVAL, dl.dl_ema_update, FAKE, FAKE + 4096, n=-1, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_ema_update, 0, FAKE, n=4, stream=0)
+    _expect(dl.DL_E_ALIGN, dl.dl_ema_update, FAKE + 2, FAKE + 4096, n=4, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_ema_update, FAKE, FAKE + 8, n=4, stream=0)  # overlap
+
+
+def test_participants_capacity():
+    lib = dl.raw_lib()
+    import ctypes
+    r = dl.dl_round_begin(1, dl.DL_MEAN, 1000, OFFS1, 1, 4, FAKE, stream=0)
+    try:
+        c = ctypes.c_int()
+        buf = (ctypes.c_int * 1)()
+        assert lib.dl_round_participants(r.handle, 0, ctypes.byref(c), buf, 0) == dl.DL_OK
+        assert c.value == 0
+        assert lib.dl_round_participants(r.handle, 0, None, None, 0) == dl.DL_E_INVAL
+        assert lib.dl_round_begin(None, 1, 0, 10, 1, None, 1, 1, None, None) == dl.DL_E_INVAL
+        assert lib.dl_round_end(None) == dl.DL_OK
+    finally:
+        dl.dl_round_end(r)
+
+
+def _kernel_instr_counts(asm_text):
+    counts = collections.OrderedDict()
+    cur = None
+    for line in asm_text.split("\n"):
+        m = re.match(r"^(_ZN3dlk\S*):", line)
+        if m:
+            cur = m.group(1)
+            counts[cur] = collections.Counter()
+            continue
+        if cur and line.startswith(".Lfunc_end"):
+            cur = None
+        if cur:
+            m = re.match(r"^\s+(v_\w+)", line)
+            if m:
+                counts[cur][m.group(1)] += 1
+    return counts
+
+
+def test_isa_has_no_contraction_and_ieee_division(tmp_path):
+    """Every fused multiply-add in the gfx950 code belongs to the correctly
+    rounded division sequence (3 v_fma_f32 + 2 v_fmac_f32 per v_div_fixup_f32);
+    the folds and the EMA have none; no packed fp32 instruction appears."""
+    asm = open(cabuild.device_asm(str(tmp_path / "k.s"))).read()
+    counts = _kernel_instr_counts(asm)
+    assert len(counts) >= 40
+    for name, c in counts.items():
+        fixups = c.get("v_div_fixup_f32", 0)
+        assert c.get("v_fma_f32", 0) == 3 * fixups, name
+        assert c.get("v_fmac_f32_e32", 0) + c.get("v_fmac_f32_e64", 0) == 2 * fixups, name
+        assert c.get("v_rcp_f32_e32", 0) + c.get("v_rcp_f32_e64", 0) == fixups, name
+        assert not [k for k in c if k.startswith(("v_pk_fma", "v_pk_mul_f32", "v_pk_add_f32",
+                                                  "v_mad", "v_fmamk", "v_fmaak"))], name
+        if "fold" in name or "k_ema" in name:
+            assert fixups == 0, name
+        else:
+            assert fixups > 0, name      # the mean and Nesterov closes divide

@@ -1,0 +1,117 @@
+"""Parity at the full sizes of the five merge workloads, in the launch
+configuration the benchmark times (checkpoint_averaging_amd.workload).
+
+The 14M-parameter workloads are compared over every element.  The
+1.08B-parameter workloads are compared on sampled windows: the merge is
+elementwise, so the oracle recomputes any window on its own from inputs the
+seeded generator regenerates on the CPU for just that window.  Windows cover
+the first and last elements of every fragment plus random positions."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from checkpoint_averaging_amd import synth
+from checkpoint_averaging_amd.workload import GpuWorkload
+from tests import merge_cases as mc
+
+pytestmark = pytest.mark.gpu
+
+ROUNDS = 2
+WIN = 4096
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def windows(w, n_random, seed):
+    """Per fragment: sorted, disjoint (start, length) windows inside it."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for f in range(w.n_frags):
+        o0, o1 = w.frag_offsets[f], w.frag_offsets[f + 1]
+        L = min(WIN, o1 - o0)
+        starts = {o0, o1 - L}
+        for s in rng.integers(o0, o1 - L + 1, size=n_random):
+            starts.add(int(s))
+        merged = []
+        for s in sorted(starts):
+            e = s + L
+            if merged and s <= merged[-1][1]:
+                merged[-1][1] = max(merged[-1][1], e)
+            else:
+                merged.append([s, e])
+        out.append([(s, e - s) for s, e in merged])
+    return out
+
+
+def oracle_on_windows(w, wins):
+    """Run the oracle over the given windows for ROUNDS rounds with inputs
+    regenerated on the CPU; returns {"theta", "m", "e"} per fragment."""
+    orc = oracle.load()
+    res = []
+    for f, fw in enumerate(wins):
+        th0 = np.concatenate([synth.global0(w.seed, L, start=s).numpy() for s, L in fw])
+        theta = th0.copy()
+        m = np.zeros_like(theta)
+        e = th0.copy() if w.ema else None
+        for r in range(ROUNDS):
+            cks = {}
+            for i in range(w.workers):
+                parts = [synth.worker_checkpoint(w.seed, r, i,
+                                                 synth.global0(w.seed, L, start=s),
+                                                 start=s, dtype=w.ckpt_dtype) for s, L in fw]
+                cks[i] = mc.to_np(torch.cat(parts))
+            order = synth.arrival_order(w, r, f)
+            if w.mode == "mean":
+                theta = orc.mean_round([cks[i] for i in order], ema=e, beta=w.beta)
+            else:
+                tok = synth.token_counts(w, r)
+                orc.nesterov_fragment_round(theta, m, [cks[i] for i in order],
+                                            [tok[i] for i in order], w.lr, w.mu, e, w.beta)
+        res.append({"theta": theta, "m": m if w.mode != "mean" else None, "e": e})
+    return res
+
+
+def gather(t, fw):
+    return np.concatenate([mc.to_np(t[s:s + L]) for s, L in fw])
+
+
+@pytest.mark.parametrize("key", ["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
+                                 "diffurefill1b_frag_nesterov_ema"])
+def test_full_size_sampled(key):
+    w = synth.WORKLOADS[key]
+    say(f"[full] {key}: allocating and generating {w.n_params} params x {w.workers} workers")
+    gw = GpuWorkload(w)
+    for r in range(ROUNDS):
+        gw.generate_checkpoints(r)
+        say(f"[full] {key}: round {r}")
+        gw.run_round(r, tag=100 + r)
+    torch.cuda.synchronize()
+    wins = windows(w, 24, seed=w.seed)
+    say(f"[full] {key}: oracle on {sum(L for fw in wins for _, L in fw)} sampled elements")
+    want = oracle_on_windows(w, wins)
+    for f, fw in enumerate(wins):
+        got = {"theta": gather(gw.theta, fw)}
+        if gw.m is not None:
+            got["m"] = gather(gw.m, fw)
+        if gw.e is not None:
+            got["e"] = gather(gw.e, fw)
+        for k, g in got.items():
+            o = want[f][k]
+            assert mc.bits_equal(g, o), f"{key} frag {f} {k}: {mc.first_mismatch(g, o)}"
+    del gw
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("key", ["pythia14m_mean", "pythia14m_frag_nesterov"])
+def test_full_size_every_element(key):
+    w = synth.WORKLOADS[key]
+    st = mc.init_state(w)
+    for r in range(3):
+        say(f"[full] {key}: round {r}")
+        res = mc.run_round(w, st, r)
+        mc.assert_round_equal(res, f"{key} round {r}")
