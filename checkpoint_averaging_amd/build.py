@@ -21,6 +21,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+DRIVER = os.path.join(PKG, "dlmerge_driver")
+DRIVER_SOURCES = [os.path.join(CSRC, "merge_driver.hip")]
 
 HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -32,8 +34,7 @@ HIPFLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [HIPCC, *HIPFLAGS, "-shared", "-o", LIB + ".tmp", *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +45,16 @@ def build(verbose: bool = False) -> str:
     if msgs and (verbose or res.returncode != 0):
         print("\n".join(msgs), file=sys.stderr)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libdlmerge.so and the dlmerge_driver executable that links it."""
+    _run([HIPCC, *HIPFLAGS, "-shared", "-o", LIB + ".tmp", *SOURCES], verbose)
     os.replace(LIB + ".tmp", LIB)
+    _run([HIPCC, *HIPFLAGS, "-o", DRIVER + ".tmp", *DRIVER_SOURCES, f"-L{PKG}", "-ldlmerge",
+          "-Wl,-rpath,$ORIGIN"], verbose)
+    os.replace(DRIVER + ".tmp", DRIVER)
     return LIB
 
 

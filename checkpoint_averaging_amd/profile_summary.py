@@ -1,0 +1,196 @@
+"""Summaries of rocprofv3 output for the merge kernels.
+
+    python -m checkpoint_averaging_amd.profile_summary stats STATS_CSV --command CMD
+        -> markdown table of the merge kernels' dispatch durations
+    python -m checkpoint_averaging_amd.profile_summary pmc FETCH_CSV WRITE_CSV \
+        --workload KEY --command-fetch CMD --command-write CMD [--json OUT]
+        -> HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by
+           what the same counter reads for the plain copy kernel of known size
+
+Kernel kinds follow the names the benchmark uses (fold, fold_first,
+fold_delta, fold_delta_first, finalize_mean[_ema], nesterov[_ema], ema).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel_kind(name: str):
+    """Benchmark kind of a merge kernel from its demangled name, or None."""
+    m = re.search(r"k_(fold_sum|fold_delta|finalize_mean|nesterov|ema)<([^>]*)>", name)
+    if not m:
+        return None
+    fn, targs = m.group(1), [t.strip() for t in m.group(2).split(",")]
+    if fn == "fold_sum":
+        kind = "fold_first" if targs[1] == "true" else "fold"
+        return kind + ("_bf16" if "short" in targs[0] else "")
+    if fn == "fold_delta":
+        kind = "fold_delta_first" if targs[1] == "true" else "fold_delta"
+        return kind + ("_bf16" if "short" in targs[0] else "")
+    if fn == "finalize_mean":
+        return "finalize_mean_ema" if targs[0] == "true" else "finalize_mean"
+    if fn == "nesterov":
+        return "nesterov_ema" if targs[0] == "true" else "nesterov"
+    return "ema"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stats_markdown(stats_csv: str, command: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = ["# Merge kernels: dispatch durations (rocprofv3 --kernel-trace --stats)", "",
+           "Command:", "", "```", command, "```", "",
+           "| kind | kernel | calls | average (us) | min (us) | max (us) | total (ms) |",
+           "|---|---|---:|---:|---:|---:|---:|"]
+    other_calls, other_ns = 0, 0.0
+    def col(r, *names):
+        low = {k.lower(): v for k, v in r.items()}
+        for n in names:
+            v = low.get(n.lower())
+            if v not in (None, ""):
+                return float(v)
+        raise KeyError(names)
+
+    for r in rows:
+        r = {k.strip(): v for k, v in r.items()}
+        name = r.get("Name") or r.get("KernelName") or ""
+        calls = int(col(r, "Calls"))
+        total = col(r, "TotalDurationNs", "DURATION (nsec)")
+        kind = kernel_kind(name)
+        if kind is None:
+            other_calls += calls
+            other_ns += total
+            continue
+        short = name.replace("void ", "").replace("dlk::(anonymous namespace)::", "")
+        short = re.sub(r"\(.*", "", short)
+        avg = col(r, "AverageNs", "AVERAGE (nsec)")
+        mn = col(r, "MinNs", "MIN (nsec)")
+        mx = col(r, "MaxNs", "MAX (nsec)")
+        out.append(f"| {kind} | `{short}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | "
+                   f"{mx / 1e3:.1f} | {total / 1e6:.2f} |")
+    out += ["", f"Other kernels in the same run (input generation): {other_calls} dispatches, "
+            f"{other_ns / 1e6:.1f} ms in total.", ""]
+    return "\n".join(out)
+
+
+def _read_pmc(path: str, counter: str):
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    return rows
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, workload: str, cmd_fetch: str, cmd_write: str,
+                copy_bytes: int):
+    fetch = _read_pmc(fetch_csv, "FETCH_SIZE")
+    write = _read_pmc(write_csv, "WRITE_SIZE")
+    # calibration: the plain copy kernel of known size (1 read + 1 write of nb bytes)
+    def copy_row(rows):
+        c = [r for r in rows if "plain_copy" in r["Kernel_Name"]]
+        if len(c) != 1:
+            raise SystemExit("expected exactly one plain_copy dispatch")
+        return c[0]
+    f_scale = copy_bytes / (float(copy_row(fetch)["Counter_Value"]) * 1024)
+    w_scale = copy_bytes / (float(copy_row(write)["Counter_Value"]) * 1024)
+    per = defaultdict(lambda: {"launches": 0, "fetch": 0.0, "write": 0.0, "elements": 0})
+    for r in fetch:
+        kind = kernel_kind(r["Kernel_Name"])
+        if kind is None:
+            continue
+        d = per[kind]
+        d["launches"] += 1
+        d["fetch"] += float(r["Counter_Value"]) * 1024 * f_scale
+    for r in write:
+        kind = kernel_kind(r["Kernel_Name"])
+        if kind is None:
+            continue
+        per[kind]["write"] += float(r["Counter_Value"]) * 1024 * w_scale
+    kernels = {}
+    for kind, d in per.items():
+        kernels[kind] = {
+            "launches": d["launches"],
+            "hbm_read_bytes_per_launch": round(d["fetch"] / d["launches"]),
+            "hbm_write_bytes_per_launch": round(d["write"] / d["launches"]),
+            "hbm_bytes_per_launch": round((d["fetch"] + d["write"]) / d["launches"]),
+        }
+    return {
+        "workload": workload,
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_scale": round(f_scale, 5),
+        "write_scale": round(w_scale, 5),
+        "copy_calibration_bytes": copy_bytes,
+        "command_fetch": cmd_fetch,
+        "command_write": cmd_write,
+        "kernels": kernels,
+    }
+
+
+def pmc_markdown(s: dict, alg_per_elem: dict, frag_elems: dict) -> str:
+    out = [f"# Merge kernels: HBM traffic per dispatch ({s['workload']})", "",
+           "FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each from its own rocprofv3 run, "
+           "scaled by what the same counter reads for a plain copy kernel of "
+           f"{s['copy_calibration_bytes']} bytes: FETCH x{s['fetch_scale']}, "
+           f"WRITE x{s['write_scale']}.", "",
+           "Commands:", "", "```", s["command_fetch"], s["command_write"], "```", "",
+           f"Kernel source hash: `{s['kernel_source_hash']}`", "",
+           "| kind | launches | HBM read / launch (GB) | HBM write / launch (GB) | "
+           "algorithmic / launch (GB) | measured / algorithmic |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for kind, k in sorted(s["kernels"].items()):
+        alg = alg_per_elem.get(kind.replace("_bf16", ""), 0) * frag_elems.get(kind, 0)
+        ratio = f"{k['hbm_bytes_per_launch'] / alg:.4f}" if alg else "n/a"
+        out.append(f"| {kind} | {k['launches']} | {k['hbm_read_bytes_per_launch'] / 1e9:.4f} | "
+                   f"{k['hbm_write_bytes_per_launch'] / 1e9:.4f} | {alg / 1e9:.4f} | {ratio} |")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("stats_csv")
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("pmc")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--workload", required=True)
+    b.add_argument("--command-fetch", required=True)
+    b.add_argument("--command-write", required=True)
+    b.add_argument("--copy-bytes", type=int, required=True,
+                   help="bytes the plain copy kernel read (and wrote)")
+    b.add_argument("--json")
+    args = ap.parse_args(argv)
+    if args.mode == "stats":
+        print(stats_markdown(args.stats_csv, args.command))
+        return
+    s = pmc_summary(args.fetch_csv, args.write_csv, args.workload, args.command_fetch,
+                    args.command_write, args.copy_bytes)
+    from . import synth
+    from .workload import algorithmic_bytes
+    w = synth.WORKLOADS[args.workload]
+    alg = algorithmic_bytes(w)["per_elem"]
+    # average elements per launch of each kind over the round (all fragments)
+    sizes = [w.frag_offsets[f + 1] - w.frag_offsets[f] for f in range(w.n_frags)]
+    avg = sum(sizes) / len(sizes)
+    frag_elems = {k: avg for k in s["kernels"]}
+    if args.json:
+        with open(args.json, "w") as fh:
+            json.dump(s, fh, indent=1)
+    sys.stdout.write(pmc_markdown(s, alg, frag_elems))
+
+
+if __name__ == "__main__":
+    main()
