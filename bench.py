@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-close", action="store_true",
+                    help="close each fragment in its own pass after the last fold, instead of "
+                         "folding the last arrival into the close")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")
@@ -176,8 +179,9 @@ def main():
     def plain(kind, n, call):
         call()
 
+    fused = not args.separate_close
     for r in range(args.warmup):
-        gw.run_round(0, tag=r + 1, timer=plain)
+        gw.run_round(0, tag=r + 1, timer=plain, fused_close=fused)
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup rounds done")
 
@@ -194,7 +198,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(args.steps):
-        gw.run_round(0, tag=1000 + r, timer=timed)
+        gw.run_round(0, tag=1000 + r, timer=timed, fused_close=fused)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -221,6 +225,7 @@ def main():
     traffic = measured_traffic(w.key, dom)
 
     value = ab["per_round"] / (ms / 1e3) / 1e9
+    moved = ab["per_round_fused"] if fused else ab["per_round"]
     out = {
         "metric": "merge-round throughput: effective HBM GB/s and merged params/s; % of HBM peak",
         "value": round(value, 1),
@@ -243,7 +248,15 @@ def main():
             "fragments": w.n_frags,
             "algorithmic_bytes_per_param": ab["per_param"],
             "algorithmic_bytes_per_round": ab["per_round"],
+            "round_schedule": ("each arrival folded on its own; the last arrival of each "
+                               "fragment folded in the same pass as the close"
+                               if fused else
+                               "each arrival folded on its own; the close a separate pass"),
         },
+        "value_basis": ("algorithmic bytes of the round with a separate close (every arrival "
+                        "folded, then every state buffer read and written once) / round time"),
+        "moved_bytes_per_param": moved // w.n_params,
+        "moved_GB_per_s": round(moved / (ms / 1e3) / 1e9, 1),
         "merged_params_per_s": round(w.n_params / (ms / 1e3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_time_ms_per_step": round(total_kernel_ms / args.steps, 4),

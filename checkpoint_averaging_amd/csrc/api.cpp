@@ -29,6 +29,7 @@ struct Fragment {
     std::vector<int> arrivals;       // worker ids in arrival order
     int64_t tokens = 0;              // exact sum (DL_DELTA_NESTEROV)
     const float* global = nullptr;   // global the deltas were taken against
+    int passes = 0;                  // kernel passes over this fragment so far
 };
 
 struct Span {
@@ -83,6 +84,101 @@ struct dl_round {
     int n_frags() const { return static_cast<int>(frags.size()); }
 };
 
+namespace {
+
+// Checks shared by every call that folds an arrival: state, indices, tag,
+// duplicate, mode-specific arguments, alignment.  Sets *esize to the
+// checkpoint element size.
+int check_arrival(const dl_round* r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                  const void* ckpt, int dtype, const float* global, int64_t tokens,
+                  int64_t* esize) {
+    if (r->failed) return DL_E_STATE;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    const Fragment& F = r->frags[frag];
+    if (F.closed) return DL_E_STATE;
+    if (worker_id < 0 || worker_id >= r->max_workers) return DL_E_INVAL;
+    if (dtype != DL_F32 && dtype != DL_BF16) return DL_E_INVAL;
+    if (ckpt_round_tag != r->tag) return DL_E_STALE;
+    if (std::find(F.arrivals.begin(), F.arrivals.end(), worker_id) != F.arrivals.end())
+        return DL_E_DUP;
+    if (r->mode == DL_MEAN) {
+        if (global != nullptr) return DL_E_INVAL;
+    } else {
+        if (global == nullptr || tokens <= 0) return DL_E_INVAL;
+        if (F.tokens > INT64_MAX - tokens) return DL_E_INVAL;
+        if (F.global != nullptr && F.global != global) return DL_E_INVAL;
+    }
+    if (ckpt == nullptr) return DL_E_INVAL;
+    *esize = dtype == DL_BF16 ? 2 : 4;
+    if (!aligned_to(ckpt, static_cast<uintptr_t>(*esize))) return DL_E_ALIGN;
+    if (global != nullptr && !aligned_to(global, alignof(float))) return DL_E_ALIGN;
+    return DL_OK;
+}
+
+// Records a launch's outcome: a failed launch fails the round.
+int after_launch(dl_round* r, hipError_t err) {
+    if (err != hipSuccess) {
+        r->failed = true;
+        return DL_E_HIP;
+    }
+    return DL_OK;
+}
+
+// Validates the buffers of a mean close over fragment frag.  `ckpt_s` is the
+// span of an arrival folded in the same pass (empty if none).
+int check_mean_close(dl_round* r, int frag, float* out_global, float* ema, const Span& ckpt_s,
+                     float** out, float** e) {
+    if (out_global == nullptr) return DL_E_INVAL;
+    if (!aligned_to(out_global, alignof(float)) || (ema && !aligned_to(ema, alignof(float))))
+        return DL_E_ALIGN;
+    const int64_t off = r->off(frag), n = r->len(frag);
+    float* acc = r->acc + off;
+    *out = out_global + off;
+    const Span acc_s = span_of(acc, n * 4), out_s = span_of(*out, n * 4);
+    if (!out_s.same(acc_s) && out_s.overlaps(acc_s)) return DL_E_INVAL;
+    if (out_s.overlaps(ckpt_s)) return DL_E_INVAL;
+    *e = nullptr;
+    if (ema != nullptr) {
+        *e = ema + off;
+        const Span e_s = span_of(*e, n * 4);
+        if (e_s.overlaps(acc_s) || e_s.overlaps(out_s) || e_s.overlaps(ckpt_s)) return DL_E_INVAL;
+        if (int st = check_device_span(*e, n * 4)) return st;
+    }
+    if (int st = check_device_span(acc, n * 4)) return st;
+    return check_device_span(*out, n * 4);
+}
+
+// Validates the buffers of a Nesterov close over fragment frag.
+int check_nesterov_close(dl_round* r, int frag, float* global, float* momentum, float* ema,
+                         const Span& ckpt_s, float** theta, float** m, float** e) {
+    if (global == nullptr || momentum == nullptr) return DL_E_INVAL;
+    if (!aligned_to(global, alignof(float)) || !aligned_to(momentum, alignof(float)) ||
+        (ema && !aligned_to(ema, alignof(float))))
+        return DL_E_ALIGN;
+    const int64_t off = r->off(frag), n = r->len(frag);
+    float* acc = r->acc + off;
+    *theta = global + off;
+    *m = momentum + off;
+    const Span acc_s = span_of(acc, n * 4), th_s = span_of(*theta, n * 4),
+               m_s = span_of(*m, n * 4);
+    if (th_s.overlaps(acc_s) || m_s.overlaps(acc_s) || m_s.overlaps(th_s)) return DL_E_INVAL;
+    if (th_s.overlaps(ckpt_s) || m_s.overlaps(ckpt_s)) return DL_E_INVAL;
+    *e = nullptr;
+    if (ema != nullptr) {
+        *e = ema + off;
+        const Span e_s = span_of(*e, n * 4);
+        if (e_s.overlaps(acc_s) || e_s.overlaps(th_s) || e_s.overlaps(m_s) ||
+            e_s.overlaps(ckpt_s))
+            return DL_E_INVAL;
+        if (int st = check_device_span(*e, n * 4)) return st;
+    }
+    if (int st = check_device_span(acc, n * 4)) return st;
+    if (int st = check_device_span(*theta, n * 4)) return st;
+    return check_device_span(*m, n * 4);
+}
+
+}  // namespace
+
 extern "C" {
 
 int dl_round_begin(dl_round** out, uint64_t round_tag, int mode, int64_t n_params, int n_frags,
@@ -120,27 +216,11 @@ int dl_round_begin(dl_round** out, uint64_t round_tag, int mode, int64_t n_param
 int dl_fold_checkpoint(dl_round* r, int frag, int worker_id, uint64_t ckpt_round_tag,
                        const void* ckpt, int dtype, const float* global, int64_t tokens) {
     if (r == nullptr) return DL_E_INVAL;
-    if (r->failed) return DL_E_STATE;
-    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    int64_t esize = 0;
+    if (int st = check_arrival(r, frag, worker_id, ckpt_round_tag, ckpt, dtype, global, tokens,
+                               &esize))
+        return st;
     Fragment& F = r->frags[frag];
-    if (F.closed) return DL_E_STATE;
-    if (worker_id < 0 || worker_id >= r->max_workers) return DL_E_INVAL;
-    if (dtype != DL_F32 && dtype != DL_BF16) return DL_E_INVAL;
-    if (ckpt_round_tag != r->tag) return DL_E_STALE;
-    if (std::find(F.arrivals.begin(), F.arrivals.end(), worker_id) != F.arrivals.end())
-        return DL_E_DUP;
-    if (r->mode == DL_MEAN) {
-        if (global != nullptr) return DL_E_INVAL;
-    } else {
-        if (global == nullptr || tokens <= 0) return DL_E_INVAL;
-        if (F.tokens > INT64_MAX - tokens) return DL_E_INVAL;
-        if (F.global != nullptr && F.global != global) return DL_E_INVAL;
-    }
-    if (ckpt == nullptr) return DL_E_INVAL;
-    const int64_t esize = dtype == DL_BF16 ? 2 : 4;
-    if (!aligned_to(ckpt, static_cast<uintptr_t>(esize))) return DL_E_ALIGN;
-    if (global != nullptr && !aligned_to(global, alignof(float))) return DL_E_ALIGN;
-
     const int64_t off = r->off(frag), n = r->len(frag);
     float* acc = r->acc + off;
     const Span acc_s = span_of(acc, n * 4), ck_s = span_of(ckpt, n * esize);
@@ -156,19 +236,19 @@ int dl_fold_checkpoint(dl_round* r, int frag, int worker_id, uint64_t ckpt_round
     if (int e = check_device_span(ckpt, n * esize)) return e;
 
     const bool first = F.arrivals.empty();
+    const bool backward = (F.passes & 1) != 0;
     (void)hipGetLastError();          // launch status below is this call's own
     hipError_t err;
     if (r->mode == DL_MEAN) {
-        err = dlk::launch_fold_sum(acc, ckpt, dtype == DL_BF16, n, first, r->stream);
+        err = dlk::launch_fold_sum(acc, ckpt, dtype == DL_BF16, n, first, backward, r->stream);
     } else {
         const float w = static_cast<float>(tokens);   // nearest-even
-        err = dlk::launch_fold_delta(acc, theta, ckpt, dtype == DL_BF16, w, n, first, r->stream);
+        err = dlk::launch_fold_delta(acc, theta, ckpt, dtype == DL_BF16, w, n, first, backward,
+                                     r->stream);
     }
-    if (err != hipSuccess) {
-        r->failed = true;
-        return DL_E_HIP;
-    }
+    if (int st = after_launch(r, err)) return st;
     F.arrivals.push_back(worker_id);
+    F.passes += 1;
     if (r->mode == DL_DELTA_NESTEROV) {
         F.tokens += tokens;
         F.global = global;
@@ -183,33 +263,16 @@ int dl_finalize_mean(dl_round* r, int frag, float* out_global, float* ema, float
     Fragment& F = r->frags[frag];
     if (F.closed) return DL_E_STATE;
     if (static_cast<int>(F.arrivals.size()) < r->quorum) return DL_E_QUORUM;
-    if (out_global == nullptr) return DL_E_INVAL;
-    if (!aligned_to(out_global, alignof(float)) || (ema && !aligned_to(ema, alignof(float))))
-        return DL_E_ALIGN;
-
-    const int64_t off = r->off(frag), n = r->len(frag);
-    float* acc = r->acc + off;
-    float* out = out_global + off;
-    const Span acc_s = span_of(acc, n * 4), out_s = span_of(out, n * 4);
-    if (!out_s.same(acc_s) && out_s.overlaps(acc_s)) return DL_E_INVAL;
-    float* e = nullptr;
-    if (ema != nullptr) {
-        e = ema + off;
-        const Span e_s = span_of(e, n * 4);
-        if (e_s.overlaps(acc_s) || e_s.overlaps(out_s)) return DL_E_INVAL;
-        if (int st = check_device_span(e, n * 4)) return st;
-    }
-    if (int st = check_device_span(acc, n * 4)) return st;
-    if (int st = check_device_span(out, n * 4)) return st;
+    float *out = nullptr, *e = nullptr;
+    if (int st = check_mean_close(r, frag, out_global, ema, Span{0, 0}, &out, &e)) return st;
 
     const float count = static_cast<float>(F.arrivals.size());
     (void)hipGetLastError();
     const hipError_t err =
-        dlk::launch_finalize_mean(out, acc, count, e, beta, one_minus(beta), n, r->stream);
-    if (err != hipSuccess) {
-        r->failed = true;
-        return DL_E_HIP;
-    }
+        dlk::launch_finalize_mean(out, r->acc + r->off(frag), count, e, beta, one_minus(beta),
+                                  r->len(frag), (F.passes & 1) != 0, r->stream);
+    if (int st = after_launch(r, err)) return st;
+    F.passes += 1;
     F.closed = true;
     return DL_OK;
 }
@@ -222,35 +285,84 @@ int dl_outer_nesterov(dl_round* r, int frag, float* global, float* momentum, flo
     Fragment& F = r->frags[frag];
     if (F.closed) return DL_E_STATE;
     if (static_cast<int>(F.arrivals.size()) < r->quorum) return DL_E_QUORUM;
-    if (global == nullptr || momentum == nullptr || global != F.global) return DL_E_INVAL;
-    if (!aligned_to(momentum, alignof(float)) || (ema && !aligned_to(ema, alignof(float))))
-        return DL_E_ALIGN;
-
-    const int64_t off = r->off(frag), n = r->len(frag);
-    float* acc = r->acc + off;
-    float* theta = global + off;
-    float* m = momentum + off;
-    const Span acc_s = span_of(acc, n * 4), th_s = span_of(theta, n * 4), m_s = span_of(m, n * 4);
-    if (m_s.overlaps(acc_s) || m_s.overlaps(th_s)) return DL_E_INVAL;
-    float* e = nullptr;
-    if (ema != nullptr) {
-        e = ema + off;
-        const Span e_s = span_of(e, n * 4);
-        if (e_s.overlaps(acc_s) || e_s.overlaps(th_s) || e_s.overlaps(m_s)) return DL_E_INVAL;
-        if (int st = check_device_span(e, n * 4)) return st;
-    }
-    if (int st = check_device_span(acc, n * 4)) return st;
-    if (int st = check_device_span(theta, n * 4)) return st;
-    if (int st = check_device_span(m, n * 4)) return st;
+    if (global == nullptr || global != F.global) return DL_E_INVAL;
+    float *theta = nullptr, *m = nullptr, *e = nullptr;
+    if (int st = check_nesterov_close(r, frag, global, momentum, ema, Span{0, 0}, &theta, &m, &e))
+        return st;
 
     const float total = static_cast<float>(F.tokens);    // exact int64 sum, rounded once
     (void)hipGetLastError();
-    const hipError_t err = dlk::launch_nesterov(theta, m, acc, total, lr, mu, e, beta,
-                                                one_minus(beta), n, r->stream);
-    if (err != hipSuccess) {
-        r->failed = true;
-        return DL_E_HIP;
-    }
+    const hipError_t err = dlk::launch_nesterov(theta, m, r->acc + r->off(frag), total, lr, mu,
+                                                e, beta, one_minus(beta), r->len(frag),
+                                                (F.passes & 1) != 0, r->stream);
+    if (int st = after_launch(r, err)) return st;
+    F.passes += 1;
+    F.closed = true;
+    return DL_OK;
+}
+
+int dl_fold_and_finalize_mean(dl_round* r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                              const void* ckpt, int dtype, float* out_global, float* ema,
+                              float beta) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->mode != DL_MEAN) return DL_E_STATE;
+    int64_t esize = 0;
+    if (int st = check_arrival(r, frag, worker_id, ckpt_round_tag, ckpt, dtype, nullptr, 0,
+                               &esize))
+        return st;
+    Fragment& F = r->frags[frag];
+    if (static_cast<int>(F.arrivals.size()) + 1 < r->quorum) return DL_E_QUORUM;
+    const int64_t off = r->off(frag), n = r->len(frag);
+    const Span ck_s = span_of(ckpt, n * esize);
+    if (span_of(r->acc + off, n * 4).overlaps(ck_s)) return DL_E_INVAL;
+    float *out = nullptr, *e = nullptr;
+    if (int st = check_mean_close(r, frag, out_global, ema, ck_s, &out, &e)) return st;
+    if (int st = check_device_span(ckpt, n * esize)) return st;
+
+    const bool first = F.arrivals.empty();
+    const float count = static_cast<float>(F.arrivals.size() + 1);
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_fold_finalize_mean(
+        out, r->acc + off, ckpt, dtype == DL_BF16, first, count, e, beta, one_minus(beta), n,
+        (F.passes & 1) != 0, r->stream);
+    if (int st = after_launch(r, err)) return st;
+    F.arrivals.push_back(worker_id);
+    F.passes += 1;
+    F.closed = true;
+    return DL_OK;
+}
+
+int dl_fold_and_outer_nesterov(dl_round* r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                               const void* ckpt, int dtype, int64_t tokens, float* global,
+                               float* momentum, float lr, float mu, float* ema, float beta) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->mode != DL_DELTA_NESTEROV) return DL_E_STATE;
+    int64_t esize = 0;
+    if (int st = check_arrival(r, frag, worker_id, ckpt_round_tag, ckpt, dtype, global, tokens,
+                               &esize))
+        return st;
+    Fragment& F = r->frags[frag];
+    if (static_cast<int>(F.arrivals.size()) + 1 < r->quorum) return DL_E_QUORUM;
+    const int64_t off = r->off(frag), n = r->len(frag);
+    const Span ck_s = span_of(ckpt, n * esize);
+    if (span_of(r->acc + off, n * 4).overlaps(ck_s)) return DL_E_INVAL;
+    float *theta = nullptr, *m = nullptr, *e = nullptr;
+    if (int st = check_nesterov_close(r, frag, global, momentum, ema, ck_s, &theta, &m, &e))
+        return st;
+    if (int st = check_device_span(ckpt, n * esize)) return st;
+
+    const bool first = F.arrivals.empty();
+    const float w = static_cast<float>(tokens);               // nearest-even
+    const float total = static_cast<float>(F.tokens + tokens);  // exact int64 sum, rounded once
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_fold_nesterov(
+        theta, m, r->acc + off, ckpt, dtype == DL_BF16, first, w, total, lr, mu, e, beta,
+        one_minus(beta), n, (F.passes & 1) != 0, r->stream);
+    if (int st = after_launch(r, err)) return st;
+    F.arrivals.push_back(worker_id);
+    F.tokens += tokens;
+    F.global = global;
+    F.passes += 1;
     F.closed = true;
     return DL_OK;
 }

@@ -2,20 +2,25 @@
 //
 // Every kernel is elementwise over a flat fp32 parameter range: no element
 // depends on another, so the work is pure HBM streaming with a few binary32
-// operations per element and no use for MFMA or LDS.  Design points:
+// operations per element and no use for MFMA or LDS.  One engine runs every
+// operation; an operation is a small functor that says which streams it
+// loads and stores and what it computes per element.
 //
 //  * 128-bit global accesses.  A lane moves one 4-element pack per stream
 //    (16 B of fp32, 8 B of bf16); consecutive lanes take consecutive packs, so
 //    each wavefront instruction reads or writes one dense 1 KiB span.
-//  * Several packs per lane (UNROLL), all loads issued before any store, so a
-//    lane keeps UNROLL x (streams) 16-byte loads in flight to cover HBM
-//    latency.
+//  * Several packs per lane (kUnroll), all loads issued before any store, so
+//    a lane keeps kUnroll x (streams) loads in flight to cover HBM latency.
 //  * Non-temporal loads and stores for ranges too large to stay in the
-//    Infinity Cache; ordinary (cached) accesses for small ranges, where a
-//    fragment's accumulator can still be resident at the next fold.
+//    256 MB Infinity Cache; ordinary (cached) accesses for small ranges, where
+//    a fragment's accumulator can still be resident at the next fold.
+//  * Alternating direction: a pass may walk its tiles from the last to the
+//    first, so that consecutive passes over the same fragment meet where the
+//    previous one ended and find part of its data still cached.  Elements
+//    are independent, so the direction never changes a result.
 //  * No workgroup reuses another's data, so the block -> XCD round-robin
 //    placement needs no remapping; each block takes one contiguous tile.
-//  * The element operation is written once, as a scalar function, and used by
+//  * The element arithmetic is written once, as scalar functions, and used by
 //    the vector body, the scalar fallback and the ragged tail alike.
 //  * Arithmetic is IEEE binary32 with one rounding per operation: the file is
 //    built with -ffp-contract=off (plus the pragma below), no fast-math,
@@ -42,6 +47,7 @@ namespace {
 constexpr int kBlock = 256;     // 4 wave64 per workgroup
 constexpr int kUnroll = 4;      // packs per lane per tile
 constexpr int kPack = 4;        // elements per pack
+constexpr int64_t kTile = int64_t(kBlock) * kUnroll;   // packs (or scalars) per block
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -58,6 +64,16 @@ __device__ __forceinline__ void st(T* p, T v) {
     else *p = v;
 }
 
+template <bool NT>
+__device__ __forceinline__ f32x4 ld4(const float* base, int64_t p) {
+    return ld<NT>(reinterpret_cast<const f32x4*>(base) + p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st4(float* base, int64_t p, f32x4 v) {
+    st<NT>(reinterpret_cast<f32x4*>(base) + p, v);
+}
+
 // ---- checkpoint element types ---------------------------------------------
 
 // bfloat16 is the high half of a binary32 word: widening is a 16-bit shift,
@@ -69,16 +85,14 @@ __device__ __forceinline__ float widen_bf16(uint16_t b) {
 template <typename CT> struct Ckpt;
 
 template <> struct Ckpt<float> {
-    using pack_t = f32x4;
     static __device__ __forceinline__ float one(const float* c, int64_t j) { return c[j]; }
     template <bool NT>
     static __device__ __forceinline__ f32x4 pack(const float* c, int64_t p) {
-        return ld<NT>(reinterpret_cast<const f32x4*>(c) + p);
+        return ld4<NT>(c, p);
     }
 };
 
 template <> struct Ckpt<uint16_t> {
-    using pack_t = u32x2;
     static __device__ __forceinline__ float one(const uint16_t* c, int64_t j) {
         return widen_bf16(c[j]);
     }
@@ -95,420 +109,422 @@ template <> struct Ckpt<uint16_t> {
     }
 };
 
-// ---- element operations (one binary32 rounding per operator) ---------------
+// ---- element arithmetic (one binary32 rounding per operator) ---------------
 
-struct FoldSumOp {          // running fp32 sum: S = c (first) or S + c
-    __device__ __forceinline__ float operator()(float s, float c, bool first) const {
-        return first ? c : s + c;
+// running fp32 sum: S = c for the first arrival, S + c after
+__device__ __forceinline__ float fold_sum(float s, float c, bool first) {
+    return first ? c : s + c;
+}
+
+// weighted delta: A = w*(theta - c) for the first arrival, A + w*(theta - c) after
+__device__ __forceinline__ float fold_delta(float a, float theta, float c, float w, bool first) {
+    const float d = theta - c;
+    const float p = w * d;
+    return first ? p : a + p;
+}
+
+// e' = beta*e + (1 - beta)*x
+__device__ __forceinline__ float ema_step(float e, float x, float beta, float omega) {
+    const float a = beta * e;
+    const float b = omega * x;
+    return a + b;
+}
+
+// dbar = A/W; m' = mu*m + dbar; u = dbar + mu*m'; theta' = theta - lr*u
+__device__ __forceinline__ void nesterov_step(float a, float total, float lr, float mu,
+                                              float& theta, float& m) {
+    const float dbar = a / total;
+    const float mm = mu * m;
+    const float m_new = mm + dbar;
+    const float mu_m = mu * m_new;
+    const float u = dbar + mu_m;
+    const float step = lr * u;
+    theta = theta - step;
+    m = m_new;
+}
+
+// ---- operations ---------------------------------------------------------------
+//
+// Each operation provides
+//   struct Regs                       the loaded values of one pack
+//   load<NT>(p, Regs&)                loads pack p of every input stream
+//   store<NT>(p, const Regs&)         computes and stores pack p
+//   scalar(j)                         the same for element j alone
+// Pointers are already offset to the fragment.
+
+template <typename CT, bool FIRST>
+struct FoldSum {                // acc = c (first) or acc + c
+    float* acc;
+    const CT* c;
+    struct Regs { f32x4 c, s; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.c = Ckpt<CT>::template pack<NT>(c, p);
+        if constexpr (!FIRST) r.s = ld4<NT>(acc, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) o[i] = fold_sum(FIRST ? 0.0f : r.s[i], r.c[i], FIRST);
+        st4<NT>(acc, p, o);
+    }
+    __device__ void scalar(int64_t j) const {
+        acc[j] = fold_sum(FIRST ? 0.0f : acc[j], Ckpt<CT>::one(c, j), FIRST);
     }
 };
 
-struct FoldDeltaOp {        // weighted delta: A = w*(theta - c) (first) or A + w*(theta - c)
+template <typename CT, bool FIRST>
+struct FoldDelta {              // acc = w*(theta - c) (first) or acc + w*(theta - c)
+    float* acc;
+    const float* theta;
+    const CT* c;
     float w;
-    __device__ __forceinline__ float operator()(float a, float theta, float c, bool first) const {
-        float d = theta - c;
-        float p = w * d;
-        return first ? p : a + p;
+    struct Regs { f32x4 a, t, c; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.t = ld4<NT>(theta, p);
+        r.c = Ckpt<CT>::template pack<NT>(c, p);
+        if constexpr (!FIRST) r.a = ld4<NT>(acc, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i)
+            o[i] = fold_delta(FIRST ? 0.0f : r.a[i], r.t[i], r.c[i], w, FIRST);
+        st4<NT>(acc, p, o);
+    }
+    __device__ void scalar(int64_t j) const {
+        acc[j] = fold_delta(FIRST ? 0.0f : acc[j], theta[j], Ckpt<CT>::one(c, j), w, FIRST);
     }
 };
 
-struct EmaOp {              // e' = beta*e + (1 - beta)*x
+template <bool EMA>
+struct MeanClose {              // out = S / N; ema = beta*ema + omega*out.  out may be sum.
+    float* out;
+    const float* sum;
+    float* ema;
+    float count, beta, omega;
+    struct Regs { f32x4 s, e; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.s = ld4<NT>(sum, p);
+        if constexpr (EMA) r.e = ld4<NT>(ema, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 g, e;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            g[i] = r.s[i] / count;
+            if constexpr (EMA) e[i] = ema_step(r.e[i], g[i], beta, omega);
+        }
+        st4<NT>(out, p, g);
+        if constexpr (EMA) st4<NT>(ema, p, e);
+    }
+    __device__ void scalar(int64_t j) const {
+        const float g = sum[j] / count;
+        out[j] = g;
+        if constexpr (EMA) ema[j] = ema_step(ema[j], g, beta, omega);
+    }
+};
+
+template <bool EMA>
+struct NesterovClose {          // outer Nesterov from the accumulated weighted deltas (+ EMA)
+    float* theta;
+    float* m;
+    const float* acc;
+    float* ema;
+    float total, lr, mu, beta, omega;
+    struct Regs { f32x4 a, t, m, e; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.a = ld4<NT>(acc, p);
+        r.t = ld4<NT>(theta, p);
+        r.m = ld4<NT>(m, p);
+        if constexpr (EMA) r.e = ld4<NT>(ema, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 t = r.t, mm = r.m, e;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            float ti = t[i], mi = mm[i];
+            nesterov_step(r.a[i], total, lr, mu, ti, mi);
+            t[i] = ti;
+            mm[i] = mi;
+            if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
+        }
+        st4<NT>(theta, p, t);
+        st4<NT>(m, p, mm);
+        if constexpr (EMA) st4<NT>(ema, p, e);
+    }
+    __device__ void scalar(int64_t j) const {
+        float t = theta[j], mj = m[j];
+        nesterov_step(acc[j], total, lr, mu, t, mj);
+        theta[j] = t;
+        m[j] = mj;
+        if constexpr (EMA) ema[j] = ema_step(ema[j], t, beta, omega);
+    }
+};
+
+// The round's last arrival folded and the fragment closed in one pass: the
+// sum is completed in registers and never written back.  Same operations, in
+// the same order, as FoldSum followed by MeanClose.  out may be sum.
+template <typename CT, bool FIRST, bool EMA>
+struct FoldMeanClose {
+    float* out;
+    const float* sum;
+    const CT* c;
+    float* ema;
+    float count, beta, omega;
+    struct Regs { f32x4 s, c, e; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.c = Ckpt<CT>::template pack<NT>(c, p);
+        if constexpr (!FIRST) r.s = ld4<NT>(sum, p);
+        if constexpr (EMA) r.e = ld4<NT>(ema, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 g, e;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            const float s = fold_sum(FIRST ? 0.0f : r.s[i], r.c[i], FIRST);
+            g[i] = s / count;
+            if constexpr (EMA) e[i] = ema_step(r.e[i], g[i], beta, omega);
+        }
+        st4<NT>(out, p, g);
+        if constexpr (EMA) st4<NT>(ema, p, e);
+    }
+    __device__ void scalar(int64_t j) const {
+        const float s = fold_sum(FIRST ? 0.0f : sum[j], Ckpt<CT>::one(c, j), FIRST);
+        const float g = s / count;
+        out[j] = g;
+        if constexpr (EMA) ema[j] = ema_step(ema[j], g, beta, omega);
+    }
+};
+
+// The round's last arrival folded and the outer Nesterov step taken in one
+// pass: theta is read once for both the delta and the update, and the
+// accumulator is completed in registers and never written back.  Same
+// operations, in the same order, as FoldDelta followed by NesterovClose.
+template <typename CT, bool FIRST, bool EMA>
+struct FoldNesterovClose {
+    float* theta;
+    float* m;
+    const float* acc;
+    const CT* c;
+    float* ema;
+    float w, total, lr, mu, beta, omega;
+    struct Regs { f32x4 a, t, c, m, e; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.t = ld4<NT>(theta, p);
+        r.c = Ckpt<CT>::template pack<NT>(c, p);
+        if constexpr (!FIRST) r.a = ld4<NT>(acc, p);
+        r.m = ld4<NT>(m, p);
+        if constexpr (EMA) r.e = ld4<NT>(ema, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 t = r.t, mm = r.m, e;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            const float a = fold_delta(FIRST ? 0.0f : r.a[i], r.t[i], r.c[i], w, FIRST);
+            float ti = t[i], mi = mm[i];
+            nesterov_step(a, total, lr, mu, ti, mi);
+            t[i] = ti;
+            mm[i] = mi;
+            if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
+        }
+        st4<NT>(theta, p, t);
+        st4<NT>(m, p, mm);
+        if constexpr (EMA) st4<NT>(ema, p, e);
+    }
+    __device__ void scalar(int64_t j) const {
+        float t = theta[j], mj = m[j];
+        const float a = fold_delta(FIRST ? 0.0f : acc[j], t, Ckpt<CT>::one(c, j), w, FIRST);
+        nesterov_step(a, total, lr, mu, t, mj);
+        theta[j] = t;
+        m[j] = mj;
+        if constexpr (EMA) ema[j] = ema_step(ema[j], t, beta, omega);
+    }
+};
+
+struct Ema {                    // ema = beta*ema + omega*g
+    float* ema;
+    const float* g;
     float beta, omega;
-    __device__ __forceinline__ float operator()(float e, float x) const {
-        float a = beta * e;
-        float b = omega * x;
-        return a + b;
+    struct Regs { f32x4 e, g; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.e = ld4<NT>(ema, p);
+        r.g = ld4<NT>(g, p);
     }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) o[i] = ema_step(r.e[i], r.g[i], beta, omega);
+        st4<NT>(ema, p, o);
+    }
+    __device__ void scalar(int64_t j) const { ema[j] = ema_step(ema[j], g[j], beta, omega); }
 };
 
-struct MeanOp {             // g = S / N
-    float count;
-    __device__ __forceinline__ float operator()(float s) const { return s / count; }
-};
+// ---- the engine -----------------------------------------------------------------
 
-struct NesterovOp {         // dbar = A/W; m' = mu*m + dbar; u = dbar + mu*m'; theta' = theta - lr*u
-    float total, lr, mu;
-    __device__ __forceinline__ void operator()(float a, float& theta, float& m) const {
-        float dbar = a / total;
-        float mm = mu * m;
-        float m_new = mm + dbar;
-        float mu_m = mu * m_new;
-        float u = dbar + mu_m;
-        float step = lr * u;
-        theta = theta - step;
-        m = m_new;
+// 128-bit path.  Block b takes tile b (forward) or tile ntiles-1-b (backward);
+// lane l of a tile takes packs tile*kTile + k*kBlock + l, k < kUnroll.  The
+// fewer than kPack elements past the last whole pack are done by the first
+// lanes of the last block.
+template <class Op, bool NT>
+__global__ __launch_bounds__(kBlock) void k_stream(Op op, int64_t n, int backward) {
+    const int64_t npacks = n / kPack;
+    const int64_t ntiles = (npacks + kTile - 1) / kTile;
+    const int64_t pos = blockIdx.x;
+    if (pos < ntiles) {
+        const int64_t tile = backward ? ntiles - 1 - pos : pos;
+        const int64_t p0 = tile * kTile + threadIdx.x;
+        typename Op::Regs r[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t p = p0 + k * kBlock;
+            if (p < npacks) op.template load<NT>(p, r[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t p = p0 + k * kBlock;
+            if (p < npacks) op.template store<NT>(p, r[k]);
+        }
     }
-};
-
-// ---- tiling helpers ---------------------------------------------------------
-
-// Packs are assigned as: tile t = blockIdx.x covers packs
-// [t*kBlock*kUnroll, (t+1)*kBlock*kUnroll); lane l of the block takes packs
-// t*kBlock*kUnroll + k*kBlock + l for k < kUnroll.  VEC = 1 runs the same
-// scheme with one-element "packs" (scalar fallback for unaligned pointers).
-__device__ __forceinline__ int64_t tile_base() {
-    return static_cast<int64_t>(blockIdx.x) * (kBlock * kUnroll) + threadIdx.x;
-}
-
-// Elements past the last whole pack (fewer than kPack) are handled by the
-// first lanes of the last block.
-__device__ __forceinline__ int64_t tail_index(int64_t npacks, int64_t n) {
-    if (blockIdx.x != gridDim.x - 1) return -1;
-    int64_t j = npacks * kPack + threadIdx.x;
-    return j < n ? j : -1;
-}
-
-// ---- kernels ----------------------------------------------------------------
-
-template <typename CT, bool FIRST, bool VEC4, bool NT>
-__global__ __launch_bounds__(kBlock) void k_fold_sum(float* __restrict__ acc,
-                                                     const CT* __restrict__ c, int64_t n) {
-    const FoldSumOp op;
-    if constexpr (VEC4) {
-        const int64_t npacks = n / kPack;
-        const int64_t p0 = tile_base();
-        f32x4 cv[kUnroll], sv[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                cv[k] = Ckpt<CT>::template pack<NT>(c, p);
-                if (!FIRST) sv[k] = ld<NT>(reinterpret_cast<const f32x4*>(acc) + p);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                f32x4 r;
-#pragma unroll
-                for (int i = 0; i < kPack; ++i) r[i] = op(FIRST ? 0.0f : sv[k][i], cv[k][i], FIRST);
-                st<NT>(reinterpret_cast<f32x4*>(acc) + p, r);
-            }
-        }
-        const int64_t j = tail_index(npacks, n);
-        if (j >= 0) acc[j] = op(FIRST ? 0.0f : acc[j], Ckpt<CT>::one(c, j), FIRST);
-    } else {
-        const int64_t j0 = tile_base();
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t j = j0 + k * kBlock;
-            if (j < n) acc[j] = op(FIRST ? 0.0f : acc[j], Ckpt<CT>::one(c, j), FIRST);
-        }
+    if (blockIdx.x == gridDim.x - 1) {
+        const int64_t j = npacks * kPack + threadIdx.x;
+        if (j < n) op.scalar(j);
     }
 }
 
-template <typename CT, bool FIRST, bool VEC4, bool NT>
-__global__ __launch_bounds__(kBlock) void k_fold_delta(float* __restrict__ acc,
-                                                       const float* __restrict__ theta,
-                                                       const CT* __restrict__ c, float w,
-                                                       int64_t n) {
-    const FoldDeltaOp op{w};
-    if constexpr (VEC4) {
-        const int64_t npacks = n / kPack;
-        const int64_t p0 = tile_base();
-        f32x4 cv[kUnroll], tv[kUnroll], av[kUnroll];
+// Scalar path (a pointer is not aligned for 128-bit access): one element per
+// lane and unroll step, same tiling.
+template <class Op>
+__global__ __launch_bounds__(kBlock) void k_stream_scalar(Op op, int64_t n) {
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kTile + threadIdx.x;
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                tv[k] = ld<NT>(reinterpret_cast<const f32x4*>(theta) + p);
-                cv[k] = Ckpt<CT>::template pack<NT>(c, p);
-                if (!FIRST) av[k] = ld<NT>(reinterpret_cast<const f32x4*>(acc) + p);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                f32x4 r;
-#pragma unroll
-                for (int i = 0; i < kPack; ++i)
-                    r[i] = op(FIRST ? 0.0f : av[k][i], tv[k][i], cv[k][i], FIRST);
-                st<NT>(reinterpret_cast<f32x4*>(acc) + p, r);
-            }
-        }
-        const int64_t j = tail_index(npacks, n);
-        if (j >= 0) acc[j] = op(FIRST ? 0.0f : acc[j], theta[j], Ckpt<CT>::one(c, j), FIRST);
-    } else {
-        const int64_t j0 = tile_base();
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t j = j0 + k * kBlock;
-            if (j < n) acc[j] = op(FIRST ? 0.0f : acc[j], theta[j], Ckpt<CT>::one(c, j), FIRST);
-        }
+    for (int k = 0; k < kUnroll; ++k) {
+        const int64_t j = j0 + k * kBlock;
+        if (j < n) op.scalar(j);
     }
 }
-
-// out may be the same array as sum (in place); each element is read and then
-// written by the same lane, so the two pointers are not marked restrict.
-template <bool EMA, bool VEC4, bool NT>
-__global__ __launch_bounds__(kBlock) void k_finalize_mean(float* out, const float* sum,
-                                                          float* __restrict__ ema, int64_t n,
-                                                          MeanOp mean, EmaOp eop) {
-    if constexpr (VEC4) {
-        const int64_t npacks = n / kPack;
-        const int64_t p0 = tile_base();
-        f32x4 sv[kUnroll], ev[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                sv[k] = ld<NT>(reinterpret_cast<const f32x4*>(sum) + p);
-                if (EMA) ev[k] = ld<NT>(reinterpret_cast<const f32x4*>(ema) + p);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                f32x4 g, e;
-#pragma unroll
-                for (int i = 0; i < kPack; ++i) {
-                    g[i] = mean(sv[k][i]);
-                    if (EMA) e[i] = eop(ev[k][i], g[i]);
-                }
-                st<NT>(reinterpret_cast<f32x4*>(out) + p, g);
-                if (EMA) st<NT>(reinterpret_cast<f32x4*>(ema) + p, e);
-            }
-        }
-        const int64_t j = tail_index(npacks, n);
-        if (j >= 0) {
-            float g = mean(sum[j]);
-            out[j] = g;
-            if (EMA) ema[j] = eop(ema[j], g);
-        }
-    } else {
-        const int64_t j0 = tile_base();
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t j = j0 + k * kBlock;
-            if (j < n) {
-                float g = mean(sum[j]);
-                out[j] = g;
-                if (EMA) ema[j] = eop(ema[j], g);
-            }
-        }
-    }
-}
-
-template <bool EMA, bool VEC4, bool NT>
-__global__ __launch_bounds__(kBlock) void k_nesterov(float* __restrict__ theta,
-                                                     float* __restrict__ m,
-                                                     const float* __restrict__ acc,
-                                                     float* __restrict__ ema, int64_t n,
-                                                     NesterovOp nop, EmaOp eop) {
-    if constexpr (VEC4) {
-        const int64_t npacks = n / kPack;
-        const int64_t p0 = tile_base();
-        f32x4 av[kUnroll], tv[kUnroll], mv[kUnroll], ev[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                av[k] = ld<NT>(reinterpret_cast<const f32x4*>(acc) + p);
-                tv[k] = ld<NT>(reinterpret_cast<const f32x4*>(theta) + p);
-                mv[k] = ld<NT>(reinterpret_cast<const f32x4*>(m) + p);
-                if (EMA) ev[k] = ld<NT>(reinterpret_cast<const f32x4*>(ema) + p);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                f32x4 t = tv[k], mm = mv[k], e;
-#pragma unroll
-                for (int i = 0; i < kPack; ++i) {
-                    float ti = t[i], mi = mm[i];
-                    nop(av[k][i], ti, mi);
-                    t[i] = ti;
-                    mm[i] = mi;
-                    if (EMA) e[i] = eop(ev[k][i], ti);
-                }
-                st<NT>(reinterpret_cast<f32x4*>(theta) + p, t);
-                st<NT>(reinterpret_cast<f32x4*>(m) + p, mm);
-                if (EMA) st<NT>(reinterpret_cast<f32x4*>(ema) + p, e);
-            }
-        }
-        const int64_t j = tail_index(npacks, n);
-        if (j >= 0) {
-            float t = theta[j], mj = m[j];
-            nop(acc[j], t, mj);
-            theta[j] = t;
-            m[j] = mj;
-            if (EMA) ema[j] = eop(ema[j], t);
-        }
-    } else {
-        const int64_t j0 = tile_base();
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t j = j0 + k * kBlock;
-            if (j < n) {
-                float t = theta[j], mj = m[j];
-                nop(acc[j], t, mj);
-                theta[j] = t;
-                m[j] = mj;
-                if (EMA) ema[j] = eop(ema[j], t);
-            }
-        }
-    }
-}
-
-template <bool VEC4, bool NT>
-__global__ __launch_bounds__(kBlock) void k_ema(float* __restrict__ ema,
-                                                const float* __restrict__ g, int64_t n,
-                                                EmaOp eop) {
-    if constexpr (VEC4) {
-        const int64_t npacks = n / kPack;
-        const int64_t p0 = tile_base();
-        f32x4 ev[kUnroll], gv[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                ev[k] = ld<NT>(reinterpret_cast<const f32x4*>(ema) + p);
-                gv[k] = ld<NT>(reinterpret_cast<const f32x4*>(g) + p);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t p = p0 + k * kBlock;
-            if (p < npacks) {
-                f32x4 r;
-#pragma unroll
-                for (int i = 0; i < kPack; ++i) r[i] = eop(ev[k][i], gv[k][i]);
-                st<NT>(reinterpret_cast<f32x4*>(ema) + p, r);
-            }
-        }
-        const int64_t j = tail_index(npacks, n);
-        if (j >= 0) ema[j] = eop(ema[j], g[j]);
-    } else {
-        const int64_t j0 = tile_base();
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const int64_t j = j0 + k * kBlock;
-            if (j < n) ema[j] = eop(ema[j], g[j]);
-        }
-    }
-}
-
-// ---- launch helpers ---------------------------------------------------------
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool ckpt_aligned(const void* c, bool bf16) { return bf16 ? aligned8(c) : aligned16(c); }
 
 // Ranges of at least this many elements (64 MiB of fp32) stream with
 // non-temporal accesses; smaller ones keep the default cache policy so that a
 // fragment's accumulator can stay in the 256 MB Infinity Cache between folds.
 constexpr int64_t kNontemporalMin = int64_t(1) << 24;
 
-unsigned grid_for(int64_t n, bool vec4) {
-    const int64_t units = vec4 ? n / kPack : n;
-    int64_t blocks = (units + kBlock * kUnroll - 1) / (kBlock * kUnroll);
-    if (blocks < 1) blocks = 1;       // the ragged tail still needs one block
-    return static_cast<unsigned>(blocks);
+// Launches op over n elements: 128-bit path when `vec4`, else scalar.
+template <class Op>
+hipError_t launch(const Op& op, int64_t n, bool vec4, bool backward, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const dim3 block(kBlock);
+    if (vec4) {
+        int64_t blocks = (n / kPack + kTile - 1) / kTile;
+        if (blocks < 1) blocks = 1;               // the ragged tail still needs one block
+        const dim3 grid(static_cast<unsigned>(blocks));
+        const int dir = backward ? 1 : 0;
+        if (n >= kNontemporalMin)
+            hipLaunchKernelGGL((k_stream<Op, true>), grid, block, 0, s, op, n, dir);
+        else
+            hipLaunchKernelGGL((k_stream<Op, false>), grid, block, 0, s, op, n, dir);
+    } else {
+        const dim3 grid(static_cast<unsigned>((n + kTile - 1) / kTile));
+        hipLaunchKernelGGL((k_stream_scalar<Op>), grid, block, 0, s, op, n);
+    }
+    return hipGetLastError();
 }
-
-// Dispatches a kernel template over the VEC4 x NT choices.
-#define DLK_DISPATCH2(VEC4, NT, LAUNCH)                           \
-    do {                                                          \
-        if (VEC4) {                                               \
-            if (NT) { LAUNCH(true, true); } else { LAUNCH(true, false); } \
-        } else {                                                  \
-            if (NT) { LAUNCH(false, true); } else { LAUNCH(false, false); } \
-        }                                                         \
-    } while (0)
 
 }  // namespace
 
 hipError_t launch_fold_sum(float* acc, const void* ckpt, bool bf16, int64_t n, bool first,
-                           hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    const bool vec4 = aligned16(acc) && (bf16 ? aligned8(ckpt) : aligned16(ckpt));
-    const bool nt = n >= kNontemporalMin;
-    const dim3 grid(grid_for(n, vec4)), block(kBlock);
-#define L(V, N)                                                                              \
-    if (bf16) {                                                                              \
-        auto c = static_cast<const uint16_t*>(ckpt);                                         \
-        if (first) hipLaunchKernelGGL((k_fold_sum<uint16_t, true, V, N>), grid, block, 0, s, acc, c, n); \
-        else hipLaunchKernelGGL((k_fold_sum<uint16_t, false, V, N>), grid, block, 0, s, acc, c, n); \
-    } else {                                                                                 \
-        auto c = static_cast<const float*>(ckpt);                                            \
-        if (first) hipLaunchKernelGGL((k_fold_sum<float, true, V, N>), grid, block, 0, s, acc, c, n); \
-        else hipLaunchKernelGGL((k_fold_sum<float, false, V, N>), grid, block, 0, s, acc, c, n); \
+                           bool backward, hipStream_t s) {
+    const bool vec4 = aligned16(acc) && ckpt_aligned(ckpt, bf16);
+    if (bf16) {
+        auto c = static_cast<const uint16_t*>(ckpt);
+        if (first) return launch(FoldSum<uint16_t, true>{acc, c}, n, vec4, backward, s);
+        return launch(FoldSum<uint16_t, false>{acc, c}, n, vec4, backward, s);
     }
-    DLK_DISPATCH2(vec4, nt, L);
-#undef L
-    return hipGetLastError();
+    auto c = static_cast<const float*>(ckpt);
+    if (first) return launch(FoldSum<float, true>{acc, c}, n, vec4, backward, s);
+    return launch(FoldSum<float, false>{acc, c}, n, vec4, backward, s);
 }
 
 hipError_t launch_fold_delta(float* acc, const float* theta, const void* ckpt, bool bf16,
-                             float w, int64_t n, bool first, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    const bool vec4 = aligned16(acc) && aligned16(theta) &&
-                      (bf16 ? aligned8(ckpt) : aligned16(ckpt));
-    const bool nt = n >= kNontemporalMin;
-    const dim3 grid(grid_for(n, vec4)), block(kBlock);
-#define L(V, N)                                                                              \
-    if (bf16) {                                                                              \
-        auto c = static_cast<const uint16_t*>(ckpt);                                         \
-        if (first) hipLaunchKernelGGL((k_fold_delta<uint16_t, true, V, N>), grid, block, 0, s, acc, theta, c, w, n); \
-        else hipLaunchKernelGGL((k_fold_delta<uint16_t, false, V, N>), grid, block, 0, s, acc, theta, c, w, n); \
-    } else {                                                                                 \
-        auto c = static_cast<const float*>(ckpt);                                            \
-        if (first) hipLaunchKernelGGL((k_fold_delta<float, true, V, N>), grid, block, 0, s, acc, theta, c, w, n); \
-        else hipLaunchKernelGGL((k_fold_delta<float, false, V, N>), grid, block, 0, s, acc, theta, c, w, n); \
+                             float w, int64_t n, bool first, bool backward, hipStream_t s) {
+    const bool vec4 = aligned16(acc) && aligned16(theta) && ckpt_aligned(ckpt, bf16);
+    if (bf16) {
+        auto c = static_cast<const uint16_t*>(ckpt);
+        if (first) return launch(FoldDelta<uint16_t, true>{acc, theta, c, w}, n, vec4, backward, s);
+        return launch(FoldDelta<uint16_t, false>{acc, theta, c, w}, n, vec4, backward, s);
     }
-    DLK_DISPATCH2(vec4, nt, L);
-#undef L
-    return hipGetLastError();
+    auto c = static_cast<const float*>(ckpt);
+    if (first) return launch(FoldDelta<float, true>{acc, theta, c, w}, n, vec4, backward, s);
+    return launch(FoldDelta<float, false>{acc, theta, c, w}, n, vec4, backward, s);
 }
 
 hipError_t launch_finalize_mean(float* out, const float* sum, float count, float* ema,
-                                float beta, float omega, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
+                                float beta, float omega, int64_t n, bool backward,
+                                hipStream_t s) {
     const bool vec4 = aligned16(out) && aligned16(sum) && (ema == nullptr || aligned16(ema));
-    const bool nt = n >= kNontemporalMin;
-    const dim3 grid(grid_for(n, vec4)), block(kBlock);
-    const MeanOp mop{count};
-    const EmaOp eop{beta, omega};
-#define L(V, N)                                                                              \
-    if (ema) hipLaunchKernelGGL((k_finalize_mean<true, V, N>), grid, block, 0, s, out, sum, ema, n, mop, eop); \
-    else hipLaunchKernelGGL((k_finalize_mean<false, V, N>), grid, block, 0, s, out, sum, ema, n, mop, eop);
-    DLK_DISPATCH2(vec4, nt, L);
-#undef L
-    return hipGetLastError();
+    if (ema) return launch(MeanClose<true>{out, sum, ema, count, beta, omega}, n, vec4, backward, s);
+    return launch(MeanClose<false>{out, sum, ema, count, beta, omega}, n, vec4, backward, s);
 }
 
 hipError_t launch_nesterov(float* theta, float* m, const float* acc, float total, float lr,
                            float mu, float* ema, float beta, float omega, int64_t n,
-                           hipStream_t s) {
-    if (n <= 0) return hipSuccess;
+                           bool backward, hipStream_t s) {
     const bool vec4 = aligned16(theta) && aligned16(m) && aligned16(acc) &&
                       (ema == nullptr || aligned16(ema));
-    const bool nt = n >= kNontemporalMin;
-    const dim3 grid(grid_for(n, vec4)), block(kBlock);
-    const NesterovOp nop{total, lr, mu};
-    const EmaOp eop{beta, omega};
-#define L(V, N)                                                                              \
-    if (ema) hipLaunchKernelGGL((k_nesterov<true, V, N>), grid, block, 0, s, theta, m, acc, ema, n, nop, eop); \
-    else hipLaunchKernelGGL((k_nesterov<false, V, N>), grid, block, 0, s, theta, m, acc, ema, n, nop, eop);
-    DLK_DISPATCH2(vec4, nt, L);
-#undef L
-    return hipGetLastError();
+    if (ema)
+        return launch(NesterovClose<true>{theta, m, acc, ema, total, lr, mu, beta, omega}, n,
+                      vec4, backward, s);
+    return launch(NesterovClose<false>{theta, m, acc, ema, total, lr, mu, beta, omega}, n, vec4,
+                  backward, s);
+}
+
+hipError_t launch_fold_finalize_mean(float* out, const float* sum, const void* ckpt, bool bf16,
+                                     bool first, float count, float* ema, float beta,
+                                     float omega, int64_t n, bool backward, hipStream_t s) {
+    const bool vec4 = aligned16(out) && aligned16(sum) && ckpt_aligned(ckpt, bf16) &&
+                      (ema == nullptr || aligned16(ema));
+#define DLK_FMC(CT, FIRST, EMA)                                                              \
+    return launch(FoldMeanClose<CT, FIRST, EMA>{out, sum, static_cast<const CT*>(ckpt), ema,  \
+                                                count, beta, omega},                         \
+                  n, vec4, backward, s)
+    if (bf16) {
+        if (first) { if (ema) DLK_FMC(uint16_t, true, true); else DLK_FMC(uint16_t, true, false); }
+        else { if (ema) DLK_FMC(uint16_t, false, true); else DLK_FMC(uint16_t, false, false); }
+    }
+    if (first) { if (ema) DLK_FMC(float, true, true); else DLK_FMC(float, true, false); }
+    if (ema) DLK_FMC(float, false, true);
+    DLK_FMC(float, false, false);
+#undef DLK_FMC
+}
+
+hipError_t launch_fold_nesterov(float* theta, float* m, const float* acc, const void* ckpt,
+                                bool bf16, bool first, float w, float total, float lr, float mu,
+                                float* ema, float beta, float omega, int64_t n, bool backward,
+                                hipStream_t s) {
+    const bool vec4 = aligned16(theta) && aligned16(m) && aligned16(acc) &&
+                      ckpt_aligned(ckpt, bf16) && (ema == nullptr || aligned16(ema));
+#define DLK_FNC(CT, FIRST, EMA)                                                              \
+    return launch(FoldNesterovClose<CT, FIRST, EMA>{theta, m, acc,                           \
+                                                    static_cast<const CT*>(ckpt), ema, w,    \
+                                                    total, lr, mu, beta, omega},             \
+                  n, vec4, backward, s)
+    if (bf16) {
+        if (first) { if (ema) DLK_FNC(uint16_t, true, true); else DLK_FNC(uint16_t, true, false); }
+        else { if (ema) DLK_FNC(uint16_t, false, true); else DLK_FNC(uint16_t, false, false); }
+    }
+    if (first) { if (ema) DLK_FNC(float, true, true); else DLK_FNC(float, true, false); }
+    if (ema) DLK_FNC(float, false, true);
+    DLK_FNC(float, false, false);
+#undef DLK_FNC
 }
 
 hipError_t launch_ema(float* ema, const float* g, float beta, float omega, int64_t n,
                       hipStream_t s) {
-    if (n <= 0) return hipSuccess;
     const bool vec4 = aligned16(ema) && aligned16(g);
-    const bool nt = n >= kNontemporalMin;
-    const dim3 grid(grid_for(n, vec4)), block(kBlock);
-    const EmaOp eop{beta, omega};
-#define L(V, N) hipLaunchKernelGGL((k_ema<V, N>), grid, block, 0, s, ema, g, n, eop);
-    DLK_DISPATCH2(vec4, nt, L);
-#undef L
-    return hipGetLastError();
+    return launch(Ema{ema, g, beta, omega}, n, vec4, false, s);
 }
 
 }  // namespace dlk

@@ -6,12 +6,13 @@
 //
 //   dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
-//                  [--rounds R] [--warmup R0] [--copy-mib M]
+//                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
-// folded (token-weighted delta in delta mode), then the fragment is closed
+// folded (token-weighted delta in delta mode) and the fragment is closed
 // (mean, or outer Nesterov lr 0.7 / momentum 0.9), with the EMA (beta 0.9)
-// fused in when enabled.  Buffer contents are a deterministic pattern; the
+// fused in when enabled.  With --fused 1 (default) the last worker is folded
+// in the same pass as the close.  Buffer contents are a deterministic pattern; the
 // timing does not depend on them.
 #include <hip/hip_runtime.h>
 
@@ -91,13 +92,14 @@ struct Args {
     int rounds = 1;
     int warmup = 1;
     int copy_mib = 0;
+    bool fused = true;
 };
 
 [[noreturn]] void usage() {
     std::fprintf(stderr,
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
-                 "       [--warmup R0] [--copy-mib M]\n");
+                 "       [--warmup R0] [--copy-mib M] [--fused 0|1]\n");
     std::exit(2);
 }
 
@@ -123,6 +125,7 @@ Args parse(int argc, char** argv) {
         else if (k == "--rounds") a.rounds = std::atoi(v.c_str());
         else if (k == "--warmup") a.warmup = std::atoi(v.c_str());
         else if (k == "--copy-mib") a.copy_mib = std::atoi(v.c_str());
+        else if (k == "--fused") a.fused = std::atoi(v.c_str()) != 0;
         else usage();
     }
     if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0) usage();
@@ -184,16 +187,29 @@ int main(int argc, char** argv) {
         const uint64_t tag = uint64_t(r) + 1;
         DLCHECK(dl_round_begin(&rd, tag, a.delta ? DL_DELTA_NESTEROV : DL_MEAN, a.n, n_frags,
                                a.offsets.data(), 1, a.workers, acc, s));
+        const int dt = a.bf16 ? DL_BF16 : DL_F32;
         for (int f = 0; f < n_frags; ++f) {
             const int64_t off = a.offsets[f];
-            for (int i = 0; i < a.workers; ++i) {
+            const int folds = a.fused ? a.workers - 1 : a.workers;
+            for (int i = 0; i < folds; ++i) {
                 const char* base = static_cast<const char*>(ck[i]) + off * (a.bf16 ? 2 : 4);
-                DLCHECK(dl_fold_checkpoint(rd, f, i, tag, base, a.bf16 ? DL_BF16 : DL_F32,
-                                           a.delta ? theta : nullptr,
+                DLCHECK(dl_fold_checkpoint(rd, f, i, tag, base, dt, a.delta ? theta : nullptr,
                                            19660800 + 1000 * int64_t(i)));
             }
-            if (a.delta) DLCHECK(dl_outer_nesterov(rd, f, theta, m, 0.7f, 0.9f, e, 0.9f));
-            else DLCHECK(dl_finalize_mean(rd, f, theta, e, 0.9f));
+            if (a.fused) {
+                const int i = a.workers - 1;
+                const char* base = static_cast<const char*>(ck[i]) + off * (a.bf16 ? 2 : 4);
+                if (a.delta)
+                    DLCHECK(dl_fold_and_outer_nesterov(rd, f, i, tag, base, dt,
+                                                       19660800 + 1000 * int64_t(i), theta, m,
+                                                       0.7f, 0.9f, e, 0.9f));
+                else
+                    DLCHECK(dl_fold_and_finalize_mean(rd, f, i, tag, base, dt, theta, e, 0.9f));
+            } else if (a.delta) {
+                DLCHECK(dl_outer_nesterov(rd, f, theta, m, 0.7f, 0.9f, e, 0.9f));
+            } else {
+                DLCHECK(dl_finalize_mean(rd, f, theta, e, 0.9f));
+            }
         }
         DLCHECK(dl_round_end(rd));
     }

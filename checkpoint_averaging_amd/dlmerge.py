@@ -36,6 +36,7 @@ DL_E_HIP = -7
 DL_E_CAPACITY = -8
 
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
+           "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
 
@@ -51,6 +52,9 @@ _lib.dl_round_begin.argtypes = [ctypes.POINTER(_p), _u64, _i32, _i64, _i32,
 _lib.dl_fold_checkpoint.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _p, _i64]
 _lib.dl_finalize_mean.argtypes = [_p, _i32, _p, _p, _f32]
 _lib.dl_outer_nesterov.argtypes = [_p, _i32, _p, _p, _f32, _f32, _p, _f32]
+_lib.dl_fold_and_finalize_mean.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _p, _p, _f32]
+_lib.dl_fold_and_outer_nesterov.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _i64, _p, _p, _f32,
+                                            _f32, _p, _f32]
 _lib.dl_ema_update.argtypes = [_p, _p, _i64, _f32, _p]
 _lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dl_round_participants.argtypes = [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32]
@@ -137,18 +141,22 @@ def dl_round_begin(round_tag: int, mode: int, n_params: int, frag_offsets: Seque
     return Round(h, len(frag_offsets) - 1)
 
 
+def _ckpt_dtype(ckpt: Array, dtype: Optional[int]) -> int:
+    if dtype is not None:
+        return int(dtype)
+    if not isinstance(ckpt, torch.Tensor):
+        raise TypeError("dtype is required for a raw checkpoint address")
+    if ckpt.dtype == torch.float32:
+        return DL_F32
+    if ckpt.dtype == torch.bfloat16:
+        return DL_BF16
+    raise TypeError("checkpoint must be float32 or bfloat16")
+
+
 def dl_fold_checkpoint(r: Round, frag: int, worker_id: int, ckpt_round_tag: int, ckpt: Array,
                        global_: Array = None, tokens: int = 0,
                        dtype: Optional[int] = None) -> None:
-    if dtype is None:
-        if not isinstance(ckpt, torch.Tensor):
-            raise TypeError("dtype is required for a raw checkpoint address")
-        if ckpt.dtype == torch.float32:
-            dtype = DL_F32
-        elif ckpt.dtype == torch.bfloat16:
-            dtype = DL_BF16
-        else:
-            raise TypeError("checkpoint must be float32 or bfloat16")
+    dtype = _ckpt_dtype(ckpt, dtype)
     _check(_lib.dl_fold_checkpoint(r.handle, int(frag), int(worker_id), int(ckpt_round_tag),
                                    _addr(ckpt), int(dtype), _f32_addr(global_, "global"),
                                    int(tokens)),
@@ -168,6 +176,30 @@ def dl_outer_nesterov(r: Round, frag: int, global_: Array, momentum: Array, lr: 
                                   _f32_addr(momentum, "momentum"), float(lr), float(mu),
                                   _f32_addr(ema, "ema"), float(beta)),
            "dl_outer_nesterov")
+
+
+def dl_fold_and_finalize_mean(r: Round, frag: int, worker_id: int, ckpt_round_tag: int,
+                              ckpt: Array, out_global: Array, ema: Array = None,
+                              beta: float = 0.9, dtype: Optional[int] = None) -> None:
+    dtype = _ckpt_dtype(ckpt, dtype)
+    _check(_lib.dl_fold_and_finalize_mean(r.handle, int(frag), int(worker_id),
+                                          int(ckpt_round_tag), _addr(ckpt), int(dtype),
+                                          _f32_addr(out_global, "out_global"),
+                                          _f32_addr(ema, "ema"), float(beta)),
+           "dl_fold_and_finalize_mean")
+
+
+def dl_fold_and_outer_nesterov(r: Round, frag: int, worker_id: int, ckpt_round_tag: int,
+                               ckpt: Array, tokens: int, global_: Array, momentum: Array,
+                               lr: float = 0.7, mu: float = 0.9, ema: Array = None,
+                               beta: float = 0.9, dtype: Optional[int] = None) -> None:
+    dtype = _ckpt_dtype(ckpt, dtype)
+    _check(_lib.dl_fold_and_outer_nesterov(r.handle, int(frag), int(worker_id),
+                                           int(ckpt_round_tag), _addr(ckpt), int(dtype),
+                                           int(tokens), _f32_addr(global_, "global"),
+                                           _f32_addr(momentum, "momentum"), float(lr),
+                                           float(mu), _f32_addr(ema, "ema"), float(beta)),
+           "dl_fold_and_outer_nesterov")
 
 
 def dl_ema_update(ema: Array, global_: Array, beta: float = 0.9, n: Optional[int] = None,

@@ -8,7 +8,9 @@
            what the same counter reads for the plain copy kernel of known size
 
 Kernel kinds follow the names the benchmark uses (fold, fold_first,
-fold_delta, fold_delta_first, finalize_mean[_ema], nesterov[_ema], ema).
+fold_delta, fold_delta_first, finalize_mean[_ema], nesterov[_ema],
+fold_finalize_mean[_ema][_first], fold_nesterov[_ema][_first], ema; _bf16
+for bf16 checkpoints).
 """
 from __future__ import annotations
 
@@ -25,21 +27,29 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def kernel_kind(name: str):
-    """Benchmark kind of a merge kernel from its demangled name, or None."""
-    m = re.search(r"k_(fold_sum|fold_delta|finalize_mean|nesterov|ema)<([^>]*)>", name)
-    if not m:
+    """Benchmark kind of a merge kernel from its demangled name, or None.
+
+    Kernels are k_stream<Op, NT> (128-bit path) or k_stream_scalar<Op>; the
+    kind comes from the operation and its template arguments."""
+    m = re.search(r"::(FoldMeanClose|FoldNesterovClose|FoldSum|FoldDelta|MeanClose|"
+                  r"NesterovClose|Ema)\b(?:<([^>]*)>)?", name)
+    if not m or "k_stream" not in name:
         return None
-    fn, targs = m.group(1), [t.strip() for t in m.group(2).split(",")]
-    if fn == "fold_sum":
-        kind = "fold_first" if targs[1] == "true" else "fold"
-        return kind + ("_bf16" if "short" in targs[0] else "")
-    if fn == "fold_delta":
-        kind = "fold_delta_first" if targs[1] == "true" else "fold_delta"
-        return kind + ("_bf16" if "short" in targs[0] else "")
-    if fn == "finalize_mean":
+    op = m.group(1)
+    targs = [t.strip() for t in (m.group(2) or "").split(",")]
+    bf16 = "_bf16" if targs and "short" in targs[0] else ""
+    if op == "FoldSum":
+        return ("fold_first" if targs[1] == "true" else "fold") + bf16
+    if op == "FoldDelta":
+        return ("fold_delta_first" if targs[1] == "true" else "fold_delta") + bf16
+    if op == "MeanClose":
         return "finalize_mean_ema" if targs[0] == "true" else "finalize_mean"
-    if fn == "nesterov":
+    if op == "NesterovClose":
         return "nesterov_ema" if targs[0] == "true" else "nesterov"
+    if op in ("FoldMeanClose", "FoldNesterovClose"):
+        base = "fold_finalize_mean" if op == "FoldMeanClose" else "fold_nesterov"
+        return (base + ("_ema" if targs[2] == "true" else "")
+                + ("_first" if targs[1] == "true" else "") + bf16)
     return "ema"
 
 

@@ -61,26 +61,40 @@ class GpuWorkload:
         return synth.token_counts(self.w, rnd)
 
     def run_round(self, rnd: int, tag: int,
-                  timer: Optional[Callable[[str, int, Callable[[], None]], None]] = None) -> None:
+                  timer: Optional[Callable[[str, int, Callable[[], None]], None]] = None,
+                  fused_close: bool = True) -> None:
         """Issue one merge round.  `timer(kind, elements, call)` (if given)
-        wraps every kernel-launching call, e.g. to record events around it."""
+        wraps every kernel-launching call, e.g. to record events around it.
+
+        With `fused_close`, the fragment's last expected arrival is folded and
+        the fragment closed in one pass (the merger closes as soon as every
+        worker of the round is in); otherwise the close is a separate pass."""
         w = self.w
         offs = list(w.frag_offsets)
         orders = self.orders(rnd)
         run = timer if timer is not None else (lambda kind, n, call: call())
+        ema = "_ema" if self.e is not None else ""
         if not self.delta:
             r = dl.dl_round_begin(tag, dl.DL_MEAN, w.n_params, offs, w.quorum, w.workers,
                                   self.acc)
             try:
                 for f in range(w.n_frags):
                     o0, o1 = offs[f], offs[f + 1]
-                    for k, i in enumerate(orders[f]):
-                        kind = "fold_first" if k == 0 else "fold"
+                    order = orders[f]
+                    folds = order[:-1] if fused_close else order
+                    for k, i in enumerate(folds):
                         ck = self.ckpts[i][o0:o1]
-                        run(kind, o1 - o0, lambda f=f, i=i, ck=ck:
-                            dl.dl_fold_checkpoint(r, f, i, tag, ck))
-                    run("finalize_mean_ema" if self.e is not None else "finalize_mean", o1 - o0,
-                        lambda f=f: dl.dl_finalize_mean(r, f, self.theta, self.e, w.beta))
+                        run("fold_first" if k == 0 else "fold", o1 - o0,
+                            lambda f=f, i=i, ck=ck: dl.dl_fold_checkpoint(r, f, i, tag, ck))
+                    if fused_close:
+                        i = order[-1]
+                        ck = self.ckpts[i][o0:o1]
+                        kind = "fold_finalize_mean" + ema + ("_first" if not folds else "")
+                        run(kind, o1 - o0, lambda f=f, i=i, ck=ck: dl.dl_fold_and_finalize_mean(
+                            r, f, i, tag, ck, self.theta, self.e, w.beta))
+                    else:
+                        run("finalize_mean" + ema, o1 - o0,
+                            lambda f=f: dl.dl_finalize_mean(r, f, self.theta, self.e, w.beta))
             finally:
                 dl.dl_round_end(r)
         else:
@@ -90,38 +104,62 @@ class GpuWorkload:
             try:
                 for f in range(w.n_frags):
                     o0, o1 = offs[f], offs[f + 1]
-                    for k, i in enumerate(orders[f]):
-                        kind = "fold_delta_first" if k == 0 else "fold_delta"
+                    order = orders[f]
+                    folds = order[:-1] if fused_close else order
+                    for k, i in enumerate(folds):
                         ck = self.ckpts[i][o0:o1]
-                        run(kind, o1 - o0, lambda f=f, i=i, ck=ck:
+                        run("fold_delta_first" if k == 0 else "fold_delta", o1 - o0,
+                            lambda f=f, i=i, ck=ck:
                             dl.dl_fold_checkpoint(r, f, i, tag, ck, self.theta, tok[i]))
-                    run("nesterov_ema" if self.e is not None else "nesterov", o1 - o0,
-                        lambda f=f: dl.dl_outer_nesterov(r, f, self.theta, self.m, w.lr, w.mu,
-                                                         self.e, w.beta))
+                    if fused_close:
+                        i = order[-1]
+                        ck = self.ckpts[i][o0:o1]
+                        kind = "fold_nesterov" + ema + ("_first" if not folds else "")
+                        run(kind, o1 - o0, lambda f=f, i=i, ck=ck: dl.dl_fold_and_outer_nesterov(
+                            r, f, i, tag, ck, tok[i], self.theta, self.m, w.lr, w.mu, self.e,
+                            w.beta))
+                    else:
+                        run("nesterov" + ema, o1 - o0,
+                            lambda f=f: dl.dl_outer_nesterov(r, f, self.theta, self.m, w.lr,
+                                                             w.mu, self.e, w.beta))
             finally:
                 dl.dl_round_end(r)
 
 
-def algorithmic_bytes(w: synth.Workload) -> Dict[str, int]:
+def algorithmic_bytes(w: synth.Workload, fused_close: bool = False) -> Dict[str, int]:
     """Bytes each kernel kind must move per element, and per round in total.
 
     Each arriving checkpoint is read once; the accumulator is read and written
     per arrival except the first, which only writes it; the delta fold also
     reads the global; the close reads and writes each state buffer once, with
-    the EMA fused in."""
+    the EMA fused in.  This is the round with a separate close (`per_param`,
+    `per_round`).  With `fused_close` the last arrival's fold and the close
+    share one pass, which moves fewer bytes (`per_param_fused`)."""
     cb = 2 if w.ckpt_dtype == "bf16" else 4
     per_elem = {
         "fold_first": cb + 4, "fold": cb + 8,
         "fold_delta_first": cb + 8, "fold_delta": cb + 12,
         "finalize_mean": 8, "finalize_mean_ema": 16,
         "nesterov": 20, "nesterov_ema": 28,
+        # last arrival folded and the fragment closed in one pass
+        "fold_finalize_mean": cb + 8, "fold_finalize_mean_ema": cb + 16,
+        "fold_finalize_mean_first": cb + 4, "fold_finalize_mean_ema_first": cb + 12,
+        "fold_nesterov": cb + 20, "fold_nesterov_ema": cb + 28,
+        "fold_nesterov_first": cb + 16, "fold_nesterov_ema_first": cb + 24,
+        "ema": 12,
     }
+    ema = "_ema" if w.ema else ""
     if w.mode == "mean":
-        close = "finalize_mean_ema" if w.ema else "finalize_mean"
-        per_param = per_elem["fold_first"] + (w.workers - 1) * per_elem["fold"] + per_elem[close]
+        first, fold, close, fused = "fold_first", "fold", "finalize_mean", "fold_finalize_mean"
     else:
-        close = "nesterov_ema" if w.ema else "nesterov"
-        per_param = (per_elem["fold_delta_first"] + (w.workers - 1) * per_elem["fold_delta"]
-                     + per_elem[close])
-    return {"per_elem": per_elem, "per_param": per_param,
-            "per_round": per_param * w.n_params}
+        first, fold, close, fused = ("fold_delta_first", "fold_delta", "nesterov",
+                                     "fold_nesterov")
+    per_param = per_elem[first] + (w.workers - 1) * per_elem[fold] + per_elem[close + ema]
+    if w.workers > 1:
+        per_param_fused = (per_elem[first] + (w.workers - 2) * per_elem[fold]
+                           + per_elem[fused + ema])
+    else:
+        per_param_fused = per_elem[fused + ema + "_first"]
+    return {"per_elem": per_elem, "per_param": per_param, "per_round": per_param * w.n_params,
+            "per_param_fused": per_param_fused,
+            "per_round_fused": per_param_fused * w.n_params}

@@ -44,7 +44,10 @@
  * flat, contiguous vectors of n_params elements; fragment f covers elements
  * [frag_offsets[f], frag_offsets[f+1]).  Full-length buffers (acc, global,
  * momentum, ema) are indexed by those offsets; a checkpoint buffer holds only
- * its fragment's elements.  Pointers must be aligned to their element type;
+ * its fragment's elements.  Consecutive passes over a fragment walk it in
+ * alternating directions (results do not depend on it; it lets a pass find
+ * the end of the previous one still cached).  Pointers must be aligned to
+ * their element type;
  * when every pointer a kernel touches is 16-byte aligned the 128-bit path
  * runs, otherwise a scalar path gives the same bits.  Each span
  * [ptr, ptr + bytes) must lie inside one device allocation, which the library
@@ -54,8 +57,9 @@
  * except DL_E_HIP happen on the host before any launch; a call that fails
  * them launches nothing and leaves the handle unchanged.  Device buffers
  * holding the global, momentum and EMA are written only by the closing calls
- * (dl_finalize_mean, dl_outer_nesterov, dl_ema_update), so an abandoned round
- * changes none of them.
+ * (dl_finalize_mean, dl_outer_nesterov, dl_fold_and_finalize_mean,
+ * dl_fold_and_outer_nesterov, dl_ema_update), so an abandoned round changes
+ * none of them.
  *
  * Threads.  A handle is used by one host thread at a time.  Several handles
  * may be open at once (two rounds in flight, GradientMail post, "Getting
@@ -192,6 +196,46 @@ int dl_finalize_mean(dl_round *r, int frag, float *out_global, float *ema, float
  */
 int dl_outer_nesterov(dl_round *r, int frag, float *global, float *momentum, float lr,
                       float mu, float *ema, float beta);
+
+/*
+ * Fold the fragment's last expected arrival and close the fragment in the
+ * same pass: identical results, bit for bit, to dl_fold_checkpoint followed
+ * by dl_finalize_mean, with one kernel launch instead of two.  The sum is
+ * completed in registers and not written back to acc (acc's fragment range
+ * is unspecified afterwards), so the pass moves 8 bytes per element fewer.
+ * For the merger that closes as soon as every expected worker of the round
+ * is in; a round closed by its grace timer uses dl_finalize_mean.  If this
+ * is the fragment's first arrival (quorum 1), the mean is that checkpoint.
+ *
+ * Arguments as in dl_fold_checkpoint and dl_finalize_mean; the quorum check
+ * counts this arrival.  ckpt must not overlap out_global or ema.
+ *
+ * Errors: those of both calls; nothing is launched and the handle is
+ * unchanged on any error but DL_E_HIP.
+ */
+int dl_fold_and_finalize_mean(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                              const void *ckpt, int dtype, float *out_global, float *ema,
+                              float beta);
+
+/*
+ * Fold the fragment's last expected arrival (token-weighted delta) and take
+ * the outer Nesterov step (+ EMA) in the same pass: identical results, bit
+ * for bit, to dl_fold_checkpoint followed by dl_outer_nesterov, with one
+ * kernel launch instead of two.  The global is read once for both the delta
+ * and the update and the accumulator is not written back (acc's fragment
+ * range is unspecified afterwards): 12 bytes per element fewer than the two
+ * calls.  The token total used is the exact sum including this arrival.
+ *
+ * Arguments as in dl_fold_checkpoint and dl_outer_nesterov; `global` must be
+ * the pointer earlier folds of the fragment used.  ckpt must not overlap
+ * global, momentum or ema.
+ *
+ * Errors: those of both calls; nothing is launched and the handle is
+ * unchanged on any error but DL_E_HIP.
+ */
+int dl_fold_and_outer_nesterov(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
+                               const void *ckpt, int dtype, int64_t tokens, float *global,
+                               float *momentum, float lr, float mu, float *ema, float beta);
 
 /*
  * Stand-alone EMA of globals: ema[j] = beta*ema[j] + (1-beta)*global[j] for

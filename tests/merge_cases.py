@@ -92,8 +92,14 @@ def participants(w: synth.Workload, rnd: int, frag: int, exactly_quorum: bool) -
 
 
 def run_round(w: synth.Workload, st: State, rnd: int, exactly_quorum: bool = False,
-              orders: Optional[Sequence[Sequence[int]]] = None, stream=None) -> dict:
-    """One round on both sides.  Returns the GPU and oracle results (numpy)."""
+              orders: Optional[Sequence[Sequence[int]]] = None, stream=None,
+              fused_last: bool = False) -> dict:
+    """One round on both sides.  Returns the GPU and oracle results (numpy).
+
+    With `fused_last` the GPU folds each fragment's last arrival and closes
+    the fragment in one call (dl_fold_and_*); the oracle always folds and
+    closes in separate steps, so the comparison also checks that the fused
+    pass gives the same bits."""
     cks_gpu = worker_inputs(w, rnd, st.theta, st.g_theta.device)
     cks_np = {i: to_np(c) for i, c in cks_gpu.items()}
     offs = list(w.frag_offsets)
@@ -109,9 +115,15 @@ def run_round(w: synth.Workload, st: State, rnd: int, exactly_quorum: bool = Fal
         try:
             for f in range(w.n_frags):
                 o0, o1 = offs[f], offs[f + 1]
-                for i in orders[f]:
+                folds = list(orders[f][:-1]) if fused_last else list(orders[f])
+                for i in folds:
                     dl.dl_fold_checkpoint(r, f, i, tag, cks_gpu[i][o0:o1])
-                dl.dl_finalize_mean(r, f, st.g_theta, st.g_e, w.beta)
+                if fused_last:
+                    i = orders[f][-1]
+                    dl.dl_fold_and_finalize_mean(r, f, i, tag, cks_gpu[i][o0:o1], st.g_theta,
+                                                 st.g_e, w.beta)
+                else:
+                    dl.dl_finalize_mean(r, f, st.g_theta, st.g_e, w.beta)
             parts = [dl.dl_round_participants(r, f) for f in range(w.n_frags)]
         finally:
             dl.dl_round_end(r)
@@ -128,10 +140,16 @@ def run_round(w: synth.Workload, st: State, rnd: int, exactly_quorum: bool = Fal
         try:
             for f in range(w.n_frags):
                 o0, o1 = offs[f], offs[f + 1]
-                for i in orders[f]:
+                folds = list(orders[f][:-1]) if fused_last else list(orders[f])
+                for i in folds:
                     dl.dl_fold_checkpoint(r, f, i, tag, cks_gpu[i][o0:o1], st.g_theta, tokens[i])
+                if fused_last:
+                    i = orders[f][-1]
+                    dl.dl_fold_and_outer_nesterov(r, f, i, tag, cks_gpu[i][o0:o1], tokens[i],
+                                                  st.g_theta, st.g_m, w.lr, w.mu, st.g_e, w.beta)
+                else:
+                    dl.dl_outer_nesterov(r, f, st.g_theta, st.g_m, w.lr, w.mu, st.g_e, w.beta)
                 assert dl.dl_round_tokens(r, f) == sum(tokens[i] for i in orders[f])
-                dl.dl_outer_nesterov(r, f, st.g_theta, st.g_m, w.lr, w.mu, st.g_e, w.beta)
             parts = [dl.dl_round_participants(r, f) for f in range(w.n_frags)]
         finally:
             dl.dl_round_end(r)

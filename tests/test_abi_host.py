@@ -25,7 +25,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 12
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -126,6 +126,38 @@ def test_host_rules_delta_mode():
         dl.dl_round_end(r)
 
 
+def test_host_rules_fused_close():
+    g = FAKE + (1 << 24)
+    r = dl.dl_round_begin(3, dl.DL_MEAN, 1000, OFFS4, 2, 4, FAKE, stream=0)
+    try:
+        # one arrival short of the quorum even counting this one
+        _expect(dl.DL_E_QUORUM, dl.dl_fold_and_finalize_mean, r, 0, 1, 3, FAKE + (1 << 22), g,
+                dtype=dl.DL_F32)
+        _expect(dl.DL_E_STALE, dl.dl_fold_and_finalize_mean, r, 0, 1, 4, FAKE + (1 << 22), g,
+                dtype=dl.DL_F32)
+        _expect(dl.DL_E_STATE, dl.dl_fold_and_outer_nesterov, r, 0, 1, 3, FAKE + (1 << 22), 5, g,
+                g + (1 << 20), dtype=dl.DL_F32)
+        _expect(dl.DL_E_ALIGN, dl.dl_fold_and_finalize_mean, r, 0, 1, 3, FAKE + (1 << 22) + 2, g,
+                dtype=dl.DL_F32)
+        assert dl.dl_round_participants(r, 0) == []
+    finally:
+        dl.dl_round_end(r)
+    r = dl.dl_round_begin(3, dl.DL_DELTA_NESTEROV, 1000, OFFS4, 1, 4, FAKE, stream=0)
+    try:
+        ck = FAKE + (1 << 22)
+        _expect(dl.DL_E_STATE, dl.dl_fold_and_finalize_mean, r, 0, 1, 3, ck, g, dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_and_outer_nesterov, r, 0, 1, 3, ck, 0, g,
+                g + (1 << 20), dtype=dl.DL_F32)                      # no tokens
+        _expect(dl.DL_E_INVAL, dl.dl_fold_and_outer_nesterov, r, 0, 1, 3, ck, 5, g, g + 4,
+                dtype=dl.DL_F32)                                     # momentum overlaps global
+        _expect(dl.DL_E_INVAL, dl.dl_fold_and_outer_nesterov, r, 0, 1, 3, g + 8, 5, g,
+                g + (1 << 20), dtype=dl.DL_F32)                      # snapshot overlaps global
+        _expect(dl.DL_E_STALE, dl.dl_fold_and_outer_nesterov, r, 0, 1, 9, ck, 5, g,
+                g + (1 << 20), dtype=dl.DL_F32)
+    finally:
+        dl.dl_round_end(r)
+
+
 def test_ema_update_host_rules():
     dl.dl_ema_update(FAKE, FAKE + 4096, n=0, stream=0)                    # empty: no-op
     _expect(dl.DL_E_INVAL, dl.dl_ema_update, FAKE, FAKE + 4096, n=-1, stream=0)
@@ -182,7 +214,7 @@ def test_isa_has_no_contraction_and_ieee_division(tmp_path):
         assert c.get("v_rcp_f32_e32", 0) + c.get("v_rcp_f32_e64", 0) == fixups, name
         assert not [k for k in c if k.startswith(("v_pk_fma", "v_pk_mul_f32", "v_pk_add_f32",
                                                   "v_mad", "v_fmamk", "v_fmaak"))], name
-        if "fold" in name or "k_ema" in name:
-            assert fixups == 0, name
-        else:
+        if "Close" in name:
             assert fixups > 0, name      # the mean and Nesterov closes divide
+        else:
+            assert fixups == 0, name     # folds and the EMA do not

@@ -88,8 +88,10 @@ def test_full_size_sampled(key):
     gw = GpuWorkload(w)
     for r in range(ROUNDS):
         gw.generate_checkpoints(r)
-        say(f"[full] {key}: round {r}")
-        gw.run_round(r, tag=100 + r)
+        # round 0 closes with the fused last arrival (the benchmark's round),
+        # round 1 with a separate close
+        say(f"[full] {key}: round {r} fused_close={r == 0}")
+        gw.run_round(r, tag=100 + r, fused_close=(r == 0))
     torch.cuda.synchronize()
     wins = windows(w, 24, seed=w.seed)
     say(f"[full] {key}: oracle on {sum(L for fw in wins for _, L in fw)} sampled elements")
@@ -113,5 +115,5 @@ def test_full_size_every_element(key):
     st = mc.init_state(w)
     for r in range(3):
         say(f"[full] {key}: round {r}")
-        res = mc.run_round(w, st, r)
+        res = mc.run_round(w, st, r, fused_last=(r != 1))
         mc.assert_round_equal(res, f"{key} round {r}")

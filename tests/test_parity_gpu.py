@@ -27,12 +27,12 @@ def small(key, n, offsets=None):
     return synth.scaled(W[key], n, offsets)
 
 
-def run_rounds(w, rounds=3, exactly_quorum=False):
+def run_rounds(w, rounds=3, exactly_quorum=False, fused_last=False):
     st = mc.init_state(w)
     for r in range(rounds):
         say(f"[parity] {w.key} n={w.n_params} frags={w.frag_offsets} round {r}"
-            f" exactly_quorum={exactly_quorum}")
-        res = mc.run_round(w, st, r, exactly_quorum=exactly_quorum)
+            f" exactly_quorum={exactly_quorum} fused_last={fused_last}")
+        res = mc.run_round(w, st, r, exactly_quorum=exactly_quorum, fused_last=fused_last)
         mc.assert_round_equal(res, f"{w.key} n={w.n_params} round {r}")
     return st
 
@@ -50,17 +50,19 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_close", "fused_close"])
 @pytest.mark.parametrize("key,n,offs", CASES, ids=[f"{k}-{n}" for k, n, _ in CASES])
-def test_parity_small(key, n, offs):
-    run_rounds(small(key, n, offs))
+def test_parity_small(key, n, offs, fused):
+    run_rounds(small(key, n, offs), fused_last=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_close", "fused_close"])
 @pytest.mark.parametrize("key", ["pythia14m_frag_nesterov", "diffurefill1b_frag_nesterov_ema"])
-def test_parity_exactly_quorum(key):
+def test_parity_exactly_quorum(key, fused):
     """Rounds close with exactly the quorum (a seeded late worker misses
     each fragment's close), as in 10 of the 348 GradientMail rounds."""
     w = small(key, 300_017, [0, 80_000, 160_000, 240_000, 300_017])
-    run_rounds(w, rounds=2, exactly_quorum=True)
+    run_rounds(w, rounds=2, exactly_quorum=True, fused_last=fused)
 
 
 def test_parity_mean_in_fragments_and_quorum_one():
@@ -72,6 +74,21 @@ def test_parity_mean_in_fragments_and_quorum_one():
     orders = [[2], [0, 1, 2], [1, 0]]
     res = mc.run_round(w, st, 0, orders=orders)
     mc.assert_round_equal(res, "mean per fragment")
+    # the same with the last arrival fused into the close (the lone arrival of
+    # fragment 0 is then both the first fold and the close)
+    res = mc.run_round(w, st, 1, orders=orders, fused_last=True)
+    mc.assert_round_equal(res, "mean per fragment, fused close")
+
+
+def test_parity_nesterov_single_participant_fused():
+    """A fragment round with one participant (quorum 1), closed by the fused
+    call: its lone snapshot is both the first fold and the last."""
+    w = dataclasses.replace(small("diffurefill1b_frag_nesterov_ema", 60_001, [0, 30_000, 60_001]),
+                            quorum=1)
+    st = mc.init_state(w)
+    for r, orders in enumerate(([[3], [1, 4]], [[0, 2, 1], [2]])):
+        res = mc.run_round(w, st, r, orders=orders, fused_last=True)
+        mc.assert_round_equal(res, f"single participant, round {r}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8, 9, 1023, 1024, 1025, 4095, 4096, 4097,
@@ -80,6 +97,7 @@ def test_parity_edge_sizes(n):
     for key in ("diffurefill1b_bf16_mean_ema", "diffurefill1b_frag_nesterov_ema"):
         w = synth.scaled(W[key], n, [0, n])
         run_rounds(w, rounds=2)
+        run_rounds(w, rounds=2, fused_last=True)
 
 
 def test_arrival_order_decides_bits():
