@@ -9,15 +9,18 @@
 //  * 128-bit global accesses.  A lane moves one 4-element pack per stream
 //    (16 B of fp32, 8 B of bf16); consecutive lanes take consecutive packs, so
 //    each wavefront instruction reads or writes one dense 1 KiB span.
-//  * Several packs per lane (kUnroll), all loads issued before any store, so
-//    a lane keeps kUnroll x (streams) loads in flight to cover HBM latency.
+//  * Every load of a tile is issued before its first store; HBM latency is
+//    covered by many resident waves (one 1024-element tile per 256-lane
+//    workgroup, about a million workgroups at 1.08B elements) rather than by
+//    deep per-lane unrolling.
 //  * Non-temporal loads and stores for ranges too large to stay in the
 //    256 MB Infinity Cache; ordinary (cached) accesses for small ranges, where
 //    a fragment's accumulator can still be resident at the next fold.
-//  * Alternating direction: a pass may walk its tiles from the last to the
-//    first, so that consecutive passes over the same fragment meet where the
-//    previous one ended and find part of its data still cached.  Elements
-//    are independent, so the direction never changes a result.
+//  * Alternating direction: on non-temporal (large) ranges a pass may walk
+//    its tiles from the last to the first, so that consecutive passes over
+//    the same fragment meet where the previous one ended and find part of its
+//    data still cached.  Elements are independent, so the direction never
+//    changes a result.  Small, cache-resident ranges always walk forward.
 //  * No workgroup reuses another's data, so the block -> XCD round-robin
 //    placement needs no remapping; each block takes one contiguous tile.
 //  * The element arithmetic is written once, as scalar functions, and used by
@@ -45,7 +48,9 @@ namespace dlk {
 namespace {
 
 constexpr int kBlock = 256;     // 4 wave64 per workgroup
-constexpr int kUnroll = 4;      // packs per lane per tile
+constexpr int kUnroll = 1;      // packs per lane per tile (1 measured fastest: many short
+                                // workgroups keep more waves resident than deeper per-lane
+                                // unrolling; 2, 4 and 8 were 2-6% slower on MI355X)
 constexpr int kPack = 4;        // elements per pack
 constexpr int64_t kTile = int64_t(kBlock) * kUnroll;   // packs (or scalars) per block
 
@@ -361,17 +366,18 @@ struct Ema {                    // ema = beta*ema + omega*g
 
 // ---- the engine -----------------------------------------------------------------
 
-// 128-bit path.  Block b takes tile b (forward) or tile ntiles-1-b (backward);
-// lane l of a tile takes packs tile*kTile + k*kBlock + l, k < kUnroll.  The
-// fewer than kPack elements past the last whole pack are done by the first
-// lanes of the last block.
+// 128-bit path.  Traversal position q (blocks take q = blockIdx.x,
+// blockIdx.x + gridDim.x, ...) is tile q (forward) or tile ntiles-1-q
+// (backward); lane l of a tile takes packs tile*kTile + k*kBlock + l,
+// k < kUnroll.  The fewer than kPack elements past the last whole pack are
+// done by the first lanes of the last block.  The grid is capped (a launch
+// may hold at most 2^32 - 1 work-items), so very large ranges loop.
 template <class Op, bool NT>
 __global__ __launch_bounds__(kBlock) void k_stream(Op op, int64_t n, int backward) {
     const int64_t npacks = n / kPack;
     const int64_t ntiles = (npacks + kTile - 1) / kTile;
-    const int64_t pos = blockIdx.x;
-    if (pos < ntiles) {
-        const int64_t tile = backward ? ntiles - 1 - pos : pos;
+    for (int64_t q = blockIdx.x; q < ntiles; q += gridDim.x) {
+        const int64_t tile = backward ? ntiles - 1 - q : q;
         const int64_t p0 = tile * kTile + threadIdx.x;
         typename Op::Regs r[kUnroll];
 #pragma unroll
@@ -392,14 +398,17 @@ __global__ __launch_bounds__(kBlock) void k_stream(Op op, int64_t n, int backwar
 }
 
 // Scalar path (a pointer is not aligned for 128-bit access): one element per
-// lane and unroll step, same tiling.
+// lane and unroll step, same tiling and grid cap.
 template <class Op>
 __global__ __launch_bounds__(kBlock) void k_stream_scalar(Op op, int64_t n) {
-    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kTile + threadIdx.x;
+    const int64_t ntiles = (n + kTile - 1) / kTile;
+    for (int64_t q = blockIdx.x; q < ntiles; q += gridDim.x) {
+        const int64_t j0 = q * kTile + threadIdx.x;
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-        const int64_t j = j0 + k * kBlock;
-        if (j < n) op.scalar(j);
+        for (int k = 0; k < kUnroll; ++k) {
+            const int64_t j = j0 + k * kBlock;
+            if (j < n) op.scalar(j);
+        }
     }
 }
 
@@ -412,22 +421,28 @@ bool ckpt_aligned(const void* c, bool bf16) { return bf16 ? aligned8(c) : aligne
 // fragment's accumulator can stay in the 256 MB Infinity Cache between folds.
 constexpr int64_t kNontemporalMin = int64_t(1) << 24;
 
+// At most this many workgroups per launch (4M x 256 lanes = 2^30 work-items,
+// well inside the 2^32 - 1 a launch may hold); beyond 4M tiles blocks loop.
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;
+
+int64_t grid_blocks(int64_t tiles) {
+    if (tiles < 1) return 1;                     // the ragged tail still needs one block
+    return tiles < kMaxBlocks ? tiles : kMaxBlocks;
+}
+
 // Launches op over n elements: 128-bit path when `vec4`, else scalar.
 template <class Op>
 hipError_t launch(const Op& op, int64_t n, bool vec4, bool backward, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const dim3 block(kBlock);
     if (vec4) {
-        int64_t blocks = (n / kPack + kTile - 1) / kTile;
-        if (blocks < 1) blocks = 1;               // the ragged tail still needs one block
-        const dim3 grid(static_cast<unsigned>(blocks));
-        const int dir = backward ? 1 : 0;
+        const dim3 grid(static_cast<unsigned>(grid_blocks((n / kPack + kTile - 1) / kTile)));
         if (n >= kNontemporalMin)
-            hipLaunchKernelGGL((k_stream<Op, true>), grid, block, 0, s, op, n, dir);
+            hipLaunchKernelGGL((k_stream<Op, true>), grid, block, 0, s, op, n, backward ? 1 : 0);
         else
-            hipLaunchKernelGGL((k_stream<Op, false>), grid, block, 0, s, op, n, dir);
+            hipLaunchKernelGGL((k_stream<Op, false>), grid, block, 0, s, op, n, 0);
     } else {
-        const dim3 grid(static_cast<unsigned>((n + kTile - 1) / kTile));
+        const dim3 grid(static_cast<unsigned>(grid_blocks((n + kTile - 1) / kTile)));
         hipLaunchKernelGGL((k_stream_scalar<Op>), grid, block, 0, s, op, n);
     }
     return hipGetLastError();
