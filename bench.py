@@ -130,6 +130,51 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
     }
 
 
+def side_averages(args, torch):
+    """Times the side averages at the DiffuRefill-1B size: folding a global
+    into the uniform-average sum (12 B/param), the average itself
+    (8 B/param), and the one-pass averages of the last 3 and last 5
+    snapshots (16 and 24 B/param).  One JSON line."""
+    from checkpoint_averaging_amd import dlmerge as dl
+    from checkpoint_averaging_amd import synth
+    n = synth.DIFFUREFILL_1B.n_params
+    dev = torch.device("cuda")
+    th0 = synth.global0(1006, n, device=dev)
+    snaps = [synth.worker_checkpoint(1006, r, 0, th0) for r in range(5)]
+    del th0
+    acc = torch.empty(n, device=dev)
+    out = torch.empty(n, device=dev)
+    torch.cuda.synchronize()
+    cases = {
+        "swa_fold": (12, lambda i: dl.dl_swa_fold(acc, snaps[i % 5], 1 + i)),
+        "swa_average": (8, lambda i: dl.dl_swa_average(out, acc, 130)),
+        "snapshot_average_3": (16, lambda i: dl.dl_snapshot_average(out, snaps[:3])),
+        "snapshot_average_5": (24, lambda i: dl.dl_snapshot_average(out, snaps)),
+    }
+    res = {}
+    for name, (bpe, call) in cases.items():
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(args.steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call(i)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        res[name] = {"avg_ms": round(ms, 4), "bytes_per_param": bpe,
+                     "GB_per_s": round(bpe * n / (ms / 1e3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(bpe * n / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] {name}: {ms:.3f} ms")
+    print(json.dumps({"metric": "side averages of the globals: effective HBM GB/s",
+                      "n_params": n, "steps": args.steps, "warmup": args.warmup,
+                      "dtype": "f32", "data": "synthetic", "kernels": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +185,8 @@ def main():
     ap.add_argument("--separate-close", action="store_true",
                     help="close each fragment in its own pass after the last fold, instead of "
                          "folding the last arrival into the close")
+    ap.add_argument("--side-averages", action="store_true",
+                    help="time the uniform average and snapshot averages instead of a round")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")
@@ -156,6 +203,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.side_averages:
+        side_averages(args, torch)
+        return
     w = synth.WORKLOADS[args.workload]
     ab = algorithmic_bytes(w)
     log(f"[bench] {w.key}: {w.n_params:,} params, {w.workers} {w.ckpt_dtype} workers, "

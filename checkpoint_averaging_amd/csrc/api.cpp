@@ -382,6 +382,58 @@ int dl_ema_update(float* ema, const float* global, int64_t n, float beta, void* 
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 
+int dl_swa_fold(float* sum, const float* global, int64_t n, int64_t folded_before,
+                void* stream) {
+    if (n < 0 || folded_before < 0) return DL_E_INVAL;
+    if (n == 0) return DL_OK;
+    if (sum == nullptr || global == nullptr || n > INT64_MAX / 4) return DL_E_INVAL;
+    if (!aligned_to(sum, alignof(float)) || !aligned_to(global, alignof(float))) return DL_E_ALIGN;
+    if (span_of(sum, n * 4).overlaps(span_of(global, n * 4))) return DL_E_INVAL;
+    if (int st = check_device_span(sum, n * 4)) return st;
+    if (int st = check_device_span(global, n * 4)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_fold_sum(sum, global, false, n, folded_before == 0, false,
+                                                static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_swa_average(float* out, const float* sum, int64_t n, int64_t count, void* stream) {
+    if (n < 0 || count < 1) return DL_E_INVAL;
+    if (n == 0) return DL_OK;
+    if (out == nullptr || sum == nullptr || n > INT64_MAX / 4) return DL_E_INVAL;
+    if (!aligned_to(out, alignof(float)) || !aligned_to(sum, alignof(float))) return DL_E_ALIGN;
+    const Span out_s = span_of(out, n * 4), sum_s = span_of(sum, n * 4);
+    if (!out_s.same(sum_s) && out_s.overlaps(sum_s)) return DL_E_INVAL;
+    if (int st = check_device_span(out, n * 4)) return st;
+    if (int st = check_device_span(sum, n * 4)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_finalize_mean(out, sum, static_cast<float>(count), nullptr,
+                                                     0.0f, 0.0f, n, false,
+                                                     static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_snapshot_average(float* out, const float* const* snapshots, int k, int64_t n,
+                        void* stream) {
+    if (n < 0 || k < 1 || k > DL_MAX_SNAPSHOTS || snapshots == nullptr) return DL_E_INVAL;
+    if (n == 0) return DL_OK;
+    if (out == nullptr || n > INT64_MAX / 4) return DL_E_INVAL;
+    if (!aligned_to(out, alignof(float))) return DL_E_ALIGN;
+    const Span out_s = span_of(out, n * 4);
+    for (int i = 0; i < k; ++i) {
+        if (snapshots[i] == nullptr) return DL_E_INVAL;
+        if (!aligned_to(snapshots[i], alignof(float))) return DL_E_ALIGN;
+        if (span_of(snapshots[i], n * 4).overlaps(out_s)) return DL_E_INVAL;
+    }
+    if (int st = check_device_span(out, n * 4)) return st;
+    for (int i = 0; i < k; ++i)
+        if (int st = check_device_span(snapshots[i], n * 4)) return st;
+    (void)hipGetLastError();
+    const hipError_t err =
+        dlk::launch_snapshot_mean(out, snapshots, k, n, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
 int dl_frag_range(const dl_round* r, int frag, int64_t* offset, int64_t* length) {
     if (r == nullptr || offset == nullptr || length == nullptr) return DL_E_INVAL;
     if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;

@@ -45,6 +45,11 @@ hipError_t launch_fold_nesterov(float* theta, float* m, const float* acc, const 
                                 float* ema, float beta, float omega, int64_t n, bool backward,
                                 hipStream_t s);
 
+// out[j] = (((s_0[j] + s_1[j]) + ...) + s_{k-1}[j]) / k, 1 <= k <= 16, in one pass.
+// out must not overlap any snapshot.
+hipError_t launch_snapshot_mean(float* out, const float* const* snaps, int k, int64_t n,
+                               hipStream_t s);
+
 // ema[j] = beta*ema[j] + omega*g[j].
 hipError_t launch_ema(float* ema, const float* g, float beta, float omega, int64_t n,
                       hipStream_t s);

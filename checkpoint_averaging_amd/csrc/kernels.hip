@@ -346,6 +346,40 @@ struct FoldNesterovClose {
     }
 };
 
+// Mean of K snapshots read in one pass: S = s_0; S = S + s_i for i = 1..K-1
+// in the given order; out = S / K.  K is a template argument so each count
+// holds only the registers it reads (higher occupancy for small K).
+constexpr int kMaxSnapshots = 16;
+
+template <int K>
+struct SnapshotMean {
+    float* out;
+    const float* snap[K];
+    float count;
+    struct Regs { f32x4 s[K]; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+#pragma unroll
+        for (int i = 0; i < K; ++i) r.s[i] = ld4<NT>(snap[i], p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 g;
+#pragma unroll
+        for (int e = 0; e < kPack; ++e) {
+            float acc = r.s[0][e];
+#pragma unroll
+            for (int i = 1; i < K; ++i) acc = fold_sum(acc, r.s[i][e], false);
+            g[e] = acc / count;
+        }
+        st4<NT>(out, p, g);
+    }
+    __device__ void scalar(int64_t j) const {
+        float acc = snap[0][j];
+#pragma unroll
+        for (int i = 1; i < K; ++i) acc = fold_sum(acc, snap[i][j], false);
+        out[j] = acc / count;
+    }
+};
+
 struct Ema {                    // ema = beta*ema + omega*g
     float* ema;
     const float* g;
@@ -534,6 +568,38 @@ hipError_t launch_fold_nesterov(float* theta, float* m, const float* acc, const 
     if (ema) DLK_FNC(float, false, true);
     DLK_FNC(float, false, false);
 #undef DLK_FNC
+}
+
+namespace {
+
+template <int K>
+hipError_t launch_snapshot_mean_k(float* out, const float* const* snaps, int64_t n,
+                                  hipStream_t s) {
+    SnapshotMean<K> op{};
+    op.out = out;
+    op.count = static_cast<float>(K);
+    bool vec4 = aligned16(out);
+    for (int i = 0; i < K; ++i) {
+        op.snap[i] = snaps[i];
+        vec4 = vec4 && aligned16(snaps[i]);
+    }
+    return launch(op, n, vec4, false, s);
+}
+
+template <int K>
+hipError_t dispatch_snapshot_mean(int k, float* out, const float* const* snaps, int64_t n,
+                                  hipStream_t s) {
+    if (k == K) return launch_snapshot_mean_k<K>(out, snaps, n, s);
+    if constexpr (K < kMaxSnapshots) return dispatch_snapshot_mean<K + 1>(k, out, snaps, n, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_snapshot_mean(float* out, const float* const* snaps, int k, int64_t n,
+                               hipStream_t s) {
+    if (k < 1 || k > kMaxSnapshots) return hipErrorInvalidValue;
+    return dispatch_snapshot_mean<1>(k, out, snaps, n, s);
 }
 
 hipError_t launch_ema(float* ema, const float* g, float beta, float omega, int64_t n,

@@ -37,8 +37,10 @@ DL_E_CAPACITY = -8
 
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
-           "dl_ema_update", "dl_frag_range", "dl_round_participants", "dl_round_tokens",
+           "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
+           "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
+DL_MAX_SNAPSHOTS = 16
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m checkpoint_averaging_amd.build` "
@@ -56,6 +58,9 @@ _lib.dl_fold_and_finalize_mean.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _p, _
 _lib.dl_fold_and_outer_nesterov.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _i64, _p, _p, _f32,
                                             _f32, _p, _f32]
 _lib.dl_ema_update.argtypes = [_p, _p, _i64, _f32, _p]
+_lib.dl_swa_fold.argtypes = [_p, _p, _i64, _i64, _p]
+_lib.dl_swa_average.argtypes = [_p, _p, _i64, _i64, _p]
+_lib.dl_snapshot_average.argtypes = [_p, ctypes.POINTER(_p), _i32, _i64, _p]
 _lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dl_round_participants.argtypes = [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32]
 _lib.dl_round_tokens.argtypes = [_p, _i32, ctypes.POINTER(_i64)]
@@ -213,6 +218,36 @@ def dl_ema_update(ema: Array, global_: Array, beta: float = 0.9, n: Optional[int
     _check(_lib.dl_ema_update(_f32_addr(ema, "ema"), _f32_addr(global_, "global"), int(n),
                               float(beta), _stream(stream)),
            "dl_ema_update")
+
+
+def _n_of(a: Array, n: Optional[int]) -> int:
+    if n is not None:
+        return int(n)
+    if not isinstance(a, torch.Tensor):
+        raise TypeError("n is required for raw addresses")
+    return a.numel()
+
+
+def dl_swa_fold(sum_: Array, global_: Array, folded_before: int, n: Optional[int] = None,
+                stream=None) -> None:
+    _check(_lib.dl_swa_fold(_f32_addr(sum_, "sum"), _f32_addr(global_, "global"),
+                            _n_of(sum_, n), int(folded_before), _stream(stream)),
+           "dl_swa_fold")
+
+
+def dl_swa_average(out: Array, sum_: Array, count: int, n: Optional[int] = None,
+                   stream=None) -> None:
+    _check(_lib.dl_swa_average(_f32_addr(out, "out"), _f32_addr(sum_, "sum"), _n_of(out, n),
+                               int(count), _stream(stream)),
+           "dl_swa_average")
+
+
+def dl_snapshot_average(out: Array, snapshots: Sequence[Array], n: Optional[int] = None,
+                        stream=None) -> None:
+    ptrs = (_p * max(1, len(snapshots)))(*[_f32_addr(x, "snapshot") for x in snapshots])
+    _check(_lib.dl_snapshot_average(_f32_addr(out, "out"), ptrs, len(snapshots), _n_of(out, n),
+                                    _stream(stream)),
+           "dl_snapshot_average")
 
 
 def dl_frag_range(r: Round, frag: int) -> Tuple[int, int]:

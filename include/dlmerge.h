@@ -246,6 +246,47 @@ int dl_fold_and_outer_nesterov(dl_round *r, int frag, int worker_id, uint64_t ck
  */
 int dl_ema_update(float *ema, const float *global, int64_t n, float beta, void *stream);
 
+/*
+ * Side averages of the globals (technical report, "Training system", Table 2,
+ * row "Side averages": besides the EMA, the merger keeps a uniform average
+ * (SWA) of the globals and periodic snapshots in the final stretch; section
+ * "Data and schedule": the released weights are the uniform average of the
+ * 130 globals merged from step ~181k to 200k; section "The final stretch",
+ * Table 5: averages of the last 3 and the last 5 snapshots).  These calls
+ * keep no state: the caller owns the running sum and its count (so the
+ * average survives a restart of the merger) and orders the calls on stream.
+ */
+
+/*
+ * Fold one committed global into the uniform-average running fp32 sum, in
+ * commit order: sum[j] = global[j] if folded_before == 0, else
+ * sum[j] + global[j].  n = 0 is a no-op.  sum and global must not overlap.
+ * Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_swa_fold(float *sum, const float *global, int64_t n, int64_t folded_before,
+                void *stream);
+
+/*
+ * out[j] = sum[j] / count (IEEE division; count rounded once to binary32),
+ * count >= 1 the number of globals folded.  out may be sum (in place),
+ * otherwise must not overlap it.  Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_swa_average(float *out, const float *sum, int64_t n, int64_t count, void *stream);
+
+/* Most snapshots dl_snapshot_average reads in one pass. */
+#define DL_MAX_SNAPSHOTS 16
+
+/*
+ * Mean of k snapshots in one pass, summed in the order given (oldest first):
+ * out[j] = (((s_0[j] + s_1[j]) + ...) + s_{k-1}[j]) / k in binary32, the same
+ * bits as folding them one by one into a running sum and dividing.
+ * snapshots: host array of k device pointers (n fp32 each), 1 <= k <=
+ * DL_MAX_SNAPSHOTS.  out must not overlap any snapshot.  n = 0 is a no-op.
+ * Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_snapshot_average(float *out, const float *const *snapshots, int k, int64_t n,
+                        void *stream);
+
 /* Element range [offset, offset + length) of fragment frag.  DL_E_INVAL. */
 int dl_frag_range(const dl_round *r, int frag, int64_t *offset, int64_t *length);
 

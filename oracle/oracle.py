@@ -142,6 +142,21 @@ class Oracle:
         self.outer_nesterov(theta, m, acc, sum(int(t) for t in tokens_in_arrival_order),
                             lr, mu, ema, beta)
 
+    # -- side averages (technical report, "Training system", Table 2, row
+    # "Side averages"; "Data and schedule": the released weights are the
+    # uniform average of the globals merged over the final stretch; "The
+    # final stretch", Table 5: averages of the last 3 and 5 snapshots) -----
+
+    def swa_average(self, globals_in_commit_order: Sequence[np.ndarray]) -> np.ndarray:
+        """Uniform average of globals: a plain mean, the globals folded into a
+        running fp32 sum in the order they were committed."""
+        return self.mean_round(globals_in_commit_order)
+
+    def snapshot_average(self, snapshots_oldest_first: Sequence[np.ndarray]) -> np.ndarray:
+        """Average of the last k snapshots: their plain mean, summed oldest
+        first."""
+        return self.mean_round(snapshots_oldest_first)
+
 
 _default: Optional[Oracle] = None
 
@@ -183,6 +198,14 @@ def mean_round(*a, **k):
 
 def nesterov_fragment_round(*a, **k):
     return load().nesterov_fragment_round(*a, **k)
+
+
+def swa_average(*a, **k):
+    return load().swa_average(*a, **k)
+
+
+def snapshot_average(*a, **k):
+    return load().snapshot_average(*a, **k)
 
 
 def threads() -> int:

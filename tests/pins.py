@@ -474,4 +474,22 @@ def pin_delta_sign_and_weights(orc):
     assert_bits_equal(acc, [2.0, -2.0, 0.0, -8 * 2.0 ** -10], "second arrival adds")
 
 
+def pin_uniform_average_of_130_globals(orc):
+    """The released weights are the uniform average of 130 globals (technical
+    report, "Data and schedule").  Dyadic globals with 14 fraction bits keep
+    every partial sum of 130 of them exact in binary32, so the average must be
+    the correctly rounded rational mean; the last-3 and last-5 snapshot
+    averages (Table 5) likewise."""
+    rng = np.random.default_rng(116)
+    n = 128
+    gs = [dyadic(rng, n, frac_bits=14) for _ in range(130)]
+    got = orc.swa_average(gs)
+    want = [f32_rne(sum(Fraction(float(g[j])) for g in gs) / 130) for j in range(n)]
+    assert_bits_equal(got, want, "uniform average of 130 globals")
+    for k in (3, 5):
+        got = orc.snapshot_average(gs[-k:])
+        want = [f32_rne(sum(Fraction(float(g[j])) for g in gs[-k:]) / k) for j in range(n)]
+        assert_bits_equal(got, want, f"average of the last {k} snapshots")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 15
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -166,6 +166,25 @@ def test_ema_update_host_rules():
     _expect(dl.DL_E_INVAL, dl.dl_ema_update, FAKE, FAKE + 8, n=4, stream=0)  # overlap
 
 
+def test_side_average_host_rules():
+    dl.dl_swa_fold(FAKE, FAKE + 4096, 0, n=0, stream=0)                   # empty: no-op
+    _expect(dl.DL_E_INVAL, dl.dl_swa_fold, FAKE, FAKE + 4096, -1, n=4, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_swa_fold, FAKE, FAKE + 8, 0, n=4, stream=0)   # overlap
+    _expect(dl.DL_E_ALIGN, dl.dl_swa_fold, FAKE + 1, FAKE + 4096, 0, n=4, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_swa_average, FAKE, FAKE + 4096, 0, n=4, stream=0)  # count 0
+    _expect(dl.DL_E_INVAL, dl.dl_swa_average, FAKE, FAKE + 4, 3, n=4, stream=0)     # partial
+    _expect(dl.DL_E_INVAL, dl.dl_snapshot_average, FAKE, [], n=4, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_snapshot_average, FAKE, [FAKE + 4096 * (i + 1) for i in range(17)],
+            n=4, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_snapshot_average, FAKE, [FAKE + 4096, FAKE + 8], n=4,
+            stream=0)                                                     # overlaps out
+    _expect(dl.DL_E_ALIGN, dl.dl_snapshot_average, FAKE, [FAKE + 4096, FAKE + 8194], n=4,
+            stream=0)
+    dl.dl_snapshot_average(FAKE, [FAKE + 4096], n=0, stream=0)            # empty: no-op
+    assert dl.DL_MAX_SNAPSHOTS == int(re.search(r"#define DL_MAX_SNAPSHOTS (\d+)",
+                                                open(HEADER).read()).group(1))
+
+
 def test_participants_capacity():
     lib = dl.raw_lib()
     import ctypes
@@ -214,7 +233,7 @@ def test_isa_has_no_contraction_and_ieee_division(tmp_path):
         assert c.get("v_rcp_f32_e32", 0) + c.get("v_rcp_f32_e64", 0) == fixups, name
         assert not [k for k in c if k.startswith(("v_pk_fma", "v_pk_mul_f32", "v_pk_add_f32",
                                                   "v_mad", "v_fmamk", "v_fmaak"))], name
-        if "Close" in name:
-            assert fixups > 0, name      # the mean and Nesterov closes divide
+        if "Close" in name or "SnapshotMean" in name:
+            assert fixups > 0, name      # the means and the Nesterov closes divide
         else:
             assert fixups == 0, name     # folds and the EMA do not

@@ -1,0 +1,78 @@
+"""GPU parity of the side averages (uniform average of globals, averages of
+the last k snapshots) against the CPU oracle, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from checkpoint_averaging_amd import dlmerge as dl
+from checkpoint_averaging_amd import synth
+from tests import merge_cases as mc
+
+pytestmark = pytest.mark.gpu
+
+
+def globals_series(n, count, seed=1006):
+    """A series of nearby globals from the seeded generator (stand-ins for
+    the globals a run commits one after another)."""
+    th0 = synth.global0(seed, n, device="cuda")
+    return [synth.worker_checkpoint(seed, r, 0, th0) for r in range(count)]
+
+
+@pytest.mark.parametrize("n", [1, 5, 4096 * 3 + 2, 1 << 20])
+def test_swa_matches_oracle(n):
+    gs = globals_series(n, 13)
+    s = torch.full((n,), float("nan"), device="cuda")
+    for k, g in enumerate(gs):
+        dl.dl_swa_fold(s, g, k)
+    out = torch.empty(n, device="cuda")
+    dl.dl_swa_average(out, s, len(gs))
+    dl.dl_swa_average(s, s, len(gs))                     # in place
+    torch.cuda.synchronize()
+    want = oracle.swa_average([mc.to_np(g) for g in gs])
+    assert mc.bits_equal(mc.to_np(out), want), mc.first_mismatch(mc.to_np(out), want)
+    assert mc.bits_equal(mc.to_np(s), want)
+
+
+def test_swa_of_130_globals():
+    n = 300_007
+    gs = globals_series(n, 130)
+    s = torch.empty(n, device="cuda")
+    for k, g in enumerate(gs):
+        dl.dl_swa_fold(s, g, k)
+    dl.dl_swa_average(s, s, 130)
+    torch.cuda.synchronize()
+    want = oracle.swa_average([mc.to_np(g) for g in gs])
+    assert mc.bits_equal(mc.to_np(s), want), mc.first_mismatch(mc.to_np(s), want)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("n", [3, 4096 * 5 + 3, 1 << 20])
+def test_snapshot_average_matches_oracle(k, n):
+    snaps = globals_series(n, k)
+    out = torch.empty(n, device="cuda")
+    dl.dl_snapshot_average(out, snaps)
+    torch.cuda.synchronize()
+    want = oracle.snapshot_average([mc.to_np(x) for x in snaps])
+    assert mc.bits_equal(mc.to_np(out), want), mc.first_mismatch(mc.to_np(out), want)
+
+
+def test_snapshot_average_scalar_path_and_order():
+    """A snapshot at a 4-byte offset runs the scalar path; the order of the
+    snapshots is the summation order (reversing it changes some bits)."""
+    n = 100_003
+    snaps = globals_series(n, 5)
+    shifted = torch.empty(n + 1, device="cuda")
+    shifted[1:] = snaps[2]
+    ptrs = [snaps[0], snaps[1], shifted.data_ptr() + 4, snaps[3], snaps[4]]
+    out = torch.empty(n, device="cuda")
+    dl.dl_snapshot_average(out, ptrs)
+    rev = torch.empty(n, device="cuda")
+    dl.dl_snapshot_average(rev, list(reversed(snaps)))
+    torch.cuda.synchronize()
+    host = [mc.to_np(x) for x in snaps]
+    want = oracle.snapshot_average(host)
+    assert mc.bits_equal(mc.to_np(out), want), mc.first_mismatch(mc.to_np(out), want)
+    want_rev = oracle.snapshot_average(host[::-1])
+    assert mc.bits_equal(mc.to_np(rev), want_rev)
+    assert not mc.bits_equal(want, want_rev)
