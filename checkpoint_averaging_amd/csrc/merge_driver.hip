@@ -7,12 +7,15 @@
 //   dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
 //                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
+//                  [--streams S]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
 // folded (token-weighted delta in delta mode) and the fragment is closed
 // (mean, or outer Nesterov lr 0.7 / momentum 0.9), with the EMA (beta 0.9)
 // fused in when enabled.  With --fused 1 (default) the last worker is folded
-// in the same pass as the close.  Buffer contents are a deterministic pattern; the
+// in the same pass as the close.  With --streams S > 1 every fragment's round
+// is its own handle on one of S streams (rounds in flight together), the
+// arrivals issued round-robin across fragments.  Buffer contents are a deterministic pattern; the
 // timing does not depend on them.
 #include <hip/hip_runtime.h>
 
@@ -93,13 +96,14 @@ struct Args {
     int warmup = 1;
     int copy_mib = 0;
     bool fused = true;
+    int streams = 1;
 };
 
 [[noreturn]] void usage() {
     std::fprintf(stderr,
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
-                 "       [--warmup R0] [--copy-mib M] [--fused 0|1]\n");
+                 "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n");
     std::exit(2);
 }
 
@@ -126,9 +130,12 @@ Args parse(int argc, char** argv) {
         else if (k == "--warmup") a.warmup = std::atoi(v.c_str());
         else if (k == "--copy-mib") a.copy_mib = std::atoi(v.c_str());
         else if (k == "--fused") a.fused = std::atoi(v.c_str()) != 0;
+        else if (k == "--streams") a.streams = std::atoi(v.c_str());
         else usage();
     }
-    if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0) usage();
+    if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0 || a.streams < 1 ||
+        a.streams > 16)
+        usage();
     if (a.offsets.empty()) a.offsets = {0, a.n};
     return a;
 }
@@ -181,37 +188,55 @@ int main(int argc, char** argv) {
     hipEvent_t e0, e1;
     HIPCHECK(hipEventCreate(&e0));
     HIPCHECK(hipEventCreate(&e1));
+    // extra streams for --streams: each waits for s at the start of a round,
+    // and s waits for each at its end
+    std::vector<hipStream_t> fs(a.streams, s);
+    std::vector<hipEvent_t> joins(a.streams);
+    for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamCreate(&fs[i]));
+    for (auto& ev : joins) HIPCHECK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    const int dt = a.bf16 ? DL_BF16 : DL_F32;
+    const int64_t esz = a.bf16 ? 2 : 4;
     for (int r = 0; r < a.warmup + a.rounds; ++r) {
         if (r == a.warmup) HIPCHECK(hipEventRecord(e0, s));
-        dl_round* rd = nullptr;
         const uint64_t tag = uint64_t(r) + 1;
-        DLCHECK(dl_round_begin(&rd, tag, a.delta ? DL_DELTA_NESTEROV : DL_MEAN, a.n, n_frags,
-                               a.offsets.data(), 1, a.workers, acc, s));
-        const int dt = a.bf16 ? DL_BF16 : DL_F32;
-        for (int f = 0; f < n_frags; ++f) {
-            const int64_t off = a.offsets[f];
-            const int folds = a.fused ? a.workers - 1 : a.workers;
-            for (int i = 0; i < folds; ++i) {
-                const char* base = static_cast<const char*>(ck[i]) + off * (a.bf16 ? 2 : 4);
-                DLCHECK(dl_fold_checkpoint(rd, f, i, tag, base, dt, a.delta ? theta : nullptr,
-                                           19660800 + 1000 * int64_t(i)));
-            }
-            if (a.fused) {
-                const int i = a.workers - 1;
-                const char* base = static_cast<const char*>(ck[i]) + off * (a.bf16 ? 2 : 4);
-                if (a.delta)
-                    DLCHECK(dl_fold_and_outer_nesterov(rd, f, i, tag, base, dt,
-                                                       19660800 + 1000 * int64_t(i), theta, m,
-                                                       0.7f, 0.9f, e, 0.9f));
-                else
-                    DLCHECK(dl_fold_and_finalize_mean(rd, f, i, tag, base, dt, theta, e, 0.9f));
-            } else if (a.delta) {
-                DLCHECK(dl_outer_nesterov(rd, f, theta, m, 0.7f, 0.9f, e, 0.9f));
-            } else {
-                DLCHECK(dl_finalize_mean(rd, f, theta, e, 0.9f));
+        HIPCHECK(hipEventRecord(joins[0], s));
+        for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamWaitEvent(fs[i], joins[0], 0));
+        std::vector<dl_round*> rd(a.streams > 1 ? n_frags : 1, nullptr);
+        for (size_t h = 0; h < rd.size(); ++h)
+            DLCHECK(dl_round_begin(&rd[h], tag, a.delta ? DL_DELTA_NESTEROV : DL_MEAN, a.n, n_frags,
+                                   a.offsets.data(), 1, a.workers, acc,
+                                   fs[h % a.streams]));
+        // One stream: one handle, fragment after fragment (as the benchmark
+        // issues a round).  Several streams: one handle per fragment, the
+        // arrivals round-robin across fragments.
+        for (int step = 0; step < a.workers * n_frags; ++step) {
+            const int f = a.streams > 1 ? step % n_frags : step / a.workers;
+            const int i = a.streams > 1 ? step / n_frags : step % a.workers;
+            {
+                dl_round* h = rd[a.streams > 1 ? f : 0];
+                const char* base = static_cast<const char*>(ck[i]) + a.offsets[f] * esz;
+                const int64_t tok = 19660800 + 1000 * int64_t(i);
+                const bool last = i == a.workers - 1;
+                if (last && a.fused) {
+                    if (a.delta)
+                        DLCHECK(dl_fold_and_outer_nesterov(h, f, i, tag, base, dt, tok, theta, m,
+                                                           0.7f, 0.9f, e, 0.9f));
+                    else
+                        DLCHECK(dl_fold_and_finalize_mean(h, f, i, tag, base, dt, theta, e, 0.9f));
+                    continue;
+                }
+                DLCHECK(dl_fold_checkpoint(h, f, i, tag, base, dt, a.delta ? theta : nullptr, tok));
+                if (last) {
+                    if (a.delta) DLCHECK(dl_outer_nesterov(h, f, theta, m, 0.7f, 0.9f, e, 0.9f));
+                    else DLCHECK(dl_finalize_mean(h, f, theta, e, 0.9f));
+                }
             }
         }
-        DLCHECK(dl_round_end(rd));
+        for (auto h : rd) DLCHECK(dl_round_end(h));
+        for (int i = 1; i < a.streams; ++i) {
+            HIPCHECK(hipEventRecord(joins[i], fs[i]));
+            HIPCHECK(hipStreamWaitEvent(s, joins[i], 0));
+        }
     }
     HIPCHECK(hipEventRecord(e1, s));
     HIPCHECK(hipEventSynchronize(e1));
@@ -221,6 +246,8 @@ int main(int argc, char** argv) {
         std::printf("%d rounds: %.4f ms per round\n", a.rounds, ms / a.rounds);
     }
 
+    for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamDestroy(fs[i]));
+    for (auto ev : joins) HIPCHECK(hipEventDestroy(ev));
     for (auto p : ck) HIPCHECK(hipFree(p));
     HIPCHECK(hipFree(theta));
     HIPCHECK(hipFree(acc));

@@ -62,13 +62,23 @@ class GpuWorkload:
 
     def run_round(self, rnd: int, tag: int,
                   timer: Optional[Callable[[str, int, Callable[[], None]], None]] = None,
-                  fused_close: bool = True) -> None:
+                  fused_close: bool = True,
+                  streams: Optional[List[torch.cuda.Stream]] = None) -> None:
         """Issue one merge round.  `timer(kind, elements, call)` (if given)
         wraps every kernel-launching call, e.g. to record events around it.
 
         With `fused_close`, the fragment's last expected arrival is folded and
         the fragment closed in one pass (the merger closes as soon as every
-        worker of the round is in); otherwise the close is a separate pass."""
+        worker of the round is in); otherwise the close is a separate pass.
+
+        With `streams`, every fragment's round is its own handle on its own
+        stream (fragment f on streams[f % len(streams)]), so the fragments'
+        rounds are in flight together; they touch disjoint element ranges.
+        The streams wait for the caller's stream first and the caller's
+        stream waits for all of them at the end."""
+        if streams:
+            self._run_round_streams(rnd, tag, timer, fused_close, streams)
+            return
         w = self.w
         offs = list(w.frag_offsets)
         orders = self.orders(rnd)
@@ -124,6 +134,69 @@ class GpuWorkload:
                                                              w.mu, self.e, w.beta))
             finally:
                 dl.dl_round_end(r)
+
+
+    def _run_round_streams(self, rnd, tag, timer, fused_close, streams):
+        w = self.w
+        offs = list(w.frag_offsets)
+        orders = self.orders(rnd)
+        tok = self.tokens(rnd)
+        run = timer if timer is not None else (lambda kind, n, call: call())
+        ema = "_ema" if self.e is not None else ""
+        cur = torch.cuda.current_stream()
+        start = torch.cuda.Event()
+        start.record(cur)
+        mode = dl.DL_DELTA_NESTEROV if self.delta else dl.DL_MEAN
+        handles = []
+        try:
+            for f in range(w.n_frags):
+                st = streams[f % len(streams)]
+                st.wait_event(start)
+                handles.append(dl.dl_round_begin(tag, mode, w.n_params, offs, w.quorum,
+                                                 w.workers, self.acc, stream=st))
+            # issue arrivals round-robin across fragments, as they would come
+            for k in range(w.workers):
+                for f in range(w.n_frags):
+                    st = streams[f % len(streams)]
+                    r = handles[f]
+                    o0, o1 = offs[f], offs[f + 1]
+                    i = orders[f][k]
+                    ck = self.ckpts[i][o0:o1]
+                    last = k == w.workers - 1
+                    with torch.cuda.stream(st):
+                        if not self.delta:
+                            if last and fused_close:
+                                kind = "fold_finalize_mean" + ema + ("_first" if k == 0 else "")
+                                run(kind, o1 - o0, lambda: dl.dl_fold_and_finalize_mean(
+                                    r, f, i, tag, ck, self.theta, self.e, w.beta))
+                            else:
+                                run("fold_first" if k == 0 else "fold", o1 - o0,
+                                    lambda: dl.dl_fold_checkpoint(r, f, i, tag, ck))
+                                if last:
+                                    run("finalize_mean" + ema, o1 - o0,
+                                        lambda: dl.dl_finalize_mean(r, f, self.theta, self.e,
+                                                                    w.beta))
+                        else:
+                            if last and fused_close:
+                                kind = "fold_nesterov" + ema + ("_first" if k == 0 else "")
+                                run(kind, o1 - o0, lambda: dl.dl_fold_and_outer_nesterov(
+                                    r, f, i, tag, ck, tok[i], self.theta, self.m, w.lr, w.mu,
+                                    self.e, w.beta))
+                            else:
+                                run("fold_delta_first" if k == 0 else "fold_delta", o1 - o0,
+                                    lambda: dl.dl_fold_checkpoint(r, f, i, tag, ck, self.theta,
+                                                                  tok[i]))
+                                if last:
+                                    run("nesterov" + ema, o1 - o0,
+                                        lambda: dl.dl_outer_nesterov(r, f, self.theta, self.m,
+                                                                     w.lr, w.mu, self.e, w.beta))
+        finally:
+            for r in handles:
+                dl.dl_round_end(r)
+        for st in streams:
+            done = torch.cuda.Event()
+            done.record(st)
+            cur.wait_event(done)
 
 
 def algorithmic_bytes(w: synth.Workload, fused_close: bool = False) -> Dict[str, int]:
