@@ -1,11 +1,13 @@
 """Parity at the full sizes of the five merge workloads, in the launch
 configuration the benchmark times (checkpoint_averaging_amd.workload).
 
-The 14M-parameter workloads are compared over every element.  The
-1.08B-parameter workloads are compared on sampled windows: the merge is
-elementwise, so the oracle recomputes any window on its own from inputs the
-seeded generator regenerates on the CPU for just that window.  Windows cover
-the first and last elements of every fragment plus random positions."""
+Every element is compared for all five workloads (for the 1.08B ones the
+generator's GPU-made inputs are copied to host memory and the oracle runs the
+whole rounds).  The 1.08B workloads are also compared on sampled windows with
+inputs the seeded generator regenerates on the CPU for just those windows (the
+merge is elementwise, so the oracle recomputes any window on its own); the
+windows cover the first and last elements of every fragment plus random
+positions."""
 import sys
 
 import numpy as np
@@ -105,6 +107,53 @@ def test_full_size_sampled(key):
         for k, g in got.items():
             o = want[f][k]
             assert mc.bits_equal(g, o), f"{key} frag {f} {k}: {mc.first_mismatch(g, o)}"
+    del gw
+    torch.cuda.empty_cache()
+
+
+def _oracle_full_round(w, r, cks, theta, m, e):
+    """The oracle's round r over whole arrays (host copies of the inputs)."""
+    orc = oracle.load()
+    tok = synth.token_counts(w, r)
+    for f in range(w.n_frags):
+        o0, o1 = w.frag_offsets[f], w.frag_offsets[f + 1]
+        order = synth.arrival_order(w, r, f)
+        parts = [np.ascontiguousarray(cks[i][o0:o1]) for i in order]
+        if w.mode == "mean":
+            theta[o0:o1] = orc.mean_round(parts, None if e is None else e[o0:o1], w.beta)
+        else:
+            orc.nesterov_fragment_round(theta[o0:o1], m[o0:o1], parts, [tok[i] for i in order],
+                                        w.lr, w.mu, None if e is None else e[o0:o1], w.beta)
+
+
+@pytest.mark.parametrize("key", ["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
+                                 "diffurefill1b_frag_nesterov_ema"])
+def test_full_size_1b_every_element(key):
+    """Every element of the 1.08B rounds, in the benchmark's launch
+    configuration: the inputs the generator made on the GPU are copied to
+    host memory and the oracle runs the same rounds over whole arrays."""
+    w = synth.WORKLOADS[key]
+    say(f"[full-all] {key}: allocating and generating")
+    gw = GpuWorkload(w)
+    theta = mc.to_np(gw.theta)
+    m = np.zeros_like(theta) if gw.m is not None else None
+    e = theta.copy() if gw.e is not None else None
+    for r in range(ROUNDS):
+        gw.generate_checkpoints(r)
+        say(f"[full-all] {key}: round {r} fused_close={r == 0}")
+        gw.run_round(r, tag=200 + r, fused_close=(r == 0))
+        cks = [mc.to_np(c) for c in gw.ckpts]
+        say(f"[full-all] {key}: oracle round {r}")
+        _oracle_full_round(w, r, cks, theta, m, e)
+        del cks
+        got = {"theta": (mc.to_np(gw.theta), theta)}
+        if m is not None:
+            got["m"] = (mc.to_np(gw.m), m)
+        if e is not None:
+            got["e"] = (mc.to_np(gw.e), e)
+        for k, (g, o) in got.items():
+            assert mc.bits_equal(g, o), f"{key} round {r} {k}: {mc.first_mismatch(g, o)}"
+        del got
     del gw
     torch.cuda.empty_cache()
 
