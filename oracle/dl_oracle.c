@@ -168,6 +168,26 @@ void oracle_ema(float *ema, const float *g, int64_t n, float beta)
         ema[j] = beta * ema[j] + one_minus_beta * g[j];
 }
 
+/*
+ * Keep-local-drift adoption on a worker (DiffuRefill-1B technical report,
+ * section "What we measured", "Distributed optimisation": instead of
+ * replacing its weights by the new global g, a worker keeps the progress it
+ * made since its push; model card, "What the run taught").  With theta the
+ * worker's current weights and pushed the checkpoint it pushed:
+ *     theta[j] = theta[j] + (g[j] - pushed[j])
+ * the difference formed first, then added (two roundings).  pushed is fp32
+ * or bf16 (widened exactly).
+ */
+void oracle_adopt_keep_drift(float *theta, const float *g, const void *pushed, int dtype,
+                             int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) {
+        float shift = g[j] - oracle_ckpt_value(pushed, dtype, j);
+        theta[j] = theta[j] + shift;
+    }
+}
+
 /* Number of threads an OpenMP loop here would use (1 without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -50,10 +50,12 @@ class Oracle:
         lib.oracle_fold_delta.argtypes = [p, p, p, i32, i64, i64, i32]
         lib.oracle_outer_nesterov.argtypes = [p, p, p, i64, i64, f32, f32, p, f32]
         lib.oracle_ema.argtypes = [p, p, i64, f32]
+        lib.oracle_adopt_keep_drift.argtypes = [p, p, p, i32, i64]
         lib.oracle_threads.restype = i32
         lib.oracle_set_threads.argtypes = [i32]
         for name in ("oracle_fold_mean", "oracle_finalize_mean", "oracle_fold_delta",
-                     "oracle_outer_nesterov", "oracle_ema", "oracle_set_threads"):
+                     "oracle_outer_nesterov", "oracle_ema", "oracle_adopt_keep_drift",
+                     "oracle_set_threads"):
             getattr(lib, name).restype = None
         self.lib = lib
         self.path = path
@@ -103,6 +105,14 @@ class Oracle:
         if ema.size != g.size:
             raise ValueError("size mismatch")
         self.lib.oracle_ema(_ptr(ema), _ptr(g), ema.size, float(beta))
+
+    def adopt_keep_drift(self, theta: np.ndarray, g: np.ndarray, pushed: np.ndarray) -> None:
+        """Worker-side adoption that keeps local drift: theta += (g - pushed)."""
+        _f32(theta, "theta"), _f32(g, "g")
+        if g.size != theta.size or pushed.size != theta.size:
+            raise ValueError("size mismatch")
+        self.lib.oracle_adopt_keep_drift(_ptr(theta), _ptr(g), _ptr(pushed), _ckpt_dtype(pushed),
+                                         theta.size)
 
     def threads(self) -> int:
         return int(self.lib.oracle_threads())
@@ -202,6 +212,10 @@ def nesterov_fragment_round(*a, **k):
 
 def swa_average(*a, **k):
     return load().swa_average(*a, **k)
+
+
+def adopt_keep_drift(*a, **k):
+    return load().adopt_keep_drift(*a, **k)
 
 
 def snapshot_average(*a, **k):

@@ -492,4 +492,36 @@ def pin_uniform_average_of_130_globals(orc):
         assert_bits_equal(got, want, f"average of the last {k} snapshots")
 
 
+def pin_adopt_keep_drift(orc):
+    """Keep-local-drift adoption theta + (g - pushed) (technical report,
+    "Distributed optimisation"): exact on dyadic data; a worker that made no
+    progress since its push (theta == pushed) lands exactly on the global
+    when the difference is exact (Sterbenz range); plain replacement is the
+    other policy and is not this function."""
+    rng = np.random.default_rng(117)
+    n = 2048
+    theta, g, pushed = (dyadic(rng, n, frac_bits=12) for _ in range(3))
+    th = theta.copy()
+    orc.adopt_keep_drift(th, g, pushed)
+    want = [f32_rne(Fraction(float(t)) + (Fraction(float(a)) - Fraction(float(b))))
+            for t, a, b in zip(theta, g, pushed)]
+    assert_bits_equal(th, want, "theta + (g - pushed)")
+    # no progress since the push: the worker takes the global
+    x = (1.0 + rng.random(n)).astype(np.float32)
+    gg = (x * np.float32(1.5)).astype(np.float32)        # within a factor 2: exact difference
+    th = x.copy()
+    orc.adopt_keep_drift(th, gg, x.copy())
+    assert_bits_equal(th, gg, "no progress -> global")
+    # bf16 pushed checkpoints are widened exactly
+    import torch
+    pb = torch.from_numpy(pushed).to(torch.bfloat16)
+    pbits = pb.view(torch.int16).numpy().view(np.uint16).copy()
+    th = theta.copy()
+    orc.adopt_keep_drift(th, g, pbits)
+    wid = pb.float().numpy()
+    want = [f32_rne(Fraction(float(t)) + (Fraction(float(a)) - Fraction(float(b))))
+            for t, a, b in zip(theta, g, wid)]
+    assert_bits_equal(th, want, "bf16 pushed")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -46,6 +46,9 @@ MUTANTS = [
      "if (ema)\n            ema[j] = beta * ema[j] + one_minus_beta * theta[j];\n        theta[j] = theta_new;"),
     ("nesterov_momentum_not_stored", "m[j] = m_new;", "m[j] = m[j];"),
     ("bf16_wrong_shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    ("adopt_sign_flipped", "float shift = g[j] - oracle_ckpt_value(pushed, dtype, j);",
+     "float shift = oracle_ckpt_value(pushed, dtype, j) - g[j];"),
+    ("adopt_replaces", "theta[j] = theta[j] + shift;", "theta[j] = g[j];"),
 ]
 
 
