@@ -133,8 +133,9 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
 def side_averages(args, torch):
     """Times the side averages at the DiffuRefill-1B size: folding a global
     into the uniform-average sum (12 B/param), the average itself
-    (8 B/param), and the one-pass averages of the last 3 and last 5
-    snapshots (16 and 24 B/param).  One JSON line."""
+    (8 B/param), the one-pass averages of the last 3 and last 5 snapshots
+    (16 and 24 B/param), and the worker-side keep-local-drift adoption
+    (16 B/param).  One JSON line."""
     from checkpoint_averaging_amd import dlmerge as dl
     from checkpoint_averaging_amd import synth
     n = synth.DIFFUREFILL_1B.n_params
@@ -150,6 +151,8 @@ def side_averages(args, torch):
         "swa_average": (8, lambda i: dl.dl_swa_average(out, acc, 130)),
         "snapshot_average_3": (16, lambda i: dl.dl_snapshot_average(out, snaps[:3])),
         "snapshot_average_5": (24, lambda i: dl.dl_snapshot_average(out, snaps)),
+        # worker-side keep-local-drift adoption: theta += global - pushed
+        "adopt_keep_drift": (16, lambda i: dl.dl_adopt_keep_drift(out, snaps[0], snaps[1])),
     }
     res = {}
     for name, (bpe, call) in cases.items():
@@ -170,7 +173,8 @@ def side_averages(args, torch):
                      "GB_per_s": round(bpe * n / (ms / 1e3) / 1e9, 1),
                      "frac_of_hbm_peak": round(bpe * n / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] {name}: {ms:.3f} ms")
-    print(json.dumps({"metric": "side averages of the globals: effective HBM GB/s",
+    print(json.dumps({"metric": "side averages of the globals and worker adoption: "
+                                "effective HBM GB/s",
                       "n_params": n, "steps": args.steps, "warmup": args.warmup,
                       "dtype": "f32", "data": "synthetic", "kernels": res}), flush=True)
 

@@ -434,6 +434,30 @@ int dl_snapshot_average(float* out, const float* const* snapshots, int k, int64_
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 
+int dl_adopt_keep_drift(float* theta, const float* global, const void* pushed, int pushed_dtype,
+                        int64_t n, void* stream) {
+    if (n < 0) return DL_E_INVAL;
+    if (pushed_dtype != DL_F32 && pushed_dtype != DL_BF16) return DL_E_INVAL;
+    if (n == 0) return DL_OK;
+    if (theta == nullptr || global == nullptr || pushed == nullptr || n > INT64_MAX / 4)
+        return DL_E_INVAL;
+    const int64_t esize = pushed_dtype == DL_BF16 ? 2 : 4;
+    if (!aligned_to(theta, alignof(float)) || !aligned_to(global, alignof(float)) ||
+        !aligned_to(pushed, static_cast<uintptr_t>(esize)))
+        return DL_E_ALIGN;
+    const Span t_s = span_of(theta, n * 4), g_s = span_of(global, n * 4),
+               p_s = span_of(pushed, n * esize);
+    if (t_s.overlaps(g_s) || t_s.overlaps(p_s)) return DL_E_INVAL;
+    if (int st = check_device_span(theta, n * 4)) return st;
+    if (int st = check_device_span(global, n * 4)) return st;
+    if (int st = check_device_span(pushed, n * esize)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::launch_adopt_keep_drift(theta, global, pushed,
+                                                        pushed_dtype == DL_BF16, n,
+                                                        static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
 int dl_frag_range(const dl_round* r, int frag, int64_t* offset, int64_t* length) {
     if (r == nullptr || offset == nullptr || length == nullptr) return DL_E_INVAL;
     if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;

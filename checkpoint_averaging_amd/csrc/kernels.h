@@ -50,6 +50,10 @@ hipError_t launch_fold_nesterov(float* theta, float* m, const float* acc, const 
 hipError_t launch_snapshot_mean(float* out, const float* const* snaps, int k, int64_t n,
                                hipStream_t s);
 
+// theta[j] = theta[j] + (g[j] - pushed[j]); pushed is fp32, or bf16 if bf16 is set.
+hipError_t launch_adopt_keep_drift(float* theta, const float* g, const void* pushed, bool bf16,
+                                   int64_t n, hipStream_t s);
+
 // ema[j] = beta*ema[j] + omega*g[j].
 hipError_t launch_ema(float* ema, const float* g, float beta, float omega, int64_t n,
                       hipStream_t s);

@@ -346,6 +346,34 @@ struct FoldNesterovClose {
     }
 };
 
+// Keep-local-drift adoption on a worker: theta = theta + (g - pushed), the
+// difference rounded first.
+template <typename CT>
+struct AdoptKeepDrift {
+    float* theta;
+    const float* g;
+    const CT* pushed;
+    struct Regs { f32x4 t, g, p; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.t = ld4<NT>(theta, p);
+        r.g = ld4<NT>(g, p);
+        r.p = Ckpt<CT>::template pack<NT>(pushed, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            const float shift = r.g[i] - r.p[i];
+            o[i] = r.t[i] + shift;
+        }
+        st4<NT>(theta, p, o);
+    }
+    __device__ void scalar(int64_t j) const {
+        const float shift = g[j] - Ckpt<CT>::one(pushed, j);
+        theta[j] = theta[j] + shift;
+    }
+};
+
 // Mean of K snapshots read in one pass: S = s_0; S = S + s_i for i = 1..K-1
 // in the given order; out = S / K.  K is a template argument so each count
 // holds only the registers it reads (higher occupancy for small K).
@@ -600,6 +628,16 @@ hipError_t launch_snapshot_mean(float* out, const float* const* snaps, int k, in
                                hipStream_t s) {
     if (k < 1 || k > kMaxSnapshots) return hipErrorInvalidValue;
     return dispatch_snapshot_mean<1>(k, out, snaps, n, s);
+}
+
+hipError_t launch_adopt_keep_drift(float* theta, const float* g, const void* pushed, bool bf16,
+                                   int64_t n, hipStream_t s) {
+    const bool vec4 = aligned16(theta) && aligned16(g) && ckpt_aligned(pushed, bf16);
+    if (bf16)
+        return launch(AdoptKeepDrift<uint16_t>{theta, g, static_cast<const uint16_t*>(pushed)}, n,
+                      vec4, false, s);
+    return launch(AdoptKeepDrift<float>{theta, g, static_cast<const float*>(pushed)}, n, vec4,
+                  false, s);
 }
 
 hipError_t launch_ema(float* ema, const float* g, float beta, float omega, int64_t n,

@@ -38,6 +38,7 @@ DL_E_CAPACITY = -8
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
+           "dl_adopt_keep_drift",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
 DL_MAX_SNAPSHOTS = 16
@@ -61,6 +62,7 @@ _lib.dl_ema_update.argtypes = [_p, _p, _i64, _f32, _p]
 _lib.dl_swa_fold.argtypes = [_p, _p, _i64, _i64, _p]
 _lib.dl_swa_average.argtypes = [_p, _p, _i64, _i64, _p]
 _lib.dl_snapshot_average.argtypes = [_p, ctypes.POINTER(_p), _i32, _i64, _p]
+_lib.dl_adopt_keep_drift.argtypes = [_p, _p, _p, _i32, _i64, _p]
 _lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dl_round_participants.argtypes = [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32]
 _lib.dl_round_tokens.argtypes = [_p, _i32, ctypes.POINTER(_i64)]
@@ -248,6 +250,14 @@ def dl_snapshot_average(out: Array, snapshots: Sequence[Array], n: Optional[int]
     _check(_lib.dl_snapshot_average(_f32_addr(out, "out"), ptrs, len(snapshots), _n_of(out, n),
                                     _stream(stream)),
            "dl_snapshot_average")
+
+
+def dl_adopt_keep_drift(theta: Array, global_: Array, pushed: Array, n: Optional[int] = None,
+                        dtype: Optional[int] = None, stream=None) -> None:
+    _check(_lib.dl_adopt_keep_drift(_f32_addr(theta, "theta"), _f32_addr(global_, "global"),
+                                    _addr(pushed), _ckpt_dtype(pushed, dtype), _n_of(theta, n),
+                                    _stream(stream)),
+           "dl_adopt_keep_drift")
 
 
 def dl_frag_range(r: Round, frag: int) -> Tuple[int, int]:

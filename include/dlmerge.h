@@ -287,6 +287,25 @@ int dl_swa_average(float *out, const float *sum, int64_t n, int64_t count, void 
 int dl_snapshot_average(float *out, const float *const *snapshots, int k, int64_t n,
                         void *stream);
 
+/*
+ * Worker-side adoption that keeps local drift (DiffuRefill-1B technical
+ * report, "What we measured", "Distributed optimisation"; model card, "What
+ * the run taught"): instead of replacing its weights by the new global, the
+ * worker keeps the progress it made since its push:
+ *     theta[j] = theta[j] + (global[j] - pushed[j])
+ * with the difference rounded first.  The report measured it worse than
+ * plain replacement (which is a copy of the global and needs no kernel).
+ *
+ *   theta         device, n fp32 in/out: the worker's current weights.
+ *   global        device, n fp32: the new global.
+ *   pushed        device, n elements of pushed_dtype (DL_F32 or DL_BF16):
+ *                 the checkpoint the worker pushed.
+ * theta must not overlap global or pushed.  n = 0 is a no-op.
+ * Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_adopt_keep_drift(float *theta, const float *global, const void *pushed, int pushed_dtype,
+                        int64_t n, void *stream);
+
 /* Element range [offset, offset + length) of fragment frag.  DL_E_INVAL. */
 int dl_frag_range(const dl_round *r, int frag, int64_t *offset, int64_t *length);
 

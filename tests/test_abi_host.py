@@ -25,7 +25,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -183,6 +183,18 @@ def test_side_average_host_rules():
     dl.dl_snapshot_average(FAKE, [FAKE + 4096], n=0, stream=0)            # empty: no-op
     assert dl.DL_MAX_SNAPSHOTS == int(re.search(r"#define DL_MAX_SNAPSHOTS (\d+)",
                                                 open(HEADER).read()).group(1))
+
+
+def test_adopt_keep_drift_host_rules():
+    dl.dl_adopt_keep_drift(FAKE, FAKE + 4096, FAKE + 8192, n=0, dtype=dl.DL_F32, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_adopt_keep_drift, FAKE, FAKE + 4096, FAKE + 8192, n=-1,
+            dtype=dl.DL_F32, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_adopt_keep_drift, FAKE, FAKE + 4096, FAKE + 8192, n=4,
+            dtype=7, stream=0)
+    _expect(dl.DL_E_INVAL, dl.dl_adopt_keep_drift, FAKE, FAKE + 8, FAKE + 8192, n=4,
+            dtype=dl.DL_F32, stream=0)                                 # theta overlaps global
+    _expect(dl.DL_E_ALIGN, dl.dl_adopt_keep_drift, FAKE, FAKE + 4096, FAKE + 8193, n=4,
+            dtype=dl.DL_BF16, stream=0)
 
 
 def test_participants_capacity():

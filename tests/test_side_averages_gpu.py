@@ -1,5 +1,6 @@
 """GPU parity of the side averages (uniform average of globals, averages of
-the last k snapshots) against the CPU oracle, bit for bit."""
+the last k snapshots) and of the worker-side keep-local-drift adoption
+against the CPU oracle, bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -76,3 +77,17 @@ def test_snapshot_average_scalar_path_and_order():
     want_rev = oracle.snapshot_average(host[::-1])
     assert mc.bits_equal(mc.to_np(rev), want_rev)
     assert not mc.bits_equal(want, want_rev)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [1, 7, 4096 * 3 + 1, 1 << 20])
+def test_adopt_keep_drift_matches_oracle(n, dtype):
+    th0 = synth.global0(1007, n, device="cuda")
+    theta = synth.worker_checkpoint(1007, 5, 0, th0)                 # the worker's weights
+    pushed = synth.worker_checkpoint(1007, 4, 0, th0, dtype=dtype)   # what it pushed
+    g = synth.worker_checkpoint(1007, 6, 1, th0)                     # the new global
+    want = mc.to_np(theta)
+    oracle.adopt_keep_drift(want, mc.to_np(g), mc.to_np(pushed))
+    dl.dl_adopt_keep_drift(theta, g, pushed)
+    torch.cuda.synchronize()
+    assert mc.bits_equal(mc.to_np(theta), want), mc.first_mismatch(mc.to_np(theta), want)
