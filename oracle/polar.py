@@ -1,0 +1,28 @@
+"""Oracle of outer orthogonalisation.
+
+TEST INFRASTRUCTURE ONLY: never imported by the product library.
+
+The DiffuRefill-1B technical report (section "What we measured",
+"Optimisers") replaced the averaged outer update of each weight matrix by its
+polar factor.  For A = U S V^T (thin SVD, fp64 here) the polar factor is
+U V^T: the orthonormal-columns (or orthonormal-rows) matrix nearest to A,
+the factor P of A = P H with H symmetric positive semi-definite.  The SVD is
+a library step (numpy.linalg.svd); nothing else is involved.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def polar_factor(a: np.ndarray) -> np.ndarray:
+    """U V^T of the thin SVD of a (rows x cols), in fp64."""
+    u, _, vt = np.linalg.svd(np.asarray(a, dtype=np.float64), full_matrices=False)
+    return u @ vt
+
+
+def outer_orthogonal_step(theta: np.ndarray, averaged: np.ndarray, scale: float) -> np.ndarray:
+    """theta - scale * polar(theta - averaged), in fp64: the outer step whose
+    update (the workers' averaged move away from theta) is replaced by its
+    polar factor."""
+    t = np.asarray(theta, dtype=np.float64)
+    return t - float(scale) * polar_factor(t - np.asarray(averaged, dtype=np.float64))
