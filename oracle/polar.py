@@ -15,8 +15,13 @@ import numpy as np
 
 
 def polar_factor(a: np.ndarray) -> np.ndarray:
-    """U V^T of the thin SVD of a (rows x cols), in fp64."""
-    u, _, vt = np.linalg.svd(np.asarray(a, dtype=np.float64), full_matrices=False)
+    """U V^T of the thin SVD of a (rows x cols), in fp64.  The zero matrix
+    has no direction; its factor is taken as zero (the outer step is then a
+    no-op)."""
+    a = np.asarray(a, dtype=np.float64)
+    if not np.any(a):
+        return np.zeros_like(a)
+    u, _, vt = np.linalg.svd(a, full_matrices=False)
     return u @ vt
 
 

@@ -82,3 +82,10 @@ def test_iteration_schedule_reaches_the_polar_factor(m, n, kappa):
     a, want = constructed(rng, m, n, kappa)
     assert np.max(np.abs(newton_schulz(a) - want)) <= 1e-9
     assert np.max(np.abs(newton_schulz(a) - polar.polar_factor(a))) <= 1e-9
+
+
+def test_zero_update_is_a_no_op():
+    z = np.zeros((5, 3))
+    assert not np.any(polar.polar_factor(z))
+    theta = np.arange(15.0).reshape(5, 3)
+    assert np.array_equal(polar.outer_orthogonal_step(theta, theta, 0.5), theta)
