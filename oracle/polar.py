@@ -31,3 +31,18 @@ def outer_orthogonal_step(theta: np.ndarray, averaged: np.ndarray, scale: float)
     polar factor."""
     t = np.asarray(theta, dtype=np.float64)
     return t - float(scale) * polar_factor(t - np.asarray(averaged, dtype=np.float64))
+
+
+def polar_factor_rows(a: np.ndarray, rows) -> np.ndarray:
+    """Selected rows of the polar factor of a full-column-rank tall matrix,
+    from the closed form P = A (A^T A)^(-1/2), in fp64: the eigendecomposition
+    A^T A = V diag(l) V^T gives (A^T A)^(-1/2) = V diag(l^-1/2) V^T, and row i
+    of P is row i of A times that.  For matrices too large for a full SVD."""
+    a = np.asarray(a, dtype=np.float64)
+    if a.shape[0] < a.shape[1]:
+        raise ValueError("tall matrices only (use the transpose)")
+    lam, v = np.linalg.eigh(a.T @ a)
+    if lam[0] <= 0:
+        raise ValueError("rank deficient")
+    inv_sqrt = (v / np.sqrt(lam)) @ v.T
+    return a[np.asarray(rows)] @ inv_sqrt

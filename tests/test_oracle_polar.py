@@ -89,3 +89,14 @@ def test_zero_update_is_a_no_op():
     assert not np.any(polar.polar_factor(z))
     theta = np.arange(15.0).reshape(5, 3)
     assert np.array_equal(polar.outer_orthogonal_step(theta, theta, 0.5), theta)
+
+
+@pytest.mark.parametrize("m,n,kappa", [(300, 40, 10), (500, 120, 1e3)])
+def test_rows_from_the_gram_closed_form(m, n, kappa):
+    """The Gram-based rows agree with the known factors Q1 Q2^T."""
+    rng = np.random.default_rng(3 * m + n)
+    a, want = constructed(rng, m, n, kappa)
+    rows = [0, 7, m // 2, m - 1]
+    assert np.max(np.abs(polar.polar_factor_rows(a, rows) - want[rows])) <= 1e-9
+    with pytest.raises(ValueError):
+        polar.polar_factor_rows(a.T, rows[:1])
