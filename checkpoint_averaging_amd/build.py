@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libdlmerge.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "api.cpp")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "polar.hip"),
+           os.path.join(CSRC, "api.cpp")]
 DRIVER = os.path.join(PKG, "dlmerge_driver")
 DRIVER_SOURCES = [os.path.join(CSRC, "merge_driver.hip")]
 
@@ -58,10 +59,10 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def device_asm(out_path: str) -> str:
-    """gfx950 assembly of the kernels (for inspecting the instruction mix)."""
+def device_asm(out_path: str, source: str = "kernels.hip") -> str:
+    """gfx950 assembly of one source's kernels (for inspecting the instruction mix)."""
     cmd = [HIPCC, *HIPFLAGS, "--cuda-device-only", "-S", "-o", out_path,
-           os.path.join(CSRC, "kernels.hip")]
+           os.path.join(CSRC, source)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out_path
 

@@ -18,6 +18,7 @@
 
 #include "dlmerge.h"
 #include "kernels.h"
+#include "polar.h"
 
 namespace {
 
@@ -455,6 +456,111 @@ int dl_adopt_keep_drift(float* theta, const float* global, const void* pushed, i
     const hipError_t err = dlk::launch_adopt_keep_drift(theta, global, pushed,
                                                         pushed_dtype == DL_BF16, n,
                                                         static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t ldb, int64_t m,
+                  int64_t n, int64_t k, float* c, int64_t ldc, const float* y, float alpha,
+                  float beta, float diag, void* stream) {
+    if (form != DL_TN && form != DL_NT) return DL_E_INVAL;
+    if (m < 0 || n < 0 || k < 0) return DL_E_INVAL;
+    if (m == 0 || n == 0) return DL_OK;
+    if (a == nullptr || b == nullptr || c == nullptr) return DL_E_INVAL;
+    if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) || dlk::gemm_tiles(m, n) > dlk::kGemmMaxTiles)
+        return DL_E_INVAL;
+    const bool tn = form == DL_TN;
+    // the operands' extents: TN reads A as k x lda (cols i < m), NT as m x lda (cols k)
+    if (tn ? (lda < m || ldb < n) : (lda < k || ldb < k)) return DL_E_INVAL;
+    if (ldc < n) return DL_E_INVAL;
+    if (!aligned_to(a, alignof(float)) || !aligned_to(b, alignof(float)) ||
+        !aligned_to(c, alignof(float)) || (y && !aligned_to(y, alignof(float))))
+        return DL_E_ALIGN;
+    const int64_t a_bytes = 4 * (tn ? (k > 0 ? (k - 1) * lda + m : 0) : (m - 1) * lda + k);
+    const int64_t b_bytes = 4 * (tn ? (k > 0 ? (k - 1) * ldb + n : 0) : (n - 1) * ldb + k);
+    const int64_t c_bytes = 4 * ((m - 1) * ldc + n);
+    const Span c_s = span_of(c, c_bytes);
+    if (k > 0 && (c_s.overlaps(span_of(a, a_bytes)) || c_s.overlaps(span_of(b, b_bytes))))
+        return DL_E_INVAL;
+    if (y != nullptr && y != c && c_s.overlaps(span_of(y, c_bytes))) return DL_E_INVAL;
+    if (k > 0) {
+        if (int st = check_device_span(a, a_bytes)) return st;
+        if (int st = check_device_span(b, b_bytes)) return st;
+    }
+    if (int st = check_device_span(c, c_bytes)) return st;
+    if (y != nullptr)
+        if (int st = check_device_span(y, c_bytes)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::gemm_probe(tn, a, lda, b, ldb, m, n, k, c, ldc, y, alpha, beta,
+                                           diag, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_polar_workspace_bytes(int64_t rows, int64_t cols, int64_t* bytes) {
+    if (bytes == nullptr || rows < 1 || cols < 1) return DL_E_INVAL;
+    if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) ||
+        dlk::gemm_tiles(rows, cols) > dlk::kGemmMaxTiles)
+        return DL_E_INVAL;
+    *bytes = dlk::polar_workspace_bytes(rows, cols);
+    return DL_OK;
+}
+
+namespace {
+
+int check_polar_args(int64_t rows, int64_t cols, int quintic, int cubic, void* ws,
+                     int64_t ws_bytes, int64_t* need) {
+    if (int st = dl_polar_workspace_bytes(rows, cols, need)) return st;
+    if (quintic < 0 || cubic < 0 || quintic + cubic < 1 || quintic > 64 || cubic > 64)
+        return DL_E_INVAL;
+    if (ws == nullptr || ws_bytes < *need) return DL_E_INVAL;
+    if (!aligned_to(ws, 256)) return DL_E_ALIGN;
+    return DL_OK;
+}
+
+}  // namespace
+
+int dl_polar_factor(float* out, const float* update, int64_t rows, int64_t cols, int quintic_steps,
+                    int cubic_steps, void* workspace, int64_t workspace_bytes, void* stream) {
+    int64_t need = 0;
+    if (int st = check_polar_args(rows, cols, quintic_steps, cubic_steps, workspace,
+                                  workspace_bytes, &need))
+        return st;
+    if (out == nullptr || update == nullptr) return DL_E_INVAL;
+    if (!aligned_to(out, alignof(float)) || !aligned_to(update, alignof(float))) return DL_E_ALIGN;
+    const int64_t bytes = rows * cols * 4;
+    const Span o_s = span_of(out, bytes), u_s = span_of(update, bytes), w_s = span_of(workspace, need);
+    if (o_s.overlaps(w_s) || u_s.overlaps(w_s)) return DL_E_INVAL;
+    if (!o_s.same(u_s) && o_s.overlaps(u_s)) return DL_E_INVAL;
+    if (int st = check_device_span(workspace, need)) return st;
+    if (int st = check_device_span(out, bytes)) return st;
+    if (int st = check_device_span(update, bytes)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::polar_iterate(update, nullptr, out, nullptr, 0.0f, rows, cols,
+                                              quintic_steps, cubic_steps, workspace,
+                                              static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_outer_orthogonal_step(float* theta, const float* averaged, int64_t rows, int64_t cols,
+                             float scale, int quintic_steps, int cubic_steps, void* workspace,
+                             int64_t workspace_bytes, void* stream) {
+    int64_t need = 0;
+    if (int st = check_polar_args(rows, cols, quintic_steps, cubic_steps, workspace,
+                                  workspace_bytes, &need))
+        return st;
+    if (theta == nullptr || averaged == nullptr) return DL_E_INVAL;
+    if (!aligned_to(theta, alignof(float)) || !aligned_to(averaged, alignof(float)))
+        return DL_E_ALIGN;
+    const int64_t bytes = rows * cols * 4;
+    const Span t_s = span_of(theta, bytes), a_s = span_of(averaged, bytes),
+               w_s = span_of(workspace, need);
+    if (t_s.overlaps(a_s) || t_s.overlaps(w_s) || a_s.overlaps(w_s)) return DL_E_INVAL;
+    if (int st = check_device_span(workspace, need)) return st;
+    if (int st = check_device_span(theta, bytes)) return st;
+    if (int st = check_device_span(averaged, bytes)) return st;
+    (void)hipGetLastError();
+    const hipError_t err = dlk::polar_iterate(theta, averaged, nullptr, theta, scale, rows, cols,
+                                              quintic_steps, cubic_steps, workspace,
+                                              static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 

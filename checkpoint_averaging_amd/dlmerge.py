@@ -38,10 +38,13 @@ DL_E_CAPACITY = -8
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
-           "dl_adopt_keep_drift",
+           "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_factor",
+           "dl_outer_orthogonal_step", "dl_matmul_f32",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
 DL_MAX_SNAPSHOTS = 16
+DL_TN = 0
+DL_NT = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m checkpoint_averaging_amd.build` "
@@ -63,6 +66,11 @@ _lib.dl_swa_fold.argtypes = [_p, _p, _i64, _i64, _p]
 _lib.dl_swa_average.argtypes = [_p, _p, _i64, _i64, _p]
 _lib.dl_snapshot_average.argtypes = [_p, ctypes.POINTER(_p), _i32, _i64, _p]
 _lib.dl_adopt_keep_drift.argtypes = [_p, _p, _p, _i32, _i64, _p]
+_lib.dl_polar_workspace_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_i64)]
+_lib.dl_polar_factor.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]
+_lib.dl_outer_orthogonal_step.argtypes = [_p, _p, _i64, _i64, _f32, _i32, _i32, _p, _i64, _p]
+_lib.dl_matmul_f32.argtypes = [_i32, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _f32,
+                               _f32, _f32, _p]
 _lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dl_round_participants.argtypes = [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32]
 _lib.dl_round_tokens.argtypes = [_p, _i32, ctypes.POINTER(_i64)]
@@ -258,6 +266,51 @@ def dl_adopt_keep_drift(theta: Array, global_: Array, pushed: Array, n: Optional
                                     _addr(pushed), _ckpt_dtype(pushed, dtype), _n_of(theta, n),
                                     _stream(stream)),
            "dl_adopt_keep_drift")
+
+
+def dl_polar_workspace_bytes(rows: int, cols: int) -> int:
+    b = _i64()
+    _check(_lib.dl_polar_workspace_bytes(int(rows), int(cols), ctypes.byref(b)),
+           "dl_polar_workspace_bytes")
+    return b.value
+
+
+def _ws(workspace: Array, workspace_bytes: Optional[int]):
+    if workspace_bytes is None:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace_bytes is required for a raw workspace address")
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return _addr(workspace), int(workspace_bytes)
+
+
+def dl_polar_factor(out: Array, update: Array, rows: int, cols: int, workspace: Array,
+                    quintic_steps: int = 12, cubic_steps: int = 6,
+                    workspace_bytes: Optional[int] = None, stream=None) -> None:
+    w, wb = _ws(workspace, workspace_bytes)
+    _check(_lib.dl_polar_factor(_f32_addr(out, "out"), _f32_addr(update, "update"), int(rows),
+                                int(cols), int(quintic_steps), int(cubic_steps), w, wb,
+                                _stream(stream)),
+           "dl_polar_factor")
+
+
+def dl_outer_orthogonal_step(theta: Array, averaged: Array, rows: int, cols: int, scale: float,
+                             workspace: Array, quintic_steps: int = 12, cubic_steps: int = 6,
+                             workspace_bytes: Optional[int] = None, stream=None) -> None:
+    w, wb = _ws(workspace, workspace_bytes)
+    _check(_lib.dl_outer_orthogonal_step(_f32_addr(theta, "theta"), _f32_addr(averaged, "averaged"),
+                                         int(rows), int(cols), float(scale), int(quintic_steps),
+                                         int(cubic_steps), w, wb, _stream(stream)),
+           "dl_outer_orthogonal_step")
+
+
+def dl_matmul_f32(form: int, a: Array, lda: int, b: Array, ldb: int, m: int, n: int, k: int,
+                  c: Array, ldc: int, y: Array = None, alpha: float = 1.0, beta: float = 0.0,
+                  diag: float = 0.0, stream=None) -> None:
+    _check(_lib.dl_matmul_f32(int(form), _f32_addr(a, "a"), int(lda), _f32_addr(b, "b"), int(ldb),
+                              int(m), int(n), int(k), _f32_addr(c, "c"), int(ldc),
+                              _f32_addr(y, "y"), float(alpha), float(beta), float(diag),
+                              _stream(stream)),
+           "dl_matmul_f32")
 
 
 def dl_frag_range(r: Round, frag: int) -> Tuple[int, int]:

@@ -306,6 +306,68 @@ int dl_snapshot_average(float *out, const float *const *snapshots, int k, int64_
 int dl_adopt_keep_drift(float *theta, const float *global, const void *pushed, int pushed_dtype,
                         int64_t n, void *stream);
 
+/*
+ * Outer orthogonalisation (DiffuRefill-1B technical report, "What we
+ * measured", "Optimisers": the averaged outer update is replaced by its
+ * polar factor; it helped on a 4-worker stand run).  For one weight matrix
+ * of rows x cols (row-major fp32) whose averaged update is A = U S V^T (thin
+ * SVD), the polar factor is P = U V^T.  It is reached by a Newton-Schulz
+ * iteration on fp32 MFMA: X_0 = A / ||A||_F, then `quintic_steps` steps of
+ * X <- X (a I + b G + c G^2) with (a, b, c) = (3.4445, -4.7750, 2.0315) and
+ * `cubic_steps` steps of X <- X (1.5 I - 0.5 G), G = X^T X (X X^T and M X for
+ * rows < cols).  With 12 + 6 steps every singular value s with
+ * s >= 1.4e-7 ||A||_F reaches 1 within fp32 rounding; directions below that
+ * are left small.  Results are deterministic (fixed reduction order).
+ *
+ * The caller provides a device workspace of dl_polar_workspace_bytes bytes,
+ * 256-byte aligned (the library never allocates); it must not overlap any
+ * argument.  Calls on one stream may share a workspace.
+ */
+
+/* Workspace bytes for a rows x cols matrix (rows, cols >= 1).  DL_E_INVAL. */
+int dl_polar_workspace_bytes(int64_t rows, int64_t cols, int64_t *bytes);
+
+/*
+ * out = polar factor of `update` (both rows x cols, device fp32; out may be
+ * update, otherwise they must not overlap).  1 <= quintic + cubic steps,
+ * each <= 64.  Errors: DL_E_INVAL (sizes, steps, workspace too small or
+ * overlapping, spans), DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_polar_factor(float *out, const float *update, int64_t rows, int64_t cols,
+                    int quintic_steps, int cubic_steps, void *workspace,
+                    int64_t workspace_bytes, void *stream);
+
+/*
+ * One outer step with the orthogonalised update, for one weight matrix:
+ *     theta = theta - scale * P(theta - averaged)
+ * where `averaged` is the round's plain mean of the workers (dl_finalize_mean)
+ * and theta the global the workers trained from, so theta - averaged is the
+ * averaged update.  With P replaced by the identity and scale 1 this would
+ * be plain replacement (theta = averaged).  The pages give no scale; the
+ * caller chooses it.  theta, averaged: device, rows x cols fp32, disjoint.
+ * Errors: as dl_polar_factor.
+ */
+int dl_outer_orthogonal_step(float *theta, const float *averaged, int64_t rows, int64_t cols,
+                             float scale, int quintic_steps, int cubic_steps, void *workspace,
+                             int64_t workspace_bytes, void *stream);
+
+enum dl_matmul_form {
+    DL_TN = 0,   /* C[i][j] = sum_k A[k*lda + i] * B[k*ldb + j] */
+    DL_NT = 1    /* C[i][j] = sum_k A[i*lda + k] * B[j*ldb + k] */
+};
+
+/*
+ * The fp32 MFMA product the orthogonalisation is built from, with its fused
+ * epilogue:  C[i][j] = alpha * sum + beta * Y[i][j] + (i == j ? diag : 0)
+ * for i < m, j < n, C and Y with leading dimension ldc (Y may be NULL or
+ * equal C; otherwise it must not overlap C; C must not overlap A or B).
+ * Accumulation is fp32 on MFMA.  m = 0 or n = 0 is a no-op.
+ * Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ */
+int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t ldb, int64_t m,
+                  int64_t n, int64_t k, float *c, int64_t ldc, const float *y, float alpha,
+                  float beta, float diag, void *stream);
+
 /* Element range [offset, offset + length) of fragment frag.  DL_E_INVAL. */
 int dl_frag_range(const dl_round *r, int frag, int64_t *offset, int64_t *length);
 

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 20
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -197,6 +197,54 @@ def test_adopt_keep_drift_host_rules():
             dtype=dl.DL_BF16, stream=0)
 
 
+def test_polar_host_rules():
+    ws_need = dl.dl_polar_workspace_bytes(300, 200)
+    r = 200
+    assert ws_need >= 2 * 300 * 200 * 4 + 2 * r * r * 4
+    assert dl.dl_polar_workspace_bytes(200, 300) == ws_need       # symmetric in the shape
+    for rows, cols in ((0, 5), (5, 0), (-1, 5), ((1 << 31) + 1, 1), (1 << 24, 1 << 17)):
+        _expect(dl.DL_E_INVAL, dl.dl_polar_workspace_bytes, rows, cols)
+    ws, up, out = FAKE, FAKE + (1 << 30), FAKE + (1 << 31)
+    call = lambda **k: dl.dl_polar_factor(**{**dict(out=out, update=up, rows=300, cols=200,
+                                                     workspace=ws, workspace_bytes=ws_need,
+                                                     stream=0), **k})
+    for kw in (dict(quintic_steps=0, cubic_steps=0), dict(quintic_steps=-1),
+               dict(cubic_steps=65), dict(quintic_steps=65),
+               dict(workspace_bytes=ws_need - 1), dict(workspace=0), dict(out=0),
+               dict(update=0), dict(rows=0),
+               dict(out=up + 4),                                   # overlaps update
+               dict(workspace=up - 256),                           # overlaps update
+               dict(out=ws + 256)):                                # overlaps workspace
+        _expect(dl.DL_E_INVAL, call, **kw)
+    _expect(dl.DL_E_ALIGN, call, workspace=ws + 128)
+    _expect(dl.DL_E_ALIGN, call, out=out + 2)
+    _expect(dl.DL_E_ALIGN, call, update=up + 1)
+    step = lambda **k: dl.dl_outer_orthogonal_step(**{**dict(theta=out, averaged=up, rows=300,
+                                                             cols=200, scale=0.1, workspace=ws,
+                                                             workspace_bytes=ws_need, stream=0),
+                                                      **k})
+    _expect(dl.DL_E_INVAL, step, averaged=out)                     # in place is not allowed
+    _expect(dl.DL_E_INVAL, step, averaged=out + 1024)
+    _expect(dl.DL_E_INVAL, step, theta=ws + 512)
+    _expect(dl.DL_E_INVAL, step, cubic_steps=-2)
+    _expect(dl.DL_E_ALIGN, step, theta=out + 3)
+
+
+def test_matmul_host_rules():
+    a, b, c = FAKE, FAKE + (1 << 28), FAKE + (1 << 29)
+    mm = lambda **k: dl.dl_matmul_f32(**{**dict(form=dl.DL_TN, a=a, lda=64, b=b, ldb=32, m=64,
+                                                n=32, k=16, c=c, ldc=32, stream=0), **k})
+    mm(m=0)                                                        # empty: no-op
+    mm(n=0)
+    for kw in (dict(form=2), dict(m=-1), dict(k=-1), dict(lda=63), dict(ldb=31), dict(ldc=31),
+               dict(form=dl.DL_NT, lda=15), dict(form=dl.DL_NT, ldb=15, lda=16),
+               dict(a=0), dict(c=0), dict(c=a + 4), dict(c=b), dict(y=c + 4),
+               dict(m=(1 << 31) + 1), dict(m=1 << 24, n=1 << 17)):
+        _expect(dl.DL_E_INVAL, mm, **kw)
+    _expect(dl.DL_E_ALIGN, mm, c=c + 2)
+    _expect(dl.DL_E_ALIGN, mm, y=b + (1 << 20) + 1)
+
+
 def test_participants_capacity():
     lib = dl.raw_lib()
     import ctypes
@@ -249,3 +297,21 @@ def test_isa_has_no_contraction_and_ieee_division(tmp_path):
             assert fixups > 0, name      # the means and the Nesterov closes divide
         else:
             assert fixups == 0, name     # folds and the EMA do not
+
+
+def test_orthogonalisation_isa(tmp_path):
+    """The product kernel runs on fp32 MFMA with no scratch and no packed fp32
+    arithmetic; its epilogue multiplies and adds separately (no contraction)."""
+    asm = open(cabuild.device_asm(str(tmp_path / "p.s"), source="polar.hip")).read()
+    counts = _kernel_instr_counts(asm)
+    gemms = [n for n in counts if "k_gemm" in n]
+    assert len(gemms) == 2
+    for name, c in counts.items():
+        assert not [k for k in c if k.startswith(("v_pk_fma", "v_pk_mul_f32", "v_pk_add_f32",
+                                                  "v_mad_f32", "v_fmamk", "v_fmaak",
+                                                  "v_fma_f32", "v_fmac_f32"))], name
+    for name in gemms:
+        assert counts[name].get("v_mfma_f32_32x32x2_f32", 0) >= 32, name
+    assert "scratch_" not in asm
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
+    assert sizes and all(int(s) == 0 for s in sizes)

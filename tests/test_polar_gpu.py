@@ -1,0 +1,273 @@
+"""Outer orthogonalisation on the GPU against the fp64 oracle (DiffuRefill-1B
+technical report, "What we measured", "Optimisers": the averaged outer
+update is replaced by its polar factor).
+
+Tolerances come from the arithmetic:
+  * the fp32 MFMA product: any summation order of k products in binary32
+    stays within gamma_(k+1) = (k+1) u / (1 - (k+1) u) of the exact sum
+    times the sum of magnitudes, plus one rounding per epilogue operation;
+  * the polar factor: the iteration's rounding errors act as a perturbation
+    of relative size ~ sqrt(r) u on each iterate, and the polar factor moves
+    by at most ~ 2 ||dX|| / sigma_min(X) under a perturbation dX, so the
+    error relative to ||P||_F is bounded by C sqrt(r) u kappa_F with
+    kappa_F = ||A||_F / sigma_min(A) (the iteration starts from A / ||A||_F)
+    and C = 16 covering the three products per step and the geometric sum
+    over steps while sigma_min grows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from checkpoint_averaging_amd import dlmerge as dl
+from checkpoint_averaging_amd import synth
+from oracle import polar as opolar
+
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24           # unit roundoff of binary32
+C_POLAR = 16.0
+DEV = torch.device("cuda")
+
+
+def gpu(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy().astype(np.float64)
+
+
+def workspace(rows, cols):
+    nbytes = dl.dl_polar_workspace_bytes(rows, cols)
+    return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=DEV)
+
+
+def orthonormal(rng, m, r):
+    q, _ = np.linalg.qr(rng.standard_normal((m, r)))
+    return q
+
+
+def constructed(rng, m, n, kappa):
+    r = min(m, n)
+    q1, q2 = orthonormal(rng, m, r), orthonormal(rng, n, r)
+    s = np.logspace(0, -np.log10(kappa), r)
+    return ((q1 * s) @ q2.T).astype(np.float32)
+
+
+def polar_bound(a64):
+    s = np.linalg.svd(a64, compute_uv=False)
+    r = min(a64.shape)
+    kappa_f = np.linalg.norm(a64) / s[-1]
+    return C_POLAR * math.sqrt(r) * U32 * kappa_f
+
+
+def polar_estimate(a64):
+    """Random-rounding estimate of the same error.  Early steps: a few
+    roundings per step (relative u each, independent across elements)
+    perturb X by ~u in norm, which moves P by ~2u/sigma_min(X); summed
+    geometrically over the steps while sigma_min grows, ~8u kappa_2.  Late
+    steps, with X already orthonormal: each element of a product is a sum of
+    r terms whose rounding errors add like a random walk, ~sqrt(r) u per
+    element and step.  Together, with margin: 16 u (kappa_2 + sqrt(r))."""
+    s = np.linalg.svd(a64, compute_uv=False)
+    return estimate_from(s[0] / s[-1], min(a64.shape))
+
+
+def estimate_from(kappa_2, r):
+    return 16.0 * U32 * (kappa_2 + math.sqrt(r))
+
+
+# -- the MFMA product ---------------------------------------------------------
+
+@pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (130, 257, 33), (300, 129, 500), (128, 128, 16),
+                                   (5, 700, 3), (640, 256, 1)])
+@pytest.mark.parametrize("epi", ["plain", "y_separate", "y_in_place"])
+def test_matmul_against_fp64(form, m, n, k, epi):
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    pad = 3
+    if form == dl.DL_TN:
+        a = rng.standard_normal((k, m + pad)).astype(np.float32)
+        b = rng.standard_normal((k, n + pad)).astype(np.float32)
+        opa, opb = a[:, :m].astype(np.float64).T, b[:, :n].astype(np.float64)
+    else:
+        a = rng.standard_normal((m, k + pad)).astype(np.float32)
+        b = rng.standard_normal((n, k + pad)).astype(np.float32)
+        opa, opb = a[:, :k].astype(np.float64), b[:, :k].astype(np.float64).T
+    ldc = n + 5
+    c0 = rng.standard_normal((m, ldc)).astype(np.float32)
+    y0 = rng.standard_normal((m, ldc)).astype(np.float32)
+    alpha, beta, diag = (1.0, 0.0, 0.0) if epi == "plain" else (-0.5, 2.0315, 3.4445)
+    a_d, b_d, c_d = gpu(a), gpu(b), gpu(c0)
+    y_d = None if epi == "plain" else (c_d if epi == "y_in_place" else gpu(y0))
+    y_h = None if epi == "plain" else (c0 if epi == "y_in_place" else y0)[:, :n].astype(np.float64)
+    dl.dl_matmul_f32(form, a_d, a.shape[1], b_d, b.shape[1], m, n, k, c_d, ldc, y_d,
+                     alpha, beta, diag)
+    got = host(c_d)
+    want = alpha * (opa @ opb)
+    mag = abs(alpha) * (np.abs(opa) @ np.abs(opb))
+    if y_h is not None:
+        want = want + beta * y_h
+        mag = mag + abs(beta) * np.abs(y_h)
+    eye = np.eye(m, n) * diag
+    want, mag = want + eye, mag + np.abs(eye)
+    g = (k + 4) * U32 / (1 - (k + 4) * U32)
+    err = np.abs(got[:, :n] - want)
+    assert np.all(err <= g * mag + 1e-30), (float(np.max(err / (mag + 1e-30))), g)
+    # columns past n are untouched
+    assert np.array_equal(got[:, n:], c0[:, n:].astype(np.float64))
+
+
+def test_matmul_k0_writes_the_epilogue():
+    m, n = 70, 90
+    c = torch.full((m, n), 7.0, device=DEV)
+    y = gpu(np.arange(m * n, dtype=np.float32).reshape(m, n))
+    a = torch.zeros(1, device=DEV)
+    dl.dl_matmul_f32(dl.DL_NT, a, 0, a, 0, m, n, 0, c, n, y, 1.0, 0.5, 2.0)
+    want = np.float32(0.5) * np.arange(m * n, dtype=np.float32).reshape(m, n) + 2.0 * np.eye(m, n)
+    assert np.array_equal(host(c), want.astype(np.float32).astype(np.float64))
+
+
+# -- the polar factor -----------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,kappa", [(256, 64, 1), (256, 64, 10), (64, 256, 10),
+                                       (200, 200, 100), (300, 130, 1e3), (130, 300, 1e3),
+                                       (1000, 257, 100), (129, 129, 1e4), (33, 517, 10)])
+def test_polar_factor_constructed(m, n, kappa):
+    rng = np.random.default_rng(int(m * 31 + n + kappa))
+    a = constructed(rng, m, n, kappa)
+    a64 = a.astype(np.float64)
+    want = opolar.polar_factor(a64)
+    out = torch.empty((m, n), device=DEV)
+    a_d = gpu(a)
+    dl.dl_polar_factor(out, a_d, m, n, workspace(m, n))
+    got = host(out)
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    bound = polar_bound(a64)
+    est = polar_estimate(a64)
+    print(f"polar {m}x{n} kappa={kappa:g}: rel_F={rel:.3e} bound={bound:.3e} estimate={est:.3e} "
+          f"max={np.max(np.abs(got - want)):.3e}", flush=True)
+    assert rel <= bound
+    assert rel <= est
+    # the input is not modified
+    assert np.array_equal(host(a_d), a64)
+
+
+def test_polar_factor_in_place_and_vectors():
+    rng = np.random.default_rng(11)
+    for m, n in ((1, 300), (300, 1), (1, 1), (2, 2)):
+        a = rng.standard_normal((m, n)).astype(np.float32)
+        a_d = gpu(a)
+        dl.dl_polar_factor(a_d, a_d, m, n, workspace(m, n))       # out == update
+        want = opolar.polar_factor(a.astype(np.float64))
+        got = host(a_d)
+        assert np.linalg.norm(got - want) <= polar_bound(a.astype(np.float64)) * np.linalg.norm(want)
+
+
+def test_polar_factor_of_zero_is_zero():
+    z = torch.zeros((40, 24), device=DEV)
+    out = torch.full((40, 24), 5.0, device=DEV)
+    dl.dl_polar_factor(out, z, 40, 24, workspace(40, 24))
+    assert not np.any(host(out))
+
+
+def test_polar_factor_scale_invariant_and_deterministic():
+    rng = np.random.default_rng(12)
+    a = constructed(rng, 300, 100, 50)
+    ws = workspace(300, 100)
+    outs = []
+    for s in (1.0, 1.0, 8.0):      # powers of two: the scaled input is exact
+        o = torch.empty((300, 100), device=DEV)
+        dl.dl_polar_factor(o, gpu(a * np.float32(s)), 300, 100, ws)
+        outs.append(host(o))
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[2])
+
+
+def test_polar_steps_schedule():
+    """Fewer cubic steps leave the factor less orthogonal; one quintic step
+    alone is far from it (the step counts reach the kernel)."""
+    rng = np.random.default_rng(13)
+    a = constructed(rng, 256, 128, 100)
+    want = opolar.polar_factor(a.astype(np.float64))
+    ws = workspace(256, 128)
+    errs = []
+    for q, c in ((1, 0), (12, 0), (12, 6)):
+        o = torch.empty((256, 128), device=DEV)
+        dl.dl_polar_factor(o, gpu(a), 256, 128, ws, quintic_steps=q, cubic_steps=c)
+        errs.append(np.linalg.norm(host(o) - want))
+    assert errs[0] > errs[1] > errs[2]
+    assert errs[2] <= polar_bound(a.astype(np.float64)) * np.linalg.norm(want)
+
+
+# -- the outer step --------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n", [(192, 64), (64, 192), (257, 255)])
+def test_outer_orthogonal_step(m, n):
+    seed = 900 + m
+    theta = synth.global0(seed, m * n, device=DEV)
+    avg = synth.worker_checkpoint(seed, 0, 0, theta)
+    th_h, avg_h = host(theta), host(avg)
+    scale = 0.02
+    want = opolar.outer_orthogonal_step(th_h.reshape(m, n), avg_h.reshape(m, n), scale).reshape(-1)
+    upd = (th_h - avg_h).reshape(m, n)
+    dl.dl_outer_orthogonal_step(theta, avg, m, n, scale, workspace(m, n))
+    got = host(theta)
+    p_err = polar_bound(upd) * math.sqrt(min(m, n))            # ||P||_F = sqrt(r)
+    err = np.linalg.norm(got - want)
+    print(f"step {m}x{n}: err_F={err:.3e} bound={scale * p_err:.3e}", flush=True)
+    assert err <= scale * p_err + 2 * U32 * np.linalg.norm(want)
+    assert np.array_equal(host(avg), avg_h)
+
+
+# -- full-size shapes of DiffuRefill-1B's weight matrices -----------------------
+
+@pytest.mark.parametrize("rows,cols", [(2048, 2048), (5632, 2048), (2048, 5632)],
+                         ids=["attn_2048x2048", "ffn_up_5632x2048", "ffn_down_2048x5632"])
+def test_polar_full_size_against_svd(rows, cols):
+    seed = 950 + rows // 64
+    theta = synth.global0(seed, rows * cols, device=DEV)
+    avg = synth.worker_checkpoint(seed, 0, 0, theta)
+    upd = host(theta) - host(avg)                     # fp64 difference of the fp32 inputs
+    a32 = torch.sub(theta, avg)                       # the kernel forms it in fp32 as well
+    out = torch.empty(rows * cols, device=DEV)
+    dl.dl_polar_factor(out, a32, rows, cols, workspace(rows, cols))
+    got = host(out).reshape(rows, cols)
+    want = opolar.polar_factor(upd.reshape(rows, cols))
+    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+    bound = polar_bound(upd.reshape(rows, cols))
+    est = polar_estimate(upd.reshape(rows, cols))
+    print(f"full {rows}x{cols}: rel_F={rel:.3e} bound={bound:.3e} estimate={est:.3e}", flush=True)
+    assert rel <= bound
+    assert rel <= est
+
+
+def test_polar_full_size_embedding_rows():
+    """The 73760 x 2048 embedding: sampled rows against the Gram closed form,
+    and orthonormal columns over the whole factor."""
+    rows, cols = 73760, 2048
+    seed = 977
+    theta = synth.global0(seed, rows * cols, device=DEV)
+    avg = synth.worker_checkpoint(seed, 0, 0, theta)
+    upd = (host(theta) - host(avg)).reshape(rows, cols)
+    out = torch.empty(rows * cols, device=DEV)
+    dl.dl_polar_factor(out, torch.sub(theta, avg), rows, cols, workspace(rows, cols))
+    got = host(out).reshape(rows, cols)
+    pick = np.random.default_rng(5).choice(rows, 64, replace=False)
+    pick = np.concatenate([[0, rows - 1], pick])
+    want = opolar.polar_factor_rows(upd, pick)
+    s = np.linalg.svd(upd.T @ upd, compute_uv=False)
+    kappa_f = np.linalg.norm(upd) / math.sqrt(s[-1])
+    bound = C_POLAR * math.sqrt(cols) * U32 * kappa_f
+    est = estimate_from(math.sqrt(s[0] / s[-1]), cols)
+    rel = np.linalg.norm(got[pick] - want) / np.linalg.norm(want)
+    print(f"embedding rows: rel_F={rel:.3e} bound={bound:.3e} estimate={est:.3e}", flush=True)
+    assert rel <= bound
+    assert rel <= est
+    gram = got.T @ got
+    orth = np.max(np.abs(gram - np.eye(cols)))
+    print(f"embedding orthonormality: {orth:.3e}", flush=True)
+    assert orth <= 2 * bound
