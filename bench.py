@@ -179,6 +179,172 @@ def side_averages(args, torch):
                       "dtype": "f32", "data": "synthetic", "kernels": res}), flush=True)
 
 
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def orthogonalize(args, torch):
+    """Times one orthogonalised outer step over every DiffuRefill-1B weight
+    matrix (theta = theta - s * P(theta - averaged), P the polar factor by 12
+    quintic + 6 cubic Newton-Schulz steps), matrix by matrix on one stream,
+    and every distinct fp32 MFMA product of the iteration launch by launch.
+    One JSON line."""
+    import numpy as np
+    from checkpoint_averaging_amd import dlmerge as dl
+    from checkpoint_averaging_amd import synth
+    from checkpoint_averaging_amd.orthogonalize import OrthogonalStep, gemm_flops
+
+    layout = synth.DIFFUREFILL_1B
+    dev = torch.device("cuda")
+    n = layout.n_params
+    theta = synth.global0(1007, n, device=dev)
+    averaged = synth.worker_checkpoint(1007, 0, 0, theta)
+    step = OrthogonalStep(layout, dev)
+    mats = step.matrices
+    n_mat = sum(m.rows * m.cols for m in mats)
+    flops = step.flops()
+    scale = 1e-4
+    torch.cuda.synchronize()
+    log(f"[bench] orthogonalise: {len(mats)} matrices, {n_mat:,} params, "
+        f"{sum(flops.values()) / 1e12:.1f} TFLOP per step")
+    for _ in range(args.warmup):
+        step.run(theta, averaged, scale)
+    torch.cuda.synchronize()
+    recs = []
+
+    def timer(m, call):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        recs.append((m, e0, e1))
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.run(theta, averaged, scale, timer)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    by_shape = {}
+    for m, e0, e1 in recs:
+        d = by_shape.setdefault((m.rows, m.cols), [0, 0.0])
+        d[0] += 1
+        d[1] += e0.elapsed_time(e1)
+    shapes = {}
+    for (r, c), (cnt, tot) in by_shape.items():
+        f = sum(gemm_flops(r, c).values())
+        shapes[f"{r}x{c}"] = {"matrices_per_step": cnt // args.steps,
+                              "avg_ms_per_matrix": round(tot / cnt, 3),
+                              "TFLOP_per_s": round(f / (tot / cnt / 1e3) / 1e12, 2)}
+    log(f"[bench] {args.steps} orthogonalised steps: {ms:.1f} ms/step")
+
+    # every distinct product of the iteration, timed launch by launch through
+    # the same kernels with the same launch shapes (values: an iterate-like X
+    # and its Gram matrix)
+    prods = {}
+    for (r_, c_), cnt in ((k, v[0] // args.steps) for k, v in by_shape.items()):
+        r, L = min(r_, c_), max(r_, c_)
+        tall = r_ >= c_
+        x = torch.randn(r_ * c_, device=dev).mul_(1.0 / np.sqrt(r_ * c_ / r))
+        g = torch.randn(r * r, device=dev).mul_(1.0 / r)
+        out_x = torch.empty(r_ * c_, device=dev)
+        out_g = torch.empty(r * r, device=dev)
+        if tall:
+            cases = [("TN", "gram", (x, c_, x, c_, r, r, L, out_g, r), 18),
+                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), 12),
+                     ("NT", "next_iterate", (x, c_, g, r, L, r, r, out_x, c_), 18)]
+        else:
+            cases = [("NT", "gram", (x, c_, x, c_, r, r, L, out_g, r), 18),
+                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), 12),
+                     ("TN", "next_iterate", (g, r, x, c_, r, L, r, out_x, c_), 18)]
+        for form, what, a, per in cases:
+            fm = dl.DL_TN if form == "TN" else dl.DL_NT
+            if what == "gram_square":
+                a = (a[0], a[1], a[2], a[3], a[4], a[5], a[6], torch.empty_like(out_g), a[8])
+            call = lambda fm=fm, a=a: dl.dl_matmul_f32(fm, *a[:7], a[7], a[8])
+            call()
+            torch.cuda.synchronize()
+            evs = []
+            for _ in range(max(3, args.steps)):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            avg = sum(p.elapsed_time(q) for p, q in evs) / len(evs)
+            M, N, K = a[4], a[5], a[6]
+            prods[f"{form} {what} {M}x{N}x{K}"] = {
+                "form": form, "launches_per_step": per * cnt, "avg_ms": round(avg, 4),
+                "flops_per_launch": 2 * M * N * K,
+                "TFLOP_per_s": round(2 * M * N * K / (avg / 1e3) / 1e12, 2)}
+        del x, g, out_x, out_g
+    kinds = {}
+    for p in prods.values():
+        d = kinds.setdefault(p["form"], {"ms": 0.0, "flops": 0, "launches": 0})
+        d["ms"] += p["avg_ms"] * p["launches_per_step"]
+        d["flops"] += p["flops_per_launch"] * p["launches_per_step"]
+        d["launches"] += p["launches_per_step"]
+    dom = max(kinds, key=lambda k: kinds[k]["ms"])
+    dd = kinds[dom]
+    achieved = dd["flops"] / (dd["ms"] / 1e3) / 1e12
+    total_flops = sum(flops.values())
+    out = {
+        "metric": "orthogonalised outer step over every DiffuRefill-1B weight matrix: "
+                  "matrix params/s",
+        "value": round(n_mat / (ms / 1e3), 1),
+        "unit": "params/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 2),
+        "higher_is_better": True,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox; DiffuRefill-1B matrix shapes)",
+        "config": {"workload": "diffurefill1b_orthogonal_step", "matrices": len(mats),
+                   "matrix_params": n_mat, "quintic_steps": 12, "cubic_steps": 6,
+                   "algorithmic_flops_per_step": total_flops},
+        "TFLOP_per_s": round(total_flops / (ms / 1e3) / 1e12, 2),
+        "frac_of_mfma_f32_peak": round(total_flops / (ms / 1e3) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4),
+        "shapes": shapes,
+        "products": prods,
+        "roofline": {"kernel": f"k_gemm<{dom}>", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "algorithmic_flops_per_launch": dd["flops"] // dd["launches"],
+                     "avg_launch_ms": round(dd["ms"] / dd["launches"], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del theta, averaged, step
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline_polar()
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_polar(max_seconds: float = 12.0):
+    """The orthogonalisation oracle (fp64 SVD polar factor, unchanged) on
+    2048 x 2048 attention-shaped updates until about max_seconds have
+    passed; matrix params per second."""
+    import numpy as np
+    from oracle import polar
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:       # threadpoolctl missing: report the CPU count numpy may use
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(1007)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < max_seconds:
+        a = (rng.standard_normal((2048, 2048)) * 1e-3).astype(np.float32)
+        polar.polar_factor(a)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done * 2048 * 2048 / el, 1), "unit": "params/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} updates of 2048x2048 (one attention matrix each), fp64 SVD polar "
+                      f"factor, {el:.1f} s on {cpu_model()}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +360,9 @@ def main():
                          "streams (rounds in flight together)")
     ap.add_argument("--side-averages", action="store_true",
                     help="time the uniform average and snapshot averages instead of a round")
+    ap.add_argument("--orthogonalize", action="store_true",
+                    help="time the orthogonalised outer step over every weight matrix instead "
+                         "of a merge round")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")
@@ -212,6 +381,9 @@ def main():
         sys.exit(2)
     if args.side_averages:
         side_averages(args, torch)
+        return
+    if args.orthogonalize:
+        orthogonalize(args, torch)
         return
     w = synth.WORKLOADS[args.workload]
     ab = algorithmic_bytes(w)

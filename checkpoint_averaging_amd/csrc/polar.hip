@@ -36,11 +36,12 @@ namespace {
 
 constexpr int kTileM = 128;
 constexpr int kTileN = 128;
-constexpr int kTileK = 16;
-constexpr int kLds = kTileM + 1;      // padded LDS row (floats)
+constexpr int kTileK = 32;
+constexpr int kLdsRow = kTileK + 4;   // LDS row of one operand row's K-tile (floats)
 constexpr int kGemmThreads = 256;
 constexpr int kXcds = 8;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct Epilogue {
@@ -51,17 +52,73 @@ struct Epilogue {
     float alpha, beta, diag;
 };
 
+// One operand's K-tile: 128 operand rows (i for A, j for B) x 32 k, held as
+// 4 float4 per thread and stored to LDS as [row][k] (16-byte rows, so the
+// MFMA operand reads below are ds_read_b128).
+//   k-major storage, element (row, k) at P[k*ld + row] (both operands of TN):
+//     thread t owns row t%128 and k = 4*(t/128) + 8p + c, p, c = 0..3; each
+//     of the 16 scalar loads is coalesced across the wave (consecutive rows);
+//   row-major storage, element (row, k) at P[row*ld + k] (both of NT):
+//     thread t owns rows t/8 + 32p and k = 4*(t%8) + c: one float4 load each
+//     where `vec` says the row is 16-byte aligned and the 4 k are in range.
+template <bool KMajor>
+__device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int64_t r0,
+                                          int64_t R, int64_t k0, int64_t K, bool vec, int tid,
+                                          f32x4 (&v)[4]) {
+    if constexpr (KMajor) {
+        const int64_t row = r0 + (tid & 127);
+        const int kg = 4 * (tid >> 7);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t k = k0 + kg + 8 * p + c;
+                v[p][c] = (row < R && k < K) ? P[k * ld + row] : 0.0f;
+            }
+    } else {
+        const int64_t k = k0 + 4 * (tid & 7);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int64_t row = r0 + (tid >> 3) + 32 * p;
+            if (vec && row < R && k + 3 < K) {
+                v[p] = *reinterpret_cast<const f32x4*>(P + row * ld + k);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    v[p][c] = (row < R && k + c < K) ? P[row * ld + k + c] : 0.0f;
+            }
+        }
+    }
+}
+
+template <bool KMajor>
+__device__ __forceinline__ void store_tile(float (*S)[kLdsRow], const f32x4 (&v)[4], int tid) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float* dst = KMajor ? &S[tid & 127][4 * (tid >> 7) + 8 * p]
+                            : &S[(tid >> 3) + 32 * p][4 * (tid & 7)];
+        *reinterpret_cast<f32x4*>(dst) = v[p];
+    }
+}
+
 // C[i][j] = epi( sum_k opA[i][k] * opB[k][j] ) for i < M, j < N, with
 //   TN:  opA[i][k] = A[k*lda + i],  opB[k][j] = B[k*ldb + j]
 //   NT:  opA[i][k] = A[i*lda + k],  opB[k][j] = B[j*ldb + k]
+// A 128 x 128 output tile per workgroup; wave w computes the 64 x 64 quarter
+// (w/2, w%2) as 2 x 2 blocks of v_mfma_f32_32x32x2f32.  The K loop is
+// double-buffered: the next K-tile's global loads are in flight while the
+// MFMAs consume the current one from LDS; one barrier per K-tile.  Within a
+// K-tile, lane half h of MFMA step s carries k = 16h + s (the same k for the
+// A and B operands), so each lane reads its 16 k of a row with 4 b128 reads.
 template <bool TN>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__ A, int64_t lda,
                                                        const float* __restrict__ B, int64_t ldb,
                                                        int64_t M, int64_t N, int64_t K,
                                                        uint32_t tiles_n, uint32_t tiles,
-                                                       uint32_t per_xcd, Epilogue e) {
-    __shared__ float As[kTileK][kLds];
-    __shared__ float Bs[kTileK][kLds];
+                                                       uint32_t per_xcd, bool vec_a, bool vec_b,
+                                                       Epilogue e) {
+    __shared__ __align__(16) float As[2][kTileM][kLdsRow];
+    __shared__ __align__(16) float Bs[2][kTileN][kLdsRow];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -83,47 +140,45 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    for (int64_t k0 = 0; k0 < K; k0 += kTileK) {
-        // ---- global -> LDS, stored as [k][row] for both operands ----------
-        if constexpr (TN) {
-            // rows of A and B run along i / j: each instruction reads 2 rows
-            // x 128 consecutive floats.
-            const int col = tid & 127;
-#pragma unroll
-            for (int q = 0; q < kTileK / 2; ++q) {
-                const int kk = (tid >> 7) + 2 * q;
-                const int64_t k = k0 + kk;
-                const int64_t i = i0 + col, j = j0 + col;
-                As[kk][col] = (k < K && i < M) ? A[k * lda + i] : 0.0f;
-                Bs[kk][col] = (k < K && j < N) ? B[k * ldb + j] : 0.0f;
-            }
-        } else {
-            // rows of A and B run along k: each instruction reads 16 rows x
-            // 16 consecutive floats, transposed into LDS.
-            const int kk = tid & 15;
-            const int64_t k = k0 + kk;
-#pragma unroll
-            for (int q = 0; q < kTileM / 16; ++q) {
-                const int rr = (tid >> 4) + 16 * q;
-                const int64_t i = i0 + rr, j = j0 + rr;
-                As[kk][rr] = (k < K && i < M) ? A[i * lda + k] : 0.0f;
-                Bs[kk][rr] = (k < K && j < N) ? B[j * ldb + k] : 0.0f;
-            }
+    const int64_t ktiles = (K + kTileK - 1) / kTileK;
+    f32x4 ra[4], rb[4];
+    if (ktiles > 0) {
+        load_tile<TN>(A, lda, i0, M, 0, K, vec_a, tid, ra);
+        load_tile<TN>(B, ldb, j0, N, 0, K, vec_b, tid, rb);
+        store_tile<TN>(As[0], ra, tid);
+        store_tile<TN>(Bs[0], rb, tid);
+    }
+    __syncthreads();
+    const int h = lane >> 5, rl = lane & 31;
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const int cur = static_cast<int>(kt & 1);
+        const bool more = kt + 1 < ktiles;
+        if (more) {
+            load_tile<TN>(A, lda, i0, M, (kt + 1) * kTileK, K, vec_a, tid, ra);
+            load_tile<TN>(B, ldb, j0, N, (kt + 1) * kTileK, K, vec_b, tid, rb);
         }
-        __syncthreads();
-        // ---- MFMA over the K tile: lane l feeds A[row l%32][k l/32] and
-        //      B[k l/32][col l%32] -------------------------------------------
-        const int kl = lane >> 5, rl = lane & 31;
+        f32x4 a[2][4], b[2][4];
 #pragma unroll
-        for (int kk = 0; kk < kTileK; kk += 2) {
-            const float a0 = As[kk + kl][wr * 64 + rl];
-            const float a1 = As[kk + kl][wr * 64 + 32 + rl];
-            const float b0 = Bs[kk + kl][wc * 64 + rl];
-            const float b1 = Bs[kk + kl][wc * 64 + 32 + rl];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                a[mb][q] = *reinterpret_cast<const f32x4*>(&As[cur][wr * 64 + mb * 32 + rl][16 * h + 4 * q]);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                b[nb][q] = *reinterpret_cast<const f32x4*>(&Bs[cur][wc * 64 + nb * 32 + rl][16 * h + 4 * q]);
+        }
+#pragma unroll
+        for (int st = 0; st < kTileK / 2; ++st) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        a[mb][st >> 2][st & 3], b[nb][st >> 2][st & 3], acc[mb][nb], 0, 0, 0);
+        }
+        if (more) {
+            store_tile<TN>(As[cur ^ 1], ra, tid);
+            store_tile<TN>(Bs[cur ^ 1], rb, tid);
         }
         __syncthreads();
     }
@@ -215,12 +270,15 @@ hipError_t gemm(bool tn, const float* A, int64_t lda, const float* B, int64_t ld
     const dim3 grid(static_cast<unsigned>(per_xcd * kXcds));
     const uint32_t tn32 = static_cast<uint32_t>(tiles_n), t32 = static_cast<uint32_t>(tiles),
                    px32 = static_cast<uint32_t>(per_xcd);
+    // float4 loads of row-major operands need 16-byte aligned rows
+    const bool vec_a = reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 4 == 0;
+    const bool vec_b = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 4 == 0;
     if (tn)
         hipLaunchKernelGGL((k_gemm<true>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           tn32, t32, px32, e);
+                           tn32, t32, px32, vec_a, vec_b, e);
     else
         hipLaunchKernelGGL((k_gemm<false>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           tn32, t32, px32, e);
+                           tn32, t32, px32, vec_a, vec_b, e);
     return hipGetLastError();
 }
 

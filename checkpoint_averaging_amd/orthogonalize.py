@@ -1,0 +1,108 @@
+"""Outer orthogonalisation over a whole model (DiffuRefill-1B technical report,
+"What we measured", "Optimisers": the averaged outer update of each weight
+matrix is replaced by its polar factor).
+
+The flat parameter buffer holds every tensor back to back; the weight
+matrices are row-major views into it.  Vectors (norm weights) have no polar
+factor of interest and are left to the plain merge.  Every matrix is one
+call of dl_outer_orthogonal_step on one stream, all sharing one workspace
+sized for the largest matrix.
+"""
+from __future__ import annotations
+
+from typing import List, NamedTuple, Optional
+
+import torch
+
+from . import dlmerge as dl
+from . import synth
+
+
+class Matrix(NamedTuple):
+    name: str
+    offset: int        # element offset in the flat buffer
+    rows: int
+    cols: int
+
+
+def _shapes(layout: synth.Layout):
+    if layout.name == "diffurefill-1b":
+        d, vocab, ff = 2048, 73760, 5632
+        shape = {"embed": (vocab, d), "attn.wq": (d, d), "attn.wk": (d, d), "attn.wv": (d, d),
+                 "attn.wo": (d, d), "ffn.w_gate": (ff, d), "ffn.w_up": (ff, d),
+                 "ffn.w_down": (d, ff)}
+    elif layout.name == "pythia-14m":
+        d, vocab, ff = 128, 50304, 512
+        shape = {"embed_in": (vocab, d), "embed_out": (vocab, d),
+                 "attention.query_key_value.weight": (3 * d, d),
+                 "attention.dense.weight": (d, d), "mlp.dense_h_to_4h.weight": (ff, d),
+                 "mlp.dense_4h_to_h.weight": (d, ff)}
+    else:
+        raise KeyError(layout.name)
+    return shape
+
+
+def weight_matrices(layout: synth.Layout) -> List[Matrix]:
+    """The layout's weight matrices in flat order, with their offsets."""
+    shape = _shapes(layout)
+    out, off = [], 0
+    for name, n in layout.tensors:
+        key = name.split(".", 2)[-1] if name.startswith(("blocks.", "layers.")) else name
+        if key in shape:
+            r, c = shape[key]
+            if r * c != n:
+                raise ValueError(f"{name}: {r}x{c} != {n}")
+            out.append(Matrix(name, off, r, c))
+        off += n
+    return out
+
+
+def gemm_flops(rows: int, cols: int, quintic: int = 12, cubic: int = 6):
+    """Multiply-add flops (2 per product term) of the iteration on one matrix,
+    by product form, as the products are written: per step the r x r Gram
+    matrix over the long side (2 r^2 L), per quintic step the square of the
+    Gram matrix (2 r^3), per step the next iterate (2 L r^2); r the short
+    side, L the long one.  Tall matrices run the Gram product as TN and the
+    next iterate as NT; wide ones the other way round; the square is TN."""
+    r, L = min(rows, cols), max(rows, cols)
+    gram, square, nxt = 2 * r * r * L, 2 * r ** 3, 2 * L * r * r
+    steps = quintic + cubic
+    tn = (gram * steps if rows >= cols else nxt * steps) + square * quintic
+    nt = (nxt * steps if rows >= cols else gram * steps)
+    return {"TN": tn, "NT": nt}
+
+
+class OrthogonalStep:
+    """theta = theta - scale * P(theta - averaged) for every weight matrix of
+    a layout, on one stream, with one workspace."""
+
+    def __init__(self, layout: synth.Layout, device: Optional[torch.device] = None,
+                 quintic: int = 12, cubic: int = 6):
+        self.matrices = weight_matrices(layout)
+        self.quintic, self.cubic = quintic, cubic
+        need = max(dl.dl_polar_workspace_bytes(m.rows, m.cols) for m in self.matrices)
+        self.workspace = torch.empty((need + 3) // 4, dtype=torch.float32,
+                                     device=device or torch.device("cuda"))
+
+    def flops(self):
+        tot = {"TN": 0, "NT": 0}
+        for m in self.matrices:
+            for k, v in gemm_flops(m.rows, m.cols, self.quintic, self.cubic).items():
+                tot[k] += v
+        return tot
+
+    def run(self, theta: torch.Tensor, averaged: torch.Tensor, scale: float, timer=None):
+        """One orthogonalised outer step over the flat buffers.  `timer`, if
+        given, is called as timer(matrix, call) and must call call()."""
+        for m in self.matrices:
+            n = m.rows * m.cols
+            t = theta[m.offset:m.offset + n]
+            a = averaged[m.offset:m.offset + n]
+
+            def call(t=t, a=a, m=m):
+                dl.dl_outer_orthogonal_step(t, a, m.rows, m.cols, scale, self.workspace,
+                                            self.quintic, self.cubic)
+            if timer is None:
+                call()
+            else:
+                timer(m, call)
