@@ -246,21 +246,26 @@ def orthogonalize(args, torch):
         tall = r_ >= c_
         x = torch.randn(r_ * c_, device=dev).mul_(1.0 / np.sqrt(r_ * c_ / r))
         g = torch.randn(r * r, device=dev).mul_(1.0 / r)
+        g = (g.view(r, r) + g.view(r, r).t()).contiguous().view(-1)      # symmetric
         out_x = torch.empty(r_ * c_, device=dev)
         out_g = torch.empty(r * r, device=dev)
+        # the same cut as inside the iteration: symmetric r x r results, and
+        # a workspace for K ranges
         if tall:
-            cases = [("TN", "gram", (x, c_, x, c_, r, r, L, out_g, r), 18),
-                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), 12),
-                     ("NT", "next_iterate", (x, c_, g, r, L, r, r, out_x, c_), 18)]
+            cases = [("TN", "gram", (x, c_, x, c_, r, r, L, out_g, r), True, 18),
+                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), True, 12),
+                     ("NT", "next_iterate", (x, c_, g, r, L, r, r, out_x, c_), False, 18)]
         else:
-            cases = [("NT", "gram", (x, c_, x, c_, r, r, L, out_g, r), 18),
-                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), 12),
-                     ("TN", "next_iterate", (g, r, x, c_, r, L, r, out_x, c_), 18)]
-        for form, what, a, per in cases:
+            cases = [("NT", "gram", (x, c_, x, c_, r, r, L, out_g, r), True, 18),
+                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), True, 12),
+                     ("TN", "next_iterate", (g, r, x, c_, r, L, r, out_x, c_), False, 18)]
+        for form, what, a, sym, per in cases:
             fm = dl.DL_TN if form == "TN" else dl.DL_NT
-            if what == "gram_square":
-                a = (a[0], a[1], a[2], a[3], a[4], a[5], a[6], torch.empty_like(out_g), a[8])
-            call = lambda fm=fm, a=a: dl.dl_matmul_f32(fm, *a[:7], a[7], a[8])
+            M, N, K = a[4], a[5], a[6]
+            wsb = dl.dl_matmul_workspace_bytes(M, N, K, sym)
+            ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=dev)
+            call = lambda fm=fm, a=a, sym=sym, ws=ws, wsb=wsb: dl.dl_matmul_f32(
+                fm, *a[:7], a[7], a[8], symmetric=sym, workspace=ws if wsb else None)
             call()
             torch.cuda.synchronize()
             evs = []
@@ -273,11 +278,12 @@ def orthogonalize(args, torch):
                 evs.append((e0, e1))
             torch.cuda.synchronize()
             avg = sum(p.elapsed_time(q) for p, q in evs) / len(evs)
-            M, N, K = a[4], a[5], a[6]
+            outs = M * (M + 1) // 2 if sym else M * N      # distinct outputs
             prods[f"{form} {what} {M}x{N}x{K}"] = {
-                "form": form, "launches_per_step": per * cnt, "avg_ms": round(avg, 4),
-                "flops_per_launch": 2 * M * N * K,
-                "TFLOP_per_s": round(2 * M * N * K / (avg / 1e3) / 1e12, 2)}
+                "form": form, "symmetric": sym, "launches_per_step": per * cnt,
+                "avg_ms": round(avg, 4), "flops_per_launch": 2 * outs * K,
+                "TFLOP_per_s": round(2 * outs * K / (avg / 1e3) / 1e12, 2)}
+            del ws
         del x, g, out_x, out_g
     kinds = {}
     for p in prods.values():

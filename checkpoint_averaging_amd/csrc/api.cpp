@@ -459,11 +459,24 @@ int dl_adopt_keep_drift(float* theta, const float* global, const void* pushed, i
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 
+int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, int64_t* bytes) {
+    if (bytes == nullptr || m < 0 || n < 0 || k < 0) return DL_E_INVAL;
+    if (symmetric != 0 && symmetric != 1) return DL_E_INVAL;
+    if (symmetric && m != n) return DL_E_INVAL;
+    if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) || dlk::gemm_tiles(m, n) > dlk::kGemmMaxTiles)
+        return DL_E_INVAL;
+    *bytes = (m == 0 || n == 0) ? 0 : dlk::matmul_workspace_bytes(m, n, k, symmetric != 0);
+    return DL_OK;
+}
+
 int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t ldb, int64_t m,
                   int64_t n, int64_t k, float* c, int64_t ldc, const float* y, float alpha,
-                  float beta, float diag, void* stream) {
+                  float beta, float diag, int symmetric, void* workspace, int64_t workspace_bytes,
+                  void* stream) {
     if (form != DL_TN && form != DL_NT) return DL_E_INVAL;
-    if (m < 0 || n < 0 || k < 0) return DL_E_INVAL;
+    if (m < 0 || n < 0 || k < 0 || workspace_bytes < 0) return DL_E_INVAL;
+    if (symmetric != 0 && symmetric != 1) return DL_E_INVAL;
+    if (symmetric && m != n) return DL_E_INVAL;
     if (m == 0 || n == 0) return DL_OK;
     if (a == nullptr || b == nullptr || c == nullptr) return DL_E_INVAL;
     if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) || dlk::gemm_tiles(m, n) > dlk::kGemmMaxTiles)
@@ -475,6 +488,11 @@ int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t
     if (!aligned_to(a, alignof(float)) || !aligned_to(b, alignof(float)) ||
         !aligned_to(c, alignof(float)) || (y && !aligned_to(y, alignof(float))))
         return DL_E_ALIGN;
+    if (workspace != nullptr && !aligned_to(workspace, 256)) return DL_E_ALIGN;
+    const int64_t ws_bytes = workspace ? workspace_bytes : 0;
+    // a symmetric result needs room for at least one K range's upper tiles
+    const int64_t tn_ = (n + 127) / 128;
+    if (symmetric && ws_bytes < tn_ * (tn_ + 1) / 2 * 128 * 128 * 4) return DL_E_INVAL;
     const int64_t a_bytes = 4 * (tn ? (k > 0 ? (k - 1) * lda + m : 0) : (m - 1) * lda + k);
     const int64_t b_bytes = 4 * (tn ? (k > 0 ? (k - 1) * ldb + n : 0) : (n - 1) * ldb + k);
     const int64_t c_bytes = 4 * ((m - 1) * ldc + n);
@@ -482,6 +500,12 @@ int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t
     if (k > 0 && (c_s.overlaps(span_of(a, a_bytes)) || c_s.overlaps(span_of(b, b_bytes))))
         return DL_E_INVAL;
     if (y != nullptr && y != c && c_s.overlaps(span_of(y, c_bytes))) return DL_E_INVAL;
+    if (ws_bytes > 0) {
+        const Span w_s = span_of(workspace, ws_bytes);
+        if (w_s.overlaps(c_s) || (y && w_s.overlaps(span_of(y, c_bytes))) ||
+            (k > 0 && (w_s.overlaps(span_of(a, a_bytes)) || w_s.overlaps(span_of(b, b_bytes)))))
+            return DL_E_INVAL;
+    }
     if (k > 0) {
         if (int st = check_device_span(a, a_bytes)) return st;
         if (int st = check_device_span(b, b_bytes)) return st;
@@ -489,9 +513,12 @@ int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t
     if (int st = check_device_span(c, c_bytes)) return st;
     if (y != nullptr)
         if (int st = check_device_span(y, c_bytes)) return st;
+    if (ws_bytes > 0)
+        if (int st = check_device_span(workspace, ws_bytes)) return st;
     (void)hipGetLastError();
-    const hipError_t err = dlk::gemm_probe(tn, a, lda, b, ldb, m, n, k, c, ldc, y, alpha, beta,
-                                           diag, static_cast<hipStream_t>(stream));
+    const hipError_t err = dlk::matmul(tn, a, lda, b, ldb, m, n, k, c, ldc, y, alpha, beta, diag,
+                                       symmetric != 0, workspace, ws_bytes,
+                                       static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 

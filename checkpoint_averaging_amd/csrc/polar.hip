@@ -52,6 +52,47 @@ struct Epilogue {
     float alpha, beta, diag;
 };
 
+constexpr int kTileElems = kTileM * kTileN;
+
+// How one product is cut into workgroups: output tiles (all of them, or only
+// the upper triangle of a symmetric square result), times `splits` ranges of
+// K of `kchunk` elements each.  With `partial`, each workgroup writes its raw
+// 128 x 128 sums to its own slot of a partial buffer, and k_reduce_tiles adds
+// the K ranges in a fixed order, applies the epilogue and writes C (and the
+// mirror image for a symmetric result).
+struct Tiling {
+    uint32_t tiles_n;    // tiles along N (and along M when symmetric)
+    uint32_t tiles;      // output tiles computed
+    uint32_t splits;     // K ranges
+    uint32_t per_xcd;    // workgroups per XCD; the grid is 8 * per_xcd
+    int64_t kchunk;      // K elements per range, a multiple of the K-tile
+    bool sym;
+    bool partial;
+};
+
+// Output tile t -> (tile row, tile column): row-major over the tile grid, or
+// over the upper triangle (ti <= tj), where row ti holds tiles_n - ti tiles.
+__device__ __forceinline__ void tile_coords(uint32_t t, const Tiling& tl, uint32_t& ti,
+                                            uint32_t& tj) {
+    const uint32_t n = tl.tiles_n;
+    if (!tl.sym) {
+        ti = t / n;
+        tj = t % n;
+        return;
+    }
+    // first tile of row r: r*n - r*(r-1)/2, increasing in r; the row of t is
+    // the last r with first(r) <= t (binary search, integer arithmetic)
+    auto first = [n](uint32_t r) { return r * n - (r * (r - 1)) / 2; };
+    uint32_t lo = 0, hi = n;      // first(lo) <= t < first(hi)
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (first(mid) <= t) lo = mid;
+        else hi = mid;
+    }
+    ti = lo;
+    tj = lo + (t - first(lo));
+}
+
 // One operand's K-tile: 128 operand rows (i for A, j for B) x 32 k, held as
 // 4 float4 per thread and stored to LDS as [row][k] (16-byte rows, so the
 // MFMA operand reads below are ds_read_b128).
@@ -65,6 +106,7 @@ template <bool KMajor>
 __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int64_t r0,
                                           int64_t R, int64_t k0, int64_t K, bool vec, int tid,
                                           f32x4 (&v)[4]) {
+    // k0: first k of the tile; K: end of this workgroup's K range
     if constexpr (KMajor) {
         const int64_t row = r0 + (tid & 127);
         const int kg = 4 * (tid >> 7);
@@ -114,9 +156,8 @@ template <bool TN>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__ A, int64_t lda,
                                                        const float* __restrict__ B, int64_t ldb,
                                                        int64_t M, int64_t N, int64_t K,
-                                                       uint32_t tiles_n, uint32_t tiles,
-                                                       uint32_t per_xcd, bool vec_a, bool vec_b,
-                                                       Epilogue e) {
+                                                       Tiling tl, bool vec_a, bool vec_b,
+                                                       Epilogue e, float* __restrict__ part) {
     __shared__ __align__(16) float As[2][kTileM][kLdsRow];
     __shared__ __align__(16) float Bs[2][kTileN][kLdsRow];
     const int tid = threadIdx.x;
@@ -126,11 +167,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
     // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
     // contiguous run of tiles (row-major over the tile grid) so that the
     // tiles sharing an A row band meet in the same L2.
-    // (tile counts stay below 2^24, so the index arithmetic is 32-bit)
-    const uint32_t t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (t >= tiles) return;   // padding workgroup: the whole group leaves before any barrier
-    const int64_t i0 = static_cast<int64_t>(t / tiles_n) * kTileM;
-    const int64_t j0 = static_cast<int64_t>(t % tiles_n) * kTileN;
+    // Consecutive workgroups of one XCD share a K range and neighbouring
+    // tiles.  (Workgroup counts stay below 2^24: 32-bit index arithmetic.)
+    const uint32_t L = (blockIdx.x % kXcds) * tl.per_xcd + blockIdx.x / kXcds;
+    if (L >= tl.tiles * tl.splits) return;   // padding: the whole group leaves before any barrier
+    const uint32_t split = L / tl.tiles, t = L % tl.tiles;
+    uint32_t ti, tj;
+    tile_coords(t, tl, ti, tj);
+    const int64_t i0 = static_cast<int64_t>(ti) * kTileM;
+    const int64_t j0 = static_cast<int64_t>(tj) * kTileN;
+    const int64_t kb = static_cast<int64_t>(split) * tl.kchunk;
+    const int64_t ke = K < kb + tl.kchunk ? K : kb + tl.kchunk;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -140,11 +187,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    const int64_t ktiles = (K + kTileK - 1) / kTileK;
+    const int64_t ktiles = ke > kb ? (ke - kb + kTileK - 1) / kTileK : 0;
     f32x4 ra[4], rb[4];
     if (ktiles > 0) {
-        load_tile<TN>(A, lda, i0, M, 0, K, vec_a, tid, ra);
-        load_tile<TN>(B, ldb, j0, N, 0, K, vec_b, tid, rb);
+        load_tile<TN>(A, lda, i0, M, kb, ke, vec_a, tid, ra);
+        load_tile<TN>(B, ldb, j0, N, kb, ke, vec_b, tid, rb);
         store_tile<TN>(As[0], ra, tid);
         store_tile<TN>(Bs[0], rb, tid);
     }
@@ -154,8 +201,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
         const int cur = static_cast<int>(kt & 1);
         const bool more = kt + 1 < ktiles;
         if (more) {
-            load_tile<TN>(A, lda, i0, M, (kt + 1) * kTileK, K, vec_a, tid, ra);
-            load_tile<TN>(B, ldb, j0, N, (kt + 1) * kTileK, K, vec_b, tid, rb);
+            load_tile<TN>(A, lda, i0, M, kb + (kt + 1) * kTileK, ke, vec_a, tid, ra);
+            load_tile<TN>(B, ldb, j0, N, kb + (kt + 1) * kTileK, ke, vec_b, tid, rb);
         }
         f32x4 a[2][4], b[2][4];
 #pragma unroll
@@ -185,6 +232,20 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
 
     // ---- epilogue: accumulator r of lane l holds C[8(r/4) + 4(l/32) + r%4][l%32]
     //      of its 32 x 32 block --------------------------------------------------
+    if (tl.partial) {
+        float* pt = part + (static_cast<int64_t>(split) * tl.tiles + t) * kTileElems;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int li = wr * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int lj = wc * 64 + bj * 32 + (lane & 31);
+                    pt[li * kTileN + lj] = acc[bi][bj][r];
+                }
+        return;
+    }
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -200,6 +261,59 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
                     e.c[i * e.ldc + j] = v;
                 }
             }
+}
+
+// Sum of the K ranges' partial tiles (in range order), epilogue, and C.
+// Workgroup b handles rows 32(b%4) .. +31 of output tile b/4; thread t owns
+// columns 4(t%32) .. +3 of rows t/32 + 8p.  For a symmetric result the
+// elements with i <= j are written in place and those with i < j also to
+// C[j][i] through an LDS transpose (rows of 32 consecutive i per store).
+__global__ __launch_bounds__(256) void k_reduce_tiles(const float* __restrict__ part, Tiling tl,
+                                                      int64_t M, int64_t N, Epilogue e) {
+    __shared__ float tr[32][kTileN + 1];
+    const uint32_t t = blockIdx.x >> 2;
+    const int q = static_cast<int>(blockIdx.x & 3);
+    uint32_t ti, tj;
+    tile_coords(t, tl, ti, tj);
+    const int tid = threadIdx.x;
+    const int lj = 4 * (tid & 31);
+    const int64_t stride = static_cast<int64_t>(tl.tiles) * kTileElems;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int ll = (tid >> 5) + 8 * p;                    // row within the quarter
+        const int li = 32 * q + ll;
+        const float* src = part + static_cast<int64_t>(t) * kTileElems + li * kTileN + lj;
+        f32x4 v = *reinterpret_cast<const f32x4*>(src);
+        for (uint32_t sp = 1; sp < tl.splits; ++sp) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(src + sp * stride);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = v[c] + w[c];
+        }
+        const int64_t i = static_cast<int64_t>(ti) * kTileM + li;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t j = static_cast<int64_t>(tj) * kTileN + lj + c;
+            float o = e.alpha * v[c];
+            // a symmetric result reads Y and writes C only on and above the
+            // diagonal (Y may be C: the mirror writes below never meet a read)
+            if (i < M && j < N && (!tl.sym || i <= j)) {
+                if (e.y) o = o + e.beta * e.y[i * e.ldy + j];
+                if (i == j) o = o + e.diag;
+                e.c[i * e.ldc + j] = o;
+            }
+            tr[ll][lj + c] = o;
+        }
+    }
+    if (!tl.sym) return;      // uniform across the workgroup
+    __syncthreads();
+    const int ii = tid & 31;
+    const int64_t i = static_cast<int64_t>(ti) * kTileM + 32 * q + ii;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+        const int jj = (tid >> 5) + 8 * p;
+        const int64_t j = static_cast<int64_t>(tj) * kTileN + jj;
+        if (i < j && j < M) e.c[j * e.ldc + i] = tr[ii][jj];
+    }
 }
 
 // ---- Frobenius norm (two-stage fp64 reduction, fixed order) ---------------
@@ -262,31 +376,95 @@ constexpr float kQa = 3.4445f, kQb = -4.7750f, kQc = 2.0315f;
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
+constexpr int64_t kTargetGroups = 512;          // two resident workgroups on each of 256 CUs
+constexpr int64_t kMinSplitK = 8 * kTileK;      // each K range spans at least 8 K-tiles
+constexpr int64_t kMaxSplits = 16;
+
+// The cut of an M x N x K product (see Tiling).  ws_bytes bounds the partial
+// buffer; fewer K ranges are used if it is short.  Returns false if a
+// symmetric product cannot get even one range's partial tiles.
+bool plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t ws_bytes, Tiling& tl,
+               int64_t* need_bytes = nullptr) {
+    const int64_t tn = (N + kTileN - 1) / kTileN, tm = (M + kTileM - 1) / kTileM;
+    const int64_t tiles = sym ? tn * (tn + 1) / 2 : tm * tn;
+    int64_t splits = 1;
+    if (K > 0) {
+        const int64_t want = (kTargetGroups + tiles - 1) / tiles;
+        int64_t most = K / kMinSplitK;
+        if (most > kMaxSplits) most = kMaxSplits;
+        if (most < 1) most = 1;
+        splits = want < most ? want : most;
+    }
+    const int64_t tile_bytes = static_cast<int64_t>(kTileElems) * 4;
+    while (splits > 1 && splits * tiles * tile_bytes > ws_bytes) --splits;
+    const bool partial = sym || splits > 1;
+    if (partial && splits * tiles * tile_bytes > ws_bytes) return false;
+    int64_t kchunk = 0;
+    if (K > 0) {
+        kchunk = ((K + splits - 1) / splits + kTileK - 1) / kTileK * kTileK;
+        splits = (K + kchunk - 1) / kchunk;
+    }
+    tl.tiles_n = static_cast<uint32_t>(tn);
+    tl.tiles = static_cast<uint32_t>(tiles);
+    tl.splits = static_cast<uint32_t>(splits);
+    tl.per_xcd = static_cast<uint32_t>((tiles * splits + kXcds - 1) / kXcds);
+    tl.kchunk = kchunk;
+    tl.sym = sym;
+    tl.partial = partial;
+    if (need_bytes) *need_bytes = partial ? splits * tiles * tile_bytes : 0;
+    return true;
+}
+
+// Partial-buffer bytes the preferred cut of a product needs (0 if none).
+int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym) {
+    Tiling tl;
+    int64_t need = 0;
+    plan_gemm(M, N, K, sym, INT64_MAX, tl, &need);
+    return need;
+}
+
 hipError_t gemm(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
-                int64_t N, int64_t K, const Epilogue& e, hipStream_t s) {
-    const int64_t tiles_n = (N + kTileN - 1) / kTileN;
-    const int64_t tiles = (M + kTileM - 1) / kTileM * tiles_n;
-    const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-    const dim3 grid(static_cast<unsigned>(per_xcd * kXcds));
-    const uint32_t tn32 = static_cast<uint32_t>(tiles_n), t32 = static_cast<uint32_t>(tiles),
-                   px32 = static_cast<uint32_t>(per_xcd);
+                int64_t N, int64_t K, const Epilogue& e, bool sym, float* part,
+                int64_t part_bytes, hipStream_t s) {
+    Tiling tl;
+    if (!plan_gemm(M, N, K, sym, part ? part_bytes : 0, tl)) return hipErrorInvalidValue;
+    const dim3 grid(tl.per_xcd * kXcds);
     // float4 loads of row-major operands need 16-byte aligned rows
     const bool vec_a = reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 4 == 0;
     const bool vec_b = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 4 == 0;
     if (tn)
         hipLaunchKernelGGL((k_gemm<true>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           tn32, t32, px32, vec_a, vec_b, e);
+                           tl, vec_a, vec_b, e, part);
     else
         hipLaunchKernelGGL((k_gemm<false>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           tn32, t32, px32, vec_a, vec_b, e);
+                           tl, vec_a, vec_b, e, part);
+    if (tl.partial)
+        hipLaunchKernelGGL(k_reduce_tiles, dim3(tl.tiles * 4), dim3(256), 0, s, part, tl, M, N, e);
     return hipGetLastError();
+}
+
+}  // namespace
+
+namespace {
+
+// Partial-buffer bytes of the iteration's three products on a rows x cols
+// matrix: the symmetric Gram matrix, its symmetric square, the next iterate.
+int64_t polar_partial_bytes(int64_t rows, int64_t cols) {
+    const int64_t r = rows < cols ? rows : cols, L = rows < cols ? cols : rows;
+    int64_t b = gemm_partial_bytes(r, r, L, true);
+    const int64_t sq = gemm_partial_bytes(r, r, r, true);
+    const int64_t nx = gemm_partial_bytes(rows, cols, r, false);
+    if (sq > b) b = sq;
+    if (nx > b) b = nx;
+    return b;
 }
 
 }  // namespace
 
 int64_t polar_workspace_bytes(int64_t rows, int64_t cols) {
     const int64_t r = rows < cols ? rows : cols;
-    return align256(kRedBlocks * 8) + 256 + 2 * align256(rows * cols * 4) + 2 * align256(r * r * 4);
+    return align256(kRedBlocks * 8) + 256 + 2 * align256(rows * cols * 4) + 2 * align256(r * r * 4) +
+           align256(polar_partial_bytes(rows, cols));
 }
 
 hipError_t polar_iterate(const float* src, const float* sub, float* out, float* theta, float scale,
@@ -307,6 +485,9 @@ hipError_t polar_iterate(const float* src, const float* sub, float* out, float* 
     float* g = reinterpret_cast<float*>(p);
     p += align256(r * r * 4);
     float* m = reinterpret_cast<float*>(p);
+    p += align256(r * r * 4);
+    float* part = reinterpret_cast<float*>(p);
+    const int64_t part_bytes = align256(polar_partial_bytes(rows, cols));
 
     // X0 = A / ||A||_F, with A = src (or src - sub, formed in fp32 into xa)
     hipLaunchKernelGGL(k_sumsq_partial, dim3(kRedBlocks), dim3(kRedThreads), 0, s, src, sub,
@@ -324,12 +505,15 @@ hipError_t polar_iterate(const float* src, const float* sub, float* out, float* 
         // epilogue forms M = 1.5 I - 0.5 G directly.
         const Epilogue eg{quin ? g : m, r, nullptr, 0, quin ? 1.0f : -0.5f, 0.0f,
                           quin ? 0.0f : 1.5f};
-        hipError_t err = tall ? gemm(true, x, cols, x, cols, r, r, rows, eg, s)      // X^T X
-                              : gemm(false, x, cols, x, cols, r, r, cols, eg, s);   // X X^T
+        // Both r x r results are symmetric: only their upper triangles are
+        // computed, and the lower ones are mirror images (exactly symmetric).
+        hipError_t err =
+            tall ? gemm(true, x, cols, x, cols, r, r, rows, eg, true, part, part_bytes, s)   // X^T X
+                 : gemm(false, x, cols, x, cols, r, r, cols, eg, true, part, part_bytes, s); // X X^T
         if (err) return err;
         if (quin) {   // M = c G^2 + b G + a I  (G symmetric: G G = G^T G)
             const Epilogue em{m, r, g, r, kQc, kQb, kQa};
-            if ((err = gemm(true, g, r, g, r, r, r, r, em, s))) return err;
+            if ((err = gemm(true, g, r, g, r, r, r, r, em, true, part, part_bytes, s))) return err;
         }
         // next iterate: X M (tall) or M X (wide); the last step writes the
         // result: the polar factor to out, or theta - scale * P onto theta
@@ -337,8 +521,9 @@ hipError_t polar_iterate(const float* src, const float* sub, float* out, float* 
         Epilogue ex{xn, cols, nullptr, 0, 1.0f, 0.0f, 0.0f};
         if (last && out) ex.c = out;
         if (last && theta) ex = Epilogue{theta, cols, theta, cols, -scale, 1.0f, 0.0f};
-        err = tall ? gemm(false, x, cols, m, r, rows, cols, r, ex, s)    // C[i][j] = sum_k X[i][k] M[j][k]
-                   : gemm(true, m, r, x, cols, rows, cols, r, ex, s);    // C[i][j] = sum_k M[k][i] X[k][j]
+        err = tall ? gemm(false, x, cols, m, r, rows, cols, r, ex, false, part, part_bytes, s)
+                   : gemm(true, m, r, x, cols, rows, cols, r, ex, false, part, part_bytes, s);
+        // (tall: C[i][j] = sum_k X[i][k] M[j][k]; wide: C[i][j] = sum_k M[k][i] X[k][j])
         if (err) return err;
         float* t = x;
         x = xn;
@@ -347,11 +532,15 @@ hipError_t polar_iterate(const float* src, const float* sub, float* out, float* 
     return hipGetLastError();
 }
 
-hipError_t gemm_probe(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb,
-                      int64_t M, int64_t N, int64_t K, float* C, int64_t ldc, const float* Y,
-                      float alpha, float beta, float diag, hipStream_t s) {
+int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym) {
+    return gemm_partial_bytes(M, N, K, sym);
+}
+
+hipError_t matmul(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
+                  int64_t N, int64_t K, float* C, int64_t ldc, const float* Y, float alpha,
+                  float beta, float diag, bool sym, void* ws, int64_t ws_bytes, hipStream_t s) {
     const Epilogue e{C, ldc, Y, ldc, alpha, beta, diag};
-    return gemm(tn, A, lda, B, ldb, M, N, K, e, s);
+    return gemm(tn, A, lda, B, ldb, M, N, K, e, sym, static_cast<float*>(ws), ws ? ws_bytes : 0, s);
 }
 
 }  // namespace dlk

@@ -39,7 +39,7 @@ SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
            "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_factor",
-           "dl_outer_orthogonal_step", "dl_matmul_f32",
+           "dl_outer_orthogonal_step", "dl_matmul_workspace_bytes", "dl_matmul_f32",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
 DL_MAX_SNAPSHOTS = 16
@@ -69,8 +69,9 @@ _lib.dl_adopt_keep_drift.argtypes = [_p, _p, _p, _i32, _i64, _p]
 _lib.dl_polar_workspace_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_i64)]
 _lib.dl_polar_factor.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]
 _lib.dl_outer_orthogonal_step.argtypes = [_p, _p, _i64, _i64, _f32, _i32, _i32, _p, _i64, _p]
+_lib.dl_matmul_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64)]
 _lib.dl_matmul_f32.argtypes = [_i32, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _f32,
-                               _f32, _f32, _p]
+                               _f32, _f32, _i32, _p, _i64, _p]
 _lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dl_round_participants.argtypes = [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32]
 _lib.dl_round_tokens.argtypes = [_p, _i32, ctypes.POINTER(_i64)]
@@ -303,13 +304,26 @@ def dl_outer_orthogonal_step(theta: Array, averaged: Array, rows: int, cols: int
            "dl_outer_orthogonal_step")
 
 
+def dl_matmul_workspace_bytes(m: int, n: int, k: int, symmetric: bool = False) -> int:
+    b = _i64()
+    _check(_lib.dl_matmul_workspace_bytes(int(m), int(n), int(k), int(bool(symmetric)),
+                                          ctypes.byref(b)),
+           "dl_matmul_workspace_bytes")
+    return b.value
+
+
 def dl_matmul_f32(form: int, a: Array, lda: int, b: Array, ldb: int, m: int, n: int, k: int,
                   c: Array, ldc: int, y: Array = None, alpha: float = 1.0, beta: float = 0.0,
-                  diag: float = 0.0, stream=None) -> None:
+                  diag: float = 0.0, symmetric: bool = False, workspace: Array = None,
+                  workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace is None:
+        w, wb = None, 0
+    else:
+        w, wb = _ws(workspace, workspace_bytes)
     _check(_lib.dl_matmul_f32(int(form), _f32_addr(a, "a"), int(lda), _f32_addr(b, "b"), int(ldb),
                               int(m), int(n), int(k), _f32_addr(c, "c"), int(ldc),
                               _f32_addr(y, "y"), float(alpha), float(beta), float(diag),
-                              _stream(stream)),
+                              int(bool(symmetric)), w, wb, _stream(stream)),
            "dl_matmul_f32")
 
 

@@ -58,14 +58,16 @@ def weight_matrices(layout: synth.Layout) -> List[Matrix]:
 
 
 def gemm_flops(rows: int, cols: int, quintic: int = 12, cubic: int = 6):
-    """Multiply-add flops (2 per product term) of the iteration on one matrix,
-    by product form, as the products are written: per step the r x r Gram
-    matrix over the long side (2 r^2 L), per quintic step the square of the
-    Gram matrix (2 r^3), per step the next iterate (2 L r^2); r the short
-    side, L the long one.  Tall matrices run the Gram product as TN and the
-    next iterate as NT; wide ones the other way round; the square is TN."""
+    """Algorithmic flops (2 per product term) of the iteration on one matrix,
+    by product form.  r is the short side, L the long one.  Per step: the
+    Gram matrix over the long side, symmetric, so r (r + 1) / 2 distinct
+    outputs of 2 L flops each; per quintic step its square, also symmetric
+    (r (r + 1) / 2 outputs of 2 r flops); per step the next iterate (2 L r^2).
+    Tall matrices run the Gram product as TN and the next iterate as NT; wide
+    ones the other way round; the square is TN."""
     r, L = min(rows, cols), max(rows, cols)
-    gram, square, nxt = 2 * r * r * L, 2 * r ** 3, 2 * L * r * r
+    sym = r * (r + 1) // 2
+    gram, square, nxt = 2 * sym * L, 2 * sym * r, 2 * L * r * r
     steps = quintic + cubic
     tn = (gram * steps if rows >= cols else nxt * steps) + square * quintic
     nt = (nxt * steps if rows >= cols else gram * steps)

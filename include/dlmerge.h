@@ -361,12 +361,26 @@ enum dl_matmul_form {
  * epilogue:  C[i][j] = alpha * sum + beta * Y[i][j] + (i == j ? diag : 0)
  * for i < m, j < n, C and Y with leading dimension ldc (Y may be NULL or
  * equal C; otherwise it must not overlap C; C must not overlap A or B).
- * Accumulation is fp32 on MFMA.  m = 0 or n = 0 is a no-op.
- * Errors: DL_E_INVAL, DL_E_ALIGN, DL_E_HIP.
+ * Accumulation is fp32 on MFMA; results are deterministic for a given call.
+ *
+ * symmetric = 1 (m == n) declares the result symmetric (A^T A, A A^T, or the
+ * product of a symmetric matrix with itself) and Y symmetric or NULL: only
+ * the upper triangle is computed and the lower one is its mirror image.
+ *
+ * workspace: device memory (256-byte aligned, disjoint from every other
+ * argument) for partial sums when the product is cut along K to fill the
+ * GPU, and for the tiles of a symmetric result; it may be NULL when
+ * symmetric = 0 (the product is then not cut along K).  A workspace of
+ * dl_matmul_workspace_bytes bytes gives the preferred cut; a smaller one
+ * gives fewer K ranges, which changes the summation order.  m = 0 or n = 0
+ * is a no-op.  Errors: DL_E_INVAL (also: symmetric with m != n or a
+ * workspace too small for one K range), DL_E_ALIGN, DL_E_HIP.
  */
+int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, int64_t *bytes);
 int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t ldb, int64_t m,
                   int64_t n, int64_t k, float *c, int64_t ldc, const float *y, float alpha,
-                  float beta, float diag, void *stream);
+                  float beta, float diag, int symmetric, void *workspace,
+                  int64_t workspace_bytes, void *stream);
 
 /* Element range [offset, offset + length) of fragment frag.  DL_E_INVAL. */
 int dl_frag_range(const dl_round *r, int frag, int64_t *offset, int64_t *length);

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 20
+    assert len(declared) == 21
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -243,6 +243,37 @@ def test_matmul_host_rules():
         _expect(dl.DL_E_INVAL, mm, **kw)
     _expect(dl.DL_E_ALIGN, mm, c=c + 2)
     _expect(dl.DL_E_ALIGN, mm, y=b + (1 << 20) + 1)
+    ws = FAKE + (1 << 32)
+    wsb = dl.dl_matmul_workspace_bytes(64, 64, 16, True)
+    _expect(dl.DL_E_INVAL, mm, symmetric=True)                     # 64 x 32 is not square
+    _expect(dl.DL_E_INVAL, mm, symmetric=True, n=64, ldb=64, ldc=64)   # no workspace
+    _expect(dl.DL_E_INVAL, mm, symmetric=True, n=64, ldb=64, ldc=64, workspace=ws,
+            workspace_bytes=wsb - 4)
+    _expect(dl.DL_E_ALIGN, mm, workspace=ws + 16, workspace_bytes=1 << 20)
+    _expect(dl.DL_E_INVAL, mm, workspace=c - 256, workspace_bytes=1 << 20)    # overlaps C
+    _expect(dl.DL_E_INVAL, mm, workspace=a, workspace_bytes=1 << 20)          # overlaps A
+    _expect(dl.DL_E_INVAL, mm, workspace=ws, workspace_bytes=-1)
+
+
+def test_matmul_workspace_sizes():
+    tile = 128 * 128 * 4
+    # a symmetric 2048 x 2048 result: 136 upper tiles, cut into 4 K ranges
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 73760, True) == 4 * 136 * tile
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, True) == 4 * 136 * tile
+    # short K: one range per tile, still the tiles of the symmetric result
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 100, True) == 136 * tile
+    # 256 tiles: two K ranges fill the GPU; 704 tiles need no cut
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, False) == 2 * 256 * tile
+    assert dl.dl_matmul_workspace_bytes(5632, 2048, 2048, False) == 0
+    assert dl.dl_matmul_workspace_bytes(0, 5, 5, False) == 0
+    # a single small tile: at most 16 ranges of at least 256 k each
+    assert dl.dl_matmul_workspace_bytes(100, 100, 1 << 20, False) == 16 * tile
+    assert dl.dl_matmul_workspace_bytes(100, 100, 1000, False) == 3 * tile
+    for bad in ((5, 6, 7, True), (-1, 5, 5, False), (5, 5, -1, False)):
+        _expect(dl.DL_E_INVAL, dl.dl_matmul_workspace_bytes, *bad)
+    # the polar workspace includes the largest partial buffer of its products
+    ws = dl.dl_polar_workspace_bytes(2048, 2048)
+    assert ws >= 2 * 2048 * 2048 * 4 * 2 + 4 * 136 * tile
 
 
 def test_participants_capacity():

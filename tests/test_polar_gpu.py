@@ -121,6 +121,84 @@ def test_matmul_against_fp64(form, m, n, k, epi):
     assert np.array_equal(got[:, n:], c0[:, n:].astype(np.float64))
 
 
+def _bound_check(got, want, mag, k):
+    g = (k + 4) * U32 / (1 - (k + 4) * U32)
+    err = np.abs(got - want)
+    assert np.all(err <= g * mag + 1e-30), (float(np.max(err / (mag + 1e-30))), g)
+
+
+@pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
+@pytest.mark.parametrize("n,k", [(1, 5), (130, 33), (300, 700), (257, 2000), (128, 4096),
+                                 (384, 300)])
+@pytest.mark.parametrize("ws_mode", ["preferred", "one_range"])
+@pytest.mark.parametrize("y_mode", ["none", "separate", "in_place"])
+def test_matmul_symmetric(form, n, k, ws_mode, y_mode):
+    """A Gram product (X^T X as TN, X X^T as NT) declared symmetric: the upper
+    triangle within the product bound, the lower one its exact mirror."""
+    rng = np.random.default_rng(n * 13 + k)
+    x = rng.standard_normal((k, n + 2) if form == dl.DL_TN else (n, k + 2)).astype(np.float32)
+    x64 = x.astype(np.float64)
+    gram = x64[:, :n].T @ x64[:, :n] if form == dl.DL_TN else x64[:, :k] @ x64[:, :k].T
+    mag = np.abs(x64[:, :n]).T @ np.abs(x64[:, :n]) if form == dl.DL_TN else \
+        np.abs(x64[:, :k]) @ np.abs(x64[:, :k]).T
+    ldc = n + 3
+    r = rng.standard_normal((n, n)).astype(np.float32)
+    ysym = np.zeros((n, ldc), np.float32)
+    ysym[:, :n] = (r + r.T) * np.float32(0.5)
+    c0 = ysym.copy() if y_mode == "in_place" else rng.standard_normal((n, ldc)).astype(np.float32)
+    alpha, beta, diag = (1.0, 0.0, 0.0) if y_mode == "none" else (2.0315, -4.775, 3.4445)
+    x_d, c_d = gpu(x), gpu(c0)
+    y_d = None if y_mode == "none" else (c_d if y_mode == "in_place" else gpu(ysym))
+    tn_ = (n + 127) // 128
+    wsb = (dl.dl_matmul_workspace_bytes(n, n, k, True) if ws_mode == "preferred"
+           else tn_ * (tn_ + 1) // 2 * 128 * 128 * 4)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=DEV)
+    dl.dl_matmul_f32(form, x_d, x.shape[1], x_d, x.shape[1], n, n, k, c_d, ldc, y_d, alpha, beta,
+                     diag, symmetric=True, workspace=ws)
+    got = host(c_d)
+    want = alpha * gram + np.eye(n) * diag
+    mg = abs(alpha) * mag + np.abs(np.eye(n) * diag)
+    if y_mode != "none":
+        want = want + beta * ysym[:, :n].astype(np.float64)
+        mg = mg + abs(beta) * np.abs(ysym[:, :n].astype(np.float64))
+    _bound_check(got[:, :n], want, mg, k)
+    assert np.array_equal(got[:, :n], got[:, :n].T)
+    assert np.array_equal(got[:, n:], c0[:, n:].astype(np.float64))
+
+
+@pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
+@pytest.mark.parametrize("m,n,k", [(100, 100, 5000), (256, 256, 2048), (129, 300, 1000),
+                                   (640, 384, 777)])
+def test_matmul_cut_along_k(form, m, n, k):
+    """With a workspace the product is cut into K ranges (summed in range
+    order); the result stays within the product bound, is the same on a
+    second call, and a workspace for fewer ranges still gives a result
+    within the bound."""
+    rng = np.random.default_rng(m + n + k)
+    if form == dl.DL_TN:
+        a = rng.standard_normal((k, m)).astype(np.float32)
+        b = rng.standard_normal((k, n)).astype(np.float32)
+        opa, opb = a.astype(np.float64).T, b.astype(np.float64)
+        lda, ldb = m, n
+    else:
+        a = rng.standard_normal((m, k)).astype(np.float32)
+        b = rng.standard_normal((n, k)).astype(np.float32)
+        opa, opb = a.astype(np.float64), b.astype(np.float64).T
+        lda, ldb = k, k
+    want, mag = opa @ opb, np.abs(opa) @ np.abs(opb)
+    a_d, b_d = gpu(a), gpu(b)
+    wsb = dl.dl_matmul_workspace_bytes(m, n, k, False)
+    assert wsb > 0
+    outs = []
+    for nbytes in (wsb, wsb, 2 * 128 * 128 * 4 * ((m + 127) // 128) * ((n + 127) // 128)):
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+        c_d = torch.empty((m, n), device=DEV)
+        dl.dl_matmul_f32(form, a_d, lda, b_d, ldb, m, n, k, c_d, n, workspace=ws)
+        outs.append(host(c_d))
+        _bound_check(outs[-1], want, mag, k)
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_matmul_k0_writes_the_epilogue():
     m, n = 70, 90
     c = torch.full((m, n), 7.0, device=DEV)
