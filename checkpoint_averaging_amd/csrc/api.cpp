@@ -490,9 +490,6 @@ int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t
         return DL_E_ALIGN;
     if (workspace != nullptr && !aligned_to(workspace, 256)) return DL_E_ALIGN;
     const int64_t ws_bytes = workspace ? workspace_bytes : 0;
-    // a symmetric result needs room for at least one K range's upper tiles
-    const int64_t tn_ = (n + 127) / 128;
-    if (symmetric && ws_bytes < tn_ * (tn_ + 1) / 2 * 128 * 128 * 4) return DL_E_INVAL;
     const int64_t a_bytes = 4 * (tn ? (k > 0 ? (k - 1) * lda + m : 0) : (m - 1) * lda + k);
     const int64_t b_bytes = 4 * (tn ? (k > 0 ? (k - 1) * ldb + n : 0) : (n - 1) * ldb + k);
     const int64_t c_bytes = 4 * ((m - 1) * ldc + n);

@@ -24,17 +24,17 @@ hipError_t polar_iterate(const float* src, const float* sub, float* out, float* 
                          int64_t rows, int64_t cols, int quintic, int cubic, void* ws,
                          hipStream_t s);
 
-// Workspace bytes the preferred cut of an M x N x K product uses (partial
-// sums of K ranges, or the tiles of a symmetric result; 0 if none).
+// Workspace bytes for the stream-K split of an M x N x K product (partial
+// sums of the tiles cut between workgroups).
 int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym);
 
 // One fp32 MFMA product C = alpha * op(A, B) + beta * Y + diag * I (Y may be
 // null or equal C):  tn: sum_k A[k*lda + i] * B[k*ldb + j];
 //                    nt: sum_k A[i*lda + k] * B[j*ldb + k]; i < M, j < N.
 // With sym (M == N, a symmetric result and a symmetric or null Y) only the
-// upper triangle is computed and mirrored.  ws (ws_bytes, may be null when
-// not sym) holds partial sums; with less than matmul_workspace_bytes fewer K
-// ranges are used.  hipErrorInvalidValue if sym and ws cannot hold one range.
+// upper triangle is computed and mirrored.  With ws_bytes >=
+// matmul_workspace_bytes the work is spread stream-K; otherwise (ws may be
+// null) one workgroup per output tile.
 hipError_t matmul(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
                   int64_t N, int64_t K, float* C, int64_t ldc, const float* Y, float alpha,
                   float beta, float diag, bool sym, void* ws, int64_t ws_bytes, hipStream_t s);

@@ -16,15 +16,19 @@
 // within fp32 rounding.  For a wide matrix (rows < cols) the same runs on
 // G = X X^T with X <- M X.
 //
-// Every product is a plain GEMM of fp32 on MFMA (v_mfma_f32_32x32x2f32):
+// Every product is a GEMM of fp32 on MFMA (v_mfma_f32_32x32x2f32):
 // workgroups of 4 wave64 compute 128 x 128 output tiles, each wave a 64 x 64
-// quarter as 2 x 2 MFMA blocks of 32 x 32, over K in steps of 16 staged
-// through LDS (row stride 129 floats: no bank conflicts on the transposed
-// writes or the operand reads).  The epilogue is fused: out = alpha*acc +
-// beta*Y + (i == j ? d : 0), which forms a I + b G + c G^2 in the G^2 product,
-// 1.5 I - 0.5 G in the Gram product, and theta - s*P in the last product.
-// The Frobenius norm is a deterministic two-stage fp64 reduction (no
-// atomics: the same input gives the same bits).
+// quarter as 2 x 2 MFMA blocks of 32 x 32, over K in tiles of 32 staged
+// through LDS with the next tile's loads in flight.  The work of a product
+// (output tiles x K-tiles) is spread evenly over as many workgroups as the
+// GPU holds at once (stream-K); tiles cut between workgroups are summed in K
+// order by a second kernel, so results are deterministic.  The Gram matrix
+// and its square are symmetric: only their upper tiles are computed and the
+// lower ones are written as mirror images.  The epilogue is fused: out =
+// alpha*acc + beta*Y + (i == j ? d : 0), which forms a I + b G + c G^2 in the
+// G^2 product, 1.5 I - 0.5 G in the Gram product, and theta - s*P in the
+// last product.  The Frobenius norm is a deterministic two-stage fp64
+// reduction (no atomics: the same input gives the same bits).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,28 +58,44 @@ struct Epilogue {
 
 constexpr int kTileElems = kTileM * kTileN;
 
-// How one product is cut into workgroups: output tiles (all of them, or only
-// the upper triangle of a symmetric square result), times `splits` ranges of
-// K of `kchunk` elements each.  With `partial`, each workgroup writes its raw
-// 128 x 128 sums to its own slot of a partial buffer, and k_reduce_tiles adds
-// the K ranges in a fixed order, applies the epilogue and writes C (and the
-// mirror image for a symmetric result).
-struct Tiling {
+// How one product is spread over workgroups.  It has `tiles` output tiles
+// of 128 x 128 (all of them, or the upper triangle of a symmetric result)
+// and `kt` K-tiles of 32 per output tile.  With `groups` workgroups:
+//   * first, dp_rounds rounds of whole tiles: in round r workgroup w takes
+//     tile r * groups + w, so the workgroups running together work on
+//     neighbouring tiles (and share operand rows in L2);
+//   * then the remaining sk_tiles tiles, stream-K: their units = sk_tiles *
+//     kt K-tiles, tile after tile, are dealt out as contiguous runs,
+//     workgroup w taking [begin(w), begin(w + 1)), begin(w) = floor(units *
+//     w / groups): whole tiles, with possibly a piece of a tile at either
+//     end.  A piece stores its raw sums in partial slot 2w (the workgroup's
+//     first stream-K piece) or 2w + 1 (its last one), and k_reduce_pieces
+//     adds the pieces of each cut tile in K order.
+// Without a workspace: groups = tiles, one round of whole tiles, no pieces.
+struct Work {
     uint32_t tiles_n;    // tiles along N (and along M when symmetric)
     uint32_t tiles;      // output tiles computed
-    uint32_t splits;     // K ranges
-    uint32_t per_xcd;    // workgroups per XCD; the grid is 8 * per_xcd
-    int64_t kchunk;      // K elements per range, a multiple of the K-tile
+    uint32_t kt;         // K-tiles per output tile (at least 1)
+    uint32_t groups;     // workgroups with work
+    uint32_t per_xcd;    // the grid is 8 * per_xcd workgroups
+    uint32_t dp_rounds;  // rounds of whole tiles
+    uint32_t units;      // stream-K units: (tiles - dp_rounds * groups) * kt, below 2^32
     bool sym;
-    bool partial;
 };
+
+// floor(units * w / groups), in 32-bit arithmetic (stream-K splits have at
+// most 512 workgroups, so r * w stays below 2^18)
+__device__ __forceinline__ uint32_t unit_begin(const Work& wk, uint32_t w) {
+    const uint32_t q = wk.units / wk.groups, r = wk.units % wk.groups;
+    return q * w + r * w / wk.groups;
+}
 
 // Output tile t -> (tile row, tile column): row-major over the tile grid, or
 // over the upper triangle (ti <= tj), where row ti holds tiles_n - ti tiles.
-__device__ __forceinline__ void tile_coords(uint32_t t, const Tiling& tl, uint32_t& ti,
+__device__ __forceinline__ void tile_coords(uint32_t t, const Work& wk, uint32_t& ti,
                                             uint32_t& tj) {
-    const uint32_t n = tl.tiles_n;
-    if (!tl.sym) {
+    const uint32_t n = wk.tiles_n;
+    if (!wk.sym) {
         ti = t / n;
         tj = t % n;
         return;
@@ -93,41 +113,55 @@ __device__ __forceinline__ void tile_coords(uint32_t t, const Tiling& tl, uint32
     tj = lo + (t - first(lo));
 }
 
-// One operand's K-tile: 128 operand rows (i for A, j for B) x 32 k, held as
-// 4 float4 per thread and stored to LDS as [row][k] (16-byte rows, so the
+// One operand's K-tile: 128 operand rows (i for A, j for B) x 32 k, loaded
+// as 4 float4 per thread and stored to LDS as [row][k] (16-byte rows, so the
 // MFMA operand reads below are ds_read_b128).
 //   k-major storage, element (row, k) at P[k*ld + row] (both operands of TN):
-//     thread t owns row t%128 and k = 4*(t/128) + 8p + c, p, c = 0..3; each
-//     of the 16 scalar loads is coalesced across the wave (consecutive rows);
+//     thread t loads rows 4(t%32) .. +3 of k = 4(t/32) .. +3: four float4
+//     loads along the rows (32 lanes cover 512 contiguous bytes), transposed
+//     in registers into four [row][k] float4 stores;
 //   row-major storage, element (row, k) at P[row*ld + k] (both of NT):
-//     thread t owns rows t/8 + 32p and k = 4*(t%8) + c: one float4 load each
-//     where `vec` says the row is 16-byte aligned and the 4 k are in range.
+//     thread t loads rows t/8 + 32p, k = 4(t%8) .. +3: one float4 each.
+// Interior tiles with 16-byte aligned rows (`vec`) load without any check;
+// edge tiles load every element from a clamped, valid address and select 0
+// outside the operand or this workgroup's K range (no branches).
+// k0: first k of the tile; K: end of the K range; R: operand rows.
 template <bool KMajor>
 __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int64_t r0,
                                           int64_t R, int64_t k0, int64_t K, bool vec, int tid,
                                           f32x4 (&v)[4]) {
-    // k0: first k of the tile; K: end of this workgroup's K range
+    const bool fast = vec && r0 + kTileM <= R && k0 + kTileK <= K;
     if constexpr (KMajor) {
-        const int64_t row = r0 + (tid & 127);
-        const int kg = 4 * (tid >> 7);
+        const int64_t row = r0 + 4 * (tid & 31);
+        const int64_t kq = k0 + 4 * (tid >> 5);
+        if (fast) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+            for (int kk = 0; kk < 4; ++kk)
+                v[kk] = *reinterpret_cast<const f32x4*>(P + (kq + kk) * ld + row);
+        } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t k = k0 + kg + 8 * p + c;
-                v[p][c] = (row < R && k < K) ? P[k * ld + row] : 0.0f;
-            }
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t k = kq + kk, rr = row + c;
+                    const float x = P[(k < K ? k : K - 1) * ld + (rr < R ? rr : R - 1)];
+                    v[kk][c] = (k < K && rr < R) ? x : 0.0f;
+                }
+        }
     } else {
         const int64_t k = k0 + 4 * (tid & 7);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int64_t row = r0 + (tid >> 3) + 32 * p;
-            if (vec && row < R && k + 3 < K) {
+            if (fast) {
                 v[p] = *reinterpret_cast<const f32x4*>(P + row * ld + k);
             } else {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    v[p][c] = (row < R && k + c < K) ? P[row * ld + k + c] : 0.0f;
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t kc = k + c;
+                    const float x = P[(row < R ? row : R - 1) * ld + (kc < K ? kc : K - 1)];
+                    v[p][c] = (row < R && kc < K) ? x : 0.0f;
+                }
             }
         }
     }
@@ -135,51 +169,48 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
 
 template <bool KMajor>
 __device__ __forceinline__ void store_tile(float (*S)[kLdsRow], const f32x4 (&v)[4], int tid) {
+    if constexpr (KMajor) {
+        const int row = 4 * (tid & 31), k = 4 * (tid >> 5);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        float* dst = KMajor ? &S[tid & 127][4 * (tid >> 7) + 8 * p]
-                            : &S[(tid >> 3) + 32 * p][4 * (tid & 7)];
-        *reinterpret_cast<f32x4*>(dst) = v[p];
+        for (int c = 0; c < 4; ++c) {
+            const f32x4 w = {v[0][c], v[1][c], v[2][c], v[3][c]};
+            *reinterpret_cast<f32x4*>(&S[row + c][k]) = w;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            *reinterpret_cast<f32x4*>(&S[(tid >> 3) + 32 * p][4 * (tid & 7)]) = v[p];
     }
 }
 
-// C[i][j] = epi( sum_k opA[i][k] * opB[k][j] ) for i < M, j < N, with
-//   TN:  opA[i][k] = A[k*lda + i],  opB[k][j] = B[k*ldb + j]
-//   NT:  opA[i][k] = A[i*lda + k],  opB[k][j] = B[j*ldb + k]
-// A 128 x 128 output tile per workgroup; wave w computes the 64 x 64 quarter
-// (w/2, w%2) as 2 x 2 blocks of v_mfma_f32_32x32x2f32.  The K loop is
-// double-buffered: the next K-tile's global loads are in flight while the
-// MFMAs consume the current one from LDS; one barrier per K-tile.  Within a
-// K-tile, lane half h of MFMA step s carries k = 16h + s (the same k for the
-// A and B operands), so each lane reads its 16 k of a row with 4 b128 reads.
+typedef float LdsRow[kLdsRow];
+constexpr int kLdsFloats = 2 * (kTileM + kTileN) * kLdsRow;   // two buffers of A and B tiles
+constexpr int kStage = kTileN + 1;                             // staged output tile row (floats)
+static_assert(kTileM * kStage <= kLdsFloats, "the staged output tile reuses the operand buffers");
+
+__device__ __forceinline__ LdsRow* lds_a(float* smem, int buf) {
+    return reinterpret_cast<LdsRow*>(smem + buf * (kTileM + kTileN) * kLdsRow);
+}
+__device__ __forceinline__ LdsRow* lds_b(float* smem, int buf) {
+    return reinterpret_cast<LdsRow*>(smem + (buf * (kTileM + kTileN) + kTileM) * kLdsRow);
+}
+
+// acc += opA[i0.., kb..ke) * opB[kb..ke), j0..] for one 128 x 128 tile.  The K
+// loop is double-buffered: the next K-tile's global loads are in flight
+// while the MFMAs consume the current one from LDS; one barrier per K-tile.
+// Within a K-tile, lane half h of MFMA step s carries k = 16h + s (the same k
+// for the A and B operands), so each lane reads its 16 k of a row with four
+// b128 reads.  Ends with a barrier: LDS is free for the caller afterwards.
 template <bool TN>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__ A, int64_t lda,
-                                                       const float* __restrict__ B, int64_t ldb,
-                                                       int64_t M, int64_t N, int64_t K,
-                                                       Tiling tl, bool vec_a, bool vec_b,
-                                                       Epilogue e, float* __restrict__ part) {
-    __shared__ __align__(16) float As[2][kTileM][kLdsRow];
-    __shared__ __align__(16) float Bs[2][kTileN][kLdsRow];
+__device__ __forceinline__ void mma_tile(const float* __restrict__ A, int64_t lda,
+                                         const float* __restrict__ B, int64_t ldb, int64_t M,
+                                         int64_t N, int64_t i0, int64_t j0, int64_t kb,
+                                         int64_t ke, bool vec_a, bool vec_b, float* smem,
+                                         f32x16 (&acc)[2][2]) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;        // 2 x 2 waves of 64 x 64
-    // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
-    // contiguous run of tiles (row-major over the tile grid) so that the
-    // tiles sharing an A row band meet in the same L2.
-    // Consecutive workgroups of one XCD share a K range and neighbouring
-    // tiles.  (Workgroup counts stay below 2^24: 32-bit index arithmetic.)
-    const uint32_t L = (blockIdx.x % kXcds) * tl.per_xcd + blockIdx.x / kXcds;
-    if (L >= tl.tiles * tl.splits) return;   // padding: the whole group leaves before any barrier
-    const uint32_t split = L / tl.tiles, t = L % tl.tiles;
-    uint32_t ti, tj;
-    tile_coords(t, tl, ti, tj);
-    const int64_t i0 = static_cast<int64_t>(ti) * kTileM;
-    const int64_t j0 = static_cast<int64_t>(tj) * kTileN;
-    const int64_t kb = static_cast<int64_t>(split) * tl.kchunk;
-    const int64_t ke = K < kb + tl.kchunk ? K : kb + tl.kchunk;
-
-    f32x16 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -192,8 +223,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
     if (ktiles > 0) {
         load_tile<TN>(A, lda, i0, M, kb, ke, vec_a, tid, ra);
         load_tile<TN>(B, ldb, j0, N, kb, ke, vec_b, tid, rb);
-        store_tile<TN>(As[0], ra, tid);
-        store_tile<TN>(Bs[0], rb, tid);
+        store_tile<TN>(lds_a(smem, 0), ra, tid);
+        store_tile<TN>(lds_b(smem, 0), rb, tid);
     }
     __syncthreads();
     const int h = lane >> 5, rl = lane & 31;
@@ -204,15 +235,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
             load_tile<TN>(A, lda, i0, M, kb + (kt + 1) * kTileK, ke, vec_a, tid, ra);
             load_tile<TN>(B, ldb, j0, N, kb + (kt + 1) * kTileK, ke, vec_b, tid, rb);
         }
+        LdsRow* as = lds_a(smem, cur);
+        LdsRow* bs = lds_b(smem, cur);
         f32x4 a[2][4], b[2][4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
-                a[mb][q] = *reinterpret_cast<const f32x4*>(&As[cur][wr * 64 + mb * 32 + rl][16 * h + 4 * q]);
+                a[mb][q] = *reinterpret_cast<const f32x4*>(&as[wr * 64 + mb * 32 + rl][16 * h + 4 * q]);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
-                b[nb][q] = *reinterpret_cast<const f32x4*>(&Bs[cur][wc * 64 + nb * 32 + rl][16 * h + 4 * q]);
+                b[nb][q] = *reinterpret_cast<const f32x4*>(&bs[wc * 64 + nb * 32 + rl][16 * h + 4 * q]);
         }
 #pragma unroll
         for (int st = 0; st < kTileK / 2; ++st) {
@@ -224,79 +257,178 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
                         a[mb][st >> 2][st & 3], b[nb][st >> 2][st & 3], acc[mb][nb], 0, 0, 0);
         }
         if (more) {
-            store_tile<TN>(As[cur ^ 1], ra, tid);
-            store_tile<TN>(Bs[cur ^ 1], rb, tid);
+            store_tile<TN>(lds_a(smem, cur ^ 1), ra, tid);
+            store_tile<TN>(lds_b(smem, cur ^ 1), rb, tid);
         }
         __syncthreads();
     }
+}
 
-    // ---- epilogue: accumulator r of lane l holds C[8(r/4) + 4(l/32) + r%4][l%32]
-    //      of its 32 x 32 block --------------------------------------------------
-    if (tl.partial) {
-        float* pt = part + (static_cast<int64_t>(split) * tl.tiles + t) * kTileElems;
+// Position of accumulator r of the calling lane in its wave's 32 x 32 block
+// (bi, bj): row 8(r/4) + 4(l/32) + r%4, column l%32, within the 128 x 128 tile.
+__device__ __forceinline__ int acc_row(int bi, int r) {
+    const int lane = threadIdx.x & 63, wr = (threadIdx.x >> 6) >> 1;
+    return wr * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int acc_col(int bj) {
+    const int lane = threadIdx.x & 63, wc = (threadIdx.x >> 6) & 1;
+    return wc * 64 + bj * 32 + (lane & 31);
+}
+
+// C[i][j] = epi( sum_k opA[i][k] * opB[k][j] ) for i < M, j < N, with
+//   TN:  opA[i][k] = A[k*lda + i],  opB[k][j] = B[k*ldb + j]
+//   NT:  opA[i][k] = A[i*lda + k],  opB[k][j] = B[j*ldb + k]
+// over the stream-K split `wk` (see Work).  For a symmetric result, whole
+// tiles write C[i][j] for i <= j in place and C[j][i] for i < j from the
+// tile staged in LDS (rows of consecutive i per store).
+template <bool TN>
+__global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__ A, int64_t lda,
+                                                       const float* __restrict__ B, int64_t ldb,
+                                                       int64_t M, int64_t N, int64_t K,
+                                                       Work wk, bool vec_a, bool vec_b,
+                                                       Epilogue e, float* __restrict__ part) {
+    __shared__ __align__(16) float smem[kLdsFloats];
+    // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+    // contiguous run of workgroup indices, hence of tiles, so that tiles
+    // sharing operand rows meet in the same L2.  (Workgroup and tile counts
+    // stay below 2^24: 32-bit index arithmetic.)
+    const uint32_t w = (blockIdx.x % kXcds) * wk.per_xcd + blockIdx.x / kXcds;
+    if (w >= wk.groups) return;   // padding: the whole group leaves before any barrier
+    // whole tiles first, then this workgroup's stream-K run; everything here
+    // is uniform across the workgroup
+    const uint32_t dp_tiles = wk.dp_rounds * wk.groups;
+    const uint32_t u_end = wk.units ? unit_begin(wk, w + 1) : 0;
+    uint32_t u = wk.units ? unit_begin(wk, w) : 0;
+    bool first_piece = true;
+    for (uint32_t seg = 0; seg < wk.dp_rounds || u < u_end; ++seg) {
+        uint32_t t, seg_end = 0;
+        int64_t kb = 0, ke = K;
+        bool whole = true;
+        if (seg < wk.dp_rounds) {
+            t = seg * wk.groups + w;
+        } else {
+            const uint32_t ts = u / wk.kt;
+            const uint32_t t_begin = ts * wk.kt, t_end = t_begin + wk.kt;
+            seg_end = u_end < t_end ? u_end : t_end;
+            kb = static_cast<int64_t>(u - t_begin) * kTileK;
+            ke = static_cast<int64_t>(seg_end - t_begin) * kTileK;
+            if (ke > K) ke = K;
+            whole = u == t_begin && seg_end == t_end;
+            t = dp_tiles + ts;
+        }
+        uint32_t ti, tj;
+        tile_coords(t, wk, ti, tj);
+        const int64_t i0 = static_cast<int64_t>(ti) * kTileM;
+        const int64_t j0 = static_cast<int64_t>(tj) * kTileN;
+        f32x16 acc[2][2];
+        mma_tile<TN>(A, lda, B, ldb, M, N, i0, j0, kb, ke, vec_a, vec_b, smem, acc);
+
+        // Stage the tile's sums in LDS (free after mma_tile), then store
+        // from there: rows of 128 consecutive columns per store, with
+        // per-thread indices that are cheap to recompute.
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int li = wr * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const int lj = wc * 64 + bj * 32 + (lane & 31);
-                    pt[li * kTileN + lj] = acc[bi][bj][r];
-                }
-        return;
-    }
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t i = i0 + wr * 64 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int64_t j = j0 + wc * 64 + bj * 32 + (lane & 31);
-                if (i < M && j < N) {
-                    float v = e.alpha * acc[bi][bj][r];
+                for (int r = 0; r < 16; ++r)
+                    smem[acc_row(bi, r) * kStage + acc_col(bj)] = acc[bi][bj][r];
+        __syncthreads();
+        const int tid = threadIdx.x;
+        const int col = tid & (kTileN - 1);
+        if (!whole) {
+            // a piece: raw sums to the workgroup's first or last slot
+            float* pt = part + (2 * static_cast<int64_t>(w) + (first_piece ? 0 : 1)) * kTileElems;
+#pragma unroll 4
+            for (int p = 0; p < kTileElems / kGemmThreads; ++p) {
+                const int row = 2 * p + (tid >> 7);
+                pt[row * kTileN + col] = smem[row * kStage + col];
+            }
+        } else {
+            // a whole tile: epilogue and C.  A symmetric result reads Y and
+            // writes C in place only on and above the diagonal (Y may be C:
+            // the mirror writes below never meet a read); its final values
+            // go back to the staged tile for the mirror pass.
+            const int64_t j = j0 + col;
+#pragma unroll 2
+            for (int p = 0; p < kTileElems / kGemmThreads; ++p) {
+                const int row = 2 * p + (tid >> 7);
+                const int64_t i = i0 + row;
+                float v = e.alpha * smem[row * kStage + col];
+                if (i < M && j < N && (!wk.sym || i <= j)) {
                     if (e.y) v = v + e.beta * e.y[i * e.ldy + j];
                     if (i == j) v = v + e.diag;
                     e.c[i * e.ldc + j] = v;
                 }
+                if (wk.sym) smem[row * kStage + col] = v;
             }
+            if (wk.sym) {   // uniform
+                __syncthreads();
+                // C[j][i] for i < j: rows jj of the mirror, consecutive i per store
+                const int64_t i = i0 + col;
+#pragma unroll 2
+                for (int p = 0; p < kTileElems / kGemmThreads; ++p) {
+                    const int jj = 2 * p + (tid >> 7);
+                    const int64_t jm = j0 + jj;
+                    if (i < jm && jm < M) e.c[jm * e.ldc + i] = smem[col * kStage + jj];
+                }
+            }
+        }
+        if (seg >= wk.dp_rounds) {
+            first_piece = false;
+            u = seg_end;
+        }
+        __syncthreads();   // LDS is reused by the next tile
+    }
 }
 
-// Sum of the K ranges' partial tiles (in range order), epilogue, and C.
-// Workgroup b handles rows 32(b%4) .. +31 of output tile b/4; thread t owns
-// columns 4(t%32) .. +3 of rows t/32 + 8p.  For a symmetric result the
-// elements with i <= j are written in place and those with i < j also to
-// C[j][i] through an LDS transpose (rows of 32 consecutive i per store).
-__global__ __launch_bounds__(256) void k_reduce_tiles(const float* __restrict__ part, Tiling tl,
-                                                      int64_t M, int64_t N, Epilogue e) {
+// The tiles cut between workgroups: the pieces summed in K order, then the
+// epilogue and C.  Workgroup 4b + q looks at the start of workgroup b
+// (b >= 1); if that falls inside a tile and no earlier workgroup start does,
+// it sums that tile's pieces (workgroup b - 1's piece, then the first pieces
+// of b, b + 1, ... that start inside the tile) for rows 32q .. 32q + 31.
+// Thread t owns columns 4(t%32) .. +3 of rows t/32 + 8p.  For a symmetric
+// result the elements with i <= j are written in place and those with i < j
+// also to C[j][i] through an LDS transpose (rows of 32 consecutive i).
+__global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__ part, Work wk,
+                                                       int64_t M, int64_t N, Epilogue e) {
     __shared__ float tr[32][kTileN + 1];
-    const uint32_t t = blockIdx.x >> 2;
+    const uint32_t b = blockIdx.x >> 2;
     const int q = static_cast<int>(blockIdx.x & 3);
+    if (b == 0 || b >= wk.groups || wk.units == 0) return;
+    const uint32_t ub = unit_begin(wk, b);
+    const uint32_t ts = ub / wk.kt;                  // stream-K tile
+    const uint32_t t_begin = ts * wk.kt, t_end = t_begin + wk.kt;
+    if (ub == t_begin) return;                       // a start between whole tiles
+    const uint32_t prev = unit_begin(wk, b - 1);
+    if (prev > t_begin) return;                      // handled at an earlier start
     uint32_t ti, tj;
-    tile_coords(t, tl, ti, tj);
+    tile_coords(wk.dp_rounds * wk.groups + ts, wk, ti, tj);
+    // workgroup b - 1 holds the tile's first piece: its first slot if it
+    // starts at the tile, else its last slot
+    const float* first = part + (2 * static_cast<int64_t>(b - 1) + (prev < t_begin ? 1 : 0)) *
+                                    kTileElems;
+    uint32_t last = b;                               // workgroups b .. last start inside the tile
+    while (last + 1 < wk.groups && unit_begin(wk, last + 1) < t_end) ++last;
     const int tid = threadIdx.x;
     const int lj = 4 * (tid & 31);
-    const int64_t stride = static_cast<int64_t>(tl.tiles) * kTileElems;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int ll = (tid >> 5) + 8 * p;                    // row within the quarter
         const int li = 32 * q + ll;
-        const float* src = part + static_cast<int64_t>(t) * kTileElems + li * kTileN + lj;
-        f32x4 v = *reinterpret_cast<const f32x4*>(src);
-        for (uint32_t sp = 1; sp < tl.splits; ++sp) {
-            const f32x4 w = *reinterpret_cast<const f32x4*>(src + sp * stride);
+        f32x4 v = *reinterpret_cast<const f32x4*>(first + li * kTileN + lj);
+        for (uint32_t w = b; w <= last; ++w) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(
+                part + 2 * static_cast<int64_t>(w) * kTileElems + li * kTileN + lj);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v[c] = v[c] + w[c];
+            for (int c = 0; c < 4; ++c) v[c] = v[c] + x[c];
         }
         const int64_t i = static_cast<int64_t>(ti) * kTileM + li;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int64_t j = static_cast<int64_t>(tj) * kTileN + lj + c;
             float o = e.alpha * v[c];
-            // a symmetric result reads Y and writes C only on and above the
-            // diagonal (Y may be C: the mirror writes below never meet a read)
-            if (i < M && j < N && (!tl.sym || i <= j)) {
+            if (i < M && j < N && (!wk.sym || i <= j)) {
                 if (e.y) o = o + e.beta * e.y[i * e.ldy + j];
                 if (i == j) o = o + e.diag;
                 e.c[i * e.ldc + j] = o;
@@ -304,7 +436,7 @@ __global__ __launch_bounds__(256) void k_reduce_tiles(const float* __restrict__ 
             tr[ll][lj + c] = o;
         }
     }
-    if (!tl.sym) return;      // uniform across the workgroup
+    if (!wk.sym) return;      // uniform across the workgroup
     __syncthreads();
     const int ii = tid & 31;
     const int64_t i = static_cast<int64_t>(ti) * kTileM + 32 * q + ii;
@@ -376,70 +508,66 @@ constexpr float kQa = 3.4445f, kQb = -4.7750f, kQc = 2.0315f;
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
-constexpr int64_t kTargetGroups = 512;          // two resident workgroups on each of 256 CUs
-constexpr int64_t kMinSplitK = 8 * kTileK;      // each K range spans at least 8 K-tiles
-constexpr int64_t kMaxSplits = 16;
+constexpr int64_t kStreamGroups = 512;          // two resident workgroups on each of 256 CUs
+constexpr int64_t kMinUnits = 8;                // K-tiles per workgroup at least
 
-// The cut of an M x N x K product (see Tiling).  ws_bytes bounds the partial
-// buffer; fewer K ranges are used if it is short.  Returns false if a
-// symmetric product cannot get even one range's partial tiles.
-bool plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t ws_bytes, Tiling& tl,
+// The split of an M x N x K product (see Work).  With a workspace of at
+// least 2 * groups tiles the units are spread over up to kStreamGroups
+// workgroups; otherwise each workgroup takes one whole tile.
+void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t ws_bytes, Work& wk,
                int64_t* need_bytes = nullptr) {
     const int64_t tn = (N + kTileN - 1) / kTileN, tm = (M + kTileM - 1) / kTileM;
     const int64_t tiles = sym ? tn * (tn + 1) / 2 : tm * tn;
-    int64_t splits = 1;
-    if (K > 0) {
-        const int64_t want = (kTargetGroups + tiles - 1) / tiles;
-        int64_t most = K / kMinSplitK;
-        if (most > kMaxSplits) most = kMaxSplits;
-        if (most < 1) most = 1;
-        splits = want < most ? want : most;
-    }
-    const int64_t tile_bytes = static_cast<int64_t>(kTileElems) * 4;
-    while (splits > 1 && splits * tiles * tile_bytes > ws_bytes) --splits;
-    const bool partial = sym || splits > 1;
-    if (partial && splits * tiles * tile_bytes > ws_bytes) return false;
-    int64_t kchunk = 0;
-    if (K > 0) {
-        kchunk = ((K + splits - 1) / splits + kTileK - 1) / kTileK * kTileK;
-        splits = (K + kchunk - 1) / kchunk;
-    }
-    tl.tiles_n = static_cast<uint32_t>(tn);
-    tl.tiles = static_cast<uint32_t>(tiles);
-    tl.splits = static_cast<uint32_t>(splits);
-    tl.per_xcd = static_cast<uint32_t>((tiles * splits + kXcds - 1) / kXcds);
-    tl.kchunk = kchunk;
-    tl.sym = sym;
-    tl.partial = partial;
-    if (need_bytes) *need_bytes = partial ? splits * tiles * tile_bytes : 0;
-    return true;
+    const int64_t kt = K > 0 ? (K + kTileK - 1) / kTileK : 1;
+    const int64_t units = tiles * kt;
+    int64_t g = units / kMinUnits;
+    if (g > kStreamGroups) g = kStreamGroups;
+    if (g >= kXcds) g -= g % kXcds;
+    if (g < 1) g = 1;
+    const int64_t need = 2 * g * kTileElems * 4;
+    // whole-tile rounds for all but the last one or two rounds' worth of
+    // tiles, which are split stream-K
+    const int64_t rounds = tiles >= 2 * g ? tiles / g - 1 : 0;
+    const int64_t sk_units = (tiles - rounds * g) * kt;
+    const bool stream = need <= ws_bytes && sk_units <= static_cast<int64_t>(UINT32_MAX) &&
+                        g != tiles;
+    const int64_t groups = stream ? g : tiles;
+    wk.tiles_n = static_cast<uint32_t>(tn);
+    wk.tiles = static_cast<uint32_t>(tiles);
+    wk.kt = static_cast<uint32_t>(kt);
+    wk.groups = static_cast<uint32_t>(groups);
+    wk.per_xcd = static_cast<uint32_t>((groups + kXcds - 1) / kXcds);
+    wk.dp_rounds = stream ? static_cast<uint32_t>(rounds) : 1;
+    wk.units = stream ? static_cast<uint32_t>(sk_units) : 0;
+    wk.sym = sym;
+    if (need_bytes) *need_bytes = need;
 }
 
-// Partial-buffer bytes the preferred cut of a product needs (0 if none).
+// Partial-buffer bytes of the preferred split of a product.
 int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym) {
-    Tiling tl;
+    Work wk;
     int64_t need = 0;
-    plan_gemm(M, N, K, sym, INT64_MAX, tl, &need);
+    plan_gemm(M, N, K, sym, INT64_MAX, wk, &need);
     return need;
 }
 
 hipError_t gemm(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
                 int64_t N, int64_t K, const Epilogue& e, bool sym, float* part,
                 int64_t part_bytes, hipStream_t s) {
-    Tiling tl;
-    if (!plan_gemm(M, N, K, sym, part ? part_bytes : 0, tl)) return hipErrorInvalidValue;
-    const dim3 grid(tl.per_xcd * kXcds);
+    Work wk;
+    plan_gemm(M, N, K, sym, part ? part_bytes : 0, wk);
+    const dim3 grid(wk.per_xcd * kXcds);
     // float4 loads of row-major operands need 16-byte aligned rows
     const bool vec_a = reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 4 == 0;
     const bool vec_b = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 4 == 0;
     if (tn)
         hipLaunchKernelGGL((k_gemm<true>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           tl, vec_a, vec_b, e, part);
+                           wk, vec_a, vec_b, e, part);
     else
         hipLaunchKernelGGL((k_gemm<false>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           tl, vec_a, vec_b, e, part);
-    if (tl.partial)
-        hipLaunchKernelGGL(k_reduce_tiles, dim3(tl.tiles * 4), dim3(256), 0, s, part, tl, M, N, e);
+                           wk, vec_a, vec_b, e, part);
+    if (wk.units != 0 && (wk.units / wk.kt) % wk.groups != 0)   // pieces of cut tiles to add
+        hipLaunchKernelGGL(k_reduce_pieces, dim3(wk.groups * 4), dim3(256), 0, s, part, wk, M, N, e);
     return hipGetLastError();
 }
 

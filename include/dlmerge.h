@@ -368,13 +368,13 @@ enum dl_matmul_form {
  * the upper triangle is computed and the lower one is its mirror image.
  *
  * workspace: device memory (256-byte aligned, disjoint from every other
- * argument) for partial sums when the product is cut along K to fill the
- * GPU, and for the tiles of a symmetric result; it may be NULL when
- * symmetric = 0 (the product is then not cut along K).  A workspace of
- * dl_matmul_workspace_bytes bytes gives the preferred cut; a smaller one
- * gives fewer K ranges, which changes the summation order.  m = 0 or n = 0
- * is a no-op.  Errors: DL_E_INVAL (also: symmetric with m != n or a
- * workspace too small for one K range), DL_E_ALIGN, DL_E_HIP.
+ * argument) or NULL.  With at least dl_matmul_workspace_bytes bytes the work
+ * (output tiles x K) is spread evenly over the workgroups the GPU holds at
+ * once, and tiles cut between workgroups are summed in K order through the
+ * workspace; without it every workgroup computes one whole output tile.
+ * The two give different (each deterministic) summation orders.  m = 0 or
+ * n = 0 is a no-op.  Errors: DL_E_INVAL (also: symmetric with m != n),
+ * DL_E_ALIGN, DL_E_HIP.
  */
 int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, int64_t *bytes);
 int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t ldb, int64_t m,

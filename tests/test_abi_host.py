@@ -245,10 +245,8 @@ def test_matmul_host_rules():
     _expect(dl.DL_E_ALIGN, mm, y=b + (1 << 20) + 1)
     ws = FAKE + (1 << 32)
     wsb = dl.dl_matmul_workspace_bytes(64, 64, 16, True)
+    assert wsb == 2 * 128 * 128 * 4            # 4 K-tiles: one workgroup, two slots
     _expect(dl.DL_E_INVAL, mm, symmetric=True)                     # 64 x 32 is not square
-    _expect(dl.DL_E_INVAL, mm, symmetric=True, n=64, ldb=64, ldc=64)   # no workspace
-    _expect(dl.DL_E_INVAL, mm, symmetric=True, n=64, ldb=64, ldc=64, workspace=ws,
-            workspace_bytes=wsb - 4)
     _expect(dl.DL_E_ALIGN, mm, workspace=ws + 16, workspace_bytes=1 << 20)
     _expect(dl.DL_E_INVAL, mm, workspace=c - 256, workspace_bytes=1 << 20)    # overlaps C
     _expect(dl.DL_E_INVAL, mm, workspace=a, workspace_bytes=1 << 20)          # overlaps A
@@ -256,24 +254,25 @@ def test_matmul_host_rules():
 
 
 def test_matmul_workspace_sizes():
+    """Two partial slots per workgroup; up to 512 workgroups (two per CU),
+    each with at least 8 K-tiles of 32, in multiples of 8 (one per XCD)."""
     tile = 128 * 128 * 4
-    # a symmetric 2048 x 2048 result: 136 upper tiles, cut into 4 K ranges
-    assert dl.dl_matmul_workspace_bytes(2048, 2048, 73760, True) == 4 * 136 * tile
-    assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, True) == 4 * 136 * tile
-    # short K: one range per tile, still the tiles of the symmetric result
-    assert dl.dl_matmul_workspace_bytes(2048, 2048, 100, True) == 136 * tile
-    # 256 tiles: two K ranges fill the GPU; 704 tiles need no cut
-    assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, False) == 2 * 256 * tile
-    assert dl.dl_matmul_workspace_bytes(5632, 2048, 2048, False) == 0
+    full = 2 * 512 * tile
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 73760, True) == full
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, True) == full
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, False) == full
+    assert dl.dl_matmul_workspace_bytes(5632, 2048, 2048, False) == full
+    assert dl.dl_matmul_workspace_bytes(100, 100, 1 << 20, False) == full
+    # 136 upper tiles x 4 K-tiles = 544 units: 68 workgroups, rounded to 64
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 100, True) == 2 * 64 * tile
+    # one tile of 32 K-tiles: 4 workgroups
+    assert dl.dl_matmul_workspace_bytes(100, 100, 1000, False) == 2 * 4 * tile
     assert dl.dl_matmul_workspace_bytes(0, 5, 5, False) == 0
-    # a single small tile: at most 16 ranges of at least 256 k each
-    assert dl.dl_matmul_workspace_bytes(100, 100, 1 << 20, False) == 16 * tile
-    assert dl.dl_matmul_workspace_bytes(100, 100, 1000, False) == 3 * tile
     for bad in ((5, 6, 7, True), (-1, 5, 5, False), (5, 5, -1, False)):
         _expect(dl.DL_E_INVAL, dl.dl_matmul_workspace_bytes, *bad)
     # the polar workspace includes the largest partial buffer of its products
     ws = dl.dl_polar_workspace_bytes(2048, 2048)
-    assert ws >= 2 * 2048 * 2048 * 4 * 2 + 4 * 136 * tile
+    assert ws >= 2 * 2048 * 2048 * 4 * 2 + full
 
 
 def test_participants_capacity():

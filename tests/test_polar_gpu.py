@@ -129,8 +129,8 @@ def _bound_check(got, want, mag, k):
 
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("n,k", [(1, 5), (130, 33), (300, 700), (257, 2000), (128, 4096),
-                                 (384, 300)])
-@pytest.mark.parametrize("ws_mode", ["preferred", "one_range"])
+                                 (384, 300), (5760, 100)])
+@pytest.mark.parametrize("ws_mode", ["stream", "none"])
 @pytest.mark.parametrize("y_mode", ["none", "separate", "in_place"])
 def test_matmul_symmetric(form, n, k, ws_mode, y_mode):
     """A Gram product (X^T X as TN, X X^T as NT) declared symmetric: the upper
@@ -149,10 +149,10 @@ def test_matmul_symmetric(form, n, k, ws_mode, y_mode):
     alpha, beta, diag = (1.0, 0.0, 0.0) if y_mode == "none" else (2.0315, -4.775, 3.4445)
     x_d, c_d = gpu(x), gpu(c0)
     y_d = None if y_mode == "none" else (c_d if y_mode == "in_place" else gpu(ysym))
-    tn_ = (n + 127) // 128
-    wsb = (dl.dl_matmul_workspace_bytes(n, n, k, True) if ws_mode == "preferred"
-           else tn_ * (tn_ + 1) // 2 * 128 * 128 * 4)
-    ws = torch.empty(wsb // 4, dtype=torch.float32, device=DEV)
+    ws = None
+    if ws_mode == "stream":
+        ws = torch.empty(dl.dl_matmul_workspace_bytes(n, n, k, True) // 4, dtype=torch.float32,
+                         device=DEV)
     dl.dl_matmul_f32(form, x_d, x.shape[1], x_d, x.shape[1], n, n, k, c_d, ldc, y_d, alpha, beta,
                      diag, symmetric=True, workspace=ws)
     got = host(c_d)
@@ -168,12 +168,16 @@ def test_matmul_symmetric(form, n, k, ws_mode, y_mode):
 
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("m,n,k", [(100, 100, 5000), (256, 256, 2048), (129, 300, 1000),
-                                   (640, 384, 777)])
-def test_matmul_cut_along_k(form, m, n, k):
-    """With a workspace the product is cut into K ranges (summed in range
-    order); the result stays within the product bound, is the same on a
-    second call, and a workspace for fewer ranges still gives a result
-    within the bound."""
+                                   (640, 384, 777), (1100, 1000, 96), (3000, 200, 4100),
+                                   (4224, 4000, 300)])
+def test_matmul_stream_k(form, m, n, k):
+    """With a workspace the work is spread over the resident workgroups
+    (whole-tile rounds while at least two rounds' worth remain, then
+    stream-K runs) and tiles cut between them are summed in K order: within
+    the product bound, the same bits on a second call; without one, one
+    workgroup per tile, also within the bound.  4224 x 4000 x 300 has 1056
+    tiles: one whole-tile round of 512, then 544 tiles in runs of ~10.6
+    K-tiles."""
     rng = np.random.default_rng(m + n + k)
     if form == dl.DL_TN:
         a = rng.standard_normal((k, m)).astype(np.float32)
@@ -190,8 +194,8 @@ def test_matmul_cut_along_k(form, m, n, k):
     wsb = dl.dl_matmul_workspace_bytes(m, n, k, False)
     assert wsb > 0
     outs = []
-    for nbytes in (wsb, wsb, 2 * 128 * 128 * 4 * ((m + 127) // 128) * ((n + 127) // 128)):
-        ws = torch.empty(nbytes // 4, dtype=torch.float32, device=DEV)
+    for use_ws in (True, True, False):
+        ws = torch.empty(wsb // 4, dtype=torch.float32, device=DEV) if use_ws else None
         c_d = torch.empty((m, n), device=DEV)
         dl.dl_matmul_f32(form, a_d, lda, b_d, ldb, m, n, k, c_d, n, workspace=ws)
         outs.append(host(c_d))
