@@ -24,6 +24,8 @@ SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "polar.hip"),
            os.path.join(CSRC, "api.cpp")]
 DRIVER = os.path.join(PKG, "dlmerge_driver")
 DRIVER_SOURCES = [os.path.join(CSRC, "merge_driver.hip")]
+POLAR_DRIVER = os.path.join(PKG, "dlpolar_driver")
+POLAR_DRIVER_SOURCES = [os.path.join(CSRC, "polar_driver.hip")]
 
 HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -50,12 +52,14 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Builds libdlmerge.so and the dlmerge_driver executable that links it."""
+    """Builds libdlmerge.so and the dlmerge_driver and dlpolar_driver
+    executables that link it."""
     _run([HIPCC, *HIPFLAGS, "-shared", "-o", LIB + ".tmp", *SOURCES], verbose)
     os.replace(LIB + ".tmp", LIB)
-    _run([HIPCC, *HIPFLAGS, "-o", DRIVER + ".tmp", *DRIVER_SOURCES, f"-L{PKG}", "-ldlmerge",
-          "-Wl,-rpath,$ORIGIN"], verbose)
-    os.replace(DRIVER + ".tmp", DRIVER)
+    for exe, srcs in ((DRIVER, DRIVER_SOURCES), (POLAR_DRIVER, POLAR_DRIVER_SOURCES)):
+        _run([HIPCC, *HIPFLAGS, "-o", exe + ".tmp", *srcs, f"-L{PKG}", "-ldlmerge",
+              "-Wl,-rpath,$ORIGIN"], verbose)
+        os.replace(exe + ".tmp", exe)
     return LIB
 
 

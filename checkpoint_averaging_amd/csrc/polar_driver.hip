@@ -1,0 +1,226 @@
+// dlpolar_driver: runs the orthogonalised outer step through the C ABI
+// (include/dlmerge.h) on buffers it allocates with hipMalloc, with no other
+// GPU work besides a fill pass and an optional plain copy kernel of known
+// size.  It is the program hardware counters are collected on for the
+// orthogonalisation kernels.
+//
+//   dlpolar_driver --shapes RxC:count[,RxC:count...] [--steps S] [--warmup W]
+//                  [--quintic Q] [--cubic C] [--copy-mib M]
+//
+// One step runs theta = theta - s * P(theta - averaged) once for every
+// matrix of the list (count matrices of each shape, in list order), on one
+// stream with one workspace sized for the largest.  The matrices of a step
+// share one theta / averaged pair of the largest size (the kernels' work
+// does not depend on where the buffers sit).  Prints the average time per
+// step and per shape, and the algorithmic TFLOP/s (symmetric Gram products
+// counted at their distinct outputs).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "dlmerge.h"
+
+#define HIPCHECK(x)                                                                   \
+    do {                                                                              \
+        hipError_t e_ = (x);                                                          \
+        if (e_ != hipSuccess) {                                                       \
+            std::fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_),  \
+                         __LINE__);                                                   \
+            std::exit(1);                                                             \
+        }                                                                             \
+    } while (0)
+
+#define DLCHECK(x)                                                                    \
+    do {                                                                              \
+        int s_ = (x);                                                                 \
+        if (s_ != DL_OK) {                                                            \
+            std::fprintf(stderr, "dlmerge error %s at line %d\n", dl_strerror(s_),    \
+                         __LINE__);                                                   \
+            std::exit(1);                                                             \
+        }                                                                             \
+    } while (0)
+
+namespace {
+
+__device__ __forceinline__ uint32_t mix(uint64_t x) {
+    x ^= x >> 33;
+    x *= 0xff51afd7ed558ccdull;
+    x ^= x >> 33;
+    return static_cast<uint32_t>(x);
+}
+
+// p[i] = base[i] + scale * uniform(-0.5, 0.5)  (base may be null: 0)
+__global__ void fill(float* p, const float* base, float scale, int64_t n, uint32_t stream) {
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const float u = static_cast<float>(mix(uint64_t(i) * 0x9E3779B97F4A7C15ull + stream) >> 8) *
+                        (1.0f / 16777216.0f);
+        p[i] = (base ? base[i] : 0.0f) + scale * (u - 0.5f);
+    }
+}
+
+// Plain copy of known size: reads npacks * 16 bytes, writes npacks * 16 bytes.
+__global__ void plain_copy(const float4* __restrict__ src, float4* __restrict__ dst,
+                           int64_t npacks) {
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < npacks;
+         i += int64_t(gridDim.x) * blockDim.x)
+        dst[i] = src[i];
+}
+
+struct Shape {
+    int64_t rows, cols;
+    int count;
+};
+
+struct Args {
+    std::vector<Shape> shapes;
+    int steps = 1;
+    int warmup = 1;
+    int quintic = 12;
+    int cubic = 6;
+    int copy_mib = 0;
+};
+
+[[noreturn]] void usage() {
+    std::fprintf(stderr,
+                 "usage: dlpolar_driver --shapes RxC:count[,RxC:count...] [--steps S]\n"
+                 "       [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]\n");
+    std::exit(2);
+}
+
+Args parse(int argc, char** argv) {
+    Args a;
+    for (int i = 1; i < argc; ++i) {
+        std::string k = argv[i];
+        if (i + 1 >= argc) usage();
+        std::string v = argv[++i];
+        if (k == "--shapes") {
+            size_t pos = 0;
+            while (pos < v.size()) {
+                size_t c = v.find(',', pos);
+                if (c == std::string::npos) c = v.size();
+                const std::string item = v.substr(pos, c - pos);
+                Shape s{0, 0, 1};
+                if (std::sscanf(item.c_str(), "%ldx%ld:%d", &s.rows, &s.cols, &s.count) < 2)
+                    usage();
+                a.shapes.push_back(s);
+                pos = c + 1;
+            }
+        } else if (k == "--steps") a.steps = std::atoi(v.c_str());
+        else if (k == "--warmup") a.warmup = std::atoi(v.c_str());
+        else if (k == "--quintic") a.quintic = std::atoi(v.c_str());
+        else if (k == "--cubic") a.cubic = std::atoi(v.c_str());
+        else if (k == "--copy-mib") a.copy_mib = std::atoi(v.c_str());
+        else usage();
+    }
+    if (a.shapes.empty() || a.steps < 1 || a.warmup < 0) usage();
+    for (const Shape& s : a.shapes)
+        if (s.rows < 1 || s.cols < 1 || s.count < 1) usage();
+    return a;
+}
+
+// Algorithmic flops of the iteration on one matrix (see the orthogonalise
+// module): symmetric Gram products at their distinct outputs.
+double flops(const Shape& s, int quintic, int cubic) {
+    const double r = s.rows < s.cols ? s.rows : s.cols, L = s.rows < s.cols ? s.cols : s.rows;
+    const double sym = r * (r + 1) / 2;
+    return (quintic + cubic) * (2 * sym * L + 2 * L * r * r) + quintic * 2 * sym * r;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+    const Args a = parse(argc, argv);
+    int64_t n_max = 0, ws_max = 0;
+    for (const Shape& s : a.shapes) {
+        int64_t ws = 0;
+        DLCHECK(dl_polar_workspace_bytes(s.rows, s.cols, &ws));
+        if (s.rows * s.cols > n_max) n_max = s.rows * s.cols;
+        if (ws > ws_max) ws_max = ws;
+    }
+    float *theta = nullptr, *avg = nullptr;
+    void* ws = nullptr;
+    HIPCHECK(hipMalloc(&theta, n_max * sizeof(float)));
+    HIPCHECK(hipMalloc(&avg, n_max * sizeof(float)));
+    HIPCHECK(hipMalloc(&ws, ws_max));
+    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, theta, nullptr, 0.04f, n_max, 1u);
+    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, avg, theta, 2e-3f, n_max, 2u);
+    HIPCHECK(hipGetLastError());
+    HIPCHECK(hipDeviceSynchronize());
+    std::printf("[driver] %zu shape(s), theta/averaged %ld floats, workspace %ld bytes\n",
+                a.shapes.size(), n_max, ws_max);
+    std::fflush(stdout);
+
+    if (a.copy_mib > 0) {
+        const int64_t nb = int64_t(a.copy_mib) << 20;
+        float4 *src = nullptr, *dst = nullptr;
+        HIPCHECK(hipMalloc(&src, nb));
+        HIPCHECK(hipMalloc(&dst, nb));
+        HIPCHECK(hipMemset(src, 0, nb));
+        hipLaunchKernelGGL(plain_copy, dim3(4096), dim3(256), 0, nullptr, src, dst, nb / 16);
+        HIPCHECK(hipGetLastError());
+        HIPCHECK(hipDeviceSynchronize());
+        HIPCHECK(hipFree(src));
+        HIPCHECK(hipFree(dst));
+        std::printf("[driver] plain copy: %ld bytes read, %ld bytes written\n", nb, nb);
+    }
+
+    const float scale = 1e-4f;
+    auto step = [&](std::vector<double>* shape_ms, std::vector<hipEvent_t>& ev) {
+        size_t e = 0;
+        for (size_t i = 0; i < a.shapes.size(); ++i) {
+            const Shape& s = a.shapes[i];
+            if (shape_ms) HIPCHECK(hipEventRecord(ev[e], nullptr));
+            for (int c = 0; c < s.count; ++c)
+                DLCHECK(dl_outer_orthogonal_step(theta, avg, s.rows, s.cols, scale, a.quintic,
+                                                 a.cubic, ws, ws_max, nullptr));
+            if (shape_ms) HIPCHECK(hipEventRecord(ev[e + 1], nullptr));
+            e += 2;
+        }
+    };
+    std::vector<hipEvent_t> ev(2 * a.shapes.size());
+    for (hipEvent_t& x : ev) HIPCHECK(hipEventCreate(&x));
+    for (int w = 0; w < a.warmup; ++w) step(nullptr, ev);
+    HIPCHECK(hipDeviceSynchronize());
+    std::vector<double> shape_ms(a.shapes.size(), 0.0);
+    hipEvent_t t0, t1;
+    HIPCHECK(hipEventCreate(&t0));
+    HIPCHECK(hipEventCreate(&t1));
+    double total_ms = 0.0;
+    for (int st = 0; st < a.steps; ++st) {
+        HIPCHECK(hipEventRecord(t0, nullptr));
+        step(&shape_ms, ev);
+        HIPCHECK(hipEventRecord(t1, nullptr));
+        HIPCHECK(hipEventSynchronize(t1));
+        float ms = 0.0f;
+        HIPCHECK(hipEventElapsedTime(&ms, t0, t1));
+        total_ms += ms;
+        for (size_t i = 0; i < a.shapes.size(); ++i) {
+            float m = 0.0f;
+            HIPCHECK(hipEventElapsedTime(&m, ev[2 * i], ev[2 * i + 1]));
+            shape_ms[i] += m;
+        }
+        std::printf("[driver] step %d: %.2f ms\n", st, ms);
+        std::fflush(stdout);
+    }
+    double fl_total = 0.0;
+    for (size_t i = 0; i < a.shapes.size(); ++i) {
+        const Shape& s = a.shapes[i];
+        const double f = flops(s, a.quintic, a.cubic) * s.count;
+        fl_total += f;
+        const double ms = shape_ms[i] / a.steps;
+        std::printf("[driver] %ldx%ld x%d: %.3f ms per matrix, %.2f TFLOP/s\n", s.rows, s.cols,
+                    s.count, ms / s.count, f / (ms / 1e3) / 1e12);
+    }
+    const double ms = total_ms / a.steps;
+    std::printf("[driver] step: %.2f ms, %.2f TFLOP/s (%.3e flops)\n", ms,
+                fl_total / (ms / 1e3) / 1e12, fl_total);
+    HIPCHECK(hipFree(theta));
+    HIPCHECK(hipFree(avg));
+    HIPCHECK(hipFree(ws));
+    return 0;
+}
