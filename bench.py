@@ -198,7 +198,7 @@ def orthogonalize(args, torch):
     n = layout.n_params
     theta = synth.global0(1007, n, device=dev)
     averaged = synth.worker_checkpoint(1007, 0, 0, theta)
-    step = OrthogonalStep(layout, dev)
+    step = OrthogonalStep(layout, dev, batch=args.orth_batch)
     mats = step.matrices
     n_mat = sum(m.rows * m.cols for m in mats)
     flops = step.flops()
@@ -211,13 +211,13 @@ def orthogonalize(args, torch):
     torch.cuda.synchronize()
     recs = []
 
-    def timer(m, call):
+    def timer(g, call):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         call()
         e1.record()
-        recs.append((m, e0, e1))
+        recs.append((g, e0, e1))
 
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -225,9 +225,9 @@ def orthogonalize(args, torch):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     by_shape = {}
-    for m, e0, e1 in recs:
-        d = by_shape.setdefault((m.rows, m.cols), [0, 0.0])
-        d[0] += 1
+    for g, e0, e1 in recs:
+        d = by_shape.setdefault((g[0].rows, g[0].cols), [0, 0.0])
+        d[0] += len(g)
         d[1] += e0.elapsed_time(e1)
     shapes = {}
     for (r, c), (cnt, tot) in by_shape.items():
@@ -238,34 +238,39 @@ def orthogonalize(args, torch):
     log(f"[bench] {args.steps} orthogonalised steps: {ms:.1f} ms/step")
 
     # every distinct product of the iteration, timed launch by launch through
-    # the same kernels with the same launch shapes (values: an iterate-like X
-    # and its Gram matrix)
+    # the same kernels with the same launch shapes: per batch of equally
+    # shaped matrices, the symmetric Gram product, its symmetric square and
+    # the next iterate, with a workspace for the stream-K split (values: an
+    # iterate-like X and a symmetric Gram-like G)
+    import collections
+    gcount = collections.Counter((g[0].rows, g[0].cols, len(g)) for g in step.groups)
     prods = {}
-    for (r_, c_), cnt in ((k, v[0] // args.steps) for k, v in by_shape.items()):
+    for (r_, c_, bsz), ngroups in gcount.items():
         r, L = min(r_, c_), max(r_, c_)
         tall = r_ >= c_
-        x = torch.randn(r_ * c_, device=dev).mul_(1.0 / np.sqrt(r_ * c_ / r))
-        g = torch.randn(r * r, device=dev).mul_(1.0 / r)
-        g = (g.view(r, r) + g.view(r, r).t()).contiguous().view(-1)      # symmetric
-        out_x = torch.empty(r_ * c_, device=dev)
-        out_g = torch.empty(r * r, device=dev)
-        # the same cut as inside the iteration: symmetric r x r results, and
-        # a workspace for K ranges
+        sx, sg = r_ * c_, r * r
+        x = torch.randn(bsz * sx, device=dev).mul_(1.0 / np.sqrt(L))
+        g = torch.randn(bsz, r, r, device=dev).mul_(1.0 / r)
+        g = (g + g.transpose(1, 2)).contiguous().view(-1)                  # symmetric
+        out_x = torch.empty(bsz * sx, device=dev)
+        out_g = torch.empty(bsz * sg, device=dev)
         if tall:
-            cases = [("TN", "gram", (x, c_, x, c_, r, r, L, out_g, r), True, 18),
-                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), True, 12),
-                     ("NT", "next_iterate", (x, c_, g, r, L, r, r, out_x, c_), False, 18)]
+            cases = [("TN", "gram", (x, c_, sx, x, c_, sx, r, r, L, out_g, r, sg), True, 18),
+                     ("TN", "gram_square", (g, r, sg, g, r, sg, r, r, r, out_g, r, sg), True, 12),
+                     ("NT", "next_iterate", (x, c_, sx, g, r, sg, L, r, r, out_x, c_, sx), False,
+                      18)]
         else:
-            cases = [("NT", "gram", (x, c_, x, c_, r, r, L, out_g, r), True, 18),
-                     ("TN", "gram_square", (g, r, g, r, r, r, r, out_g, r), True, 12),
-                     ("TN", "next_iterate", (g, r, x, c_, r, L, r, out_x, c_), False, 18)]
+            cases = [("NT", "gram", (x, c_, sx, x, c_, sx, r, r, L, out_g, r, sg), True, 18),
+                     ("TN", "gram_square", (g, r, sg, g, r, sg, r, r, r, out_g, r, sg), True, 12),
+                     ("TN", "next_iterate", (g, r, sg, x, c_, sx, r, L, r, out_x, c_, sx), False,
+                      18)]
         for form, what, a, sym, per in cases:
             fm = dl.DL_TN if form == "TN" else dl.DL_NT
-            M, N, K = a[4], a[5], a[6]
-            wsb = dl.dl_matmul_workspace_bytes(M, N, K, sym)
+            M, N, K = a[6], a[7], a[8]
+            wsb = dl.dl_matmul_workspace_bytes_batch(M, N, K, sym, bsz)
             ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=dev)
-            call = lambda fm=fm, a=a, sym=sym, ws=ws, wsb=wsb: dl.dl_matmul_f32(
-                fm, *a[:7], a[7], a[8], symmetric=sym, workspace=ws if wsb else None)
+            call = lambda fm=fm, a=a, sym=sym, ws=ws, bsz=bsz: dl.dl_matmul_f32_batch(
+                fm, *a, bsz, symmetric=sym, workspace=ws)
             call()
             torch.cuda.synchronize()
             evs = []
@@ -279,10 +284,11 @@ def orthogonalize(args, torch):
             torch.cuda.synchronize()
             avg = sum(p.elapsed_time(q) for p, q in evs) / len(evs)
             outs = M * (M + 1) // 2 if sym else M * N      # distinct outputs
-            prods[f"{form} {what} {M}x{N}x{K}"] = {
-                "form": form, "symmetric": sym, "launches_per_step": per * cnt,
-                "avg_ms": round(avg, 4), "flops_per_launch": 2 * outs * K,
-                "TFLOP_per_s": round(2 * outs * K / (avg / 1e3) / 1e12, 2)}
+            fl = 2 * outs * K * bsz
+            prods[f"{form} {what} {M}x{N}x{K} batch {bsz} of {r_}x{c_}"] = {
+                "form": form, "symmetric": sym, "batch": bsz, "launches_per_step": per * ngroups,
+                "avg_ms": round(avg, 4), "flops_per_launch": fl,
+                "TFLOP_per_s": round(fl / (avg / 1e3) / 1e12, 2)}
             del ws
         del x, g, out_x, out_g
     kinds = {}
@@ -306,6 +312,7 @@ def orthogonalize(args, torch):
         "dtype": "f32",
         "data": "synthetic (seeded Philox; DiffuRefill-1B matrix shapes)",
         "config": {"workload": "diffurefill1b_orthogonal_step", "matrices": len(mats),
+                   "batch": args.orth_batch,
                    "matrix_params": n_mat, "quintic_steps": 12, "cubic_steps": 6,
                    "algorithmic_flops_per_step": total_flops},
         "TFLOP_per_s": round(total_flops / (ms / 1e3) / 1e12, 2),
@@ -369,6 +376,8 @@ def main():
     ap.add_argument("--orthogonalize", action="store_true",
                     help="time the orthogonalised outer step over every weight matrix instead "
                          "of a merge round")
+    ap.add_argument("--orth-batch", type=int, default=8,
+                    help="equally shaped matrices orthogonalised together (1: one by one)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")

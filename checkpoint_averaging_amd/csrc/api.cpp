@@ -459,27 +459,38 @@ int dl_adopt_keep_drift(float* theta, const float* global, const void* pushed, i
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 
-int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, int64_t* bytes) {
+int dl_matmul_workspace_bytes_batch(int64_t m, int64_t n, int64_t k, int symmetric, int batch,
+                                    int64_t* bytes) {
     if (bytes == nullptr || m < 0 || n < 0 || k < 0) return DL_E_INVAL;
     if (symmetric != 0 && symmetric != 1) return DL_E_INVAL;
     if (symmetric && m != n) return DL_E_INVAL;
-    if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) || dlk::gemm_tiles(m, n) > dlk::kGemmMaxTiles)
+    if (batch < 1 || batch > DL_MAX_BATCH) return DL_E_INVAL;
+    if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) ||
+        dlk::gemm_tiles(m, n) * batch > dlk::kGemmMaxTiles)
         return DL_E_INVAL;
-    *bytes = (m == 0 || n == 0) ? 0 : dlk::matmul_workspace_bytes(m, n, k, symmetric != 0);
+    *bytes = (m == 0 || n == 0) ? 0
+                                : dlk::matmul_workspace_bytes(m, n, k, symmetric != 0, batch);
     return DL_OK;
 }
 
-int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t ldb, int64_t m,
-                  int64_t n, int64_t k, float* c, int64_t ldc, const float* y, float alpha,
-                  float beta, float diag, int symmetric, void* workspace, int64_t workspace_bytes,
-                  void* stream) {
+int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, int64_t* bytes) {
+    return dl_matmul_workspace_bytes_batch(m, n, k, symmetric, 1, bytes);
+}
+
+int dl_matmul_f32_batch(int form, const float* a, int64_t lda, int64_t stride_a, const float* b,
+                        int64_t ldb, int64_t stride_b, int64_t m, int64_t n, int64_t k, float* c,
+                        int64_t ldc, int64_t stride_c, const float* y, int64_t stride_y,
+                        float alpha, float beta, float diag, int symmetric, int batch,
+                        void* workspace, int64_t workspace_bytes, void* stream) {
     if (form != DL_TN && form != DL_NT) return DL_E_INVAL;
     if (m < 0 || n < 0 || k < 0 || workspace_bytes < 0) return DL_E_INVAL;
     if (symmetric != 0 && symmetric != 1) return DL_E_INVAL;
     if (symmetric && m != n) return DL_E_INVAL;
+    if (batch < 1 || batch > DL_MAX_BATCH) return DL_E_INVAL;
     if (m == 0 || n == 0) return DL_OK;
     if (a == nullptr || b == nullptr || c == nullptr) return DL_E_INVAL;
-    if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) || dlk::gemm_tiles(m, n) > dlk::kGemmMaxTiles)
+    if (m > (int64_t(1) << 31) || n > (int64_t(1) << 31) ||
+        dlk::gemm_tiles(m, n) * batch > dlk::kGemmMaxTiles)
         return DL_E_INVAL;
     const bool tn = form == DL_TN;
     // the operands' extents: TN reads A as k x lda (cols i < m), NT as m x lda (cols k)
@@ -490,16 +501,23 @@ int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t
         return DL_E_ALIGN;
     if (workspace != nullptr && !aligned_to(workspace, 256)) return DL_E_ALIGN;
     const int64_t ws_bytes = workspace ? workspace_bytes : 0;
-    const int64_t a_bytes = 4 * (tn ? (k > 0 ? (k - 1) * lda + m : 0) : (m - 1) * lda + k);
-    const int64_t b_bytes = 4 * (tn ? (k > 0 ? (k - 1) * ldb + n : 0) : (n - 1) * ldb + k);
-    const int64_t c_bytes = 4 * ((m - 1) * ldc + n);
+    const int64_t a_one = 4 * (tn ? (k > 0 ? (k - 1) * lda + m : 0) : (m - 1) * lda + k);
+    const int64_t b_one = 4 * (tn ? (k > 0 ? (k - 1) * ldb + n : 0) : (n - 1) * ldb + k);
+    const int64_t c_one = 4 * ((m - 1) * ldc + n);
+    // results must not overlap each other: C strides at least one matrix
+    if (batch > 1 && (stride_c < 0 || 4 * stride_c < c_one)) return DL_E_INVAL;
+    if (stride_a < 0 || stride_b < 0 || stride_y < 0) return DL_E_INVAL;
+    const int64_t bm = batch - 1;
+    const int64_t a_bytes = a_one + 4 * bm * stride_a, b_bytes = b_one + 4 * bm * stride_b;
+    const int64_t c_bytes = c_one + 4 * bm * stride_c, y_bytes = c_one + 4 * bm * stride_y;
     const Span c_s = span_of(c, c_bytes);
     if (k > 0 && (c_s.overlaps(span_of(a, a_bytes)) || c_s.overlaps(span_of(b, b_bytes))))
         return DL_E_INVAL;
-    if (y != nullptr && y != c && c_s.overlaps(span_of(y, c_bytes))) return DL_E_INVAL;
+    if (y != nullptr && !(y == c && stride_y == stride_c) && c_s.overlaps(span_of(y, y_bytes)))
+        return DL_E_INVAL;
     if (ws_bytes > 0) {
         const Span w_s = span_of(workspace, ws_bytes);
-        if (w_s.overlaps(c_s) || (y && w_s.overlaps(span_of(y, c_bytes))) ||
+        if (w_s.overlaps(c_s) || (y && w_s.overlaps(span_of(y, y_bytes))) ||
             (k > 0 && (w_s.overlaps(span_of(a, a_bytes)) || w_s.overlaps(span_of(b, b_bytes)))))
             return DL_E_INVAL;
     }
@@ -509,30 +527,44 @@ int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t
     }
     if (int st = check_device_span(c, c_bytes)) return st;
     if (y != nullptr)
-        if (int st = check_device_span(y, c_bytes)) return st;
+        if (int st = check_device_span(y, y_bytes)) return st;
     if (ws_bytes > 0)
         if (int st = check_device_span(workspace, ws_bytes)) return st;
     (void)hipGetLastError();
-    const hipError_t err = dlk::matmul(tn, a, lda, b, ldb, m, n, k, c, ldc, y, alpha, beta, diag,
-                                       symmetric != 0, workspace, ws_bytes,
+    const hipError_t err = dlk::matmul(tn, a, lda, stride_a, b, ldb, stride_b, m, n, k, c, ldc,
+                                       stride_c, y, stride_y, alpha, beta, diag, symmetric != 0,
+                                       batch, workspace, ws_bytes,
                                        static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
 
-int dl_polar_workspace_bytes(int64_t rows, int64_t cols, int64_t* bytes) {
-    if (bytes == nullptr || rows < 1 || cols < 1) return DL_E_INVAL;
-    if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) ||
-        dlk::gemm_tiles(rows, cols) > dlk::kGemmMaxTiles)
+int dl_matmul_f32(int form, const float* a, int64_t lda, const float* b, int64_t ldb, int64_t m,
+                  int64_t n, int64_t k, float* c, int64_t ldc, const float* y, float alpha,
+                  float beta, float diag, int symmetric, void* workspace, int64_t workspace_bytes,
+                  void* stream) {
+    return dl_matmul_f32_batch(form, a, lda, 0, b, ldb, 0, m, n, k, c, ldc, 0, y, 0, alpha, beta,
+                               diag, symmetric, 1, workspace, workspace_bytes, stream);
+}
+
+int dl_polar_workspace_bytes_batch(int64_t rows, int64_t cols, int batch, int64_t* bytes) {
+    if (bytes == nullptr || rows < 1 || cols < 1 || batch < 1 || batch > DL_MAX_BATCH)
         return DL_E_INVAL;
-    *bytes = dlk::polar_workspace_bytes(rows, cols);
+    if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31) ||
+        dlk::gemm_tiles(rows, cols) * batch > dlk::kGemmMaxTiles)
+        return DL_E_INVAL;
+    *bytes = dlk::polar_workspace_bytes(rows, cols, batch);
     return DL_OK;
+}
+
+int dl_polar_workspace_bytes(int64_t rows, int64_t cols, int64_t* bytes) {
+    return dl_polar_workspace_bytes_batch(rows, cols, 1, bytes);
 }
 
 namespace {
 
-int check_polar_args(int64_t rows, int64_t cols, int quintic, int cubic, void* ws,
+int check_polar_args(int64_t rows, int64_t cols, int batch, int quintic, int cubic, void* ws,
                      int64_t ws_bytes, int64_t* need) {
-    if (int st = dl_polar_workspace_bytes(rows, cols, need)) return st;
+    if (int st = dl_polar_workspace_bytes_batch(rows, cols, batch, need)) return st;
     if (quintic < 0 || cubic < 0 || quintic + cubic < 1 || quintic > 64 || cubic > 64)
         return DL_E_INVAL;
     if (ws == nullptr || ws_bytes < *need) return DL_E_INVAL;
@@ -545,7 +577,7 @@ int check_polar_args(int64_t rows, int64_t cols, int quintic, int cubic, void* w
 int dl_polar_factor(float* out, const float* update, int64_t rows, int64_t cols, int quintic_steps,
                     int cubic_steps, void* workspace, int64_t workspace_bytes, void* stream) {
     int64_t need = 0;
-    if (int st = check_polar_args(rows, cols, quintic_steps, cubic_steps, workspace,
+    if (int st = check_polar_args(rows, cols, 1, quintic_steps, cubic_steps, workspace,
                                   workspace_bytes, &need))
         return st;
     if (out == nullptr || update == nullptr) return DL_E_INVAL;
@@ -558,8 +590,43 @@ int dl_polar_factor(float* out, const float* update, int64_t rows, int64_t cols,
     if (int st = check_device_span(out, bytes)) return st;
     if (int st = check_device_span(update, bytes)) return st;
     (void)hipGetLastError();
-    const hipError_t err = dlk::polar_iterate(update, nullptr, out, nullptr, 0.0f, rows, cols,
+    const hipError_t err = dlk::polar_iterate(&update, nullptr, &out, nullptr, 0.0f, 1, rows, cols,
                                               quintic_steps, cubic_steps, workspace,
+                                              static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
+int dl_outer_orthogonal_step_batch(float* const* theta, const float* const* averaged, int batch,
+                                   int64_t rows, int64_t cols, float scale, int quintic_steps,
+                                   int cubic_steps, void* workspace, int64_t workspace_bytes,
+                                   void* stream) {
+    int64_t need = 0;
+    if (int st = check_polar_args(rows, cols, batch, quintic_steps, cubic_steps, workspace,
+                                  workspace_bytes, &need))
+        return st;
+    if (theta == nullptr || averaged == nullptr) return DL_E_INVAL;
+    const int64_t bytes = rows * cols * 4;
+    const Span w_s = span_of(workspace, need);
+    for (int b = 0; b < batch; ++b) {
+        if (theta[b] == nullptr || averaged[b] == nullptr) return DL_E_INVAL;
+        if (!aligned_to(theta[b], alignof(float)) || !aligned_to(averaged[b], alignof(float)))
+            return DL_E_ALIGN;
+        const Span t_s = span_of(theta[b], bytes), a_s = span_of(averaged[b], bytes);
+        if (t_s.overlaps(a_s) || t_s.overlaps(w_s) || a_s.overlaps(w_s)) return DL_E_INVAL;
+        // the matrices are written: no theta may meet another matrix's theta or averaged
+        for (int c = 0; c < b; ++c)
+            if (t_s.overlaps(span_of(theta[c], bytes)) || t_s.overlaps(span_of(averaged[c], bytes)) ||
+                a_s.overlaps(span_of(theta[c], bytes)))
+                return DL_E_INVAL;
+    }
+    if (int st = check_device_span(workspace, need)) return st;
+    for (int b = 0; b < batch; ++b) {
+        if (int st = check_device_span(theta[b], bytes)) return st;
+        if (int st = check_device_span(averaged[b], bytes)) return st;
+    }
+    (void)hipGetLastError();
+    const hipError_t err = dlk::polar_iterate(theta, averaged, nullptr, theta, scale, batch, rows,
+                                              cols, quintic_steps, cubic_steps, workspace,
                                               static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
 }
@@ -567,25 +634,8 @@ int dl_polar_factor(float* out, const float* update, int64_t rows, int64_t cols,
 int dl_outer_orthogonal_step(float* theta, const float* averaged, int64_t rows, int64_t cols,
                              float scale, int quintic_steps, int cubic_steps, void* workspace,
                              int64_t workspace_bytes, void* stream) {
-    int64_t need = 0;
-    if (int st = check_polar_args(rows, cols, quintic_steps, cubic_steps, workspace,
-                                  workspace_bytes, &need))
-        return st;
-    if (theta == nullptr || averaged == nullptr) return DL_E_INVAL;
-    if (!aligned_to(theta, alignof(float)) || !aligned_to(averaged, alignof(float)))
-        return DL_E_ALIGN;
-    const int64_t bytes = rows * cols * 4;
-    const Span t_s = span_of(theta, bytes), a_s = span_of(averaged, bytes),
-               w_s = span_of(workspace, need);
-    if (t_s.overlaps(a_s) || t_s.overlaps(w_s) || a_s.overlaps(w_s)) return DL_E_INVAL;
-    if (int st = check_device_span(workspace, need)) return st;
-    if (int st = check_device_span(theta, bytes)) return st;
-    if (int st = check_device_span(averaged, bytes)) return st;
-    (void)hipGetLastError();
-    const hipError_t err = dlk::polar_iterate(theta, averaged, nullptr, theta, scale, rows, cols,
-                                              quintic_steps, cubic_steps, workspace,
-                                              static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? DL_OK : DL_E_HIP;
+    return dl_outer_orthogonal_step_batch(&theta, &averaged, 1, rows, cols, scale, quintic_steps,
+                                          cubic_steps, workspace, workspace_bytes, stream);
 }
 
 int dl_frag_range(const dl_round* r, int frag, int64_t* offset, int64_t* length) {

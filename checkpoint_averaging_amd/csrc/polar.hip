@@ -54,6 +54,7 @@ struct Epilogue {
     const float* y;      // may be null; may equal c
     int64_t ldy;
     float alpha, beta, diag;
+    int64_t sc = 0, sy = 0;   // element strides between the matrices of a batch
 };
 
 constexpr int kTileElems = kTileM * kTileN;
@@ -72,9 +73,12 @@ constexpr int kTileElems = kTileM * kTileN;
 //     first stream-K piece) or 2w + 1 (its last one), and k_reduce_pieces
 //     adds the pieces of each cut tile in K order.
 // Without a workspace: groups = tiles, one round of whole tiles, no pieces.
+// A batch of equally shaped products is one product whose tiles are the
+// batch's tiles, matrix after matrix.
 struct Work {
     uint32_t tiles_n;    // tiles along N (and along M when symmetric)
-    uint32_t tiles;      // output tiles computed
+    uint32_t tiles_per;  // output tiles computed per matrix of the batch
+    uint32_t tiles;      // output tiles computed in all (tiles_per * batch)
     uint32_t kt;         // K-tiles per output tile (at least 1)
     uint32_t groups;     // workgroups with work
     uint32_t per_xcd;    // the grid is 8 * per_xcd workgroups
@@ -285,8 +289,9 @@ template <bool TN>
 __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__ A, int64_t lda,
                                                        const float* __restrict__ B, int64_t ldb,
                                                        int64_t M, int64_t N, int64_t K,
-                                                       Work wk, bool vec_a, bool vec_b,
-                                                       Epilogue e, float* __restrict__ part) {
+                                                       int64_t sa, int64_t sb, Work wk,
+                                                       bool vec_a, bool vec_b, Epilogue e,
+                                                       float* __restrict__ part) {
     __shared__ __align__(16) float smem[kLdsFloats];
     // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
     // contiguous run of workgroup indices, hence of tiles, so that tiles
@@ -316,12 +321,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
             whole = u == t_begin && seg_end == t_end;
             t = dp_tiles + ts;
         }
+        // matrix mb of the batch, tile tm within it
+        const uint32_t mb = t / wk.tiles_per, tm = t - mb * wk.tiles_per;
         uint32_t ti, tj;
-        tile_coords(t, wk, ti, tj);
+        tile_coords(tm, wk, ti, tj);
         const int64_t i0 = static_cast<int64_t>(ti) * kTileM;
         const int64_t j0 = static_cast<int64_t>(tj) * kTileN;
         f32x16 acc[2][2];
-        mma_tile<TN>(A, lda, B, ldb, M, N, i0, j0, kb, ke, vec_a, vec_b, smem, acc);
+        mma_tile<TN>(A + mb * sa, lda, B + mb * sb, ldb, M, N, i0, j0, kb, ke, vec_a, vec_b, smem,
+                     acc);
+        float* const ec = e.c + mb * e.sc;
+        const float* const ey = e.y ? e.y + mb * e.sy : nullptr;
 
         // Stage the tile's sums in LDS (free after mma_tile), then store
         // from there: rows of 128 consecutive columns per store, with
@@ -356,9 +366,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
                 const int64_t i = i0 + row;
                 float v = e.alpha * smem[row * kStage + col];
                 if (i < M && j < N && (!wk.sym || i <= j)) {
-                    if (e.y) v = v + e.beta * e.y[i * e.ldy + j];
+                    if (ey) v = v + e.beta * ey[i * e.ldy + j];
                     if (i == j) v = v + e.diag;
-                    e.c[i * e.ldc + j] = v;
+                    ec[i * e.ldc + j] = v;
                 }
                 if (wk.sym) smem[row * kStage + col] = v;
             }
@@ -370,7 +380,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
                 for (int p = 0; p < kTileElems / kGemmThreads; ++p) {
                     const int jj = 2 * p + (tid >> 7);
                     const int64_t jm = j0 + jj;
-                    if (i < jm && jm < M) e.c[jm * e.ldc + i] = smem[col * kStage + jj];
+                    if (i < jm && jm < M) ec[jm * e.ldc + i] = smem[col * kStage + jj];
                 }
             }
         }
@@ -402,8 +412,12 @@ __global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__
     if (ub == t_begin) return;                       // a start between whole tiles
     const uint32_t prev = unit_begin(wk, b - 1);
     if (prev > t_begin) return;                      // handled at an earlier start
+    const uint32_t t = wk.dp_rounds * wk.groups + ts;
+    const uint32_t mb = t / wk.tiles_per;
     uint32_t ti, tj;
-    tile_coords(wk.dp_rounds * wk.groups + ts, wk, ti, tj);
+    tile_coords(t - mb * wk.tiles_per, wk, ti, tj);
+    float* const ec = e.c + mb * e.sc;
+    const float* const ey = e.y ? e.y + mb * e.sy : nullptr;
     // workgroup b - 1 holds the tile's first piece: its first slot if it
     // starts at the tile, else its last slot
     const float* first = part + (2 * static_cast<int64_t>(b - 1) + (prev < t_begin ? 1 : 0)) *
@@ -429,9 +443,9 @@ __global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__
             const int64_t j = static_cast<int64_t>(tj) * kTileN + lj + c;
             float o = e.alpha * v[c];
             if (i < M && j < N && (!wk.sym || i <= j)) {
-                if (e.y) o = o + e.beta * e.y[i * e.ldy + j];
+                if (ey) o = o + e.beta * ey[i * e.ldy + j];
                 if (i == j) o = o + e.diag;
-                e.c[i * e.ldc + j] = o;
+                ec[i * e.ldc + j] = o;
             }
             tr[ll][lj + c] = o;
         }
@@ -444,7 +458,7 @@ __global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__
     for (int p = 0; p < 16; ++p) {
         const int jj = (tid >> 5) + 8 * p;
         const int64_t j = static_cast<int64_t>(tj) * kTileN + jj;
-        if (i < j && j < M) e.c[j * e.ldc + i] = tr[ii][jj];
+        if (i < j && j < M) ec[j * e.ldc + i] = tr[ii][jj];
     }
 }
 
@@ -511,13 +525,14 @@ int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 constexpr int64_t kStreamGroups = 512;          // two resident workgroups on each of 256 CUs
 constexpr int64_t kMinUnits = 8;                // K-tiles per workgroup at least
 
-// The split of an M x N x K product (see Work).  With a workspace of at
-// least 2 * groups tiles the units are spread over up to kStreamGroups
-// workgroups; otherwise each workgroup takes one whole tile.
-void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t ws_bytes, Work& wk,
-               int64_t* need_bytes = nullptr) {
+// The split of a batch of M x N x K products (see Work).  With a workspace
+// of at least 2 * groups tiles the units are spread over up to
+// kStreamGroups workgroups; otherwise each workgroup takes one whole tile.
+void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch, int64_t ws_bytes,
+               Work& wk, int64_t* need_bytes = nullptr) {
     const int64_t tn = (N + kTileN - 1) / kTileN, tm = (M + kTileM - 1) / kTileM;
-    const int64_t tiles = sym ? tn * (tn + 1) / 2 : tm * tn;
+    const int64_t per = sym ? tn * (tn + 1) / 2 : tm * tn;
+    const int64_t tiles = per * batch;
     const int64_t kt = K > 0 ? (K + kTileK - 1) / kTileK : 1;
     const int64_t units = tiles * kt;
     int64_t g = units / kMinUnits;
@@ -533,6 +548,7 @@ void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t ws_bytes, Work
                         g != tiles;
     const int64_t groups = stream ? g : tiles;
     wk.tiles_n = static_cast<uint32_t>(tn);
+    wk.tiles_per = static_cast<uint32_t>(per);
     wk.tiles = static_cast<uint32_t>(tiles);
     wk.kt = static_cast<uint32_t>(kt);
     wk.groups = static_cast<uint32_t>(groups);
@@ -543,29 +559,32 @@ void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t ws_bytes, Work
     if (need_bytes) *need_bytes = need;
 }
 
-// Partial-buffer bytes of the preferred split of a product.
-int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym) {
+// Partial-buffer bytes of the preferred split of a batch of products.
+int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch = 1) {
     Work wk;
     int64_t need = 0;
-    plan_gemm(M, N, K, sym, INT64_MAX, wk, &need);
+    plan_gemm(M, N, K, sym, batch, INT64_MAX, wk, &need);
     return need;
 }
 
-hipError_t gemm(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
-                int64_t N, int64_t K, const Epilogue& e, bool sym, float* part,
-                int64_t part_bytes, hipStream_t s) {
+// A batch of `batch` products: operand b at A + b*sa and B + b*sb, result and
+// Y at e.c + b*e.sc and e.y + b*e.sy.
+hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B, int64_t ldb,
+                int64_t sb, int64_t M, int64_t N, int64_t K, const Epilogue& e, bool sym,
+                int64_t batch, float* part, int64_t part_bytes, hipStream_t s) {
     Work wk;
-    plan_gemm(M, N, K, sym, part ? part_bytes : 0, wk);
+    plan_gemm(M, N, K, sym, batch, part ? part_bytes : 0, wk);
     const dim3 grid(wk.per_xcd * kXcds);
-    // float4 loads of row-major operands need 16-byte aligned rows
-    const bool vec_a = reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 4 == 0;
-    const bool vec_b = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 4 == 0;
+    // float4 loads of row-major operands need 16-byte aligned rows (and
+    // batch strides)
+    const bool vec_a = reinterpret_cast<uintptr_t>(A) % 16 == 0 && lda % 4 == 0 && sa % 4 == 0;
+    const bool vec_b = reinterpret_cast<uintptr_t>(B) % 16 == 0 && ldb % 4 == 0 && sb % 4 == 0;
     if (tn)
         hipLaunchKernelGGL((k_gemm<true>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           wk, vec_a, vec_b, e, part);
+                           sa, sb, wk, vec_a, vec_b, e, part);
     else
         hipLaunchKernelGGL((k_gemm<false>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
-                           wk, vec_a, vec_b, e, part);
+                           sa, sb, wk, vec_a, vec_b, e, part);
     if (wk.units != 0 && (wk.units / wk.kt) % wk.groups != 0)   // pieces of cut tiles to add
         hipLaunchKernelGGL(k_reduce_pieces, dim3(wk.groups * 4), dim3(256), 0, s, part, wk, M, N, e);
     return hipGetLastError();
@@ -575,100 +594,163 @@ hipError_t gemm(bool tn, const float* A, int64_t lda, const float* B, int64_t ld
 
 namespace {
 
-// Partial-buffer bytes of the iteration's three products on a rows x cols
-// matrix: the symmetric Gram matrix, its symmetric square, the next iterate.
-int64_t polar_partial_bytes(int64_t rows, int64_t cols) {
+// Partial-buffer bytes of the iteration's three products on a batch of
+// rows x cols matrices: the symmetric Gram matrix, its symmetric square, the
+// next iterate.
+int64_t polar_partial_bytes(int64_t rows, int64_t cols, int64_t batch) {
     const int64_t r = rows < cols ? rows : cols, L = rows < cols ? cols : rows;
-    int64_t b = gemm_partial_bytes(r, r, L, true);
-    const int64_t sq = gemm_partial_bytes(r, r, r, true);
-    const int64_t nx = gemm_partial_bytes(rows, cols, r, false);
+    int64_t b = gemm_partial_bytes(r, r, L, true, batch);
+    const int64_t sq = gemm_partial_bytes(r, r, r, true, batch);
+    const int64_t nx = gemm_partial_bytes(rows, cols, r, false, batch);
     if (sq > b) b = sq;
     if (nx > b) b = nx;
     return b;
 }
 
-}  // namespace
+// Workspace layout of a batch: per matrix the norm partials, then the
+// inverse norms, then per matrix two iterates and the Gram and polynomial
+// matrices (each region 256-byte aligned per matrix), then the partial tiles.
+struct PolarSpace {
+    double* partial;
+    float* inv;
+    float *xa, *xb, *g, *m, *part;
+    int64_t sx, sg, part_bytes, total;
+};
 
-int64_t polar_workspace_bytes(int64_t rows, int64_t cols) {
-    const int64_t r = rows < cols ? rows : cols;
-    return align256(kRedBlocks * 8) + 256 + 2 * align256(rows * cols * 4) + 2 * align256(r * r * 4) +
-           align256(polar_partial_bytes(rows, cols));
+PolarSpace polar_space(void* ws, int64_t rows, int64_t cols, int64_t batch) {
+    const int64_t n = rows * cols, r = rows < cols ? rows : cols;
+    PolarSpace sp{};
+    sp.sx = align256(n * 4) / 4;
+    sp.sg = align256(r * r * 4) / 4;
+    sp.part_bytes = align256(polar_partial_bytes(rows, cols, batch));
+    char* p = static_cast<char*>(ws);
+    const int64_t o_inv = align256(batch * kRedBlocks * 8);
+    const int64_t o_xa = o_inv + align256(batch * 4);
+    const int64_t o_xb = o_xa + batch * sp.sx * 4;
+    const int64_t o_g = o_xb + batch * sp.sx * 4;
+    const int64_t o_m = o_g + batch * sp.sg * 4;
+    const int64_t o_part = o_m + batch * sp.sg * 4;
+    sp.total = o_part + sp.part_bytes;
+    if (p) {
+        sp.partial = reinterpret_cast<double*>(p);
+        sp.inv = reinterpret_cast<float*>(p + o_inv);
+        sp.xa = reinterpret_cast<float*>(p + o_xa);
+        sp.xb = reinterpret_cast<float*>(p + o_xb);
+        sp.g = reinterpret_cast<float*>(p + o_g);
+        sp.m = reinterpret_cast<float*>(p + o_m);
+        sp.part = reinterpret_cast<float*>(p + o_part);
+    }
+    return sp;
 }
 
-hipError_t polar_iterate(const float* src, const float* sub, float* out, float* theta, float scale,
-                         int64_t rows, int64_t cols, int quintic, int cubic, void* ws,
-                         hipStream_t s) {
+// theta = theta - scale * P, the same two roundings as the fused epilogue:
+// fl(fl(-scale * P) + theta).
+__global__ __launch_bounds__(256) void k_step(float* __restrict__ theta, const float* __restrict__ P,
+                                              float scale, int64_t n) {
+    const float ns = -scale;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+         e += static_cast<int64_t>(gridDim.x) * 256)
+        theta[e] = ns * P[e] + theta[e];
+}
+
+}  // namespace
+
+int64_t polar_workspace_bytes(int64_t rows, int64_t cols, int64_t batch) {
+    return polar_space(nullptr, rows, cols, batch).total;
+}
+
+hipError_t polar_iterate(const float* const* src, const float* const* sub, float* const* out,
+                         float* const* theta, float scale, int64_t batch, int64_t rows,
+                         int64_t cols, int quintic, int cubic, void* ws, hipStream_t s) {
+    if (batch < 1 || (batch > 1 && (out || !theta))) return hipErrorInvalidValue;
     const int64_t n = rows * cols;
     const bool tall = rows >= cols;
     const int64_t r = tall ? cols : rows;
-    char* p = static_cast<char*>(ws);
-    double* partial = reinterpret_cast<double*>(p);
-    p += align256(kRedBlocks * 8);
-    float* inv = reinterpret_cast<float*>(p);
-    p += 256;
-    float* xa = reinterpret_cast<float*>(p);
-    p += align256(n * 4);
-    float* xb = reinterpret_cast<float*>(p);
-    p += align256(n * 4);
-    float* g = reinterpret_cast<float*>(p);
-    p += align256(r * r * 4);
-    float* m = reinterpret_cast<float*>(p);
-    p += align256(r * r * 4);
-    float* part = reinterpret_cast<float*>(p);
-    const int64_t part_bytes = align256(polar_partial_bytes(rows, cols));
+    const PolarSpace sp = polar_space(ws, rows, cols, batch);
 
-    // X0 = A / ||A||_F, with A = src (or src - sub, formed in fp32 into xa)
-    hipLaunchKernelGGL(k_sumsq_partial, dim3(kRedBlocks), dim3(kRedThreads), 0, s, src, sub,
-                       sub ? xa : nullptr, n, partial);
-    hipLaunchKernelGGL(k_sumsq_final, dim3(1), dim3(kRedThreads), 0, s, partial, kRedBlocks, inv);
-    hipLaunchKernelGGL(k_scale, dim3(4096), dim3(256), 0, s, xa, sub ? xa : src, inv, n);
+    // X0 = A / ||A||_F per matrix, with A = src (or src - sub, formed in fp32
+    // into the first iterate)
+    for (int64_t b = 0; b < batch; ++b) {
+        float* xa = sp.xa + b * sp.sx;
+        double* partial = sp.partial + b * kRedBlocks;
+        const float* sb = sub ? sub[b] : nullptr;
+        hipLaunchKernelGGL(k_sumsq_partial, dim3(kRedBlocks), dim3(kRedThreads), 0, s, src[b], sb,
+                           sb ? xa : nullptr, n, partial);
+        hipLaunchKernelGGL(k_sumsq_final, dim3(1), dim3(kRedThreads), 0, s, partial, kRedBlocks,
+                           sp.inv + b);
+        hipLaunchKernelGGL(k_scale, dim3(4096), dim3(256), 0, s, xa, sb ? xa : src[b], sp.inv + b,
+                           n);
+    }
     if (hipError_t err = hipGetLastError()) return err;
 
-    float* x = xa;
-    float* xn = xb;
+    // A single matrix writes its result straight from the last product's
+    // epilogue; a batch writes P to the workspace and finishes per matrix.
+    const bool direct = batch == 1;
+    float* x = sp.xa;
+    float* xn = sp.xb;
     const int steps = quintic + cubic;
     for (int st = 0; st < steps; ++st) {
         const bool quin = st < quintic;
         // Gram matrix (r x r) of the current iterate; for the cubic steps the
         // epilogue forms M = 1.5 I - 0.5 G directly.
-        const Epilogue eg{quin ? g : m, r, nullptr, 0, quin ? 1.0f : -0.5f, 0.0f,
-                          quin ? 0.0f : 1.5f};
+        Epilogue eg{quin ? sp.g : sp.m, r, nullptr, 0, quin ? 1.0f : -0.5f, 0.0f,
+                    quin ? 0.0f : 1.5f};
+        eg.sc = sp.sg;
         // Both r x r results are symmetric: only their upper triangles are
         // computed, and the lower ones are mirror images (exactly symmetric).
         hipError_t err =
-            tall ? gemm(true, x, cols, x, cols, r, r, rows, eg, true, part, part_bytes, s)   // X^T X
-                 : gemm(false, x, cols, x, cols, r, r, cols, eg, true, part, part_bytes, s); // X X^T
+            tall ? gemm(true, x, cols, sp.sx, x, cols, sp.sx, r, r, rows, eg, true, batch,
+                        sp.part, sp.part_bytes, s)                                    // X^T X
+                 : gemm(false, x, cols, sp.sx, x, cols, sp.sx, r, r, cols, eg, true, batch,
+                        sp.part, sp.part_bytes, s);                                   // X X^T
         if (err) return err;
         if (quin) {   // M = c G^2 + b G + a I  (G symmetric: G G = G^T G)
-            const Epilogue em{m, r, g, r, kQc, kQb, kQa};
-            if ((err = gemm(true, g, r, g, r, r, r, r, em, true, part, part_bytes, s))) return err;
+            Epilogue em{sp.m, r, sp.g, r, kQc, kQb, kQa};
+            em.sc = sp.sg;
+            em.sy = sp.sg;
+            if ((err = gemm(true, sp.g, r, sp.sg, sp.g, r, sp.sg, r, r, r, em, true, batch,
+                            sp.part, sp.part_bytes, s)))
+                return err;
         }
-        // next iterate: X M (tall) or M X (wide); the last step writes the
-        // result: the polar factor to out, or theta - scale * P onto theta
+        // next iterate: X M (tall) or M X (wide); the last step of a single
+        // matrix writes the result: the polar factor to out, or theta -
+        // scale * P onto theta
         const bool last = st == steps - 1;
         Epilogue ex{xn, cols, nullptr, 0, 1.0f, 0.0f, 0.0f};
-        if (last && out) ex.c = out;
-        if (last && theta) ex = Epilogue{theta, cols, theta, cols, -scale, 1.0f, 0.0f};
-        err = tall ? gemm(false, x, cols, m, r, rows, cols, r, ex, false, part, part_bytes, s)
-                   : gemm(true, m, r, x, cols, rows, cols, r, ex, false, part, part_bytes, s);
+        ex.sc = sp.sx;
+        if (last && direct && out) ex = Epilogue{out[0], cols, nullptr, 0, 1.0f, 0.0f, 0.0f};
+        if (last && direct && theta)
+            ex = Epilogue{theta[0], cols, theta[0], cols, -scale, 1.0f, 0.0f};
+        err = tall ? gemm(false, x, cols, sp.sx, sp.m, r, sp.sg, rows, cols, r, ex, false, batch,
+                          sp.part, sp.part_bytes, s)
+                   : gemm(true, sp.m, r, sp.sg, x, cols, sp.sx, rows, cols, r, ex, false, batch,
+                          sp.part, sp.part_bytes, s);
         // (tall: C[i][j] = sum_k X[i][k] M[j][k]; wide: C[i][j] = sum_k M[k][i] X[k][j])
         if (err) return err;
         float* t = x;
         x = xn;
         xn = t;
     }
+    if (!direct)   // x holds the batch's polar factors
+        for (int64_t b = 0; b < batch; ++b)
+            hipLaunchKernelGGL(k_step, dim3(4096), dim3(256), 0, s, theta[b], x + b * sp.sx, scale,
+                               n);
     return hipGetLastError();
 }
 
-int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym) {
-    return gemm_partial_bytes(M, N, K, sym);
+int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch) {
+    return gemm_partial_bytes(M, N, K, sym, batch);
 }
 
-hipError_t matmul(bool tn, const float* A, int64_t lda, const float* B, int64_t ldb, int64_t M,
-                  int64_t N, int64_t K, float* C, int64_t ldc, const float* Y, float alpha,
-                  float beta, float diag, bool sym, void* ws, int64_t ws_bytes, hipStream_t s) {
-    const Epilogue e{C, ldc, Y, ldc, alpha, beta, diag};
-    return gemm(tn, A, lda, B, ldb, M, N, K, e, sym, static_cast<float*>(ws), ws ? ws_bytes : 0, s);
+hipError_t matmul(bool tn, const float* A, int64_t lda, int64_t sa, const float* B, int64_t ldb,
+                  int64_t sb, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc, int64_t sc,
+                  const float* Y, int64_t sy, float alpha, float beta, float diag, bool sym,
+                  int64_t batch, void* ws, int64_t ws_bytes, hipStream_t s) {
+    Epilogue e{C, ldc, Y, ldc, alpha, beta, diag};
+    e.sc = sc;
+    e.sy = sy;
+    return gemm(tn, A, lda, sa, B, ldb, sb, M, N, K, e, sym, batch, static_cast<float*>(ws),
+                ws ? ws_bytes : 0, s);
 }
 
 }  // namespace dlk

@@ -6,6 +6,11 @@
 //
 //   dlpolar_driver --shapes RxC:count[,RxC:count...] [--steps S] [--warmup W]
 //                  [--quintic Q] [--cubic C] [--copy-mib M]
+//   dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--steps S] [--warmup W]
+//
+// The second form times one product of dl_matmul_f32 (S launches, each
+// bracketed by events) with the workspace of dl_matmul_workspace_bytes
+// (none with :nows); `sym` declares the result symmetric (A = B, M = N).
 //
 // One step runs theta = theta - s * P(theta - averaged) once for every
 // matrix of the list (count matrices of each shape, in list order), on one
@@ -76,8 +81,15 @@ struct Shape {
     int count;
 };
 
+struct Gemm {
+    bool tn = true, sym = false, ws = true;
+    int64_t m = 0, n = 0, k = 0;
+};
+
 struct Args {
     std::vector<Shape> shapes;
+    Gemm gemm;
+    bool has_gemm = false;
     int steps = 1;
     int warmup = 1;
     int quintic = 12;
@@ -88,7 +100,8 @@ struct Args {
 [[noreturn]] void usage() {
     std::fprintf(stderr,
                  "usage: dlpolar_driver --shapes RxC:count[,RxC:count...] [--steps S]\n"
-                 "       [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]\n");
+                 "       [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]\n"
+                 "       dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--steps S] [--warmup W]\n");
     std::exit(2);
 }
 
@@ -110,6 +123,15 @@ Args parse(int argc, char** argv) {
                 a.shapes.push_back(s);
                 pos = c + 1;
             }
+        } else if (k == "--gemm") {
+            char form[3] = {0, 0, 0};
+            if (std::sscanf(v.c_str(), "%2[TN]:%ldx%ldx%ld", form, &a.gemm.m, &a.gemm.n,
+                            &a.gemm.k) != 4)
+                usage();
+            a.gemm.tn = std::string(form) == "TN";
+            a.gemm.sym = v.find(":sym") != std::string::npos;
+            a.gemm.ws = v.find(":nows") == std::string::npos;
+            a.has_gemm = true;
         } else if (k == "--steps") a.steps = std::atoi(v.c_str());
         else if (k == "--warmup") a.warmup = std::atoi(v.c_str());
         else if (k == "--quintic") a.quintic = std::atoi(v.c_str());
@@ -117,7 +139,10 @@ Args parse(int argc, char** argv) {
         else if (k == "--copy-mib") a.copy_mib = std::atoi(v.c_str());
         else usage();
     }
-    if (a.shapes.empty() || a.steps < 1 || a.warmup < 0) usage();
+    if ((a.shapes.empty() && !a.has_gemm) || a.steps < 1 || a.warmup < 0) usage();
+    if (a.has_gemm && (a.gemm.m < 1 || a.gemm.n < 1 || a.gemm.k < 1 ||
+                       (a.gemm.sym && a.gemm.m != a.gemm.n)))
+        usage();
     for (const Shape& s : a.shapes)
         if (s.rows < 1 || s.cols < 1 || s.count < 1) usage();
     return a;
@@ -133,8 +158,64 @@ double flops(const Shape& s, int quintic, int cubic) {
 
 }  // namespace
 
+// One product, timed launch by launch.  A and B are filled with a pattern;
+// for a symmetric result B is A (A^T A as TN, A A^T as NT).
+int run_gemm(const Args& a) {
+    const Gemm& g = a.gemm;
+    const int64_t na = g.tn ? g.k * g.m : g.m * g.k;
+    const int64_t nb = g.tn ? g.k * g.n : g.n * g.k;
+    float *A = nullptr, *B = nullptr, *C = nullptr;
+    void* ws = nullptr;
+    int64_t wsb = 0;
+    DLCHECK(dl_matmul_workspace_bytes(g.m, g.n, g.k, g.sym ? 1 : 0, &wsb));
+    HIPCHECK(hipMalloc(&A, na * sizeof(float)));
+    if (!g.sym) HIPCHECK(hipMalloc(&B, nb * sizeof(float)));
+    HIPCHECK(hipMalloc(&C, g.m * g.n * sizeof(float)));
+    if (g.ws && wsb > 0) HIPCHECK(hipMalloc(&ws, wsb));
+    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, A, nullptr, 0.04f, na, 3u);
+    if (!g.sym) hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, B, nullptr, 0.04f, nb, 4u);
+    HIPCHECK(hipGetLastError());
+    HIPCHECK(hipDeviceSynchronize());
+    const float* Bp = g.sym ? A : B;
+    const int64_t lda = g.tn ? g.m : g.k, ldb = g.tn ? g.n : g.k;
+    auto launch = [&]() {
+        DLCHECK(dl_matmul_f32(g.tn ? DL_TN : DL_NT, A, lda, Bp, ldb, g.m, g.n, g.k, C, g.n,
+                              nullptr, 1.0f, 0.0f, 0.0f, g.sym ? 1 : 0, ws, ws ? wsb : 0,
+                              nullptr));
+    };
+    for (int w = 0; w < a.warmup; ++w) launch();
+    HIPCHECK(hipDeviceSynchronize());
+    std::vector<hipEvent_t> ev(2 * a.steps);
+    for (hipEvent_t& x : ev) HIPCHECK(hipEventCreate(&x));
+    for (int st = 0; st < a.steps; ++st) {
+        HIPCHECK(hipEventRecord(ev[2 * st], nullptr));
+        launch();
+        HIPCHECK(hipEventRecord(ev[2 * st + 1], nullptr));
+    }
+    HIPCHECK(hipDeviceSynchronize());
+    double tot = 0.0, best = 1e30;
+    for (int st = 0; st < a.steps; ++st) {
+        float ms = 0.0f;
+        HIPCHECK(hipEventElapsedTime(&ms, ev[2 * st], ev[2 * st + 1]));
+        tot += ms;
+        if (ms < best) best = ms;
+    }
+    const double outs = g.sym ? double(g.m) * (g.m + 1) / 2 : double(g.m) * g.n;
+    const double fl = 2.0 * outs * g.k, avg = tot / a.steps;
+    std::printf("[driver] gemm %s %ldx%ldx%ld%s%s: avg %.4f ms (%.2f TFLOP/s), best %.4f ms "
+                "(%.2f TFLOP/s), workspace %ld bytes\n",
+                g.tn ? "TN" : "NT", g.m, g.n, g.k, g.sym ? " sym" : "", ws ? "" : " nows", avg,
+                fl / (avg / 1e3) / 1e12, best, fl / (best / 1e3) / 1e12, ws ? wsb : 0);
+    HIPCHECK(hipFree(A));
+    if (B) HIPCHECK(hipFree(B));
+    HIPCHECK(hipFree(C));
+    if (ws) HIPCHECK(hipFree(ws));
+    return 0;
+}
+
 int main(int argc, char** argv) {
     const Args a = parse(argc, argv);
+    if (a.has_gemm) return run_gemm(a);
     int64_t n_max = 0, ws_max = 0;
     for (const Shape& s : a.shapes) {
         int64_t ws = 0;

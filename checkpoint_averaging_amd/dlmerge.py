@@ -38,11 +38,13 @@ DL_E_CAPACITY = -8
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
-           "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_factor",
-           "dl_outer_orthogonal_step", "dl_matmul_workspace_bytes", "dl_matmul_f32",
+           "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_workspace_bytes_batch",
+           "dl_polar_factor", "dl_outer_orthogonal_step", "dl_outer_orthogonal_step_batch", "dl_matmul_workspace_bytes", "dl_matmul_f32",
+           "dl_matmul_workspace_bytes_batch", "dl_matmul_f32_batch",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
 DL_MAX_SNAPSHOTS = 16
+DL_MAX_BATCH = 64
 DL_TN = 0
 DL_NT = 1
 
@@ -67,9 +69,17 @@ _lib.dl_swa_average.argtypes = [_p, _p, _i64, _i64, _p]
 _lib.dl_snapshot_average.argtypes = [_p, ctypes.POINTER(_p), _i32, _i64, _p]
 _lib.dl_adopt_keep_drift.argtypes = [_p, _p, _p, _i32, _i64, _p]
 _lib.dl_polar_workspace_bytes.argtypes = [_i64, _i64, ctypes.POINTER(_i64)]
+_lib.dl_polar_workspace_bytes_batch.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_i64)]
 _lib.dl_polar_factor.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]
+_lib.dl_outer_orthogonal_step_batch.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32,
+                                                _i64, _i64, _f32, _i32, _i32, _p, _i64, _p]
 _lib.dl_outer_orthogonal_step.argtypes = [_p, _p, _i64, _i64, _f32, _i32, _i32, _p, _i64, _p]
 _lib.dl_matmul_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64)]
+_lib.dl_matmul_workspace_bytes_batch.argtypes = [_i64, _i64, _i64, _i32, _i32,
+                                                 ctypes.POINTER(_i64)]
+_lib.dl_matmul_f32_batch.argtypes = [_i32, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _i64, _p,
+                                     _i64, _i64, _p, _i64, _f32, _f32, _f32, _i32, _i32, _p, _i64,
+                                     _p]
 _lib.dl_matmul_f32.argtypes = [_i32, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _f32,
                                _f32, _f32, _i32, _p, _i64, _p]
 _lib.dl_frag_range.argtypes = [_p, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
@@ -304,6 +314,29 @@ def dl_outer_orthogonal_step(theta: Array, averaged: Array, rows: int, cols: int
            "dl_outer_orthogonal_step")
 
 
+def dl_polar_workspace_bytes_batch(rows: int, cols: int, batch: int) -> int:
+    b = _i64()
+    _check(_lib.dl_polar_workspace_bytes_batch(int(rows), int(cols), int(batch), ctypes.byref(b)),
+           "dl_polar_workspace_bytes_batch")
+    return b.value
+
+
+def dl_outer_orthogonal_step_batch(thetas: Sequence[Array], averaged: Sequence[Array], rows: int,
+                                   cols: int, scale: float, workspace: Array,
+                                   quintic_steps: int = 12, cubic_steps: int = 6,
+                                   workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if len(thetas) != len(averaged):
+        raise ValueError("one averaged matrix per theta")
+    n = len(thetas)
+    tp = (_p * max(1, n))(*[_f32_addr(t, "theta") for t in thetas])
+    ap = (_p * max(1, n))(*[_f32_addr(a, "averaged") for a in averaged])
+    w, wb = _ws(workspace, workspace_bytes)
+    _check(_lib.dl_outer_orthogonal_step_batch(tp, ap, n, int(rows), int(cols), float(scale),
+                                               int(quintic_steps), int(cubic_steps), w, wb,
+                                               _stream(stream)),
+           "dl_outer_orthogonal_step_batch")
+
+
 def dl_matmul_workspace_bytes(m: int, n: int, k: int, symmetric: bool = False) -> int:
     b = _i64()
     _check(_lib.dl_matmul_workspace_bytes(int(m), int(n), int(k), int(bool(symmetric)),
@@ -325,6 +358,33 @@ def dl_matmul_f32(form: int, a: Array, lda: int, b: Array, ldb: int, m: int, n: 
                               _f32_addr(y, "y"), float(alpha), float(beta), float(diag),
                               int(bool(symmetric)), w, wb, _stream(stream)),
            "dl_matmul_f32")
+
+
+def dl_matmul_workspace_bytes_batch(m: int, n: int, k: int, symmetric: bool, batch: int) -> int:
+    b = _i64()
+    _check(_lib.dl_matmul_workspace_bytes_batch(int(m), int(n), int(k), int(bool(symmetric)),
+                                                int(batch), ctypes.byref(b)),
+           "dl_matmul_workspace_bytes_batch")
+    return b.value
+
+
+def dl_matmul_f32_batch(form: int, a: Array, lda: int, stride_a: int, b: Array, ldb: int,
+                        stride_b: int, m: int, n: int, k: int, c: Array, ldc: int, stride_c: int,
+                        batch: int, y: Array = None, stride_y: int = 0, alpha: float = 1.0,
+                        beta: float = 0.0, diag: float = 0.0, symmetric: bool = False,
+                        workspace: Array = None, workspace_bytes: Optional[int] = None,
+                        stream=None) -> None:
+    if workspace is None:
+        w, wb = None, 0
+    else:
+        w, wb = _ws(workspace, workspace_bytes)
+    _check(_lib.dl_matmul_f32_batch(int(form), _f32_addr(a, "a"), int(lda), int(stride_a),
+                                    _f32_addr(b, "b"), int(ldb), int(stride_b), int(m), int(n),
+                                    int(k), _f32_addr(c, "c"), int(ldc), int(stride_c),
+                                    _f32_addr(y, "y"), int(stride_y), float(alpha), float(beta),
+                                    float(diag), int(bool(symmetric)), int(batch), w, wb,
+                                    _stream(stream)),
+           "dl_matmul_f32_batch")
 
 
 def dl_frag_range(r: Round, frag: int) -> Tuple[int, int]:

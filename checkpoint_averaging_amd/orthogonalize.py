@@ -4,9 +4,9 @@ matrix is replaced by its polar factor).
 
 The flat parameter buffer holds every tensor back to back; the weight
 matrices are row-major views into it.  Vectors (norm weights) have no polar
-factor of interest and are left to the plain merge.  Every matrix is one
-call of dl_outer_orthogonal_step on one stream, all sharing one workspace
-sized for the largest matrix.
+factor of interest and are left to the plain merge.  Matrices of one shape
+go through dl_outer_orthogonal_step_batch together (up to a batch size), on
+one stream, all sharing one workspace sized for the largest batch.
 """
 from __future__ import annotations
 
@@ -76,13 +76,23 @@ def gemm_flops(rows: int, cols: int, quintic: int = 12, cubic: int = 6):
 
 class OrthogonalStep:
     """theta = theta - scale * P(theta - averaged) for every weight matrix of
-    a layout, on one stream, with one workspace."""
+    a layout, on one stream, with one workspace.  Matrices of one shape run
+    in batches of up to `batch` (one launch per product for the whole batch);
+    batch 1 runs them one by one."""
 
     def __init__(self, layout: synth.Layout, device: Optional[torch.device] = None,
-                 quintic: int = 12, cubic: int = 6):
+                 quintic: int = 12, cubic: int = 6, batch: int = 8):
         self.matrices = weight_matrices(layout)
         self.quintic, self.cubic = quintic, cubic
-        need = max(dl.dl_polar_workspace_bytes(m.rows, m.cols) for m in self.matrices)
+        by_shape = {}
+        for m in self.matrices:
+            by_shape.setdefault((m.rows, m.cols), []).append(m)
+        self.groups = []
+        for ms in by_shape.values():
+            for i in range(0, len(ms), batch):
+                self.groups.append(ms[i:i + batch])
+        need = max(dl.dl_polar_workspace_bytes_batch(g[0].rows, g[0].cols, len(g))
+                   for g in self.groups)
         self.workspace = torch.empty((need + 3) // 4, dtype=torch.float32,
                                      device=device or torch.device("cuda"))
 
@@ -95,16 +105,22 @@ class OrthogonalStep:
 
     def run(self, theta: torch.Tensor, averaged: torch.Tensor, scale: float, timer=None):
         """One orthogonalised outer step over the flat buffers.  `timer`, if
-        given, is called as timer(matrix, call) and must call call()."""
-        for m in self.matrices:
-            n = m.rows * m.cols
-            t = theta[m.offset:m.offset + n]
-            a = averaged[m.offset:m.offset + n]
+        given, is called as timer(matrices, call) for each batch and must
+        call call()."""
+        for g in self.groups:
+            rows, cols = g[0].rows, g[0].cols
+            n = rows * cols
+            ts = [theta[m.offset:m.offset + n] for m in g]
+            avs = [averaged[m.offset:m.offset + n] for m in g]
 
-            def call(t=t, a=a, m=m):
-                dl.dl_outer_orthogonal_step(t, a, m.rows, m.cols, scale, self.workspace,
-                                            self.quintic, self.cubic)
+            def call(ts=ts, avs=avs, rows=rows, cols=cols):
+                if len(ts) == 1:
+                    dl.dl_outer_orthogonal_step(ts[0], avs[0], rows, cols, scale, self.workspace,
+                                                self.quintic, self.cubic)
+                else:
+                    dl.dl_outer_orthogonal_step_batch(ts, avs, rows, cols, scale, self.workspace,
+                                                      self.quintic, self.cubic)
             if timer is None:
                 call()
             else:
-                timer(m, call)
+                timer(g, call)

@@ -327,6 +327,11 @@ int dl_adopt_keep_drift(float *theta, const float *global, const void *pushed, i
 /* Workspace bytes for a rows x cols matrix (rows, cols >= 1).  DL_E_INVAL. */
 int dl_polar_workspace_bytes(int64_t rows, int64_t cols, int64_t *bytes);
 
+/* Workspace bytes for a batch of 1 <= batch <= DL_MAX_BATCH rows x cols
+ * matrices (dl_outer_orthogonal_step_batch).  DL_E_INVAL. */
+#define DL_MAX_BATCH 64
+int dl_polar_workspace_bytes_batch(int64_t rows, int64_t cols, int batch, int64_t *bytes);
+
 /*
  * out = polar factor of `update` (both rows x cols, device fp32; out may be
  * update, otherwise they must not overlap).  1 <= quintic + cubic steps,
@@ -350,6 +355,23 @@ int dl_polar_factor(float *out, const float *update, int64_t rows, int64_t cols,
 int dl_outer_orthogonal_step(float *theta, const float *averaged, int64_t rows, int64_t cols,
                              float scale, int quintic_steps, int cubic_steps, void *workspace,
                              int64_t workspace_bytes, void *stream);
+
+/*
+ * The same step for a batch of equally shaped weight matrices (the model's
+ * matrices of one kind, e.g. every layer's attention projections): theta[b]
+ * = theta[b] - scale * P(theta[b] - averaged[b]) for b < batch.  The
+ * batch's products run as one launch each, which fills the GPU where one
+ * matrix's products would not.  theta and averaged are host arrays of
+ * `batch` device pointers; no theta may overlap any other argument matrix
+ * or the workspace (dl_polar_workspace_bytes_batch bytes).  With batch 1
+ * this is dl_outer_orthogonal_step; with more, the products are cut into
+ * workgroups differently, so results agree with the one-matrix call to
+ * rounding, not bit for bit.  Errors: as dl_polar_factor.
+ */
+int dl_outer_orthogonal_step_batch(float *const *theta, const float *const *averaged, int batch,
+                                   int64_t rows, int64_t cols, float scale, int quintic_steps,
+                                   int cubic_steps, void *workspace, int64_t workspace_bytes,
+                                   void *stream);
 
 enum dl_matmul_form {
     DL_TN = 0,   /* C[i][j] = sum_k A[k*lda + i] * B[k*ldb + j] */
@@ -381,6 +403,22 @@ int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t
                   int64_t n, int64_t k, float *c, int64_t ldc, const float *y, float alpha,
                   float beta, float diag, int symmetric, void *workspace,
                   int64_t workspace_bytes, void *stream);
+
+/*
+ * A batch of 1 <= batch <= DL_MAX_BATCH such products in one launch: matrix
+ * b reads a + b*stride_a, b + b*stride_b (and y + b*stride_y) and writes
+ * c + b*stride_c (strides in elements, >= 0; the results must not overlap:
+ * stride_c covers one result).  The workspace is that of
+ * dl_matmul_workspace_bytes_batch; dl_matmul_f32 is the batch of one.
+ * Errors: as dl_matmul_f32.
+ */
+int dl_matmul_workspace_bytes_batch(int64_t m, int64_t n, int64_t k, int symmetric, int batch,
+                                    int64_t *bytes);
+int dl_matmul_f32_batch(int form, const float *a, int64_t lda, int64_t stride_a, const float *b,
+                        int64_t ldb, int64_t stride_b, int64_t m, int64_t n, int64_t k, float *c,
+                        int64_t ldc, int64_t stride_c, const float *y, int64_t stride_y,
+                        float alpha, float beta, float diag, int symmetric, int batch,
+                        void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Element range [offset, offset + length) of fragment frag.  DL_E_INVAL. */
 int dl_frag_range(const dl_round *r, int frag, int64_t *offset, int64_t *length);

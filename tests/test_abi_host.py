@@ -25,7 +25,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 25
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -228,6 +228,30 @@ def test_polar_host_rules():
     _expect(dl.DL_E_INVAL, step, theta=ws + 512)
     _expect(dl.DL_E_INVAL, step, cubic_steps=-2)
     _expect(dl.DL_E_ALIGN, step, theta=out + 3)
+
+
+def test_polar_batch_host_rules():
+    wsb = dl.dl_polar_workspace_bytes_batch(300, 200, 4)
+    assert wsb > 2 * 4 * 300 * 200 * 4
+    assert dl.dl_polar_workspace_bytes_batch(300, 200, 1) == dl.dl_polar_workspace_bytes(300, 200)
+    for bad in ((300, 200, 0), (300, 200, 65), (0, 200, 2)):
+        _expect(dl.DL_E_INVAL, dl.dl_polar_workspace_bytes_batch, *bad)
+    ws = FAKE + (1 << 34)
+    th = [FAKE + (i << 24) for i in range(4)]
+    av = [FAKE + (1 << 30) + (i << 24) for i in range(4)]
+    step = lambda **k: dl.dl_outer_orthogonal_step_batch(**{**dict(
+        thetas=th, averaged=av, rows=300, cols=200, scale=0.1, workspace=ws,
+        workspace_bytes=wsb, stream=0), **k})
+    _expect(dl.DL_E_INVAL, step, workspace_bytes=wsb - 1)
+    _expect(dl.DL_E_INVAL, step, thetas=th[:3] + [0])
+    _expect(dl.DL_E_INVAL, step, thetas=th[:3] + [th[1] + 4096])        # two thetas meet
+    _expect(dl.DL_E_INVAL, step, thetas=th[:3] + [av[0] + 4])           # theta meets an averaged
+    _expect(dl.DL_E_INVAL, step, thetas=th[:3] + [ws + 256])            # theta meets the workspace
+    _expect(dl.DL_E_ALIGN, step, averaged=av[:3] + [av[3] + 2])
+    with pytest.raises(ValueError):
+        step(averaged=av[:3])
+    # averaged matrices may be shared (read only): fails only at the device check
+    _expect(dl.DL_E_INVAL, step, averaged=[av[0]] * 4)
 
 
 def test_matmul_host_rules():

@@ -305,6 +305,62 @@ def test_outer_orthogonal_step(m, n):
     assert np.array_equal(host(avg), avg_h)
 
 
+@pytest.mark.parametrize("m,n,batch", [(192, 64, 3), (64, 192, 2), (257, 255, 4), (300, 130, 5)])
+def test_outer_orthogonal_step_batch(m, n, batch):
+    """A batch of equally shaped matrices, each against the oracle within
+    the same bounds; the inputs are untouched; a batch of one is the
+    one-matrix call bit for bit."""
+    dev = DEV
+    thetas, avgs = [], []
+    for b in range(batch):
+        th = synth.global0(700 + b, m * n, device=dev)
+        thetas.append(th)
+        avgs.append(synth.worker_checkpoint(700 + b, 0, 0, th))
+    th_h = [host(t).reshape(m, n) for t in thetas]
+    av_h = [host(a).reshape(m, n) for a in avgs]
+    scale = 0.02
+    ws = torch.empty(dl.dl_polar_workspace_bytes_batch(m, n, batch) // 4 + 1, device=dev)
+    dl.dl_outer_orthogonal_step_batch(thetas, avgs, m, n, scale, ws)
+    for b in range(batch):
+        want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
+        upd = th_h[b] - av_h[b]
+        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        bound = scale * polar_bound(upd) * math.sqrt(min(m, n)) + 2 * U32 * np.linalg.norm(want)
+        est = scale * polar_estimate(upd) * math.sqrt(min(m, n)) + 2 * U32 * np.linalg.norm(want)
+        print(f"batch {m}x{n} [{b}]: err_F={err:.3e} estimate={est:.3e}", flush=True)
+        assert err <= bound and err <= est
+        assert np.array_equal(host(avgs[b]).reshape(m, n), av_h[b])
+    t1 = synth.global0(700, m * n, device=dev)
+    t2 = t1.clone()
+    a1 = synth.worker_checkpoint(700, 0, 0, t1)
+    dl.dl_outer_orthogonal_step_batch([t1], [a1], m, n, scale, ws)
+    dl.dl_outer_orthogonal_step(t2, a1, m, n, scale, ws)
+    assert np.array_equal(host(t1), host(t2))
+
+
+def test_outer_orthogonal_step_batch_full_size():
+    """Three 2048 x 2048 attention updates in one batch against the SVD."""
+    rows = cols = 2048
+    batch = 3
+    thetas = [synth.global0(960 + b, rows * cols, device=DEV) for b in range(batch)]
+    avgs = [synth.worker_checkpoint(960 + b, 0, 0, t) for b, t in enumerate(thetas)]
+    th_h = [host(t).reshape(rows, cols) for t in thetas]
+    av_h = [host(a).reshape(rows, cols) for a in avgs]
+    scale = 1e-3
+    ws = torch.empty(dl.dl_polar_workspace_bytes_batch(rows, cols, batch) // 4 + 1, device=DEV)
+    dl.dl_outer_orthogonal_step_batch(thetas, avgs, rows, cols, scale, ws)
+    for b in range(batch):
+        upd = th_h[b] - av_h[b]
+        p_got = (th_h[b] - host(thetas[b]).reshape(rows, cols)) / scale
+        want = opolar.polar_factor(upd)
+        rel = np.linalg.norm(p_got - want) / np.linalg.norm(want)
+        # theta - s P loses |theta| u per element: bound that on top
+        extra = 2 * U32 * np.linalg.norm(th_h[b]) / scale / np.linalg.norm(want)
+        est = polar_estimate(upd) + extra
+        print(f"batch full 2048x2048 [{b}]: rel_F={rel:.3e} estimate={est:.3e}", flush=True)
+        assert rel <= est
+
+
 # -- full-size shapes of DiffuRefill-1B's weight matrices -----------------------
 
 @pytest.mark.parametrize("rows,cols", [(2048, 2048), (5632, 2048), (2048, 5632)],
