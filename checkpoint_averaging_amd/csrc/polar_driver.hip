@@ -4,8 +4,8 @@
 // size.  It is the program hardware counters are collected on for the
 // orthogonalisation kernels.
 //
-//   dlpolar_driver --shapes RxC:count[,RxC:count...] [--steps S] [--warmup W]
-//                  [--quintic Q] [--cubic C] [--copy-mib M]
+//   dlpolar_driver --shapes RxC:count[,RxC:count...] [--batch B] [--steps S]
+//                  [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]
 //   dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--steps S] [--warmup W]
 //
 // The second form times one product of dl_matmul_f32 (S launches, each
@@ -13,10 +13,12 @@
 // (none with :nows); `sym` declares the result symmetric (A = B, M = N).
 //
 // One step runs theta = theta - s * P(theta - averaged) once for every
-// matrix of the list (count matrices of each shape, in list order), on one
-// stream with one workspace sized for the largest.  The matrices of a step
-// share one theta / averaged pair of the largest size (the kernels' work
-// does not depend on where the buffers sit).  Prints the average time per
+// matrix of the list (count matrices of each shape, in list order), in
+// batches of up to B equally shaped matrices (dl_outer_orthogonal_step_batch;
+// B = 1: one by one), on one stream with one workspace sized for the
+// largest batch.  The batches of a step share B theta / averaged pairs of
+// the largest size (the kernels' work does not depend on where the buffers
+// sit).  Prints the average time per
 // step and per shape, and the algorithmic TFLOP/s (symmetric Gram products
 // counted at their distinct outputs).
 #include <hip/hip_runtime.h>
@@ -95,12 +97,13 @@ struct Args {
     int quintic = 12;
     int cubic = 6;
     int copy_mib = 0;
+    int batch = 1;
 };
 
 [[noreturn]] void usage() {
     std::fprintf(stderr,
-                 "usage: dlpolar_driver --shapes RxC:count[,RxC:count...] [--steps S]\n"
-                 "       [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]\n"
+                 "usage: dlpolar_driver --shapes RxC:count[,RxC:count...] [--batch B]\n"
+                 "       [--steps S] [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]\n"
                  "       dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--steps S] [--warmup W]\n");
     std::exit(2);
 }
@@ -137,9 +140,12 @@ Args parse(int argc, char** argv) {
         else if (k == "--quintic") a.quintic = std::atoi(v.c_str());
         else if (k == "--cubic") a.cubic = std::atoi(v.c_str());
         else if (k == "--copy-mib") a.copy_mib = std::atoi(v.c_str());
+        else if (k == "--batch") a.batch = std::atoi(v.c_str());
         else usage();
     }
-    if ((a.shapes.empty() && !a.has_gemm) || a.steps < 1 || a.warmup < 0) usage();
+    if ((a.shapes.empty() && !a.has_gemm) || a.steps < 1 || a.warmup < 0 || a.batch < 1 ||
+        a.batch > DL_MAX_BATCH)
+        usage();
     if (a.has_gemm && (a.gemm.m < 1 || a.gemm.n < 1 || a.gemm.k < 1 ||
                        (a.gemm.sym && a.gemm.m != a.gemm.n)))
         usage();
@@ -219,21 +225,27 @@ int main(int argc, char** argv) {
     int64_t n_max = 0, ws_max = 0;
     for (const Shape& s : a.shapes) {
         int64_t ws = 0;
-        DLCHECK(dl_polar_workspace_bytes(s.rows, s.cols, &ws));
+        const int b = s.count < a.batch ? s.count : a.batch;
+        DLCHECK(dl_polar_workspace_bytes_batch(s.rows, s.cols, b, &ws));
         if (s.rows * s.cols > n_max) n_max = s.rows * s.cols;
         if (ws > ws_max) ws_max = ws;
     }
-    float *theta = nullptr, *avg = nullptr;
+    std::vector<float*> theta(a.batch, nullptr), avg(a.batch, nullptr);
     void* ws = nullptr;
-    HIPCHECK(hipMalloc(&theta, n_max * sizeof(float)));
-    HIPCHECK(hipMalloc(&avg, n_max * sizeof(float)));
+    for (int b = 0; b < a.batch; ++b) {
+        HIPCHECK(hipMalloc(&theta[b], n_max * sizeof(float)));
+        HIPCHECK(hipMalloc(&avg[b], n_max * sizeof(float)));
+        hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, theta[b], nullptr, 0.04f,
+                           n_max, 1u + 2u * b);
+        hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, avg[b], theta[b], 2e-3f, n_max,
+                           2u + 2u * b);
+    }
     HIPCHECK(hipMalloc(&ws, ws_max));
-    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, theta, nullptr, 0.04f, n_max, 1u);
-    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, avg, theta, 2e-3f, n_max, 2u);
     HIPCHECK(hipGetLastError());
     HIPCHECK(hipDeviceSynchronize());
-    std::printf("[driver] %zu shape(s), theta/averaged %ld floats, workspace %ld bytes\n",
-                a.shapes.size(), n_max, ws_max);
+    std::printf("[driver] %zu shape(s), batch %d, theta/averaged %ld floats each, workspace %ld "
+                "bytes\n",
+                a.shapes.size(), a.batch, n_max, ws_max);
     std::fflush(stdout);
 
     if (a.copy_mib > 0) {
@@ -256,9 +268,12 @@ int main(int argc, char** argv) {
         for (size_t i = 0; i < a.shapes.size(); ++i) {
             const Shape& s = a.shapes[i];
             if (shape_ms) HIPCHECK(hipEventRecord(ev[e], nullptr));
-            for (int c = 0; c < s.count; ++c)
-                DLCHECK(dl_outer_orthogonal_step(theta, avg, s.rows, s.cols, scale, a.quintic,
-                                                 a.cubic, ws, ws_max, nullptr));
+            for (int c = 0; c < s.count; c += a.batch) {
+                const int b = s.count - c < a.batch ? s.count - c : a.batch;
+                DLCHECK(dl_outer_orthogonal_step_batch(theta.data(), avg.data(), b, s.rows, s.cols,
+                                                       scale, a.quintic, a.cubic, ws, ws_max,
+                                                       nullptr));
+            }
             if (shape_ms) HIPCHECK(hipEventRecord(ev[e + 1], nullptr));
             e += 2;
         }
@@ -300,8 +315,10 @@ int main(int argc, char** argv) {
     const double ms = total_ms / a.steps;
     std::printf("[driver] step: %.2f ms, %.2f TFLOP/s (%.3e flops)\n", ms,
                 fl_total / (ms / 1e3) / 1e12, fl_total);
-    HIPCHECK(hipFree(theta));
-    HIPCHECK(hipFree(avg));
+    for (int b = 0; b < a.batch; ++b) {
+        HIPCHECK(hipFree(theta[b]));
+        HIPCHECK(hipFree(avg[b]));
+    }
     HIPCHECK(hipFree(ws));
     return 0;
 }
