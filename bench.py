@@ -58,6 +58,25 @@ def measured_traffic(workload: str, kind: str):
     return k.get("hbm_bytes_per_launch")
 
 
+def measured_polar_traffic(kind: str):
+    """HBM bytes per launch of an orthogonalisation kernel kind from the
+    committed counter summary, if it was taken on the current source of the
+    product kernels; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_diffurefill1b_orthogonal_step.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    h = hashlib.sha256()
+    for f in ("polar.hip", "polar.h"):
+        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if d.get("kernel_source_hash") != h.hexdigest()[:16]:
+        return None
+    k = d.get("kernels", {}).get(kind)
+    return k.get("hbm_bytes_per_launch") if k else None
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -322,7 +341,7 @@ def orthogonalize(args, torch):
         "roofline": {"kernel": f"k_gemm<{dom}>", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_polar_traffic(f"gemm_{dom}"),
                      "algorithmic_flops_per_launch": dd["flops"] // dd["launches"],
                      "avg_launch_ms": round(dd["ms"] / dd["launches"], 4)},
         "cpu_baseline": None,

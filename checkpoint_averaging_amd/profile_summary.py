@@ -1,4 +1,5 @@
-"""Summaries of rocprofv3 output for the merge kernels.
+"""Summaries of rocprofv3 output for the merge kernels and the
+orthogonalisation kernels.
 
     python -m checkpoint_averaging_amd.profile_summary stats STATS_CSV --command CMD
         -> markdown table of the merge kernels' dispatch durations
@@ -6,6 +7,13 @@
         --workload KEY --command-fetch CMD --command-write CMD [--json OUT]
         -> HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by
            what the same counter reads for the plain copy kernel of known size
+
+    python -m checkpoint_averaging_amd.profile_summary polar-stats STATS_CSV --command CMD
+    python -m checkpoint_averaging_amd.profile_summary polar-pmc RUN_DIR --command CMD \
+        --copy-bytes B [--json OUT]
+        -> the same for the orthogonalisation kernels; RUN_DIR holds one
+           rocprofv3 --pmc output directory per pass (FETCH_SIZE, WRITE_SIZE,
+           TCC_HIT_sum, SQ_VALU_MFMA_BUSY_CYCLES), each from the same command
 
 Kernel kinds follow the names the benchmark uses (fold, fold_first,
 fold_delta, fold_delta_first, finalize_mean[_ema], nesterov[_ema],
@@ -59,6 +67,121 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def polar_kind(name: str):
+    """Kind of an orthogonalisation kernel from its demangled name, or None."""
+    if "k_gemm<true>" in name:
+        return "gemm_TN"
+    if "k_gemm<false>" in name:
+        return "gemm_NT"
+    for k in ("k_reduce_pieces", "k_sumsq_partial", "k_sumsq_final", "k_scale", "k_step"):
+        if f"::{k}(" in name or name.startswith(k + "("):
+            return k[2:]
+    return None
+
+
+def polar_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("polar.hip", "polar.h"):
+        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def polar_stats_markdown(stats_csv: str, command: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = ["# Orthogonalisation kernels: dispatch durations (rocprofv3 --kernel-trace --stats)",
+           "", "Command:", "", "```", command, "```", "",
+           "| kind | calls | average (us) | min (us) | max (us) | total (ms) |",
+           "|---|---:|---:|---:|---:|---:|"]
+    other_calls, other_ns = 0, 0.0
+    for r in rows:
+        kind = polar_kind(r["Name"])
+        calls, total = int(r["Calls"]), float(r["TotalDurationNs"])
+        if kind is None:
+            other_calls += calls
+            other_ns += total
+            continue
+        out.append(f"| {kind} | {calls} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{total / 1e6:.2f} |")
+    out += ["", f"Other kernels in the same run (input generation, torch): {other_calls} "
+            f"dispatches, {other_ns / 1e6:.1f} ms in total.", ""]
+    return "\n".join(out)
+
+
+def polar_pmc_summary(run_dir: str, command: str, copy_bytes: int) -> dict:
+    """Per-kind sums over one pass per counter group, FETCH_SIZE / WRITE_SIZE
+    scaled by the plain copy of known size; MFMA busy as a fraction of SIMD
+    cycles (GRBM_GUI_ACTIVE counts per XCD: the max over the 8 is the
+    dispatch's active cycles, here taken as the sum / 8); L2 hit rate."""
+    def rows(tag):
+        path = os.path.join(run_dir, tag, "run_counter_collection.csv")
+        return list(csv.DictReader(open(path))) if os.path.exists(path) else []
+
+    acc = defaultdict(lambda: defaultdict(float))
+    launches = defaultdict(set)
+    scale = {}
+    for tag, counters in (("FETCH_SIZE", ("FETCH_SIZE",)), ("WRITE_SIZE", ("WRITE_SIZE",)),
+                          ("TCC_HIT_sum", ("TCC_HIT_sum", "TCC_MISS_sum")),
+                          ("SQ_VALU_MFMA_BUSY_CYCLES", ("SQ_VALU_MFMA_BUSY_CYCLES",
+                                                       "GRBM_GUI_ACTIVE",
+                                                       "SQ_INSTS_VALU_MFMA_MOPS_F32"))):
+        rs = rows(tag)
+        for c in counters:
+            if c in ("FETCH_SIZE", "WRITE_SIZE"):
+                cp = [r for r in rs if "plain_copy" in r["Kernel_Name"] and r["Counter_Name"] == c]
+                if len(cp) != 1:
+                    raise SystemExit(f"{tag}: expected exactly one plain_copy dispatch")
+                scale[c] = copy_bytes / (float(cp[0]["Counter_Value"]) * 1024)
+        for r in rs:
+            kind = polar_kind(r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+            if kind is None or r["Counter_Name"] not in counters:
+                continue
+            v = float(r["Counter_Value"])
+            if r["Counter_Name"] in scale:
+                v *= 1024 * scale[r["Counter_Name"]]
+            acc[kind][r["Counter_Name"]] += v
+            if tag == "FETCH_SIZE":
+                launches[kind].add(r["Dispatch_Id"])
+    kernels = {}
+    simds = 1024
+    for kind, a in acc.items():
+        n = len(launches[kind]) or 1
+        k = {"launches": n,
+             "hbm_read_bytes_per_launch": round(a.get("FETCH_SIZE", 0) / n),
+             "hbm_write_bytes_per_launch": round(a.get("WRITE_SIZE", 0) / n)}
+        k["hbm_bytes_per_launch"] = k["hbm_read_bytes_per_launch"] + k["hbm_write_bytes_per_launch"]
+        if a.get("TCC_HIT_sum", 0) + a.get("TCC_MISS_sum", 0) > 0:
+            k["l2_hit_rate"] = round(a["TCC_HIT_sum"] / (a["TCC_HIT_sum"] + a["TCC_MISS_sum"]), 4)
+        if a.get("GRBM_GUI_ACTIVE", 0) > 0:
+            k["mfma_busy_fraction"] = round(
+                a["SQ_VALU_MFMA_BUSY_CYCLES"] / (a["GRBM_GUI_ACTIVE"] / 8 * simds), 4)
+        kernels[kind] = k
+    return {"workload": "diffurefill1b_orthogonal_step", "kernel_source_hash": polar_source_hash(),
+            "fetch_scale": round(scale.get("FETCH_SIZE", 0), 5),
+            "write_scale": round(scale.get("WRITE_SIZE", 0), 5),
+            "copy_calibration_bytes": copy_bytes, "command": command, "kernels": kernels}
+
+
+def polar_pmc_markdown(s: dict) -> str:
+    out = ["# Orthogonalisation kernels: counters per dispatch (" + s["workload"] + ")", "",
+           "One rocprofv3 --pmc run per counter group, all of the same command; FETCH_SIZE and "
+           "WRITE_SIZE (KiB per dispatch) scaled by what the same counter reads for a plain copy "
+           f"kernel of {s['copy_calibration_bytes']} bytes: FETCH x{s['fetch_scale']}, "
+           f"WRITE x{s['write_scale']}.", "",
+           "Command (the counter list after --pmc changes per pass: FETCH_SIZE; WRITE_SIZE; "
+           "TCC_HIT_sum TCC_MISS_sum; SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 "
+           "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE):", "", "```", s["command"], "```", "",
+           f"Kernel source hash: `{s['kernel_source_hash']}`", "",
+           "| kind | launches | HBM read / launch (MB) | HBM write / launch (MB) | L2 hit rate | "
+           "MFMA busy (of SIMD cycles) |", "|---|---:|---:|---:|---:|---:|"]
+    for kind, k in sorted(s["kernels"].items()):
+        out.append(f"| {kind} | {k['launches']} | {k['hbm_read_bytes_per_launch'] / 1e6:.1f} | "
+                   f"{k['hbm_write_bytes_per_launch'] / 1e6:.1f} | {k.get('l2_hit_rate', 'n/a')} | "
+                   f"{k.get('mfma_busy_fraction', 'n/a')} |")
+    return "\n".join(out) + "\n"
 
 
 def stats_markdown(stats_csv: str, command: str) -> str:
@@ -182,7 +305,25 @@ def main(argv=None):
     b.add_argument("--copy-bytes", type=int, required=True,
                    help="bytes the plain copy kernel read (and wrote)")
     b.add_argument("--json")
+    c = sub.add_parser("polar-stats")
+    c.add_argument("stats_csv")
+    c.add_argument("--command", required=True)
+    d = sub.add_parser("polar-pmc")
+    d.add_argument("run_dir")
+    d.add_argument("--command", required=True)
+    d.add_argument("--copy-bytes", type=int, required=True)
+    d.add_argument("--json")
     args = ap.parse_args(argv)
+    if args.mode == "polar-stats":
+        print(polar_stats_markdown(args.stats_csv, args.command))
+        return
+    if args.mode == "polar-pmc":
+        s = polar_pmc_summary(args.run_dir, args.command, args.copy_bytes)
+        if args.json:
+            with open(args.json, "w") as fh:
+                json.dump(s, fh, indent=1)
+        sys.stdout.write(polar_pmc_markdown(s))
+        return
     if args.mode == "stats":
         print(stats_markdown(args.stats_csv, args.command))
         return
