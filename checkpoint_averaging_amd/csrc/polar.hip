@@ -121,9 +121,11 @@ __device__ __forceinline__ void tile_coords(uint32_t t, const Work& wk, uint32_t
 // as 4 float4 per thread and stored to LDS as [row][k] (16-byte rows, so the
 // MFMA operand reads below are ds_read_b128).
 //   k-major storage, element (row, k) at P[k*ld + row] (both operands of TN):
-//     thread t loads rows 4(t%32) .. +3 of k = 4(t/32) .. +3: four float4
-//     loads along the rows (32 lanes cover 512 contiguous bytes), transposed
-//     in registers into four [row][k] float4 stores;
+//     thread t loads rows 4j .. 4j+3, j = (t/2)%32, of k = 4g .. 4g+3,
+//     g = 2(t/64) + t%2: four float4 loads along the rows (each load of a
+//     wave covers two runs of 512 contiguous bytes), transposed in registers
+//     into four [row][k] float4 stores; pairing neighbouring lanes on two k
+//     groups puts every 8 consecutive lanes' stores in distinct LDS banks;
 //   row-major storage, element (row, k) at P[row*ld + k] (both of NT):
 //     thread t loads rows t/8 + 32p, k = 4(t%8) .. +3: one float4 each.
 // Interior tiles with 16-byte aligned rows (`vec`) load without any check;
@@ -136,8 +138,8 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
                                           f32x4 (&v)[4]) {
     const bool fast = vec && r0 + kTileM <= R && k0 + kTileK <= K;
     if constexpr (KMajor) {
-        const int64_t row = r0 + 4 * (tid & 31);
-        const int64_t kq = k0 + 4 * (tid >> 5);
+        const int64_t row = r0 + 4 * ((tid >> 1) & 31);
+        const int64_t kq = k0 + 4 * (2 * (tid >> 6) + (tid & 1));
         if (fast) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
@@ -174,7 +176,7 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
 template <bool KMajor>
 __device__ __forceinline__ void store_tile(float (*S)[kLdsRow], const f32x4 (&v)[4], int tid) {
     if constexpr (KMajor) {
-        const int row = 4 * (tid & 31), k = 4 * (tid >> 5);
+        const int row = 4 * ((tid >> 1) & 31), k = 4 * (2 * (tid >> 6) + (tid & 1));
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const f32x4 w = {v[0][c], v[1][c], v[2][c], v[3][c]};
