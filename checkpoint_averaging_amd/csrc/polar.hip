@@ -128,19 +128,18 @@ __device__ __forceinline__ void tile_coords(uint32_t t, const Work& wk, uint32_t
 //     groups puts every 8 consecutive lanes' stores in distinct LDS banks;
 //   row-major storage, element (row, k) at P[row*ld + k] (both of NT):
 //     thread t loads rows t/8 + 32p, k = 4(t%8) .. +3: one float4 each.
-// Interior tiles with 16-byte aligned rows (`vec`) load without any check;
-// edge tiles load every element from a clamped, valid address and select 0
-// outside the operand or this workgroup's K range (no branches).
-// k0: first k of the tile; K: end of the K range; R: operand rows.
-template <bool KMajor>
+// Guard = false (interior tiles with 16-byte aligned rows): plain float4
+// loads.  Guard = true (edge tiles, a partial K-tile): every element from a
+// clamped, valid address, 0 outside the operand or the K range (no
+// branches).  k0: first k of the tile; K: end of the K range; R: rows.
+template <bool KMajor, bool Guard>
 __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int64_t r0,
-                                          int64_t R, int64_t k0, int64_t K, bool vec, int tid,
+                                          int64_t R, int64_t k0, int64_t K, int tid,
                                           f32x4 (&v)[4]) {
-    const bool fast = vec && r0 + kTileM <= R && k0 + kTileK <= K;
     if constexpr (KMajor) {
         const int64_t row = r0 + 4 * ((tid >> 1) & 31);
         const int64_t kq = k0 + 4 * (2 * (tid >> 6) + (tid & 1));
-        if (fast) {
+        if constexpr (!Guard) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 v[kk] = *reinterpret_cast<const f32x4*>(P + (kq + kk) * ld + row);
@@ -159,7 +158,7 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int64_t row = r0 + (tid >> 3) + 32 * p;
-            if (fast) {
+            if constexpr (!Guard) {
                 v[p] = *reinterpret_cast<const f32x4*>(P + row * ld + k);
             } else {
 #pragma unroll
@@ -201,73 +200,131 @@ __device__ __forceinline__ LdsRow* lds_b(float* smem, int buf) {
     return reinterpret_cast<LdsRow*>(smem + (buf * (kTileM + kTileN) + kTileM) * kLdsRow);
 }
 
-// acc += opA[i0.., kb..ke) * opB[kb..ke), j0..] for one 128 x 128 tile.  The K
-// loop is double-buffered: the next K-tile's global loads are in flight
-// while the MFMAs consume the current one from LDS; one barrier per K-tile.
-// Within a K-tile, lane half h of MFMA step s carries k = 16h + s (the same k
-// for the A and B operands), so each lane reads its 16 k of a row with four
-// b128 reads.  Ends with a barrier: LDS is free for the caller afterwards.
-template <bool TN>
-__device__ __forceinline__ void mma_tile(const float* __restrict__ A, int64_t lda,
-                                         const float* __restrict__ B, int64_t ldb, int64_t M,
-                                         int64_t N, int64_t i0, int64_t j0, int64_t kb,
-                                         int64_t ke, bool vec_a, bool vec_b, float* smem,
-                                         f32x16 (&acc)[2][2]) {
+// Loads of the next K-tile inside one step of the K loop.
+enum class Next { None, Plain, Guarded };
+
+struct TileCtx {
+    const float* A;
+    int64_t lda;
+    const float* B;
+    int64_t ldb;
+    int64_t M, N, i0, j0, kb, ke;
+    float* smem;
+};
+
+// One K-tile: the next tile's loads (if any) in flight while the MFMAs
+// consume the current one from LDS buffer kt % 2; then the next tile goes
+// to the other buffer and one barrier closes the step.  Within a K-tile,
+// lane half h of MFMA step s carries k = 16h + s (the same k for the A and
+// B operands), so each lane reads its 16 k of a row with four b128 reads.
+// In the plain steps, scheduling barriers spread the global loads and LDS
+// stores among the MFMAs instead of leaving them bunched.
+template <bool TN, Next L>
+__device__ __forceinline__ void k_step_tile(const TileCtx& c, int64_t kt, f32x4 (&ra)[4],
+                                            f32x4 (&rb)[4], f32x16 (&acc)[2][2]) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;        // 2 x 2 waves of 64 x 64
+    const int wr = wave >> 1, wc = wave & 1;
+    const int cur = static_cast<int>(kt & 1);
+    if constexpr (L != Next::None) {
+        const int64_t k0 = c.kb + (kt + 1) * kTileK;
+        load_tile<TN, L == Next::Guarded>(c.A, c.lda, c.i0, c.M, k0, c.ke, tid, ra);
+        load_tile<TN, L == Next::Guarded>(c.B, c.ldb, c.j0, c.N, k0, c.ke, tid, rb);
+    }
+    LdsRow* as = lds_a(c.smem, cur);
+    LdsRow* bs = lds_b(c.smem, cur);
+    const int h = lane >> 5, rl = lane & 31;
+    f32x4 a[2][4], b[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+            a[mb][q] = *reinterpret_cast<const f32x4*>(&as[wr * 64 + mb * 32 + rl][16 * h + 4 * q]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            b[nb][q] = *reinterpret_cast<const f32x4*>(&bs[wc * 64 + nb * 32 + rl][16 * h + 4 * q]);
+    }
+#pragma unroll
+    for (int st = 0; st < kTileK / 2; ++st) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    a[mb][st >> 2][st & 3], b[nb][st >> 2][st & 3], acc[mb][nb], 0, 0, 0);
+    }
+    if constexpr (L != Next::None) {
+        store_tile<TN>(lds_a(c.smem, cur ^ 1), ra, tid);
+        store_tile<TN>(lds_b(c.smem, cur ^ 1), rb, tid);
+    }
+    if constexpr (L == Next::Plain && !TN) {
+        // row-major operands: operand reads first, the next tile's global
+        // loads one per 4 MFMAs over the first half, its LDS stores one per 4
+        // MFMAs over the second half
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+    }
+    if constexpr (L == Next::Plain && TN) {
+        // k-major operands: loads first, then the operand reads, and the LDS
+        // stores one per MFMA over the last eight
+        __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 56, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        }
+    }
+
+    __syncthreads();
+}
+
+// acc = opA[i0.., kb..ke) * opB[kb..ke), j0..] for one 128 x 128 tile.
+// Interior tiles with 16-byte aligned rows run their full K-tiles through a
+// branch-free loop of plain loads; the last steps, a partial K-tile and edge
+// tiles use guarded loads.  Ends with a barrier: LDS is free afterwards.
+template <bool TN>
+__device__ __forceinline__ void mma_tile(const TileCtx& c, bool vec_a, bool vec_b,
+                                         f32x16 (&acc)[2][2]) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-    const int64_t ktiles = ke > kb ? (ke - kb + kTileK - 1) / kTileK : 0;
+    const int tid = threadIdx.x;
+    const int64_t span = c.ke > c.kb ? c.ke - c.kb : 0;
+    const int64_t ktiles = (span + kTileK - 1) / kTileK, nfull = span / kTileK;
+    const bool plain = vec_a && vec_b && c.i0 + kTileM <= c.M && c.j0 + kTileN <= c.N;
     f32x4 ra[4], rb[4];
     if (ktiles > 0) {
-        load_tile<TN>(A, lda, i0, M, kb, ke, vec_a, tid, ra);
-        load_tile<TN>(B, ldb, j0, N, kb, ke, vec_b, tid, rb);
-        store_tile<TN>(lds_a(smem, 0), ra, tid);
-        store_tile<TN>(lds_b(smem, 0), rb, tid);
+        if (plain && nfull > 0) {
+            load_tile<TN, false>(c.A, c.lda, c.i0, c.M, c.kb, c.ke, tid, ra);
+            load_tile<TN, false>(c.B, c.ldb, c.j0, c.N, c.kb, c.ke, tid, rb);
+        } else {
+            load_tile<TN, true>(c.A, c.lda, c.i0, c.M, c.kb, c.ke, tid, ra);
+            load_tile<TN, true>(c.B, c.ldb, c.j0, c.N, c.kb, c.ke, tid, rb);
+        }
+        store_tile<TN>(lds_a(c.smem, 0), ra, tid);
+        store_tile<TN>(lds_b(c.smem, 0), rb, tid);
     }
     __syncthreads();
-    const int h = lane >> 5, rl = lane & 31;
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        const int cur = static_cast<int>(kt & 1);
-        const bool more = kt + 1 < ktiles;
-        if (more) {
-            load_tile<TN>(A, lda, i0, M, kb + (kt + 1) * kTileK, ke, vec_a, tid, ra);
-            load_tile<TN>(B, ldb, j0, N, kb + (kt + 1) * kTileK, ke, vec_b, tid, rb);
-        }
-        LdsRow* as = lds_a(smem, cur);
-        LdsRow* bs = lds_b(smem, cur);
-        f32x4 a[2][4], b[2][4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                a[mb][q] = *reinterpret_cast<const f32x4*>(&as[wr * 64 + mb * 32 + rl][16 * h + 4 * q]);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                b[nb][q] = *reinterpret_cast<const f32x4*>(&bs[wc * 64 + nb * 32 + rl][16 * h + 4 * q]);
-        }
-#pragma unroll
-        for (int st = 0; st < kTileK / 2; ++st) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        a[mb][st >> 2][st & 3], b[nb][st >> 2][st & 3], acc[mb][nb], 0, 0, 0);
-        }
-        if (more) {
-            store_tile<TN>(lds_a(smem, cur ^ 1), ra, tid);
-            store_tile<TN>(lds_b(smem, cur ^ 1), rb, tid);
-        }
-        __syncthreads();
-    }
+    int64_t kt = 0;
+    if (plain)
+        for (; kt + 1 < nfull; ++kt) k_step_tile<TN, Next::Plain>(c, kt, ra, rb, acc);
+    for (; kt + 1 < ktiles; ++kt) k_step_tile<TN, Next::Guarded>(c, kt, ra, rb, acc);
+    if (kt < ktiles) k_step_tile<TN, Next::None>(c, kt, ra, rb, acc);
 }
 
 // Position of accumulator r of the calling lane in its wave's 32 x 32 block
@@ -330,8 +387,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
         const int64_t i0 = static_cast<int64_t>(ti) * kTileM;
         const int64_t j0 = static_cast<int64_t>(tj) * kTileN;
         f32x16 acc[2][2];
-        mma_tile<TN>(A + mb * sa, lda, B + mb * sb, ldb, M, N, i0, j0, kb, ke, vec_a, vec_b, smem,
-                     acc);
+        const TileCtx ctx{A + mb * sa, lda, B + mb * sb, ldb, M, N, i0, j0, kb, ke, smem};
+        mma_tile<TN>(ctx, vec_a, vec_b, acc);
         float* const ec = e.c + mb * e.sc;
         const float* const ey = e.y ? e.y + mb * e.sy : nullptr;
 
