@@ -277,6 +277,22 @@ def test_matmul_host_rules():
     _expect(dl.DL_E_INVAL, mm, workspace=ws, workspace_bytes=-1)
 
 
+def test_matmul_batch_host_rules():
+    a, b, c = FAKE, FAKE + (1 << 28), FAKE + (1 << 29)
+    mm = lambda **k: dl.dl_matmul_f32_batch(**{**dict(
+        form=dl.DL_NT, a=a, lda=16, stride_a=64 * 16, b=b, ldb=16, stride_b=32 * 16, m=64, n=32,
+        k=16, c=c, ldc=32, stride_c=64 * 32, batch=4, stream=0), **k})
+    for kw in (dict(batch=0), dict(batch=65), dict(stride_c=64 * 32 - 1),   # results overlap
+               dict(stride_a=-1), dict(c=a + 4 * 64 * 16 * 3),             # C meets A's last matrix
+               dict(y=c + 4, stride_y=64 * 32)):                           # Y meets C, not equal
+        _expect(dl.DL_E_INVAL, mm, **kw)
+    assert dl.dl_matmul_workspace_bytes_batch(2048, 2048, 2048, True, 8) == 2 * 512 * 128 * 128 * 4
+    assert dl.dl_matmul_workspace_bytes_batch(64, 32, 16, False, 1) == \
+        dl.dl_matmul_workspace_bytes(64, 32, 16, False)
+    for bad in ((64, 32, 16, False, 0), (64, 64, 16, True, 65), (64, 32, 16, True, 2)):
+        _expect(dl.DL_E_INVAL, dl.dl_matmul_workspace_bytes_batch, *bad)
+
+
 def test_matmul_workspace_sizes():
     """Two partial slots per workgroup; up to 512 workgroups (two per CU),
     each with at least 8 K-tiles of 32, in multiples of 8 (one per XCD)."""

@@ -203,6 +203,64 @@ def test_matmul_stream_k(form, m, n, k):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
+@pytest.mark.parametrize("sym", [False, True], ids=["general", "symmetric"])
+@pytest.mark.parametrize("ws_mode", ["stream", "none"])
+def test_matmul_batch(form, sym, ws_mode):
+    """A strided batch of products in one launch: every matrix within the
+    product bound (and exactly mirrored when symmetric); Y read with its own
+    stride; the gaps between the batch's results untouched."""
+    rng = np.random.default_rng(91 + int(sym) + 2 * form)
+    batch, m, k = 5, 300, 260
+    n = m if sym else 170
+    if form == dl.DL_TN:
+        lda, sa = m + 1, (m + 1) * k + 7
+        ldb, sb = (lda, sa) if sym else (n + 3, (n + 3) * k + 5)
+    else:
+        lda, ldb, sa = k + 2, k + 2, m * (k + 2) + 3
+        sb = sa if sym else n * (k + 2) + 9
+    a = rng.standard_normal(sa * batch).astype(np.float32)
+    b = a if sym else rng.standard_normal(sb * batch).astype(np.float32)
+    ldc, sc = n + 4, (n + 4) * m + 64
+    c0 = rng.standard_normal(sc * batch).astype(np.float32)
+    sy = sc + 32
+    yv = rng.standard_normal(sy * batch).astype(np.float32)
+    for i in range(batch):        # a symmetric Y for the symmetric case
+        yy = yv[i * sy:i * sy + m * ldc].reshape(m, ldc)
+        if sym:
+            yy[:, :n] = (yy[:, :n] + yy[:, :n].T) * np.float32(0.5)
+    a_d, c_d, y_d = gpu(a), gpu(c0), gpu(yv)
+    b_d = a_d if sym else gpu(b)
+    ws = None
+    if ws_mode == "stream":
+        ws = torch.empty(dl.dl_matmul_workspace_bytes_batch(m, n, k, sym, batch) // 4 + 64,
+                         device=DEV)
+    alpha, beta, diag = -0.5, 2.0315, 3.4445
+    dl.dl_matmul_f32_batch(form, a_d, lda, sa, b_d, ldb, sb, m, n, k, c_d, ldc, sc, batch, y=y_d,
+                           stride_y=sy, alpha=alpha, beta=beta, diag=diag, symmetric=sym,
+                           workspace=ws)
+    got = host(c_d)
+    for i in range(batch):
+        ai = a[i * sa:].astype(np.float64)
+        bi = b[i * sb:].astype(np.float64)
+        if form == dl.DL_TN:
+            opa = ai[:k * lda].reshape(k, lda)[:, :m].T
+            opb = bi[:k * ldb].reshape(k, ldb)[:, :n]
+        else:
+            opa = ai[:m * lda].reshape(m, lda)[:, :k]
+            opb = bi[:n * ldb].reshape(n, ldb)[:, :k].T
+        yi = yv[i * sy:i * sy + m * ldc].reshape(m, ldc)[:, :n].astype(np.float64)
+        want = alpha * (opa @ opb) + beta * yi + diag * np.eye(m, n)
+        mag = abs(alpha) * (np.abs(opa) @ np.abs(opb)) + abs(beta) * np.abs(yi) + abs(diag) * np.eye(m, n)
+        gi = got[i * sc:i * sc + m * ldc].reshape(m, ldc)
+        _bound_check(gi[:, :n], want, mag, k)
+        if sym:
+            assert np.array_equal(gi[:, :n], gi[:, :n].T)
+        assert np.array_equal(gi[:, n:], c0[i * sc:i * sc + m * ldc].reshape(m, ldc)[:, n:])
+        gap = slice(i * sc + m * ldc, (i + 1) * sc)
+        assert np.array_equal(got[gap], c0[gap].astype(np.float64))
+
+
 def test_matmul_k0_writes_the_epilogue():
     m, n = 70, 90
     c = torch.full((m, n), 7.0, device=DEV)
