@@ -20,15 +20,18 @@
 // workgroups of 4 wave64 compute 128 x 128 output tiles, each wave a 64 x 64
 // quarter as 2 x 2 MFMA blocks of 32 x 32, over K in tiles of 32 staged
 // through LDS with the next tile's loads in flight.  The work of a product
-// (output tiles x K-tiles) is spread evenly over as many workgroups as the
-// GPU holds at once (stream-K); tiles cut between workgroups are summed in K
-// order by a second kernel, so results are deterministic.  The Gram matrix
-// and its square are symmetric: only their upper tiles are computed and the
-// lower ones are written as mirror images.  The epilogue is fused: out =
-// alpha*acc + beta*Y + (i == j ? d : 0), which forms a I + b G + c G^2 in the
-// G^2 product, 1.5 I - 0.5 G in the Gram product, and theta - s*P in the
-// last product.  The Frobenius norm is a deterministic two-stage fp64
-// reduction (no atomics: the same input gives the same bits).
+// (output tiles x K-tiles; for a batch of equally shaped matrices, all their
+// tiles) goes to as many workgroups as the GPU holds at once: whole tiles in
+// rounds, then the last round or two's worth split stream-K; tiles cut
+// between workgroups are summed in K order by a second kernel, so results
+// are deterministic.  The Gram matrix and its square are symmetric: only
+// their upper tiles are computed and the lower ones are written as mirror
+// images.  The epilogue is fused: out = alpha*acc + beta*Y + (i == j ? d :
+// 0), which forms a I + b G + c G^2 in the G^2 product, 1.5 I - 0.5 G in the
+// Gram product, and theta - s*P in the last product of a single matrix (a
+// batch finishes with an elementwise pass of the same arithmetic).  The
+// Frobenius norm is a deterministic two-stage fp64 reduction (no atomics:
+// the same input gives the same bits).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
