@@ -17,8 +17,8 @@ orthogonalisation kernels.
 
 Kernel kinds follow the names the benchmark uses (fold, fold_first,
 fold_delta, fold_delta_first, finalize_mean[_ema], nesterov[_ema],
-fold_finalize_mean[_ema][_first], fold_nesterov[_ema][_first], ema; _bf16
-for bf16 checkpoints).
+fold_finalize_mean[_ema][_first], fold_nesterov[_ema][_first], ema,
+snapshot_mean_K, adopt_keep_drift; _bf16 for bf16 checkpoints).
 """
 from __future__ import annotations
 
@@ -40,11 +40,15 @@ def kernel_kind(name: str):
     Kernels are k_stream<Op, NT> (128-bit path) or k_stream_scalar<Op>; the
     kind comes from the operation and its template arguments."""
     m = re.search(r"::(FoldMeanClose|FoldNesterovClose|FoldSum|FoldDelta|MeanClose|"
-                  r"NesterovClose|Ema)\b(?:<([^>]*)>)?", name)
+                  r"NesterovClose|Ema|SnapshotMean|AdoptKeepDrift)\b(?:<([^>]*)>)?", name)
     if not m or "k_stream" not in name:
         return None
     op = m.group(1)
     targs = [t.strip() for t in (m.group(2) or "").split(",")]
+    if op == "SnapshotMean":
+        return f"snapshot_mean_{targs[0]}"
+    if op == "AdoptKeepDrift":
+        return "adopt_keep_drift" + ("_bf16" if "short" in targs[0] else "")
     bf16 = "_bf16" if targs and "short" in targs[0] else ""
     if op == "FoldSum":
         return ("fold_first" if targs[1] == "true" else "fold") + bf16
@@ -184,9 +188,9 @@ def polar_pmc_markdown(s: dict) -> str:
     return "\n".join(out) + "\n"
 
 
-def stats_markdown(stats_csv: str, command: str) -> str:
+def stats_markdown(stats_csv: str, command: str, title: str = "Merge kernels") -> str:
     rows = list(csv.DictReader(open(stats_csv)))
-    out = ["# Merge kernels: dispatch durations (rocprofv3 --kernel-trace --stats)", "",
+    out = [f"# {title}: dispatch durations (rocprofv3 --kernel-trace --stats)", "",
            "Command:", "", "```", command, "```", "",
            "| kind | kernel | calls | average (us) | min (us) | max (us) | total (ms) |",
            "|---|---|---:|---:|---:|---:|---:|"]
@@ -296,6 +300,7 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("stats_csv")
     a.add_argument("--command", required=True)
+    a.add_argument("--title", default="Merge kernels")
     b = sub.add_parser("pmc")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -325,7 +330,7 @@ def main(argv=None):
         sys.stdout.write(polar_pmc_markdown(s))
         return
     if args.mode == "stats":
-        print(stats_markdown(args.stats_csv, args.command))
+        print(stats_markdown(args.stats_csv, args.command, args.title))
         return
     s = pmc_summary(args.fetch_csv, args.write_csv, args.workload, args.command_fetch,
                     args.command_write, args.copy_bytes)
