@@ -419,6 +419,37 @@ def test_outer_orthogonal_step_batch_full_size():
         assert rel <= est
 
 
+def test_orthogonal_step_over_pythia14m_layout():
+    """The whole-model step over the Pythia-14M layout (26 matrices in five
+    shapes: the two 50304 x 128 embeddings, QKV 384 x 128, dense 128 x 128,
+    MLP 512 x 128 and 128 x 512; equally shaped ones batched by 8): every
+    matrix against the oracle's step, and every parameter outside the
+    matrices (the norms and biases) untouched."""
+    from checkpoint_averaging_amd.orthogonalize import OrthogonalStep
+    layout = synth.PYTHIA_14M
+    n = layout.n_params
+    theta = synth.global0(1201, n, device=DEV)
+    avg = synth.worker_checkpoint(1201, 0, 0, theta)
+    th_h, av_h = host(theta), host(avg)
+    step = OrthogonalStep(layout, DEV, batch=8)
+    assert len(step.matrices) == 26
+    scale = 2e-3
+    step.run(theta, avg, scale)
+    got = host(theta)
+    touched = np.zeros(n, bool)
+    for m in step.matrices:
+        sl = slice(m.offset, m.offset + m.rows * m.cols)
+        touched[sl] = True
+        t, a = th_h[sl].reshape(m.rows, m.cols), av_h[sl].reshape(m.rows, m.cols)
+        want = opolar.outer_orthogonal_step(t, a, scale)
+        upd = t - a
+        r = min(m.rows, m.cols)
+        err = np.linalg.norm(got[sl].reshape(m.rows, m.cols) - want)
+        est = scale * polar_estimate(upd) * math.sqrt(r) + 2 * U32 * np.linalg.norm(want)
+        assert err <= est, (m.name, err, est)
+    assert np.array_equal(got[~touched], th_h[~touched])
+
+
 # -- full-size shapes of DiffuRefill-1B's weight matrices -----------------------
 
 @pytest.mark.parametrize("rows,cols", [(2048, 2048), (5632, 2048), (2048, 5632)],
