@@ -121,24 +121,29 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
     tok = synth.token_counts(w, 0)
     from checkpoint_averaging_amd.workload import algorithmic_bytes
     bytes_per_round = algorithmic_bytes(w)["per_param"] * n_s
-    rounds = 0
-    t0 = time.perf_counter()
-    while True:
-        for f, F in enumerate(frags):
-            order = orders[f]
-            if w.mode == "mean":
-                F["theta"] = orc.mean_round([F["cks"][i] for i in order], ema=F["e"],
-                                            beta=w.beta)
-            else:
-                orc.nesterov_fragment_round(F["theta"], F["m"], [F["cks"][i] for i in order],
-                                            [tok[i] for i in order], w.lr, w.mu, F["e"],
-                                            w.beta)
-        rounds += 1
-        el = time.perf_counter() - t0
-        if el >= max_seconds:
-            break
+
+    def time_rounds(limit):
+        rounds = 0
+        t0 = time.perf_counter()
+        while True:
+            for f, F in enumerate(frags):
+                order = orders[f]
+                if w.mode == "mean":
+                    F["theta"] = orc.mean_round([F["cks"][i] for i in order], ema=F["e"],
+                                                beta=w.beta)
+                else:
+                    orc.nesterov_fragment_round(F["theta"], F["m"],
+                                                [F["cks"][i] for i in order],
+                                                [tok[i] for i in order], w.lr, w.mu, F["e"],
+                                                w.beta)
+            rounds += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return rounds, el
+
+    rounds, el = time_rounds(max_seconds)
     sec = el / rounds
-    return {
+    out = {
         "value": round(bytes_per_round / sec / 1e9, 3), "unit": "GB/s",
         "params_per_s": round(n_s / sec, 1),
         "cores": orc.threads(), "kind": "oracle",
@@ -147,6 +152,16 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
                    f"structure, {rounds} rounds in {el:.1f} s"),
         "cpu": cpu_model(),
     }
+    if w.n_params < (1 << 26):
+        # the small (Pythia-14M) workloads are also timed on one thread
+        orc.set_threads(1)
+        r1, el1 = time_rounds(max_seconds / 2)
+        orc.set_threads(cores)
+        sec1 = el1 / r1
+        out["single_core"] = {"value": round(bytes_per_round / sec1 / 1e9, 3), "unit": "GB/s",
+                              "params_per_s": round(n_s / sec1, 1), "cores": 1,
+                              "sample": f"{r1} rounds in {el1:.1f} s"}
+    return out
 
 
 def side_averages(args, torch):
@@ -515,15 +530,31 @@ def main():
         e1.record()
         records.append((kind, n, e0, e1))
 
+    spans = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(args.steps):
+        if streams is None:
+            # each round's span on the stream, first launch to last
+            r0 = torch.cuda.Event(enable_timing=True)
+            r1 = torch.cuda.Event(enable_timing=True)
+            r0.record()
         gw.run_round(0, tag=1000 + r, timer=timed if streams is None else plain,
                      fused_close=fused, streams=streams)
+        if streams is None:
+            r1.record()
+            spans.append((r0, r1))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     log(f"[bench] {args.steps} timed rounds: {ms:.3f} ms/round")
+    round_ms = None
+    if spans:
+        per = sorted(a.elapsed_time(b) for a, b in spans)
+        mid = len(per) // 2
+        med = per[mid] if len(per) % 2 else 0.5 * (per[mid - 1] + per[mid])
+        round_ms = {"median": round(med, 4), "min": round(per[0], 4), "max": round(per[-1], 4),
+                    "basis": "stream events around each timed round"}
 
     kinds = {}
     for kind, n, e0, e1 in records:
@@ -591,6 +622,7 @@ def main():
         "merged_params_per_s": round(w.n_params / (ms / 1e3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_time_ms_per_step": (round(total_kernel_ms / args.steps, 4) if kinds else None),
+        "round_ms": round_ms,
         "fragment_streams": args.fragment_streams,
         "kernels": kern,
         "roofline": roofline,
