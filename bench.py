@@ -164,6 +164,12 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
     return out
 
 
+# kernel kind (as the counter summaries name it) of each side-average call
+SIDE_KERNEL_KIND = {"swa_fold": "fold", "swa_average": "finalize_mean",
+                    "snapshot_average_3": "snapshot_mean_3",
+                    "snapshot_average_5": "snapshot_mean_5", "adopt_keep_drift": "adopt_keep_drift"}
+
+
 def side_averages(args, torch):
     """Times the side averages at the DiffuRefill-1B size: folding a global
     into the uniform-average sum (12 B/param), the average itself
@@ -220,7 +226,8 @@ def side_averages(args, torch):
         "kernels": res,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic("diffurefill1b_side_averages",
+                                                 SIDE_KERNEL_KIND[dom]),
                      "algorithmic_bytes_per_launch": dd["bytes_per_param"] * n},
         "cpu_baseline": None,
     }

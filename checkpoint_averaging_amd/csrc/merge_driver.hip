@@ -7,7 +7,7 @@
 //   dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
 //                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
-//                  [--streams S]
+//                  [--streams S] [--side 1]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
 // folded (token-weighted delta in delta mode) and the fragment is closed
@@ -15,8 +15,13 @@
 // fused in when enabled.  With --fused 1 (default) the last worker is folded
 // in the same pass as the close.  With --streams S > 1 every fragment's round
 // is its own handle on one of S streams (rounds in flight together), the
-// arrivals issued round-robin across fragments.  Buffer contents are a deterministic pattern; the
-// timing does not depend on them.
+// arrivals issued round-robin across fragments.  With --side 1 a round is
+// instead the side averages and the worker adoption over the whole buffer:
+// one fold of a global into the uniform-average sum, the average of 130
+// globals, the means of the last 3 and last 5 snapshots (the checkpoints
+// stand in for them; --workers >= 5), and the keep-local-drift adoption.
+// Buffer contents are a deterministic pattern; the timing does not depend on
+// them.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -97,13 +102,15 @@ struct Args {
     int copy_mib = 0;
     bool fused = true;
     int streams = 1;
+    bool side = false;
 };
 
 [[noreturn]] void usage() {
     std::fprintf(stderr,
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
-                 "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n");
+                 "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n"
+                 "       [--side 0|1]\n");
     std::exit(2);
 }
 
@@ -131,10 +138,11 @@ Args parse(int argc, char** argv) {
         else if (k == "--copy-mib") a.copy_mib = std::atoi(v.c_str());
         else if (k == "--fused") a.fused = std::atoi(v.c_str()) != 0;
         else if (k == "--streams") a.streams = std::atoi(v.c_str());
+        else if (k == "--side") a.side = std::atoi(v.c_str()) != 0;
         else usage();
     }
     if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0 || a.streams < 1 ||
-        a.streams > 16)
+        a.streams > 16 || (a.side && (a.workers < 5 || a.bf16 || !a.ema)))
         usage();
     if (a.offsets.empty()) a.offsets = {0, a.n};
     return a;
@@ -198,6 +206,16 @@ int main(int argc, char** argv) {
     const int64_t esz = a.bf16 ? 2 : 4;
     for (int r = 0; r < a.warmup + a.rounds; ++r) {
         if (r == a.warmup) HIPCHECK(hipEventRecord(e0, s));
+        if (a.side) {
+            const float* snaps[5];
+            for (int i = 0; i < 5; ++i) snaps[i] = static_cast<const float*>(ck[i]);
+            DLCHECK(dl_swa_fold(acc, theta, a.n, r, s));
+            DLCHECK(dl_swa_average(e, acc, a.n, 130, s));
+            DLCHECK(dl_snapshot_average(e, snaps, 3, a.n, s));
+            DLCHECK(dl_snapshot_average(e, snaps, 5, a.n, s));
+            DLCHECK(dl_adopt_keep_drift(e, theta, ck[1], DL_F32, a.n, s));
+            continue;
+        }
         const uint64_t tag = uint64_t(r) + 1;
         HIPCHECK(hipEventRecord(joins[0], s));
         for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamWaitEvent(fs[i], joins[0], 0));

@@ -65,6 +65,17 @@ def kernel_kind(name: str):
     return "ema"
 
 
+# The side averages and the worker adoption, counted on dlmerge_driver --side 1:
+# algorithmic bytes per element of each kernel kind (the uniform-average fold
+# reads the sum and the global and writes the sum; the first fold only copies;
+# the average reads the sum and writes the result; the k-snapshot mean reads k
+# buffers and writes one; the adoption reads theta, the global and the pushed
+# checkpoint and writes theta).
+SIDE_WORKLOAD = "diffurefill1b_side_averages"
+SIDE_BYTES_PER_ELEM = {"fold": 12, "fold_first": 8, "finalize_mean": 8, "snapshot_mean_3": 16,
+                       "snapshot_mean_5": 24, "adopt_keep_drift": 16}
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("kernels.hip", "kernels.h"):
@@ -276,7 +287,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, workload: str, cmd_fetch: str, c
 
 
 def pmc_markdown(s: dict, alg_per_elem: dict, frag_elems: dict) -> str:
-    out = [f"# Merge kernels: HBM traffic per dispatch ({s['workload']})", "",
+    title = ("Side averages and adoption" if s["workload"] == SIDE_WORKLOAD else "Merge kernels")
+    out = [f"# {title}: HBM traffic per dispatch ({s['workload']})", "",
            "FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each from its own rocprofv3 run, "
            "scaled by what the same counter reads for a plain copy kernel of "
            f"{s['copy_calibration_bytes']} bytes: FETCH x{s['fetch_scale']}, "
@@ -335,13 +347,18 @@ def main(argv=None):
     s = pmc_summary(args.fetch_csv, args.write_csv, args.workload, args.command_fetch,
                     args.command_write, args.copy_bytes)
     from . import synth
-    from .workload import algorithmic_bytes
-    w = synth.WORKLOADS[args.workload]
-    alg = algorithmic_bytes(w)["per_elem"]
-    # average elements per launch of each kind over the round (all fragments)
-    sizes = [w.frag_offsets[f + 1] - w.frag_offsets[f] for f in range(w.n_frags)]
-    avg = sum(sizes) / len(sizes)
-    frag_elems = {k: avg for k in s["kernels"]}
+    if args.workload == SIDE_WORKLOAD:
+        # every side-average call runs over the whole DiffuRefill-1B buffer
+        alg = dict(SIDE_BYTES_PER_ELEM)
+        frag_elems = {k: synth.DIFFUREFILL_1B.n_params for k in s["kernels"]}
+    else:
+        from .workload import algorithmic_bytes
+        w = synth.WORKLOADS[args.workload]
+        alg = algorithmic_bytes(w)["per_elem"]
+        # average elements per launch of each kind over the round (all fragments)
+        sizes = [w.frag_offsets[f + 1] - w.frag_offsets[f] for f in range(w.n_frags)]
+        avg = sum(sizes) / len(sizes)
+        frag_elems = {k: avg for k in s["kernels"]}
     if args.json:
         with open(args.json, "w") as fh:
             json.dump(s, fh, indent=1)

@@ -1,0 +1,88 @@
+"""Host checks of the counter and trace summaries: kernel kinds from
+demangled names, the copy-calibrated byte counts, and the committed HBM
+traffic summaries against the algorithmic bytes of each kernel."""
+import csv
+import json
+import os
+
+import pytest
+
+from checkpoint_averaging_amd import profile_summary as ps
+from checkpoint_averaging_amd import synth
+from checkpoint_averaging_amd.workload import algorithmic_bytes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("name,kind", [
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldSum<float, true>, true>"
+     "(dlk::(anonymous namespace)::FoldSum<float, true>, long, int)", "fold_first"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldSum<unsigned short, "
+     "false>, true>(...)", "fold_bf16"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldDelta<float, false>, "
+     "true>(...)", "fold_delta"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldNesterovClose<float, "
+     "false, true>, true>(...)", "fold_nesterov_ema"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::MeanClose<false>, true>(...)",
+     "finalize_mean"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::SnapshotMean<5>, true>(...)",
+     "snapshot_mean_5"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::AdoptKeepDrift<float>, "
+     "true>(...)", "adopt_keep_drift"),
+    ("void at::native::vectorized_elementwise_kernel<4, ...>(...)", None),
+])
+def test_kernel_kind(name, kind):
+    assert ps.kernel_kind(name) == kind
+
+
+def _write_csv(path, counter, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, val in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_pmc_summary_scales_by_the_copy_kernel(tmp_path):
+    fold = ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldSum<float, "
+            "false>, true>(...)")
+    nb = 1 << 30
+    # the fetch counter reads half of what is moved, the write counter all of it
+    _write_csv(tmp_path / "f.csv", "FETCH_SIZE",
+               [("plain_copy(float4 const*, float4*, long)", nb / 2 / 1024),
+                (fold, 3 * nb / 2 / 1024), (fold, 3 * nb / 2 / 1024)])
+    _write_csv(tmp_path / "w.csv", "WRITE_SIZE",
+               [("plain_copy(float4 const*, float4*, long)", nb / 1024), (fold, nb / 1024),
+                (fold, nb / 1024)])
+    s = ps.pmc_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "x", "cf", "cw", nb)
+    assert s["fetch_scale"] == pytest.approx(2.0) and s["write_scale"] == pytest.approx(1.0)
+    k = s["kernels"]["fold"]
+    assert k["launches"] == 2
+    assert k["hbm_read_bytes_per_launch"] == 3 * nb
+    assert k["hbm_bytes_per_launch"] == 4 * nb
+
+
+def _committed(name):
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        pytest.skip(f"{name} not present")
+    with open(path) as fh:
+        return json.load(fh)
+
+
+def test_merge_kernels_move_their_algorithmic_bytes():
+    d = _committed("pmc_diffurefill1b_frag_nesterov_ema.json")
+    w = synth.WORKLOADS[d["workload"]]
+    per = algorithmic_bytes(w)["per_elem"]
+    avg = w.n_params / w.n_frags
+    for kind, k in d["kernels"].items():
+        assert k["hbm_bytes_per_launch"] == pytest.approx(per[kind] * avg, rel=5e-3), kind
+
+
+def test_side_average_kernels_move_their_algorithmic_bytes():
+    d = _committed("pmc_diffurefill1b_side_averages.json")
+    n = synth.DIFFUREFILL_1B.n_params
+    assert set(d["kernels"]) <= set(ps.SIDE_BYTES_PER_ELEM)
+    for kind, k in d["kernels"].items():
+        assert k["hbm_bytes_per_launch"] == pytest.approx(ps.SIDE_BYTES_PER_ELEM[kind] * n,
+                                                          rel=5e-3), kind
