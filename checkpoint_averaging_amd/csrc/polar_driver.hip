@@ -6,11 +6,13 @@
 //
 //   dlpolar_driver --shapes RxC:count[,RxC:count...] [--batch B] [--steps S]
 //                  [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]
-//   dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--steps S] [--warmup W]
+//   dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--batch B] [--steps S]
+//                  [--warmup W]
 //
-// The second form times one product of dl_matmul_f32 (S launches, each
-// bracketed by events) with the workspace of dl_matmul_workspace_bytes
-// (none with :nows); `sym` declares the result symmetric (A = B, M = N).
+// The second form times one launch of dl_matmul_f32_batch over B products
+// of that shape (S launches, each bracketed by events) with the workspace of
+// dl_matmul_workspace_bytes_batch (none with :nows); `sym` declares the
+// results symmetric (A = B, M = N).
 //
 // One step runs theta = theta - s * P(theta - averaged) once for every
 // matrix of the list (count matrices of each shape, in list order), in
@@ -104,7 +106,8 @@ struct Args {
     std::fprintf(stderr,
                  "usage: dlpolar_driver --shapes RxC:count[,RxC:count...] [--batch B]\n"
                  "       [--steps S] [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]\n"
-                 "       dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--steps S] [--warmup W]\n");
+                 "       dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--batch B] [--steps S]\n"
+                 "       [--warmup W]\n");
     std::exit(2);
 }
 
@@ -164,30 +167,32 @@ double flops(const Shape& s, int quintic, int cubic) {
 
 }  // namespace
 
-// One product, timed launch by launch.  A and B are filled with a pattern;
-// for a symmetric result B is A (A^T A as TN, A A^T as NT).
+// One batched product launch, timed launch by launch.  A and B are filled
+// with a pattern; for a symmetric result B is A (A^T A as TN, A A^T as NT).
 int run_gemm(const Args& a) {
     const Gemm& g = a.gemm;
+    const int bt = a.batch;
     const int64_t na = g.tn ? g.k * g.m : g.m * g.k;
     const int64_t nb = g.tn ? g.k * g.n : g.n * g.k;
     float *A = nullptr, *B = nullptr, *C = nullptr;
     void* ws = nullptr;
     int64_t wsb = 0;
-    DLCHECK(dl_matmul_workspace_bytes(g.m, g.n, g.k, g.sym ? 1 : 0, &wsb));
-    HIPCHECK(hipMalloc(&A, na * sizeof(float)));
-    if (!g.sym) HIPCHECK(hipMalloc(&B, nb * sizeof(float)));
-    HIPCHECK(hipMalloc(&C, g.m * g.n * sizeof(float)));
+    DLCHECK(dl_matmul_workspace_bytes_batch(g.m, g.n, g.k, g.sym ? 1 : 0, bt, &wsb));
+    HIPCHECK(hipMalloc(&A, bt * na * sizeof(float)));
+    if (!g.sym) HIPCHECK(hipMalloc(&B, bt * nb * sizeof(float)));
+    HIPCHECK(hipMalloc(&C, bt * g.m * g.n * sizeof(float)));
     if (g.ws && wsb > 0) HIPCHECK(hipMalloc(&ws, wsb));
-    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, A, nullptr, 0.04f, na, 3u);
-    if (!g.sym) hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, B, nullptr, 0.04f, nb, 4u);
+    hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, A, nullptr, 0.04f, bt * na, 3u);
+    if (!g.sym)
+        hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, B, nullptr, 0.04f, bt * nb, 4u);
     HIPCHECK(hipGetLastError());
     HIPCHECK(hipDeviceSynchronize());
     const float* Bp = g.sym ? A : B;
     const int64_t lda = g.tn ? g.m : g.k, ldb = g.tn ? g.n : g.k;
     auto launch = [&]() {
-        DLCHECK(dl_matmul_f32(g.tn ? DL_TN : DL_NT, A, lda, Bp, ldb, g.m, g.n, g.k, C, g.n,
-                              nullptr, 1.0f, 0.0f, 0.0f, g.sym ? 1 : 0, ws, ws ? wsb : 0,
-                              nullptr));
+        DLCHECK(dl_matmul_f32_batch(g.tn ? DL_TN : DL_NT, A, lda, na, Bp, ldb, g.sym ? na : nb,
+                                    g.m, g.n, g.k, C, g.n, g.m * g.n, nullptr, 0, 1.0f, 0.0f,
+                                    0.0f, g.sym ? 1 : 0, bt, ws, ws ? wsb : 0, nullptr));
     };
     for (int w = 0; w < a.warmup; ++w) launch();
     HIPCHECK(hipDeviceSynchronize());
@@ -207,10 +212,10 @@ int run_gemm(const Args& a) {
         if (ms < best) best = ms;
     }
     const double outs = g.sym ? double(g.m) * (g.m + 1) / 2 : double(g.m) * g.n;
-    const double fl = 2.0 * outs * g.k, avg = tot / a.steps;
-    std::printf("[driver] gemm %s %ldx%ldx%ld%s%s: avg %.4f ms (%.2f TFLOP/s), best %.4f ms "
-                "(%.2f TFLOP/s), workspace %ld bytes\n",
-                g.tn ? "TN" : "NT", g.m, g.n, g.k, g.sym ? " sym" : "", ws ? "" : " nows", avg,
+    const double fl = 2.0 * outs * g.k * bt, avg = tot / a.steps;
+    std::printf("[driver] gemm %s %ldx%ldx%ld%s%s batch %d: avg %.4f ms (%.2f TFLOP/s), best "
+                "%.4f ms (%.2f TFLOP/s), workspace %ld bytes\n",
+                g.tn ? "TN" : "NT", g.m, g.n, g.k, g.sym ? " sym" : "", ws ? "" : " nows", bt, avg,
                 fl / (avg / 1e3) / 1e12, best, fl / (best / 1e3) / 1e12, ws ? wsb : 0);
     HIPCHECK(hipFree(A));
     if (B) HIPCHECK(hipFree(B));
