@@ -58,10 +58,11 @@ def measured_traffic(workload: str, kind: str):
     return k.get("hbm_bytes_per_launch")
 
 
-def measured_polar_traffic(kind: str):
+def measured_polar_traffic(kind: str, batching: str):
     """HBM bytes per launch of an orthogonalisation kernel kind from the
     committed counter summary, if it was taken on the current source of the
-    product kernels; else None."""
+    product kernels and with the same batching of the matrices (which sets
+    the size of a launch); else None."""
     path = os.path.join(ROOT, "profiles", "pmc_diffurefill1b_orthogonal_step.json")
     if not os.path.exists(path):
         return None
@@ -71,7 +72,7 @@ def measured_polar_traffic(kind: str):
     for f in ("polar.hip", "polar.h"):
         with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if d.get("kernel_source_hash") != h.hexdigest()[:16]:
+    if d.get("kernel_source_hash") != h.hexdigest()[:16] or d.get("batching") != batching:
         return None
     k = d.get("kernels", {}).get(kind)
     return k.get("hbm_bytes_per_launch") if k else None
@@ -292,7 +293,7 @@ def orthogonalize(args, torch):
     n = layout.n_params
     theta = synth.global0(1007, n, device=dev)
     averaged = synth.worker_checkpoint(1007, 0, 0, theta)
-    step = OrthogonalStep(layout, dev, batch=args.orth_batch)
+    step = OrthogonalStep(layout, dev, batch=args.orth_batch or None)
     mats = step.matrices
     n_mat = sum(m.rows * m.cols for m in mats)
     flops = step.flops()
@@ -406,7 +407,11 @@ def orthogonalize(args, torch):
         "dtype": "f32",
         "data": "synthetic (seeded Philox; DiffuRefill-1B matrix shapes)",
         "config": {"workload": "diffurefill1b_orthogonal_step", "matrices": len(mats),
-                   "batch": args.orth_batch,
+                   "batch": (args.orth_batch or
+                             "each shape's matrices together, split evenly into launches of "
+                             "at most 64"),
+                   "batches": sorted({f"{len(g)} x {g[0].rows}x{g[0].cols}"
+                                      for g in step.groups}),
                    "matrix_params": n_mat, "quintic_steps": 12, "cubic_steps": 6,
                    "algorithmic_flops_per_step": total_flops},
         "TFLOP_per_s": round(total_flops / (ms / 1e3) / 1e12, 2),
@@ -416,7 +421,8 @@ def orthogonalize(args, torch):
         "roofline": {"kernel": f"k_gemm<{dom}>", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4),
-                     "traffic": measured_polar_traffic(f"gemm_{dom}"),
+                     "traffic": measured_polar_traffic(f"gemm_{dom}",
+                                                       str(args.orth_batch or "even")),
                      "algorithmic_flops_per_launch": dd["flops"] // dd["launches"],
                      "avg_launch_ms": round(dd["ms"] / dd["launches"], 4)},
         "cpu_baseline": None,
@@ -470,8 +476,9 @@ def main():
     ap.add_argument("--orthogonalize", action="store_true",
                     help="time the orthogonalised outer step over every weight matrix instead "
                          "of a merge round")
-    ap.add_argument("--orth-batch", type=int, default=8,
-                    help="equally shaped matrices orthogonalised together (1: one by one)")
+    ap.add_argument("--orth-batch", type=int, default=0,
+                    help="equally shaped matrices orthogonalised together (1: one by one; "
+                         "0: all of a shape, split evenly into launches of at most 64)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")

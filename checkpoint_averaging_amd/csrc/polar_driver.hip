@@ -6,6 +6,8 @@
 //
 //   dlpolar_driver --shapes RxC:count[,RxC:count...] [--batch B] [--steps S]
 //                  [--warmup W] [--quintic Q] [--cubic C] [--copy-mib M]
+//                  (--batch 0: each shape's matrices split evenly into as few
+//                  batches of at most DL_MAX_BATCH as hold them)
 //   dlpolar_driver --gemm TN|NT:MxNxK[:sym][:nows] [--batch B] [--steps S]
 //                  [--warmup W]
 //
@@ -146,8 +148,8 @@ Args parse(int argc, char** argv) {
         else if (k == "--batch") a.batch = std::atoi(v.c_str());
         else usage();
     }
-    if ((a.shapes.empty() && !a.has_gemm) || a.steps < 1 || a.warmup < 0 || a.batch < 1 ||
-        a.batch > DL_MAX_BATCH)
+    if ((a.shapes.empty() && !a.has_gemm) || a.steps < 1 || a.warmup < 0 || a.batch < 0 ||
+        a.batch > DL_MAX_BATCH || (a.has_gemm && a.batch < 1))
         usage();
     if (a.has_gemm && (a.gemm.m < 1 || a.gemm.n < 1 || a.gemm.k < 1 ||
                        (a.gemm.sym && a.gemm.m != a.gemm.n)))
@@ -163,6 +165,19 @@ double flops(const Shape& s, int quintic, int cubic) {
     const double r = s.rows < s.cols ? s.rows : s.cols, L = s.rows < s.cols ? s.cols : s.rows;
     const double sym = r * (r + 1) / 2;
     return (quintic + cubic) * (2 * sym * L + 2 * L * r * r) + quintic * 2 * sym * r;
+}
+
+// Sizes of the batches `count` matrices of one shape run in: chunks of
+// `batch`, or (batch 0) an even split into ceil(count / DL_MAX_BATCH).
+std::vector<int> batches(int count, int batch) {
+    std::vector<int> out;
+    if (batch > 0) {
+        for (int c = 0; c < count; c += batch) out.push_back(count - c < batch ? count - c : batch);
+        return out;
+    }
+    const int n = (count + DL_MAX_BATCH - 1) / DL_MAX_BATCH;
+    for (int i = 0; i < n; ++i) out.push_back(count / n + (i < count % n ? 1 : 0));
+    return out;
 }
 
 }  // namespace
@@ -227,23 +242,32 @@ int run_gemm(const Args& a) {
 int main(int argc, char** argv) {
     const Args a = parse(argc, argv);
     if (a.has_gemm) return run_gemm(a);
-    int64_t n_max = 0, ws_max = 0;
+    // slot b of the theta / averaged pairs holds the largest matrix that
+    // runs in a batch of more than b
+    int64_t ws_max = 0;
+    int b_max = 0;
+    std::vector<int64_t> slot;
     for (const Shape& s : a.shapes) {
-        int64_t ws = 0;
-        const int b = s.count < a.batch ? s.count : a.batch;
-        DLCHECK(dl_polar_workspace_bytes_batch(s.rows, s.cols, b, &ws));
-        if (s.rows * s.cols > n_max) n_max = s.rows * s.cols;
-        if (ws > ws_max) ws_max = ws;
+        for (int b : batches(s.count, a.batch)) {
+            int64_t ws = 0;
+            DLCHECK(dl_polar_workspace_bytes_batch(s.rows, s.cols, b, &ws));
+            if (ws > ws_max) ws_max = ws;
+            if (b > b_max) b_max = b;
+            if (static_cast<int>(slot.size()) < b) slot.resize(b, 0);
+            for (int i = 0; i < b; ++i)
+                if (s.rows * s.cols > slot[i]) slot[i] = s.rows * s.cols;
+        }
     }
-    std::vector<float*> theta(a.batch, nullptr), avg(a.batch, nullptr);
+    const int64_t n_max = slot.empty() ? 0 : slot[0];
+    std::vector<float*> theta(b_max, nullptr), avg(b_max, nullptr);
     void* ws = nullptr;
-    for (int b = 0; b < a.batch; ++b) {
-        HIPCHECK(hipMalloc(&theta[b], n_max * sizeof(float)));
-        HIPCHECK(hipMalloc(&avg[b], n_max * sizeof(float)));
+    for (int b = 0; b < b_max; ++b) {
+        HIPCHECK(hipMalloc(&theta[b], slot[b] * sizeof(float)));
+        HIPCHECK(hipMalloc(&avg[b], slot[b] * sizeof(float)));
         hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, theta[b], nullptr, 0.04f,
-                           n_max, 1u + 2u * b);
-        hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, avg[b], theta[b], 2e-3f, n_max,
-                           2u + 2u * b);
+                           slot[b], 1u + 2u * b);
+        hipLaunchKernelGGL(fill, dim3(4096), dim3(256), 0, nullptr, avg[b], theta[b], 2e-3f,
+                           slot[b], 2u + 2u * b);
     }
     HIPCHECK(hipMalloc(&ws, ws_max));
     HIPCHECK(hipGetLastError());
@@ -273,8 +297,7 @@ int main(int argc, char** argv) {
         for (size_t i = 0; i < a.shapes.size(); ++i) {
             const Shape& s = a.shapes[i];
             if (shape_ms) HIPCHECK(hipEventRecord(ev[e], nullptr));
-            for (int c = 0; c < s.count; c += a.batch) {
-                const int b = s.count - c < a.batch ? s.count - c : a.batch;
+            for (int b : batches(s.count, a.batch)) {
                 DLCHECK(dl_outer_orthogonal_step_batch(theta.data(), avg.data(), b, s.rows, s.cols,
                                                        scale, a.quintic, a.cubic, ws, ws_max,
                                                        nullptr));
@@ -320,7 +343,7 @@ int main(int argc, char** argv) {
     const double ms = total_ms / a.steps;
     std::printf("[driver] step: %.2f ms, %.2f TFLOP/s (%.3e flops)\n", ms,
                 fl_total / (ms / 1e3) / 1e12, fl_total);
-    for (int b = 0; b < a.batch; ++b) {
+    for (int b = 0; b < b_max; ++b) {
         HIPCHECK(hipFree(theta[b]));
         HIPCHECK(hipFree(avg[b]));
     }

@@ -5,11 +5,13 @@ matrix is replaced by its polar factor).
 The flat parameter buffer holds every tensor back to back; the weight
 matrices are row-major views into it.  Vectors (norm weights) have no polar
 factor of interest and are left to the plain merge.  Matrices of one shape
-go through dl_outer_orthogonal_step_batch together (up to a batch size), on
+go through dl_outer_orthogonal_step_batch together (by default all of them,
+split evenly into as few launches of at most DL_MAX_BATCH as hold them), on
 one stream, all sharing one workspace sized for the largest batch.
 """
 from __future__ import annotations
 
+import math
 from typing import List, NamedTuple, Optional
 
 import torch
@@ -74,14 +76,26 @@ def gemm_flops(rows: int, cols: int, quintic: int = 12, cubic: int = 6):
     return {"TN": tn, "NT": nt}
 
 
+def batch_sizes(count: int, batch: Optional[int] = None) -> List[int]:
+    """Sizes of the batches `count` equally shaped matrices run in: chunks
+    of `batch`, or (None) an even split into ceil(count / DL_MAX_BATCH)."""
+    if batch is not None:
+        if not 1 <= batch <= dl.DL_MAX_BATCH:
+            raise ValueError(f"batch {batch} not in [1, {dl.DL_MAX_BATCH}]")
+        return [min(batch, count - c) for c in range(0, count, batch)]
+    n = math.ceil(count / dl.DL_MAX_BATCH)
+    return [count // n + (1 if i < count % n else 0) for i in range(n)]
+
+
 class OrthogonalStep:
     """theta = theta - scale * P(theta - averaged) for every weight matrix of
     a layout, on one stream, with one workspace.  Matrices of one shape run
-    in batches of up to `batch` (one launch per product for the whole batch);
-    batch 1 runs them one by one."""
+    in batches (one launch per product for the whole batch): of up to
+    `batch`, or by default all of a shape, split evenly into launches of at
+    most DL_MAX_BATCH; batch 1 runs them one by one."""
 
     def __init__(self, layout: synth.Layout, device: Optional[torch.device] = None,
-                 quintic: int = 12, cubic: int = 6, batch: int = 8):
+                 quintic: int = 12, cubic: int = 6, batch: Optional[int] = None):
         self.matrices = weight_matrices(layout)
         self.quintic, self.cubic = quintic, cubic
         by_shape = {}
@@ -89,8 +103,10 @@ class OrthogonalStep:
             by_shape.setdefault((m.rows, m.cols), []).append(m)
         self.groups = []
         for ms in by_shape.values():
-            for i in range(0, len(ms), batch):
-                self.groups.append(ms[i:i + batch])
+            i = 0
+            for b in batch_sizes(len(ms), batch):
+                self.groups.append(ms[i:i + b])
+                i += b
         need = max(dl.dl_polar_workspace_bytes_batch(g[0].rows, g[0].cols, len(g))
                    for g in self.groups)
         self.workspace = torch.empty((need + 3) // 4, dtype=torch.float32,

@@ -126,7 +126,8 @@ def polar_stats_markdown(stats_csv: str, command: str) -> str:
     return "\n".join(out)
 
 
-def polar_pmc_summary(run_dir: str, command: str, copy_bytes: int) -> dict:
+def polar_pmc_summary(run_dir: str, command: str, copy_bytes: int,
+                      batching: str = "even") -> dict:
     """Per-kind sums over one pass per counter group, FETCH_SIZE / WRITE_SIZE
     scaled by the plain copy of known size; MFMA busy as a fraction of SIMD
     cycles (GRBM_GUI_ACTIVE counts per XCD: the max over the 8 is the
@@ -175,6 +176,7 @@ def polar_pmc_summary(run_dir: str, command: str, copy_bytes: int) -> dict:
                 a["SQ_VALU_MFMA_BUSY_CYCLES"] / (a["GRBM_GUI_ACTIVE"] / 8 * simds), 4)
         kernels[kind] = k
     return {"workload": "diffurefill1b_orthogonal_step", "kernel_source_hash": polar_source_hash(),
+            "batching": batching,
             "fetch_scale": round(scale.get("FETCH_SIZE", 0), 5),
             "write_scale": round(scale.get("WRITE_SIZE", 0), 5),
             "copy_calibration_bytes": copy_bytes, "command": command, "kernels": kernels}
@@ -330,12 +332,15 @@ def main(argv=None):
     d.add_argument("--command", required=True)
     d.add_argument("--copy-bytes", type=int, required=True)
     d.add_argument("--json")
+    d.add_argument("--batching", default="even",
+                   help="how the run batched equally shaped matrices: 'even' (all of a shape, "
+                        "split evenly into launches of at most 64) or the fixed batch size")
     args = ap.parse_args(argv)
     if args.mode == "polar-stats":
         print(polar_stats_markdown(args.stats_csv, args.command))
         return
     if args.mode == "polar-pmc":
-        s = polar_pmc_summary(args.run_dir, args.command, args.copy_bytes)
+        s = polar_pmc_summary(args.run_dir, args.command, args.copy_bytes, args.batching)
         if args.json:
             with open(args.json, "w") as fh:
                 json.dump(s, fh, indent=1)
