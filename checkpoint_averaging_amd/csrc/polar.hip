@@ -131,10 +131,14 @@ __device__ __forceinline__ void tile_coords(uint32_t t, const Work& wk, uint32_t
 //     groups puts every 8 consecutive lanes' stores in distinct LDS banks;
 //   row-major storage, element (row, k) at P[row*ld + k] (both of NT):
 //     thread t loads rows t/8 + 32p, k = 4(t%8) .. +3: one float4 each.
-// Guard = false (interior tiles with 16-byte aligned rows): plain float4
-// loads.  Guard = true (edge tiles, a partial K-tile): every element from a
-// clamped, valid address, 0 outside the operand or the K range (no
-// branches).  k0: first k of the tile; K: end of the K range; R: rows.
+// Guard = false (full K-tiles, 16-byte aligned rows): plain float4 loads,
+// rows past the operand's last clamped to it (a k-major operand's rows come
+// in groups of 4, so it needs R % 4 == 0: a group is then wholly in or out);
+// the clamped rows only feed outputs past the last row, which are never
+// stored.  Guard = true (a partial K-tile, or an edge that cannot be
+// clamped): every element from a clamped, valid address, 0 outside the
+// operand or the K range (no branches).  k0: first k of the tile; K: end of
+// the K range; R: rows.
 template <bool KMajor, bool Guard>
 __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t ld, int64_t r0,
                                           int64_t R, int64_t k0, int64_t K, int tid,
@@ -143,9 +147,10 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
         const int64_t row = r0 + 4 * ((tid >> 1) & 31);
         const int64_t kq = k0 + 4 * (2 * (tid >> 6) + (tid & 1));
         if constexpr (!Guard) {
+            const int64_t rc = row < R - 4 ? row : R - 4;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                v[kk] = *reinterpret_cast<const f32x4*>(P + (kq + kk) * ld + row);
+                v[kk] = *reinterpret_cast<const f32x4*>(P + (kq + kk) * ld + rc);
         } else {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
@@ -162,7 +167,8 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ P, int64_t l
         for (int p = 0; p < 4; ++p) {
             const int64_t row = r0 + (tid >> 3) + 32 * p;
             if constexpr (!Guard) {
-                v[p] = *reinterpret_cast<const f32x4*>(P + row * ld + k);
+                const int64_t rc = row < R - 1 ? row : R - 1;
+                v[p] = *reinterpret_cast<const f32x4*>(P + rc * ld + k);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -213,6 +219,7 @@ struct TileCtx {
     int64_t ldb;
     int64_t M, N, i0, j0, kb, ke;
     float* smem;
+    bool clamp_rows;   // edge tiles may take the plain loads with clamped rows
 };
 
 // One K-tile: the next tile's loads (if any) in flight while the MFMAs
@@ -294,9 +301,10 @@ __device__ __forceinline__ void k_step_tile(const TileCtx& c, int64_t kt, f32x4 
 }
 
 // acc = opA[i0.., kb..ke) * opB[kb..ke), j0..] for one 128 x 128 tile.
-// Interior tiles with 16-byte aligned rows run their full K-tiles through a
-// branch-free loop of plain loads; the last steps, a partial K-tile and edge
-// tiles use guarded loads.  Ends with a barrier: LDS is free afterwards.
+// Tiles with 16-byte aligned rows run their full K-tiles through a
+// branch-free loop of plain loads (edge tiles too, with clamped rows, when
+// the rows allow it); a partial K-tile, and edge tiles that cannot be
+// clamped, use guarded loads.  Ends with a barrier: LDS is free afterwards.
 template <bool TN>
 __device__ __forceinline__ void mma_tile(const TileCtx& c, bool vec_a, bool vec_b,
                                          f32x16 (&acc)[2][2]) {
@@ -309,7 +317,8 @@ __device__ __forceinline__ void mma_tile(const TileCtx& c, bool vec_a, bool vec_
     const int tid = threadIdx.x;
     const int64_t span = c.ke > c.kb ? c.ke - c.kb : 0;
     const int64_t ktiles = (span + kTileK - 1) / kTileK, nfull = span / kTileK;
-    const bool plain = vec_a && vec_b && c.i0 + kTileM <= c.M && c.j0 + kTileN <= c.N;
+    const bool plain =
+        vec_a && vec_b && (c.clamp_rows || (c.i0 + kTileM <= c.M && c.j0 + kTileN <= c.N));
     f32x4 ra[4], rb[4];
     if (ktiles > 0) {
         if (plain && nfull > 0) {
@@ -390,7 +399,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
         const int64_t i0 = static_cast<int64_t>(ti) * kTileM;
         const int64_t j0 = static_cast<int64_t>(tj) * kTileN;
         f32x16 acc[2][2];
-        const TileCtx ctx{A + mb * sa, lda, B + mb * sb, ldb, M, N, i0, j0, kb, ke, smem};
+        const TileCtx ctx{A + mb * sa, lda, B + mb * sb, ldb, M, N, i0, j0, kb, ke, smem,
+                          TN ? ((M | N) & 3) == 0 : true};
         mma_tile<TN>(ctx, vec_a, vec_b, acc);
         float* const ec = e.c + mb * e.sc;
         const float* const ey = e.y ? e.y + mb * e.sy : nullptr;

@@ -127,6 +127,47 @@ def _bound_check(got, want, mag, k):
     assert np.all(err <= g * mag + 1e-30), (float(np.max(err / (mag + 1e-30))), g)
 
 
+@pytest.mark.parametrize("form,m,n,k,lda_pad", [
+    # k-major operands with row counts divisible by 4 and aligned pitches:
+    # the edge tiles take the plain loads with clamped rows
+    (dl.DL_TN, 132, 260, 96, 0), (dl.DL_TN, 1100, 1000, 64, 4), (dl.DL_TN, 4, 388, 32, 0),
+    # aligned pitches but row counts not divisible by 4: guarded edge tiles
+    (dl.DL_TN, 130, 258, 96, 2), (dl.DL_TN, 7, 129, 64, 1),
+    # row-major operands with aligned pitches: any row count clamps
+    (dl.DL_NT, 129, 131, 96, 0), (dl.DL_NT, 1, 300, 64, 4), (dl.DL_NT, 257, 3, 160, 0),
+    # and with a partial last K-tile
+    (dl.DL_NT, 200, 130, 100, 0), (dl.DL_TN, 200, 132, 100, 0),
+])
+@pytest.mark.parametrize("ws_mode", ["stream", "none"])
+def test_matmul_edge_tiles(form, m, n, k, lda_pad, ws_mode):
+    """Edge tiles (rows past the last output row or column) against fp64,
+    for the pitch and row-count combinations that pick the clamped plain
+    loads or the guarded ones, with and without the stream-K split."""
+    rng = np.random.default_rng(m * 5 + n * 11 + k + lda_pad)
+    if form == dl.DL_TN:
+        lda, ldb = m + lda_pad, n + lda_pad
+        a = rng.standard_normal((k, lda)).astype(np.float32)
+        b = rng.standard_normal((k, ldb)).astype(np.float32)
+        opa, opb = a[:, :m].astype(np.float64).T, b[:, :n].astype(np.float64)
+    else:
+        lda = ldb = k + lda_pad
+        a = rng.standard_normal((m, lda)).astype(np.float32)
+        b = rng.standard_normal((n, ldb)).astype(np.float32)
+        opa, opb = a[:, :k].astype(np.float64), b[:, :k].astype(np.float64).T
+    want, mag = opa @ opb, np.abs(opa) @ np.abs(opb)
+    ldc = n + 3
+    c0 = rng.standard_normal((m, ldc)).astype(np.float32)
+    c_d = gpu(c0)
+    ws = None
+    if ws_mode == "stream":
+        wsb = dl.dl_matmul_workspace_bytes(m, n, k, False)
+        ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV)
+    dl.dl_matmul_f32(form, gpu(a), lda, gpu(b), ldb, m, n, k, c_d, ldc, workspace=ws)
+    got = host(c_d)
+    _bound_check(got[:, :n], want, mag, k)
+    assert np.array_equal(got[:, n:], c0[:, n:].astype(np.float64))
+
+
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("n,k", [(1, 5), (130, 33), (300, 700), (257, 2000), (128, 4096),
                                  (384, 300), (5760, 100)])
