@@ -76,6 +76,14 @@ constexpr int kTileElems = kTileM * kTileN;
 //     first stream-K piece) or 2w + 1 (its last one), and k_reduce_pieces
 //     adds the pieces of each cut tile in K order.
 // Without a workspace: groups = tiles, one round of whole tiles, no pieces.
+// Split mode (ksplit > 1; few tiles over a long K): K is cut into ksplit
+// ranges of kspan K-tiles, and the units (range r, tile t), numbered
+// r * tiles + t, are dealt out in rounds (round n: workgroup w takes unit
+// n * groups + w).  The workgroups running together then work on the same K
+// range of neighbouring tiles, so an XCD's workgroups read the same operand
+// rows at about the same time (one fetch into its L2 serves them all).
+// Every unit is a piece, stored in partial slot = its number, and
+// k_reduce_splits adds each tile's pieces in K order.
 // A batch of equally shaped products is one product whose tiles are the
 // batch's tiles, matrix after matrix.
 struct Work {
@@ -87,6 +95,8 @@ struct Work {
     uint32_t per_xcd;    // the grid is 8 * per_xcd workgroups
     uint32_t dp_rounds;  // rounds of whole tiles
     uint32_t units;      // stream-K units: (tiles - dp_rounds * groups) * kt, below 2^32
+    uint32_t ksplit;     // split mode: K ranges (0 or 1: off)
+    uint32_t kspan;      // split mode: K-tiles per range
     bool sym;
 };
 
@@ -376,11 +386,22 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
     const uint32_t u_end = wk.units ? unit_begin(wk, w + 1) : 0;
     uint32_t u = wk.units ? unit_begin(wk, w) : 0;
     bool first_piece = true;
-    for (uint32_t seg = 0; seg < wk.dp_rounds || u < u_end; ++seg) {
-        uint32_t t, seg_end = 0;
+    const bool split = wk.ksplit > 1;
+    const uint32_t split_units = split ? wk.tiles * wk.ksplit : 0;
+    for (uint32_t seg = 0;
+         split ? seg * wk.groups + w < split_units : (seg < wk.dp_rounds || u < u_end); ++seg) {
+        uint32_t t, seg_end = 0, slot = 0;
         int64_t kb = 0, ke = K;
         bool whole = true;
-        if (seg < wk.dp_rounds) {
+        if (split) {
+            slot = seg * wk.groups + w;
+            const uint32_t r = slot / wk.tiles;
+            t = slot - r * wk.tiles;
+            kb = static_cast<int64_t>(r) * wk.kspan * kTileK;
+            ke = kb + static_cast<int64_t>(wk.kspan) * kTileK;
+            if (ke > K) ke = K;
+            whole = false;
+        } else if (seg < wk.dp_rounds) {
             t = seg * wk.groups + w;
         } else {
             const uint32_t ts = u / wk.kt;
@@ -391,6 +412,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
             if (ke > K) ke = K;
             whole = u == t_begin && seg_end == t_end;
             t = dp_tiles + ts;
+            slot = 2 * w + (first_piece ? 0 : 1);
         }
         // matrix mb of the batch, tile tm within it
         const uint32_t mb = t / wk.tiles_per, tm = t - mb * wk.tiles_per;
@@ -419,8 +441,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
         const int tid = threadIdx.x;
         const int col = tid & (kTileN - 1);
         if (!whole) {
-            // a piece: raw sums to the workgroup's first or last slot
-            float* pt = part + (2 * static_cast<int64_t>(w) + (first_piece ? 0 : 1)) * kTileElems;
+            // a piece: raw sums to its slot (stream-K: the workgroup's first
+            // or last; split mode: the unit's number)
+            float* pt = part + static_cast<int64_t>(slot) * kTileElems;
 #pragma unroll 4
             for (int p = 0; p < kTileElems / kGemmThreads; ++p) {
                 const int row = 2 * p + (tid >> 7);
@@ -456,7 +479,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
                 }
             }
         }
-        if (seg >= wk.dp_rounds) {
+        if (!split && seg >= wk.dp_rounds) {
             first_piece = false;
             u = seg_end;
         }
@@ -464,48 +487,31 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
     }
 }
 
-// The tiles cut between workgroups: the pieces summed in K order, then the
-// epilogue and C.  Workgroup 4b + q looks at the start of workgroup b
-// (b >= 1); if that falls inside a tile and no earlier workgroup start does,
-// it sums that tile's pieces (workgroup b - 1's piece, then the first pieces
-// of b, b + 1, ... that start inside the tile) for rows 32q .. 32q + 31.
-// Thread t owns columns 4(t%32) .. +3 of rows t/32 + 8p.  For a symmetric
-// result the elements with i <= j are written in place and those with i < j
-// also to C[j][i] through an LDS transpose (rows of 32 consecutive i).
-__global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__ part, Work wk,
-                                                       int64_t M, int64_t N, Epilogue e) {
+// One tile's pieces summed in K order (piece(0) + piece(1) + ... +
+// piece(count - 1), each a 128 x 128 tile of raw sums), then the epilogue and
+// C, for rows 32q .. 32q + 31 of the tile.  Thread t owns columns 4(t%32) ..
+// +3 of rows t/32 + 8p.  For a symmetric result the elements with i <= j are
+// written in place and those with i < j also to C[j][i] through an LDS
+// transpose (rows of 32 consecutive i).
+template <class Piece>
+__device__ __forceinline__ void reduce_tile_rows(const Piece& piece, uint32_t count, uint32_t t,
+                                                 int q, const Work& wk, int64_t M, int64_t N,
+                                                 const Epilogue& e) {
     __shared__ float tr[32][kTileN + 1];
-    const uint32_t b = blockIdx.x >> 2;
-    const int q = static_cast<int>(blockIdx.x & 3);
-    if (b == 0 || b >= wk.groups || wk.units == 0) return;
-    const uint32_t ub = unit_begin(wk, b);
-    const uint32_t ts = ub / wk.kt;                  // stream-K tile
-    const uint32_t t_begin = ts * wk.kt, t_end = t_begin + wk.kt;
-    if (ub == t_begin) return;                       // a start between whole tiles
-    const uint32_t prev = unit_begin(wk, b - 1);
-    if (prev > t_begin) return;                      // handled at an earlier start
-    const uint32_t t = wk.dp_rounds * wk.groups + ts;
     const uint32_t mb = t / wk.tiles_per;
     uint32_t ti, tj;
     tile_coords(t - mb * wk.tiles_per, wk, ti, tj);
     float* const ec = e.c + mb * e.sc;
     const float* const ey = e.y ? e.y + mb * e.sy : nullptr;
-    // workgroup b - 1 holds the tile's first piece: its first slot if it
-    // starts at the tile, else its last slot
-    const float* first = part + (2 * static_cast<int64_t>(b - 1) + (prev < t_begin ? 1 : 0)) *
-                                    kTileElems;
-    uint32_t last = b;                               // workgroups b .. last start inside the tile
-    while (last + 1 < wk.groups && unit_begin(wk, last + 1) < t_end) ++last;
     const int tid = threadIdx.x;
     const int lj = 4 * (tid & 31);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int ll = (tid >> 5) + 8 * p;                    // row within the quarter
         const int li = 32 * q + ll;
-        f32x4 v = *reinterpret_cast<const f32x4*>(first + li * kTileN + lj);
-        for (uint32_t w = b; w <= last; ++w) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(
-                part + 2 * static_cast<int64_t>(w) * kTileElems + li * kTileN + lj);
+        f32x4 v = *reinterpret_cast<const f32x4*>(piece(0) + li * kTileN + lj);
+        for (uint32_t n = 1; n < count; ++n) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(piece(n) + li * kTileN + lj);
 #pragma unroll
             for (int c = 0; c < 4; ++c) v[c] = v[c] + x[c];
         }
@@ -532,6 +538,47 @@ __global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__
         const int64_t j = static_cast<int64_t>(tj) * kTileN + jj;
         if (i < j && j < M) ec[j * e.ldc + i] = tr[ii][jj];
     }
+}
+
+// The tiles cut between workgroups (stream-K): workgroup 4b + q looks at the
+// start of workgroup b (b >= 1); if that falls inside a tile and no earlier
+// workgroup start does, it sums that tile's pieces (workgroup b - 1's piece,
+// then the first pieces of b, b + 1, ... that start inside the tile) for
+// rows 32q .. 32q + 31.
+__global__ __launch_bounds__(256) void k_reduce_pieces(const float* __restrict__ part, Work wk,
+                                                       int64_t M, int64_t N, Epilogue e) {
+    const uint32_t b = blockIdx.x >> 2;
+    const int q = static_cast<int>(blockIdx.x & 3);
+    if (b == 0 || b >= wk.groups || wk.units == 0) return;
+    const uint32_t ub = unit_begin(wk, b);
+    const uint32_t ts = ub / wk.kt;                  // stream-K tile
+    const uint32_t t_begin = ts * wk.kt, t_end = t_begin + wk.kt;
+    if (ub == t_begin) return;                       // a start between whole tiles
+    const uint32_t prev = unit_begin(wk, b - 1);
+    if (prev > t_begin) return;                      // handled at an earlier start
+    // workgroup b - 1 holds the tile's first piece: its first slot if it
+    // starts at the tile, else its last slot
+    const float* first = part + (2 * static_cast<int64_t>(b - 1) + (prev < t_begin ? 1 : 0)) *
+                                    kTileElems;
+    uint32_t last = b;                               // workgroups b .. last start inside the tile
+    while (last + 1 < wk.groups && unit_begin(wk, last + 1) < t_end) ++last;
+    auto piece = [&](uint32_t n) {
+        return n == 0 ? first : part + 2 * static_cast<int64_t>(b + n - 1) * kTileElems;
+    };
+    reduce_tile_rows(piece, last - b + 2, wk.dp_rounds * wk.groups + ts, q, wk, M, N, e);
+}
+
+// Split mode: workgroup 4t + q sums the ksplit pieces of tile t (slots
+// r * tiles + t, r = 0 .. ksplit - 1, in K order) for rows 32q .. 32q + 31.
+__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, Work wk,
+                                                       int64_t M, int64_t N, Epilogue e) {
+    const uint32_t t = blockIdx.x >> 2;
+    const int q = static_cast<int>(blockIdx.x & 3);
+    if (t >= wk.tiles) return;
+    auto piece = [&](uint32_t r) {
+        return part + (static_cast<int64_t>(r) * wk.tiles + t) * kTileElems;
+    };
+    reduce_tile_rows(piece, wk.ksplit, t, q, wk, M, N, e);
 }
 
 // ---- Frobenius norm (two-stage fp64 reduction, fixed order) ---------------
@@ -596,6 +643,7 @@ int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
 constexpr int64_t kStreamGroups = 512;          // two resident workgroups on each of 256 CUs
 constexpr int64_t kMinUnits = 8;                // K-tiles per workgroup at least
+constexpr int64_t kSplitMinSpan = 64;           // split mode: K-tiles per range at least
 
 // The split of a batch of M x N x K products (see Work).  With a workspace
 // of at least 2 * groups tiles the units are spread over up to
@@ -619,6 +667,46 @@ void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch, int64_t
     const bool stream = need <= ws_bytes && sk_units <= static_cast<int64_t>(UINT32_MAX) &&
                         g != tiles;
     const int64_t groups = stream ? g : tiles;
+    wk.ksplit = 0;
+    wk.kspan = 0;
+    // Split mode, for fewer tiles than resident workgroups over a long K:
+    // R rounds of units (range, tile) with S = R * 512 / tiles ranges (at
+    // least kSplitMinSpan K-tiles each); taken when some R brings the
+    // busiest workgroup's K-tiles within 3% of an even stream-K split.
+    if (tiles < kStreamGroups && kt >= 2 * kSplitMinSpan) {
+        int64_t best = INT64_MAX, best_s = 0, best_span = 0;
+        for (int64_t R = 1; R <= 8; ++R) {
+            int64_t S = R * kStreamGroups / tiles;
+            if (S * kSplitMinSpan > kt) S = kt / kSplitMinSpan;
+            if (S < 2) continue;
+            const int64_t span = (kt + S - 1) / S;
+            S = (kt + span - 1) / span;                // ranges actually needed
+            const int64_t load = (tiles * S + kStreamGroups - 1) / kStreamGroups * span;
+            if (load < best) {
+                best = load;
+                best_s = S;
+                best_span = span;
+            }
+        }
+        const int64_t even = (units + kStreamGroups - 1) / kStreamGroups;
+        const int64_t split_need = tiles * best_s * kTileElems * 4;
+        if (best_s > 1 && best * 100 <= even * 103 && split_need <= ws_bytes) {
+            wk.tiles_n = static_cast<uint32_t>(tn);
+            wk.tiles_per = static_cast<uint32_t>(per);
+            wk.tiles = static_cast<uint32_t>(tiles);
+            wk.kt = static_cast<uint32_t>(kt);
+            const int64_t sg = tiles * best_s < kStreamGroups ? tiles * best_s : kStreamGroups;
+            wk.groups = static_cast<uint32_t>(sg);
+            wk.per_xcd = static_cast<uint32_t>((sg + kXcds - 1) / kXcds);
+            wk.dp_rounds = 0;
+            wk.units = 0;
+            wk.ksplit = static_cast<uint32_t>(best_s);
+            wk.kspan = static_cast<uint32_t>(best_span);
+            wk.sym = sym;
+            if (need_bytes) *need_bytes = split_need;
+            return;
+        }
+    }
     wk.tiles_n = static_cast<uint32_t>(tn);
     wk.tiles_per = static_cast<uint32_t>(per);
     wk.tiles = static_cast<uint32_t>(tiles);
@@ -657,7 +745,9 @@ hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B
     else
         hipLaunchKernelGGL((k_gemm<false>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, M, N, K,
                            sa, sb, wk, vec_a, vec_b, e, part);
-    if (wk.units != 0 && (wk.units / wk.kt) % wk.groups != 0)   // pieces of cut tiles to add
+    if (wk.ksplit > 1)                                         // every tile in pieces
+        hipLaunchKernelGGL(k_reduce_splits, dim3(wk.tiles * 4), dim3(256), 0, s, part, wk, M, N, e);
+    else if (wk.units != 0 && (wk.units / wk.kt) % wk.groups != 0)   // pieces of cut tiles to add
         hipLaunchKernelGGL(k_reduce_pieces, dim3(wk.groups * 4), dim3(256), 0, s, part, wk, M, N, e);
     return hipGetLastError();
 }

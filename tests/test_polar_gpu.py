@@ -245,6 +245,53 @@ def test_matmul_stream_k(form, m, n, k):
 
 
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
+@pytest.mark.parametrize("m,k,sym,epi", [(1000, 30000, True, False), (1024, 28672, True, True),
+                                         (512, 65536, False, True)])
+def test_matmul_split_k(form, m, k, sym, epi):
+    """Few output tiles over a long K (the Gram product of a tall matrix): K
+    is cut into ranges dealt out range by range over the tiles, and each
+    tile's pieces are summed in K order by a second kernel.  Within the
+    product bound of fp64, the same bits on a second call, an exactly
+    symmetric result; without a workspace (one workgroup per tile, the
+    whole K in order) also within the bound."""
+    n = m
+    rng = np.random.default_rng(m + k)
+    if form == dl.DL_TN:
+        a = rng.standard_normal((k, m)).astype(np.float32)
+        b = a if sym else rng.standard_normal((k, n)).astype(np.float32)
+        opa, opb = a.astype(np.float64).T, b.astype(np.float64)
+        lda = ldb = m
+    else:
+        a = rng.standard_normal((m, k)).astype(np.float32)
+        b = a if sym else rng.standard_normal((n, k)).astype(np.float32)
+        opa, opb = a.astype(np.float64), b.astype(np.float64).T
+        lda = ldb = k
+    alpha, beta, diag = (-0.5, 2.0, 1.5) if epi else (1.0, 0.0, 0.0)
+    y0 = rng.standard_normal((m, n)).astype(np.float32)
+    if sym:
+        y0 = (y0 + y0.T) / 2
+    want = alpha * (opa @ opb) + (beta * y0.astype(np.float64) if epi else 0) + diag * np.eye(m)
+    mag = abs(alpha) * (np.abs(opa) @ np.abs(opb)) + (abs(beta) * np.abs(y0) if epi else 0) + \
+        abs(diag) * np.eye(m)
+    a_d = gpu(a)
+    b_d = a_d if sym else gpu(b)
+    y_d = gpu(y0) if epi else None
+    wsb = dl.dl_matmul_workspace_bytes(m, n, k, sym)
+    assert wsb > 0
+    outs = []
+    for ws_bytes in (wsb, wsb, 0):
+        ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=DEV) if ws_bytes else None
+        c_d = torch.empty((m, n), device=DEV)
+        dl.dl_matmul_f32(form, a_d, lda, b_d, ldb, m, n, k, c_d, n, y_d, alpha, beta, diag,
+                         symmetric=sym, workspace=ws)
+        outs.append(host(c_d))
+        _bound_check(outs[-1], want, mag, k)
+        if sym:
+            assert np.array_equal(outs[-1], outs[-1].T)
+    assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("sym", [False, True], ids=["general", "symmetric"])
 @pytest.mark.parametrize("ws_mode", ["stream", "none"])
 def test_matmul_batch(form, sym, ws_mode):
