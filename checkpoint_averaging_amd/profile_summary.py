@@ -90,7 +90,8 @@ def polar_kind(name: str):
         return "gemm_TN"
     if "k_gemm<false>" in name:
         return "gemm_NT"
-    for k in ("k_reduce_pieces", "k_sumsq_partial", "k_sumsq_final", "k_scale", "k_step"):
+    for k in ("k_reduce_pieces", "k_reduce_splits", "k_sumsq_partial", "k_sumsq_final", "k_scale",
+              "k_step"):
         if f"::{k}(" in name or name.startswith(k + "("):
             return k[2:]
     return None
