@@ -294,15 +294,27 @@ def test_matmul_batch_host_rules():
 
 
 def test_matmul_workspace_sizes():
-    """Two partial slots per workgroup; up to 512 workgroups (two per CU),
-    each with at least 8 K-tiles of 32, in multiples of 8 (one per XCD)."""
+    """Stream-K: two partial slots per workgroup; up to 512 workgroups (two
+    per CU), each with at least 8 K-tiles of 32, in multiples of 8 (one per
+    XCD).  Split-K (fewer tiles than 512 over a long K): one slot per (K
+    range, tile) unit, S ranges of at least 64 K-tiles filling R rounds of
+    512 units, taken when the busiest workgroup stays within 3% of an even
+    split."""
     tile = 128 * 128 * 4
     full = 2 * 512 * tile
-    assert dl.dl_matmul_workspace_bytes(2048, 2048, 73760, True) == full
+    # 136 upper tiles x 2305 K-tiles: S = 15 ranges of 154 (4 rounds)
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 73760, True) == 136 * 15 * tile
+    # 36 upper tiles x 896 K-tiles: S = 14 ranges of 64 (1 round)
+    assert dl.dl_matmul_workspace_bytes(1024, 1024, 28672, True) == 36 * 14 * tile
+    # 16 tiles x 2048 K-tiles: 32 ranges of 64; 1 tile x 32768: 512 of 64
+    assert dl.dl_matmul_workspace_bytes(512, 512, 65536, False) == 16 * 32 * tile
+    assert dl.dl_matmul_workspace_bytes(100, 100, 1 << 20, False) == 512 * tile
+    # too short a K for ranges of 64 K-tiles to fill the rounds: stream-K
+    assert dl.dl_matmul_workspace_bytes(512, 512, 40000, False) == full
+    assert dl.dl_matmul_workspace_bytes(2048, 2048, 5632, True) == full
     assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, True) == full
     assert dl.dl_matmul_workspace_bytes(2048, 2048, 2048, False) == full
     assert dl.dl_matmul_workspace_bytes(5632, 2048, 2048, False) == full
-    assert dl.dl_matmul_workspace_bytes(100, 100, 1 << 20, False) == full
     # 136 upper tiles x 4 K-tiles = 544 units: 68 workgroups, rounded to 64
     assert dl.dl_matmul_workspace_bytes(2048, 2048, 100, True) == 2 * 64 * tile
     # one tile of 32 K-tiles: 4 workgroups
