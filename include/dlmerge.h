@@ -393,10 +393,12 @@ enum dl_matmul_form {
  * argument) or NULL.  With at least dl_matmul_workspace_bytes bytes the work
  * (output tiles x K) is spread evenly over the workgroups the GPU holds at
  * once, and tiles cut between workgroups are summed in K order through the
- * workspace; without it every workgroup computes one whole output tile.
- * The two give different (each deterministic) summation orders.  m = 0 or
- * n = 0 is a no-op.  Errors: DL_E_INVAL (also: symmetric with m != n),
- * DL_E_ALIGN, DL_E_HIP.
+ * workspace (few output tiles over a long K: K cut into ranges, every tile
+ * in pieces, summed in K order); a smaller workspace may still hold the
+ * stream-K split's pieces; otherwise, or without one, every workgroup
+ * computes one whole output tile.  The plans give different (each
+ * deterministic) summation orders.  m = 0 or n = 0 is a no-op.  Errors:
+ * DL_E_INVAL (also: symmetric with m != n), DL_E_ALIGN, DL_E_HIP.
  */
 int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, int64_t *bytes);
 int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t ldb, int64_t m,
