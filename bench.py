@@ -52,7 +52,9 @@ def measured_traffic(workload: str, kind: str):
         d = json.load(fh)
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    k = d.get("kernels", {}).get(kind)
+    ks = d.get("kernels", {})
+    # counter summaries name bf16-checkpoint kernels with a _bf16 suffix
+    k = ks.get(kind) or ks.get(kind + "_bf16")
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
