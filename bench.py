@@ -295,7 +295,7 @@ def orthogonalize(args, torch):
     n = layout.n_params
     theta = synth.global0(1007, n, device=dev)
     averaged = synth.worker_checkpoint(1007, 0, 0, theta)
-    step = OrthogonalStep(layout, dev, batch=args.orth_batch or None)
+    step = OrthogonalStep(layout, dev, batch=args.orth_batch or None, streams=args.orth_streams)
     mats = step.matrices
     n_mat = sum(m.rows * m.cols for m in mats)
     flops = step.flops()
@@ -414,6 +414,7 @@ def orthogonalize(args, torch):
                              "at most 64"),
                    "batches": sorted({f"{len(g)} x {g[0].rows}x{g[0].cols}"
                                       for g in step.groups}),
+                   "streams": args.orth_streams,
                    "matrix_params": n_mat, "quintic_steps": 12, "cubic_steps": 6,
                    "algorithmic_flops_per_step": total_flops},
         "TFLOP_per_s": round(total_flops / (ms / 1e3) / 1e12, 2),
@@ -481,6 +482,8 @@ def main():
     ap.add_argument("--orth-batch", type=int, default=0,
                     help="equally shaped matrices orthogonalised together (1: one by one; "
                          "0: all of a shape, split evenly into launches of at most 64)")
+    ap.add_argument("--orth-streams", type=int, default=1,
+                    help="streams the orthogonalised step's batches are spread over")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")

@@ -95,7 +95,8 @@ class OrthogonalStep:
     most DL_MAX_BATCH; batch 1 runs them one by one."""
 
     def __init__(self, layout: synth.Layout, device: Optional[torch.device] = None,
-                 quintic: int = 12, cubic: int = 6, batch: Optional[int] = None):
+                 quintic: int = 12, cubic: int = 6, batch: Optional[int] = None,
+                 streams: int = 1):
         self.matrices = weight_matrices(layout)
         self.quintic, self.cubic = quintic, cubic
         by_shape = {}
@@ -107,10 +108,27 @@ class OrthogonalStep:
             for b in batch_sizes(len(ms), batch):
                 self.groups.append(ms[i:i + b])
                 i += b
-        need = max(dl.dl_polar_workspace_bytes_batch(g[0].rows, g[0].cols, len(g))
-                   for g in self.groups)
-        self.workspace = torch.empty((need + 3) // 4, dtype=torch.float32,
-                                     device=device or torch.device("cuda"))
+        if streams < 1:
+            raise ValueError("streams must be at least 1")
+        # batches dealt to the streams, largest first to the least loaded
+        self.lanes: List[List[List[Matrix]]] = [[] for _ in range(streams)]
+        load = [0] * streams
+        for g in sorted(self.groups, key=self._group_flops, reverse=True):
+            s = load.index(min(load))
+            self.lanes[s].append(g)
+            load[s] += self._group_flops(g)
+        dev = device or torch.device("cuda")
+        # one workspace per stream (batches in flight together must not share one)
+        self.workspaces = []
+        for lane in self.lanes:
+            need = max((dl.dl_polar_workspace_bytes_batch(g[0].rows, g[0].cols, len(g))
+                        for g in lane), default=256)
+            self.workspaces.append(torch.empty((need + 3) // 4, dtype=torch.float32, device=dev))
+        self.workspace = self.workspaces[0]
+        self._streams = None
+
+    def _group_flops(self, g: List[Matrix]) -> int:
+        return len(g) * sum(gemm_flops(g[0].rows, g[0].cols, self.quintic, self.cubic).values())
 
     def flops(self):
         tot = {"TN": 0, "NT": 0}
@@ -122,8 +140,10 @@ class OrthogonalStep:
     def run(self, theta: torch.Tensor, averaged: torch.Tensor, scale: float, timer=None):
         """One orthogonalised outer step over the flat buffers.  `timer`, if
         given, is called as timer(matrices, call) for each batch and must
-        call call()."""
-        for g in self.groups:
+        call call().  With several streams, stream s runs lane s's batches
+        in order; the streams start after the caller's stream and the
+        caller's stream waits for all of them."""
+        def issue(g, ws):
             rows, cols = g[0].rows, g[0].cols
             n = rows * cols
             ts = [theta[m.offset:m.offset + n] for m in g]
@@ -131,12 +151,28 @@ class OrthogonalStep:
 
             def call(ts=ts, avs=avs, rows=rows, cols=cols):
                 if len(ts) == 1:
-                    dl.dl_outer_orthogonal_step(ts[0], avs[0], rows, cols, scale, self.workspace,
+                    dl.dl_outer_orthogonal_step(ts[0], avs[0], rows, cols, scale, ws,
                                                 self.quintic, self.cubic)
                 else:
-                    dl.dl_outer_orthogonal_step_batch(ts, avs, rows, cols, scale, self.workspace,
+                    dl.dl_outer_orthogonal_step_batch(ts, avs, rows, cols, scale, ws,
                                                       self.quintic, self.cubic)
             if timer is None:
                 call()
             else:
                 timer(g, call)
+
+        if len(self.lanes) == 1:
+            for g in self.lanes[0]:
+                issue(g, self.workspaces[0])
+            return
+        if self._streams is None:
+            self._streams = [torch.cuda.Stream(device=theta.device) for _ in self.lanes]
+        cur = torch.cuda.current_stream(theta.device)
+        for st in self._streams:
+            st.wait_stream(cur)
+        for st, lane, ws in zip(self._streams, self.lanes, self.workspaces):
+            with torch.cuda.stream(st):
+                for g in lane:
+                    issue(g, ws)
+        for st in self._streams:
+            cur.wait_stream(st)

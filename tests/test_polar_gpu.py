@@ -507,19 +507,21 @@ def test_outer_orthogonal_step_batch_full_size():
         assert rel <= est
 
 
-def test_orthogonal_step_over_pythia14m_layout():
+@pytest.mark.parametrize("batch,streams", [(8, 1), (None, 1), (None, 2), (4, 3)])
+def test_orthogonal_step_over_pythia14m_layout(batch, streams):
     """The whole-model step over the Pythia-14M layout (26 matrices in five
     shapes: the two 50304 x 128 embeddings, QKV 384 x 128, dense 128 x 128,
-    MLP 512 x 128 and 128 x 512; equally shaped ones batched by 8): every
-    matrix against the oracle's step, and every parameter outside the
-    matrices (the norms and biases) untouched."""
+    MLP 512 x 128 and 128 x 512; equally shaped ones batched by 8, 4 or all
+    together, on one stream or spread over several): every matrix against the
+    oracle's step, and every parameter outside the matrices (the norms and
+    biases) untouched."""
     from checkpoint_averaging_amd.orthogonalize import OrthogonalStep
     layout = synth.PYTHIA_14M
     n = layout.n_params
     theta = synth.global0(1201, n, device=DEV)
     avg = synth.worker_checkpoint(1201, 0, 0, theta)
     th_h, av_h = host(theta), host(avg)
-    step = OrthogonalStep(layout, DEV, batch=8)
+    step = OrthogonalStep(layout, DEV, batch=batch, streams=streams)
     assert len(step.matrices) == 26
     scale = 2e-3
     step.run(theta, avg, scale)
