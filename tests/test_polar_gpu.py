@@ -402,6 +402,36 @@ def test_polar_factor_of_zero_is_zero():
     assert not np.any(host(out))
 
 
+@pytest.mark.parametrize("m,n,rank", [(300, 120, 80), (120, 300, 80), (256, 256, 1)])
+def test_polar_factor_rank_deficient(m, n, rank):
+    """A rank-deficient update (the degenerate case): U V^T is unique only on
+    the row space of A, where it maps V_r to U_r; on the null space any
+    completion is a polar factor.  The unique part is checked against the SVD
+    factors of A; for the rest, that the result is still a valid contraction
+    (no singular value above 1 beyond rounding: the iteration maps [0, 1]
+    into [0, 1]).  fp32 rounding gives the null space singular values of
+    order u, which the iteration amplifies, so it is not left at zero."""
+    rng = np.random.default_rng(m + 3 * n + rank)
+    u, _ = np.linalg.qr(rng.standard_normal((m, rank)))
+    v, _ = np.linalg.qr(rng.standard_normal((n, rank)))
+    sv = np.logspace(0, -1, rank)
+    a = ((u * sv) @ v.T).astype(np.float32)
+    a64 = a.astype(np.float64)
+    uu, ss, vvt = np.linalg.svd(a64, full_matrices=False)
+    ur, vr = uu[:, :rank], vvt[:rank].T
+    out = torch.empty((m, n), device=DEV)
+    dl.dl_polar_factor(out, gpu(a), m, n, workspace(m, n))
+    got = host(out)
+    est = estimate_from(ss[0] / ss[rank - 1], rank)
+    rel = np.linalg.norm(got @ vr - ur) / np.linalg.norm(ur)
+    s_got = np.linalg.svd(got, compute_uv=False)
+    null = np.linalg.norm(got @ vvt[rank:].T) if vvt.shape[0] > rank else 0.0
+    print(f"rank-deficient {m}x{n} rank {rank}: unique part rel {rel:.2e} (estimate {est:.2e}), "
+          f"sigma_max {s_got[0]:.6f}, null-space part {null:.2e}", flush=True)
+    assert rel <= est, (rel, est)
+    assert s_got[0] <= 1 + 1e-4
+
+
 def test_polar_factor_scale_invariant_and_deterministic():
     rng = np.random.default_rng(12)
     a = constructed(rng, 300, 100, 50)
