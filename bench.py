@@ -18,7 +18,6 @@ Default workload: DiffuRefill-1B (1,075,980,288 fp32 params) in 4 fragments,
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -35,11 +34,8 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from checkpoint_averaging_amd.profile_summary import kernel_source_hash as h
+    return h()
 
 
 def measured_traffic(workload: str, kind: str):
@@ -70,11 +66,8 @@ def measured_polar_traffic(kind: str, batching: str):
         return None
     with open(path) as fh:
         d = json.load(fh)
-    h = hashlib.sha256()
-    for f in ("polar.hip", "polar.h"):
-        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if d.get("kernel_source_hash") != h.hexdigest()[:16] or d.get("batching") != batching:
+    from checkpoint_averaging_amd.profile_summary import polar_source_hash
+    if d.get("kernel_source_hash") != polar_source_hash() or d.get("batching") != batching:
         return None
     k = d.get("kernels", {}).get(kind)
     return k.get("hbm_bytes_per_launch") if k else None

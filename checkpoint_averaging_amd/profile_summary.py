@@ -76,12 +76,44 @@ SIDE_BYTES_PER_ELEM = {"fold": 12, "fold_first": 8, "finalize_mean": 8, "snapsho
                        "snapshot_mean_5": 24, "adopt_keep_drift": 16}
 
 
-def kernel_source_hash() -> str:
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments (string and character literals kept)
+    and with runs of whitespace collapsed: what the compiler sees."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def source_hash(*names: str) -> str:
+    """Hash of the given csrc files' code (comments and layout ignored), so
+    that counter summaries stay valid across comment edits and go stale
+    with any change to the code itself."""
     h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h"):
-        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in names:
+        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f)) as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return source_hash("kernels.hip", "kernels.h")
 
 
 def polar_kind(name: str):
@@ -98,11 +130,7 @@ def polar_kind(name: str):
 
 
 def polar_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("polar.hip", "polar.h"):
-        with open(os.path.join(ROOT, "checkpoint_averaging_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    return source_hash("polar.hip", "polar.h")
 
 
 def polar_stats_markdown(stats_csv: str, command: str) -> str:

@@ -86,3 +86,15 @@ def test_side_average_kernels_move_their_algorithmic_bytes():
     for kind, k in d["kernels"].items():
         assert k["hbm_bytes_per_launch"] == pytest.approx(ps.SIDE_BYTES_PER_ELEM[kind] * n,
                                                           rel=5e-3), kind
+
+
+def test_source_hash_ignores_comments_only():
+    src = ('// header\nint f(int a) { /* inline */ return a + 1; }  // tail\n'
+           'const char* s = "http://x /* kept */";\n')
+    same = ('/* another header */\nint f(int a) {\n    return a + 1;\n}\n'
+            'const char* s = "http://x /* kept */";  // other tail\n')
+    code = src.replace("a + 1", "a + 2")
+    strip = ps.strip_comments
+    assert strip(src) == strip(same)
+    assert strip(src) != strip(code)
+    assert '"http://x /* kept */"' in strip(src)      # string literals untouched
