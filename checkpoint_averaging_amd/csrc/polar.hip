@@ -24,7 +24,12 @@
 // tiles) goes to as many workgroups as the GPU holds at once: whole tiles in
 // rounds, then the last round or two's worth split stream-K; tiles cut
 // between workgroups are summed in K order by a second kernel, so results
-// are deterministic.  The Gram matrix and its square are symmetric: only
+// are deterministic.  A product with fewer tiles than workgroups over a long
+// K (the Gram matrix of a tall embedding) is split along K instead, its
+// (K range, tile) units dealt range by range so that the workgroups of an
+// XCD read the same operand rows together, and each tile's pieces summed in
+// K order.  Edge tiles take the plain loads with clamped rows where the
+// layout allows it.  The Gram matrix and its square are symmetric: only
 // their upper tiles are computed and the lower ones are written as mirror
 // images.  The epilogue is fused: out = alpha*acc + beta*Y + (i == j ? d :
 // 0), which forms a I + b G + c G^2 in the G^2 product, 1.5 I - 0.5 G in the
