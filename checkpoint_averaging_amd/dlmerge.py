@@ -39,7 +39,8 @@ SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
            "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_workspace_bytes_batch",
-           "dl_polar_factor", "dl_outer_orthogonal_step", "dl_outer_orthogonal_step_batch", "dl_matmul_workspace_bytes", "dl_matmul_f32",
+           "dl_polar_factor", "dl_outer_orthogonal_step", "dl_outer_orthogonal_step_batch",
+           "dl_matmul_workspace_bytes", "dl_matmul_f32",
            "dl_matmul_workspace_bytes_batch", "dl_matmul_f32_batch",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
