@@ -492,6 +492,187 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
     }
 }
 
+// ---- large-tile kernel for plain row-major products -----------------------
+//
+// C = alpha * A B^T (+ beta * Y) for row-major A (M x K) and B (N x K), with
+// M and N multiples of 256 and K of 16 (the main block of a product; the
+// rest goes to k_gemm).  One workgroup per CU (4 waves, one per SIMD), each
+// wave a 128 x 128 quarter of a 256 x 256 tile as 4 x 4 MFMA blocks of 32 x
+// 32 whose sums fill the 256 accumulation registers.  With one wave per
+// SIMD the latency is hidden inside the wave: K-tiles of 16 in two LDS
+// buffers; the operands of a K-tile come in two halves of 4 k-steps (k = 8h
+// + 4c + e for lane half h, chunk c), the second half read while the first
+// runs and the next K-tile's first half read while the second runs; the next
+// K-tile's LDS stores, the loads of the one after and the operand reads are
+// spread among the MFMAs, one per two, by scheduling barriers; one
+// barrier per K-tile.  Workgroups take tiles in rounds, the 32 of an XCD on
+// consecutive tiles (sharing operand rows in L2).
+constexpr int kBigM = 256, kBigN = 256, kBigK = 16;
+constexpr int kBigRow = kBigK + 4;                    // LDS row (floats): 16 k + 4 padding
+constexpr int kBigTile = kBigM * kBigRow;             // one operand tile of one buffer
+constexpr int kBigGroups = 256;                       // one workgroup per CU
+
+// 256 rows x 16 k of a row-major operand: thread t loads rows t/4 + 64p, k
+// 4(t%4) .. +3 (4 float4)
+__device__ __forceinline__ void big_load(const float* __restrict__ P, int64_t ld, int64_t k0,
+                                         int tid, f32x4 (&g)[4]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        g[p] = *reinterpret_cast<const f32x4*>(P + ((tid >> 2) + 64 * p) * ld + k0 +
+                                               4 * (tid & 3));
+}
+__device__ __forceinline__ void big_store(float* S, int tid, const f32x4 (&g)[4]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<f32x4*>(S + ((tid >> 2) + 64 * p) * kBigRow + 4 * (tid & 3)) = g[p];
+}
+// chunk c of this lane's operand rows base + 32 i + l%32 (i < 4)
+__device__ __forceinline__ void big_read(const float* S, int base, int lane, int c,
+                                         f32x4 (&r)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = *reinterpret_cast<const f32x4*>(S + (base + 32 * i + (lane & 31)) * kBigRow +
+                                               8 * (lane >> 5) + 4 * c);
+}
+__device__ __forceinline__ void big_mma(int e, const f32x4 (&a)[4], const f32x4 (&b)[4],
+                                        f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0,
+                                                             0);
+}
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
+    const float* __restrict__ A, int64_t lda, int64_t sa, const float* __restrict__ B,
+    int64_t ldb, int64_t sb, int64_t K, uint32_t tiles_m, uint32_t tiles_n, uint32_t tiles,
+    Epilogue e) {
+    __shared__ __align__(16) float smem[4 * kBigTile];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int64_t nk = K / kBigK;
+    const uint32_t per_xcd = kBigGroups / kXcds;
+    const uint32_t w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    for (uint32_t t = w; t < tiles; t += kBigGroups) {
+        const uint32_t per = tiles_m * tiles_n;
+        const uint32_t mb = t / per, tm = t - mb * per;
+        const uint32_t ti = tm / tiles_n, tj = tm - ti * tiles_n;
+        const float* Ab = A + mb * sa + static_cast<int64_t>(ti) * kBigM * lda;
+        const float* Bb = B + mb * sb + static_cast<int64_t>(tj) * kBigN * ldb;
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        f32x4 ga[4], gb[4], a0[4], b0[4], a1[4], b1[4];
+        big_load(Ab, lda, 0, tid, ga);
+        big_load(Bb, ldb, 0, tid, gb);
+        big_store(smem, tid, ga);
+        big_store(smem + kBigTile, tid, gb);
+        __syncthreads();
+        big_read(smem, wr * 128, lane, 0, a0);
+        big_read(smem + kBigTile, wc * 128, lane, 0, b0);
+        if (nk > 1) {
+            big_load(Ab, lda, kBigK, tid, ga);
+            big_load(Bb, ldb, kBigK, tid, gb);
+        }
+        // K-tile kt (in buffer kt % 2, chunk 0 already in a0/b0): store
+        // K-tile kt+1 (in ga/gb) to the other buffer, load K-tile kt+2, read
+        // chunk 1 into a1/b1, barrier, read chunk 0 of K-tile kt+1.
+        auto ktile = [&](int64_t kt, bool store_next, bool load_next2) {
+            const int cur = static_cast<int>(kt & 1), nxt = cur ^ 1;
+            const float* sa_ = smem + 2 * cur * kBigTile;
+            const float* sb_ = sa_ + kBigTile;
+            float* na = smem + 2 * nxt * kBigTile;
+            float* nb = na + kBigTile;
+            big_mma(0, a0, b0, acc);
+            if (store_next) {
+                big_store(na, tid, ga);
+                big_store(nb, tid, gb);
+            }
+            big_mma(1, a0, b0, acc);
+            if (load_next2) {
+                big_load(Ab, lda, (kt + 2) * kBigK, tid, ga);
+                big_load(Bb, ldb, (kt + 2) * kBigK, tid, gb);
+            }
+            big_mma(2, a0, b0, acc);
+            big_read(sa_, wr * 128, lane, 1, a1);
+            big_read(sb_, wc * 128, lane, 1, b1);
+            big_mma(3, a0, b0, acc);
+            if (store_next && load_next2) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();
+            big_mma(0, a1, b1, acc);
+            if (store_next) {
+                big_read(na, wr * 128, lane, 0, a0);
+                big_read(nb, wc * 128, lane, 0, b0);
+            }
+            big_mma(1, a1, b1, acc);
+            big_mma(2, a1, b1, acc);
+            big_mma(3, a1, b1, acc);
+            if (store_next && load_next2) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 48, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        int64_t kt = 0;
+        for (; kt + 2 < nk; ++kt) ktile(kt, true, true);   // branch-free body
+        if (kt + 1 < nk) {
+            ktile(kt, true, false);
+            ++kt;
+        }
+        if (kt < nk) ktile(kt, false, false);
+        __syncthreads();   // LDS is free for the next tile
+        // epilogue: C = alpha * acc (+ beta * Y); accumulator r of block
+        // (i, j) is row 32i + 8(r/4) + r%4 + 4(l/32), column 32j + l%32 of the
+        // wave's quarter: a per-lane base plus a uniform offset, so that the
+        // offsets stay scalar; per store, 32 lanes write 32 consecutive floats
+        const int64_t i0 = static_cast<int64_t>(ti) * kBigM + wr * 128 + 4 * (lane >> 5);
+        const int64_t j0 = static_cast<int64_t>(tj) * kBigN + wc * 128 + (lane & 31);
+        float* const ec = e.c + mb * e.sc + i0 * e.ldc + j0;
+        const float* const ey = e.y ? e.y + mb * e.sy + i0 * e.ldy + j0 : nullptr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r >> 2) + (r & 3);
+                float* const crow = ec + row * e.ldc;
+                const float* const yrow = ey ? ey + row * e.ldy : nullptr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = e.alpha * acc[i][j][r];
+                    if (yrow) v = v + e.beta * yrow[32 * j];
+                    crow[32 * j] = v;
+                }
+            }
+    }
+}
+
 // One tile's pieces summed in K order (piece(0) + piece(1) + ... +
 // piece(count - 1), each a 128 x 128 tile of raw sums), then the epilogue and
 // C, for rows 32q .. 32q + 31 of the tile.  Thread t owns columns 4(t%32) ..
@@ -732,11 +913,12 @@ int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t ba
     return need;
 }
 
-// A batch of `batch` products: operand b at A + b*sa and B + b*sb, result and
-// Y at e.c + b*e.sc and e.y + b*e.sy.
-hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B, int64_t ldb,
-                int64_t sb, int64_t M, int64_t N, int64_t K, const Epilogue& e, bool sym,
-                int64_t batch, float* part, int64_t part_bytes, hipStream_t s) {
+// A batch of `batch` products on k_gemm: operand b at A + b*sa and B + b*sb,
+// result and Y at e.c + b*e.sc and e.y + b*e.sy.
+hipError_t gemm_general(bool tn, const float* A, int64_t lda, int64_t sa, const float* B,
+                        int64_t ldb, int64_t sb, int64_t M, int64_t N, int64_t K,
+                        const Epilogue& e, bool sym, int64_t batch, float* part,
+                        int64_t part_bytes, hipStream_t s) {
     Work wk;
     plan_gemm(M, N, K, sym, batch, part ? part_bytes : 0, wk);
     const dim3 grid(wk.per_xcd * kXcds);
@@ -755,6 +937,56 @@ hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B
     else if (wk.units != 0 && (wk.units / wk.kt) % wk.groups != 0)   // pieces of cut tiles to add
         hipLaunchKernelGGL(k_reduce_pieces, dim3(wk.groups * 4), dim3(256), 0, s, part, wk, M, N, e);
     return hipGetLastError();
+}
+
+// A plain row-major product (NT, not symmetric, no diagonal term) whose
+// 256 x 256 tiles fill the GPU in rounds of at least 90%: its main block on
+// k_gemm_big, the strips past the last whole 256 rows and columns on k_gemm.
+bool big_tiles_pay(bool tn, bool sym, const Epilogue& e, const float* A, int64_t lda, int64_t sa,
+                   const float* B, int64_t ldb, int64_t sb, int64_t M, int64_t N, int64_t K,
+                   int64_t batch) {
+    if (tn || sym || e.diag != 0.0f || K < kBigK || K % kBigK != 0) return false;
+    if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(B) % 16 ||
+        lda % 4 || ldb % 4 || sa % 4 || sb % 4)
+        return false;
+    const int64_t tiles = (M / kBigM) * (N / kBigN) * batch;
+    const int64_t rounds = (tiles + kBigGroups - 1) / kBigGroups;
+    return tiles >= kBigGroups && tiles <= static_cast<int64_t>(UINT32_MAX) &&
+           tiles * 10 >= rounds * kBigGroups * 9;
+}
+
+// A batch of `batch` products: operand b at A + b*sa and B + b*sb, result and
+// Y at e.c + b*e.sc and e.y + b*e.sy.
+hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B, int64_t ldb,
+                int64_t sb, int64_t M, int64_t N, int64_t K, const Epilogue& e, bool sym,
+                int64_t batch, float* part, int64_t part_bytes, hipStream_t s) {
+    if (!big_tiles_pay(tn, sym, e, A, lda, sa, B, ldb, sb, M, N, K, batch))
+        return gemm_general(tn, A, lda, sa, B, ldb, sb, M, N, K, e, sym, batch, part, part_bytes,
+                            s);
+    const int64_t mm = M / kBigM * kBigM, nm = N / kBigN * kBigN;
+    const uint32_t tiles_m = static_cast<uint32_t>(mm / kBigM);
+    const uint32_t tiles_n = static_cast<uint32_t>(nm / kBigN);
+    hipLaunchKernelGGL(k_gemm_big, dim3(kBigGroups), dim3(kGemmThreads), 0, s, A, lda, sa, B, ldb,
+                       sb, K, tiles_m, tiles_n, static_cast<uint32_t>(tiles_m * tiles_n * batch),
+                       e);
+    if (hipError_t err = hipGetLastError()) return err;
+    if (mm < M) {   // rows mm .. M-1, every column
+        Epilogue eb = e;
+        eb.c = e.c + mm * e.ldc;
+        eb.y = e.y ? e.y + mm * e.ldy : nullptr;
+        if (hipError_t err = gemm_general(false, A + mm * lda, lda, sa, B, ldb, sb, M - mm, N, K,
+                                          eb, false, batch, part, part_bytes, s))
+            return err;
+    }
+    if (nm < N) {   // rows 0 .. mm-1, columns nm .. N-1
+        Epilogue er = e;
+        er.c = e.c + nm;
+        er.y = e.y ? e.y + nm : nullptr;
+        if (hipError_t err = gemm_general(false, A, lda, sa, B + nm * ldb, ldb, sb, mm, N - nm, K,
+                                          er, false, batch, part, part_bytes, s))
+            return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
