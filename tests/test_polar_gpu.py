@@ -291,6 +291,46 @@ def test_matmul_split_k(form, m, k, sym, epi):
     assert np.array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("m,n,k,batch,epi", [
+    (4096 + 37, 4096 + 64, 80, 1, "plain"),       # main block + both strips
+    (4096 + 37, 4096 + 64, 80, 1, "y_in_place"),  # theta - s P style epilogue
+    (2048, 2048, 512, 4, "plain"),                # a batch filling one round exactly
+    (2048, 2048 + 200, 96, 4, "y_separate"),      # batch, right strip, separate Y
+])
+def test_matmul_large_tiles(m, n, k, batch, epi):
+    """Plain row-major (NT) products with at least 256 tiles of 256 x 256
+    run their main block on the large-tile kernel (one wave per SIMD) and
+    the ragged strips on the general one: every element within the product
+    bound of fp64, the same bits on a second call."""
+    rng = np.random.default_rng(m + n + k + batch)
+    a = rng.standard_normal((batch, m, k)).astype(np.float32)
+    b = rng.standard_normal((batch, n, k)).astype(np.float32)
+    c0 = rng.standard_normal((batch, m, n)).astype(np.float32)
+    y0 = rng.standard_normal((batch, m, n)).astype(np.float32)
+    alpha, beta = (1.0, 0.0) if epi == "plain" else (-0.25, 1.0)
+    a_d, b_d = gpu(a), gpu(b)
+    y_h = None if epi == "plain" else (c0 if epi == "y_in_place" else y0)
+    wsb = dl.dl_matmul_workspace_bytes_batch(m, n, k, False, batch)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV)
+    outs = []
+    for _ in range(2):
+        c_d = gpu(c0)
+        y_d = None if epi == "plain" else (c_d if epi == "y_in_place" else gpu(y0))
+        dl.dl_matmul_f32_batch(dl.DL_NT, a_d, k, m * k, b_d, k, n * k, m, n, k, c_d, n, m * n,
+                               batch, y=y_d, stride_y=m * n if y_d is not None else 0,
+                               alpha=alpha, beta=beta, workspace=ws)
+        outs.append(host(c_d))
+    assert np.array_equal(outs[0], outs[1])
+    for i in range(batch):
+        a64, b64 = a[i].astype(np.float64), b[i].astype(np.float64)
+        want = alpha * (a64 @ b64.T)
+        mag = abs(alpha) * (np.abs(a64) @ np.abs(b64).T)
+        if y_h is not None:
+            want = want + beta * y_h[i].astype(np.float64)
+            mag = mag + abs(beta) * np.abs(y_h[i].astype(np.float64))
+        _bound_check(outs[0][i], want, mag, k)
+
+
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("sym", [False, True], ids=["general", "symmetric"])
 @pytest.mark.parametrize("ws_mode", ["stream", "none"])
@@ -515,9 +555,11 @@ def test_outer_orthogonal_step_batch(m, n, batch):
 
 
 def test_outer_orthogonal_step_batch_full_size():
-    """Three 2048 x 2048 attention updates in one batch against the SVD."""
+    """Four 2048 x 2048 attention updates in one batch against the SVD (the
+    batch's 4 x 64 tiles of 256 x 256 send its next-iterate products to the
+    large-tile kernel)."""
     rows = cols = 2048
-    batch = 3
+    batch = 4
     thetas = [synth.global0(960 + b, rows * cols, device=DEV) for b in range(batch)]
     avgs = [synth.worker_checkpoint(960 + b, 0, 0, t) for b, t in enumerate(thetas)]
     th_h = [host(t).reshape(rows, cols) for t in thetas]
