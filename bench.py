@@ -160,6 +160,9 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
     return out
 
 
+# kind (as the counter summaries name it) of each product kernel
+POLAR_KIND = {"k_gemm_big": "gemm_big", "k_gemm<NT>": "gemm_NT", "k_gemm<TN>": "gemm_TN"}
+
 # kernel kind (as the counter summaries name it) of each side-average call
 SIDE_KERNEL_KIND = {"swa_fold": "fold", "swa_average": "finalize_mean",
                     "snapshot_average_3": "snapshot_mean_3",
@@ -281,7 +284,7 @@ def orthogonalize(args, torch):
     import numpy as np
     from checkpoint_averaging_amd import dlmerge as dl
     from checkpoint_averaging_amd import synth
-    from checkpoint_averaging_amd.orthogonalize import OrthogonalStep, gemm_flops
+    from checkpoint_averaging_amd.orthogonalize import OrthogonalStep, gemm_flops, product_kernel
 
     layout = synth.DIFFUREFILL_1B
     dev = torch.device("cuda")
@@ -346,12 +349,12 @@ def orthogonalize(args, torch):
         out_g = torch.empty(bsz * sg, device=dev)
         if tall:
             cases = [("TN", "gram", (x, c_, sx, x, c_, sx, r, r, L, out_g, r, sg), True, 18),
-                     ("TN", "gram_square", (g, r, sg, g, r, sg, r, r, r, out_g, r, sg), True, 12),
+                     ("NT", "gram_square", (g, r, sg, g, r, sg, r, r, r, out_g, r, sg), True, 12),
                      ("NT", "next_iterate", (x, c_, sx, g, r, sg, L, r, r, out_x, c_, sx), False,
                       18)]
         else:
             cases = [("NT", "gram", (x, c_, sx, x, c_, sx, r, r, L, out_g, r, sg), True, 18),
-                     ("TN", "gram_square", (g, r, sg, g, r, sg, r, r, r, out_g, r, sg), True, 12),
+                     ("NT", "gram_square", (g, r, sg, g, r, sg, r, r, r, out_g, r, sg), True, 12),
                      ("TN", "next_iterate", (g, r, sg, x, c_, sx, r, L, r, out_x, c_, sx), False,
                       18)]
         for form, what, a, sym, per in cases:
@@ -376,14 +379,15 @@ def orthogonalize(args, torch):
             outs = M * (M + 1) // 2 if sym else M * N      # distinct outputs
             fl = 2 * outs * K * bsz
             prods[f"{form} {what} {M}x{N}x{K} batch {bsz} of {r_}x{c_}"] = {
-                "form": form, "symmetric": sym, "batch": bsz, "launches_per_step": per * ngroups,
+                "form": form, "kernel": product_kernel(form, M, N, K, bsz, sym),
+                "symmetric": sym, "batch": bsz, "launches_per_step": per * ngroups,
                 "avg_ms": round(avg, 4), "flops_per_launch": fl,
                 "TFLOP_per_s": round(fl / (avg / 1e3) / 1e12, 2)}
             del ws
         del x, g, out_x, out_g
     kinds = {}
     for p in prods.values():
-        d = kinds.setdefault(p["form"], {"ms": 0.0, "flops": 0, "launches": 0})
+        d = kinds.setdefault(p["kernel"], {"ms": 0.0, "flops": 0, "launches": 0})
         d["ms"] += p["avg_ms"] * p["launches_per_step"]
         d["flops"] += p["flops_per_launch"] * p["launches_per_step"]
         d["launches"] += p["launches_per_step"]
@@ -414,10 +418,10 @@ def orthogonalize(args, torch):
         "frac_of_mfma_f32_peak": round(total_flops / (ms / 1e3) / 1e12 / MFMA_F32_PEAK_TFLOPS, 4),
         "shapes": shapes,
         "products": prods,
-        "roofline": {"kernel": f"k_gemm<{dom}>", "bound": "mfma",
+        "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MFMA_F32_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4),
-                     "traffic": measured_polar_traffic(f"gemm_{dom}",
+                     "traffic": measured_polar_traffic(POLAR_KIND[dom],
                                                        str(args.orth_batch or "even")),
                      "algorithmic_flops_per_launch": dd["flops"] // dd["launches"],
                      "avg_launch_ms": round(dd["ms"] / dd["launches"], 4)},

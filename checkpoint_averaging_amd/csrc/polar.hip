@@ -512,14 +512,17 @@ constexpr int kBigRow = kBigK + 4;                    // LDS row (floats): 16 k 
 constexpr int kBigTile = kBigM * kBigRow;             // one operand tile of one buffer
 constexpr int kBigGroups = 256;                       // one workgroup per CU
 
-// 256 rows x 16 k of a row-major operand: thread t loads rows t/4 + 64p, k
-// 4(t%4) .. +3 (4 float4)
-__device__ __forceinline__ void big_load(const float* __restrict__ P, int64_t ld, int64_t k0,
-                                         int tid, f32x4 (&g)[4]) {
+// 256 rows x 16 k of a row-major operand from P (the tile's first row at
+// its K-tile's first k): thread t loads rows t/4 + 64p, k 4(t%4) .. +3 (4
+// float4).  `off` is the lane's byte offset for p = 0, ((t/4) ld + 4(t%4)) *
+// 4 < 2^32; the row-block start P + 64 p ld is uniform, so each load takes a
+// scalar base and the one 32-bit lane offset.
+__device__ __forceinline__ void big_load(const float* __restrict__ P, int64_t ld, uint32_t off,
+                                         f32x4 (&g)[4]) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-        g[p] = *reinterpret_cast<const f32x4*>(P + ((tid >> 2) + 64 * p) * ld + k0 +
-                                               4 * (tid & 3));
+        g[p] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(P + 64 * p * ld) +
+                                               off);
 }
 __device__ __forceinline__ void big_store(float* S, int tid, const f32x4 (&g)[4]) {
 #pragma unroll
@@ -554,6 +557,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
     const int64_t nk = K / kBigK;
     const uint32_t per_xcd = kBigGroups / kXcds;
     const uint32_t w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const uint32_t offa = static_cast<uint32_t>(((tid >> 2) * lda + 4 * (tid & 3)) * 4);
+    const uint32_t offb = static_cast<uint32_t>(((tid >> 2) * ldb + 4 * (tid & 3)) * 4);
     for (uint32_t t = w; t < tiles; t += kBigGroups) {
         const uint32_t per = tiles_m * tiles_n;
         const uint32_t mb = t / per, tm = t - mb * per;
@@ -568,16 +573,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         f32x4 ga[4], gb[4], a0[4], b0[4], a1[4], b1[4];
-        big_load(Ab, lda, 0, tid, ga);
-        big_load(Bb, ldb, 0, tid, gb);
+        big_load(Ab, lda, offa, ga);
+        big_load(Bb, ldb, offb, gb);
         big_store(smem, tid, ga);
         big_store(smem + kBigTile, tid, gb);
         __syncthreads();
         big_read(smem, wr * 128, lane, 0, a0);
         big_read(smem + kBigTile, wc * 128, lane, 0, b0);
         if (nk > 1) {
-            big_load(Ab, lda, kBigK, tid, ga);
-            big_load(Bb, ldb, kBigK, tid, gb);
+            big_load(Ab + kBigK, lda, offa, ga);
+            big_load(Bb + kBigK, ldb, offb, gb);
         }
         // K-tile kt (in buffer kt % 2, chunk 0 already in a0/b0): store
         // K-tile kt+1 (in ga/gb) to the other buffer, load K-tile kt+2, read
@@ -595,8 +600,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
             }
             big_mma(1, a0, b0, acc);
             if (load_next2) {
-                big_load(Ab, lda, (kt + 2) * kBigK, tid, ga);
-                big_load(Bb, ldb, (kt + 2) * kBigK, tid, gb);
+                big_load(Ab + (kt + 2) * kBigK, lda, offa, ga);
+                big_load(Bb + (kt + 2) * kBigK, ldb, offb, gb);
             }
             big_mma(2, a0, b0, acc);
             big_read(sa_, wr * 128, lane, 1, a1);
@@ -656,20 +661,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
         const int64_t j0 = static_cast<int64_t>(tj) * kBigN + wc * 128 + (lane & 31);
         float* const ec = e.c + mb * e.sc + i0 * e.ldc + j0;
         const float* const ey = e.y ? e.y + mb * e.sy + i0 * e.ldy + j0 : nullptr;
+        // one 32 x 32 block at a time: the empty asm takes the block's 16
+        // sums out of the accumulation registers at that point, so that no
+        // more than one block's worth waits in ordinary registers
+        if (ey) {   // uniform
+            // Y of block b + 1 is loaded before block b is stored (Y is C
+            // itself or apart from it, so every element's Y is read before
+            // its C is written), which keeps 16 loads in flight
+            float yv[2][16];
+            auto load_y = [&](int b, float (&y)[16]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+                for (int r = 0; r < 16; ++r)
+                    y[r] = ey[(32 * (b >> 2) + 8 * (r >> 2) + (r & 3)) * e.ldy + 32 * (b & 3)];
+            };
+            load_y(0, yv[0]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r >> 2) + (r & 3);
-                float* const crow = ec + row * e.ldc;
-                const float* const yrow = ey ? ey + row * e.ldy : nullptr;
+            for (int b = 0; b < 16; ++b) {
+                if (b + 1 < 16) load_y(b + 1, yv[(b + 1) & 1]);
+                f32x16 v = acc[b >> 2][b & 3];
+                asm volatile("" : "+v"(v));
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    ec[(32 * (b >> 2) + 8 * (r >> 2) + (r & 3)) * e.ldc + 32 * (b & 3)] =
+                        e.alpha * v[r] + e.beta * yv[b & 1][r];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float v = e.alpha * acc[i][j][r];
-                    if (yrow) v = v + e.beta * yrow[32 * j];
-                    crow[32 * j] = v;
+                    f32x16 v = acc[i][j];
+                    asm volatile("" : "+v"(v));
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        ec[(32 * i + 8 * (r >> 2) + (r & 3)) * e.ldc + 32 * j] = e.alpha * v[r];
                 }
-            }
+        }
     }
 }
 
@@ -949,6 +976,7 @@ bool big_tiles_pay(bool tn, bool sym, const Epilogue& e, const float* A, int64_t
     if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(B) % 16 ||
         lda % 4 || ldb % 4 || sa % 4 || sb % 4)
         return false;
+    if (lda >= (int64_t{1} << 24) || ldb >= (int64_t{1} << 24)) return false;   // 32-bit lane offsets
     const int64_t tiles = (M / kBigM) * (N / kBigN) * batch;
     const int64_t rounds = (tiles + kBigGroups - 1) / kBigGroups;
     return tiles >= kBigGroups && tiles <= static_cast<int64_t>(UINT32_MAX) &&
@@ -1103,11 +1131,12 @@ hipError_t polar_iterate(const float* const* src, const float* const* sub, float
                  : gemm(false, x, cols, sp.sx, x, cols, sp.sx, r, r, cols, eg, true, batch,
                         sp.part, sp.part_bytes, s);                                   // X X^T
         if (err) return err;
-        if (quin) {   // M = c G^2 + b G + a I  (G symmetric: G G = G^T G)
+        if (quin) {   // M = c G^2 + b G + a I  (G exactly symmetric: G G = G G^T, so the
+                      // row-major (NT) path, the faster one, applies)
             Epilogue em{sp.m, r, sp.g, r, kQc, kQb, kQa};
             em.sc = sp.sg;
             em.sy = sp.sg;
-            if ((err = gemm(true, sp.g, r, sp.sg, sp.g, r, sp.sg, r, r, r, em, true, batch,
+            if ((err = gemm(false, sp.g, r, sp.sg, sp.g, r, sp.sg, r, r, r, em, true, batch,
                             sp.part, sp.part_bytes, s)))
                 return err;
         }

@@ -66,13 +66,14 @@ def gemm_flops(rows: int, cols: int, quintic: int = 12, cubic: int = 6):
     outputs of 2 L flops each; per quintic step its square, also symmetric
     (r (r + 1) / 2 outputs of 2 r flops); per step the next iterate (2 L r^2).
     Tall matrices run the Gram product as TN and the next iterate as NT; wide
-    ones the other way round; the square is TN."""
+    ones the other way round; the square (of an exactly symmetric matrix, so
+    G G = G G^T) is NT."""
     r, L = min(rows, cols), max(rows, cols)
     sym = r * (r + 1) // 2
     gram, square, nxt = 2 * sym * L, 2 * sym * r, 2 * L * r * r
     steps = quintic + cubic
-    tn = (gram * steps if rows >= cols else nxt * steps) + square * quintic
-    nt = (nxt * steps if rows >= cols else gram * steps)
+    tn = (gram * steps if rows >= cols else nxt * steps)
+    nt = (nxt * steps if rows >= cols else gram * steps) + square * quintic
     return {"TN": tn, "NT": nt}
 
 
@@ -85,6 +86,22 @@ def batch_sizes(count: int, batch: Optional[int] = None) -> List[int]:
         return [min(batch, count - c) for c in range(0, count, batch)]
     n = math.ceil(count / dl.DL_MAX_BATCH)
     return [count // n + (1 if i < count % n else 0) for i in range(n)]
+
+
+def product_kernel(form: str, m: int, n: int, k: int, batch: int, symmetric: bool,
+                   diag: float = 0.0) -> str:
+    """The kernel a product's main block runs on (the rule the library's
+    dispatch applies, given aligned operands): plain row-major (NT) products,
+    not symmetric and without a diagonal term, with K a multiple of 16 and at
+    least 256 tiles of 256 x 256 filling their rounds to 90% or more, go to
+    the large-tile kernel (their ragged strips to the general one);
+    everything else to the general kernel of its form."""
+    if form == "NT" and not symmetric and diag == 0.0 and k >= 16 and k % 16 == 0:
+        tiles = (m // 256) * (n // 256) * batch
+        rounds = -(-tiles // 256)
+        if tiles >= 256 and tiles * 10 >= rounds * 256 * 9:
+            return "k_gemm_big"
+    return f"k_gemm<{form}>"
 
 
 class OrthogonalStep:

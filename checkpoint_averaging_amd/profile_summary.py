@@ -122,6 +122,8 @@ def polar_kind(name: str):
         return "gemm_TN"
     if "k_gemm<false>" in name:
         return "gemm_NT"
+    if "k_gemm_big(" in name:
+        return "gemm_big"
     for k in ("k_reduce_pieces", "k_reduce_splits", "k_sumsq_partial", "k_sumsq_final", "k_scale",
               "k_step"):
         if f"::{k}(" in name or name.startswith(k + "("):

@@ -408,7 +408,8 @@ int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t
 
 /*
  * A batch of 1 <= batch <= DL_MAX_BATCH such products in one launch: matrix
- * b reads a + b*stride_a, b + b*stride_b (and y + b*stride_y) and writes
+ * b reads a + b*stride_a, b + b*stride_b (and y + b*stride_y, which is
+ * either that matrix's own result or overlaps no result) and writes
  * c + b*stride_c (strides in elements, >= 0; the results must not overlap:
  * stride_c covers one result).  The workspace is that of
  * dl_matmul_workspace_bytes_batch; dl_matmul_f32 is the batch of one.

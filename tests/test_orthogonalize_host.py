@@ -82,13 +82,28 @@ def test_flops_square_and_rectangular():
     f = gemm_flops(r, r)
     sym = r * (r + 1) // 2
     # per step: the Gram product (TN) and the next iterate (NT); per quintic
-    # step also the square of the Gram matrix (TN); symmetric products at
+    # step also the square of the Gram matrix (NT); symmetric products at
     # their distinct outputs
-    assert f["TN"] == 18 * 2 * sym * r + 12 * 2 * sym * r
-    assert f["NT"] == 18 * 2 * r ** 3
+    assert f["TN"] == 18 * 2 * sym * r
+    assert f["NT"] == 18 * 2 * r ** 3 + 12 * 2 * sym * r
     tall, wide = gemm_flops(5632, 2048), gemm_flops(2048, 5632)
     assert tall["TN"] + tall["NT"] == wide["TN"] + wide["NT"]   # the same work, transposed
     # the whole DiffuRefill-1B step
     total = sum(sum(gemm_flops(m.rows, m.cols).values())
                 for m in weight_matrices(synth.DIFFUREFILL_1B))
     assert total == 132103250509824
+
+
+def test_product_kernel_rule():
+    from checkpoint_averaging_amd.orthogonalize import product_kernel
+    # the step's next-iterate products (tall: X M as NT) fill their rounds
+    assert product_kernel("NT", 2048, 2048, 2048, 36, False) == "k_gemm_big"   # 2304 tiles
+    assert product_kernel("NT", 5632, 2048, 2048, 36, False) == "k_gemm_big"   # 6336 tiles
+    assert product_kernel("NT", 73760, 2048, 2048, 1, False) == "k_gemm_big"   # 2304 + strip
+    # symmetric, k-major, a diagonal term, too few tiles, a partly filled round, K % 16
+    assert product_kernel("NT", 2048, 2048, 5632, 18, True) == "k_gemm<NT>"
+    assert product_kernel("TN", 2048, 5632, 2048, 18, False) == "k_gemm<TN>"
+    assert product_kernel("NT", 2048, 2048, 2048, 36, False, diag=1.5) == "k_gemm<NT>"
+    assert product_kernel("NT", 2048, 2048, 2048, 3, False) == "k_gemm<NT>"      # 192 tiles
+    assert product_kernel("NT", 2048, 2048, 2048, 5, False) == "k_gemm<NT>"      # 320: 62%
+    assert product_kernel("NT", 2048, 2048, 2040, 36, False) == "k_gemm<NT>"
