@@ -161,7 +161,8 @@ def cpu_baseline(w, torch, max_seconds: float = 12.0):
 
 
 # kind (as the counter summaries name it) of each product kernel
-POLAR_KIND = {"k_gemm_big": "gemm_big", "k_gemm<NT>": "gemm_NT", "k_gemm<TN>": "gemm_TN"}
+POLAR_KIND = {"k_gemm_big<NT>": "gemm_big_NT", "k_gemm_big<TN>": "gemm_big_TN",
+              "k_gemm<NT>": "gemm_NT", "k_gemm<TN>": "gemm_TN"}
 
 # kernel kind (as the counter summaries name it) of each side-average call
 SIDE_KERNEL_KIND = {"swa_fold": "fold", "swa_average": "finalize_mean",

@@ -477,6 +477,19 @@ int dl_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int symmetric, in
     return dl_matmul_workspace_bytes_batch(m, n, k, symmetric, 1, bytes);
 }
 
+int dl_matmul_large_tiles(int64_t m, int64_t n, int64_t k, int symmetric, int batch,
+                          int64_t workspace_bytes, int* large) {
+    int64_t unused = 0;
+    if (large == nullptr || workspace_bytes < 0) return DL_E_INVAL;
+    if (const int rc = dl_matmul_workspace_bytes_batch(m, n, k, symmetric, batch, &unused))
+        return rc;
+    *large = (m > 0 && n > 0 &&
+              dlk::matmul_large_tiles(m, n, k, symmetric != 0, batch, workspace_bytes))
+                 ? 1
+                 : 0;
+    return DL_OK;
+}
+
 int dl_matmul_f32_batch(int form, const float* a, int64_t lda, int64_t stride_a, const float* b,
                         int64_t ldb, int64_t stride_b, int64_t m, int64_t n, int64_t k, float* c,
                         int64_t ldc, int64_t stride_c, const float* y, int64_t stride_y,

@@ -30,6 +30,12 @@ hipError_t polar_iterate(const float* const* src, const float* const* sub, float
 // (partial sums of the tiles cut between workgroups).
 int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch);
 
+// Whether the main block of such a batch runs on the large-tile kernel when
+// its operands are 16-byte aligned and contiguous (leading dimension K) and
+// the workspace holds ws_bytes.
+bool matmul_large_tiles(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch,
+                        int64_t ws_bytes);
+
 // A batch of fp32 MFMA products, matrix b: C_b = alpha * op(A_b, B_b) + beta
 // * Y_b + diag * I with A_b = A + b*sa, B_b = B + b*sb, C_b = C + b*sc, Y_b =
 // Y + b*sy (Y may be null or equal C):  tn: sum_k A[k*lda + i] * B[k*ldb + j];

@@ -40,6 +40,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "polar.h"
 
 namespace dlk {
@@ -492,42 +495,99 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const float* __restrict__
     }
 }
 
-// ---- large-tile kernel for plain row-major products -----------------------
+// ---- large-tile kernel ------------------------------------------------------
 //
-// C = alpha * A B^T (+ beta * Y) for row-major A (M x K) and B (N x K), with
-// M and N multiples of 256 and K of 16 (the main block of a product; the
-// rest goes to k_gemm).  One workgroup per CU (4 waves, one per SIMD), each
-// wave a 128 x 128 quarter of a 256 x 256 tile as 4 x 4 MFMA blocks of 32 x
-// 32 whose sums fill the 256 accumulation registers.  With one wave per
-// SIMD the latency is hidden inside the wave: K-tiles of 16 in two LDS
-// buffers; the operands of a K-tile come in two halves of 4 k-steps (k = 8h
-// + 4c + e for lane half h, chunk c), the second half read while the first
-// runs and the next K-tile's first half read while the second runs; the next
-// K-tile's LDS stores, the loads of the one after and the operand reads are
-// spread among the MFMAs, one per two, by scheduling barriers; one
-// barrier per K-tile.  Workgroups take tiles in rounds, the 32 of an XCD on
-// consecutive tiles (sharing operand rows in L2).
+// C = alpha * sum + beta * Y (+ diag where i == j) over the main block of a
+// product: M and N multiples of 256, K of 16.  Row-major operands (NT: A is
+// M x K, B is N x K) or k-major ones (TN: A is K x M, B is K x N; each 4 x 4
+// piece transposed in registers on its way to LDS), LDS holding [row][k]
+// either way.  One workgroup per CU (4 waves, one per SIMD), each wave a 128
+// x 128 quarter of a 256 x 256 tile as 4 x 4 MFMA blocks of 32 x 32 whose
+// sums fill the 256 accumulation registers.  With one wave per SIMD the
+// latency is hidden inside the wave: K-tiles of 16 in two LDS buffers; the
+// operands of a K-tile come in two halves of 4 k-steps (k = 8h + 4c + e for
+// lane half h, chunk c), the second half read while the first runs and the
+// next K-tile's first half read while the second runs; the next K-tile's
+// LDS stores, the loads of the one after and the operand reads are spread
+// among the MFMAs, one per two, by scheduling barriers; one barrier per
+// K-tile.  A symmetric result has only its upper tiles computed: an
+// off-diagonal tile is written and mirrored, a diagonal one writes its
+// elements with i <= j and mirrors those with i < j.
+//
+// Work items are dealt in rounds, the 32 workgroups of an XCD on
+// consecutive items (sharing operand rows in L2): first the whole tiles 0 ..
+// dp - 1, then the last `tail` tiles in `ksplit` pieces of K each, dealt
+// piece by piece (the workgroups running together work on the same K range
+// of neighbouring tiles).  A piece's raw sums go to the partial buffer, and
+// k_reduce_big adds each tail tile's pieces in K order before the epilogue.
 constexpr int kBigM = 256, kBigN = 256, kBigK = 16;
 constexpr int kBigRow = kBigK + 4;                    // LDS row (floats): 16 k + 4 padding
 constexpr int kBigTile = kBigM * kBigRow;             // one operand tile of one buffer
 constexpr int kBigGroups = 256;                       // one workgroup per CU
+constexpr int64_t kBigElems = kBigM * kBigN;          // one tile's sums (a piece)
 
-// 256 rows x 16 k of a row-major operand from P (the tile's first row at
-// its K-tile's first k): thread t loads rows t/4 + 64p, k 4(t%4) .. +3 (4
-// float4).  `off` is the lane's byte offset for p = 0, ((t/4) ld + 4(t%4)) *
-// 4 < 2^32; the row-block start P + 64 p ld is uniform, so each load takes a
+struct BigWork {
+    uint32_t tiles_n;    // tiles along N (and along M when symmetric)
+    uint32_t tiles_per;  // tiles per matrix of the batch: the grid or its upper triangle
+    uint32_t dp;         // tiles 0 .. dp - 1: whole
+    uint32_t tail;       // tiles dp .. dp + tail - 1: in ksplit pieces each
+    uint32_t ksplit;     // pieces per tail tile
+    uint32_t kspan;      // K-tiles per piece (the last piece: the rest)
+    uint32_t nk;         // K-tiles of a tile
+    bool sym;
+};
+
+// tile t -> matrix mb of the batch, tile row ti, tile column tj (row-major
+// over the grid, or over the upper triangle, whose row r starts at
+// r n - r (r - 1) / 2)
+__device__ __forceinline__ void big_coords(uint32_t t, const BigWork& wk, uint32_t& mb,
+                                           uint32_t& ti, uint32_t& tj) {
+    mb = t / wk.tiles_per;
+    const uint32_t u = t - mb * wk.tiles_per, n = wk.tiles_n;
+    if (!wk.sym) {
+        ti = u / n;
+        tj = u - ti * n;
+        return;
+    }
+    uint32_t r = 0;
+    while (r + 1 < n && (r + 1) * n - ((r + 1) * r) / 2 <= u) ++r;
+    ti = r;
+    tj = u - (r * n - (r * (r - 1)) / 2) + r;
+}
+
+// One K-tile of an operand, from P (row-major: the tile's first row at the
+// K-tile's first k; k-major: the K-tile's first k at the tile's first
+// column).  Row-major: thread t loads rows t/4 + 64p, k 4(t%4) .. +3;
+// k-major: k 4(t%4) + p, columns 4(t/4) .. +3.  `off` is the lane's byte
+// offset (below 2^32); P plus the p term is uniform, so each load takes a
 // scalar base and the one 32-bit lane offset.
+template <bool KM>
+__device__ __forceinline__ uint32_t big_offset(int64_t ld, int tid) {
+    return KM ? static_cast<uint32_t>((4 * (tid & 3) * ld + 4 * (tid >> 2)) * 4)
+              : static_cast<uint32_t>(((tid >> 2) * ld + 4 * (tid & 3)) * 4);
+}
+template <bool KM>
 __device__ __forceinline__ void big_load(const float* __restrict__ P, int64_t ld, uint32_t off,
                                          f32x4 (&g)[4]) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-        g[p] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(P + 64 * p * ld) +
-                                               off);
+        g[p] = *reinterpret_cast<const f32x4*>(
+            reinterpret_cast<const char*>(P + (KM ? p : 64 * p) * ld) + off);
 }
+// to LDS as [row][k]: row-major, row t/4 + 64p gets load p; k-major, row
+// 4(t/4) + p gets element p of the four loads (k 4(t%4) .. +3)
+template <bool KM>
 __device__ __forceinline__ void big_store(float* S, int tid, const f32x4 (&g)[4]) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        *reinterpret_cast<f32x4*>(S + ((tid >> 2) + 64 * p) * kBigRow + 4 * (tid & 3)) = g[p];
+    for (int p = 0; p < 4; ++p) {
+        if (KM) {
+            const f32x4 v = {g[0][p], g[1][p], g[2][p], g[3][p]};
+            *reinterpret_cast<f32x4*>(S + (4 * (tid >> 2) + p) * kBigRow + 4 * (tid & 3)) = v;
+        } else {
+            *reinterpret_cast<f32x4*>(S + ((tid >> 2) + 64 * p) * kBigRow + 4 * (tid & 3)) =
+                g[p];
+        }
+    }
 }
 // chunk c of this lane's operand rows base + 32 i + l%32 (i < 4)
 __device__ __forceinline__ void big_read(const float* S, int base, int lane, int c,
@@ -547,24 +607,45 @@ __device__ __forceinline__ void big_mma(int e, const f32x4 (&a)[4], const f32x4 
                                                              0);
 }
 
+// f(integral_constant<int, b>) for the 16 MFMA blocks b of a wave's quarter,
+// so that every accumulator index is a constant
+template <class F, int... Bs>
+__device__ __forceinline__ void each_block_(F&& f, std::integer_sequence<int, Bs...>) {
+    (f(std::integral_constant<int, Bs>{}), ...);
+}
+template <class F>
+__device__ __forceinline__ void each_block(F&& f) {
+    each_block_(f, std::make_integer_sequence<int, 16>{});
+}
+
+template <bool KM>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
     const float* __restrict__ A, int64_t lda, int64_t sa, const float* __restrict__ B,
-    int64_t ldb, int64_t sb, int64_t K, uint32_t tiles_m, uint32_t tiles_n, uint32_t tiles,
-    Epilogue e) {
+    int64_t ldb, int64_t sb, BigWork wk, Epilogue e, float* __restrict__ part) {
     __shared__ __align__(16) float smem[4 * kBigTile];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
-    const int64_t nk = K / kBigK;
     const uint32_t per_xcd = kBigGroups / kXcds;
     const uint32_t w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    const uint32_t offa = static_cast<uint32_t>(((tid >> 2) * lda + 4 * (tid & 3)) * 4);
-    const uint32_t offb = static_cast<uint32_t>(((tid >> 2) * ldb + 4 * (tid & 3)) * 4);
-    for (uint32_t t = w; t < tiles; t += kBigGroups) {
-        const uint32_t per = tiles_m * tiles_n;
-        const uint32_t mb = t / per, tm = t - mb * per;
-        const uint32_t ti = tm / tiles_n, tj = tm - ti * tiles_n;
-        const float* Ab = A + mb * sa + static_cast<int64_t>(ti) * kBigM * lda;
-        const float* Bb = B + mb * sb + static_cast<int64_t>(tj) * kBigN * ldb;
+    const uint32_t offa = big_offset<KM>(lda, tid), offb = big_offset<KM>(ldb, tid);
+    const int64_t stepa = KM ? kBigK * lda : kBigK;   // one K-tile further
+    const int64_t stepb = KM ? kBigK * ldb : kBigK;
+    const uint32_t items = wk.dp + wk.tail * wk.ksplit;
+    for (uint32_t it = w; it < items; it += kBigGroups) {
+        uint32_t t = it, k0 = 0, nk = wk.nk;
+        int64_t slot = -1;   // a piece's partial slot (uniform)
+        if (it >= wk.dp) {
+            const uint32_t v = it - wk.dp, seg = v / wk.tail;
+            t = wk.dp + (v - seg * wk.tail);
+            k0 = seg * wk.kspan;
+            nk = wk.nk - k0 < wk.kspan ? wk.nk - k0 : wk.kspan;
+            slot = v;
+        }
+        uint32_t mb, ti, tj;
+        big_coords(t, wk, mb, ti, tj);
+        const int64_t ri = static_cast<int64_t>(ti) * kBigM, rj = static_cast<int64_t>(tj) * kBigN;
+        const float* Ab = A + mb * sa + k0 * stepa + (KM ? ri : ri * lda);
+        const float* Bb = B + mb * sb + k0 * stepb + (KM ? rj : rj * ldb);
         f32x16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -573,16 +654,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
         f32x4 ga[4], gb[4], a0[4], b0[4], a1[4], b1[4];
-        big_load(Ab, lda, offa, ga);
-        big_load(Bb, ldb, offb, gb);
-        big_store(smem, tid, ga);
-        big_store(smem + kBigTile, tid, gb);
+        big_load<KM>(Ab, lda, offa, ga);
+        big_load<KM>(Bb, ldb, offb, gb);
+        big_store<KM>(smem, tid, ga);
+        big_store<KM>(smem + kBigTile, tid, gb);
         __syncthreads();
         big_read(smem, wr * 128, lane, 0, a0);
         big_read(smem + kBigTile, wc * 128, lane, 0, b0);
         if (nk > 1) {
-            big_load(Ab + kBigK, lda, offa, ga);
-            big_load(Bb + kBigK, ldb, offb, gb);
+            big_load<KM>(Ab + stepa, lda, offa, ga);
+            big_load<KM>(Bb + stepb, ldb, offb, gb);
         }
         // K-tile kt (in buffer kt % 2, chunk 0 already in a0/b0): store
         // K-tile kt+1 (in ga/gb) to the other buffer, load K-tile kt+2, read
@@ -595,13 +676,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
             float* nb = na + kBigTile;
             big_mma(0, a0, b0, acc);
             if (store_next) {
-                big_store(na, tid, ga);
-                big_store(nb, tid, gb);
+                big_store<KM>(na, tid, ga);
+                big_store<KM>(nb, tid, gb);
             }
             big_mma(1, a0, b0, acc);
             if (load_next2) {
-                big_load(Ab + (kt + 2) * kBigK, lda, offa, ga);
-                big_load(Bb + (kt + 2) * kBigK, ldb, offb, gb);
+                big_load<KM>(Ab + (kt + 2) * stepa, lda, offa, ga);
+                big_load<KM>(Bb + (kt + 2) * stepb, ldb, offb, gb);
             }
             big_mma(2, a0, b0, acc);
             big_read(sa_, wr * 128, lane, 1, a1);
@@ -652,51 +733,89 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_big(
             ++kt;
         }
         if (kt < nk) ktile(kt, false, false);
-        __syncthreads();   // LDS is free for the next tile
-        // epilogue: C = alpha * acc (+ beta * Y); accumulator r of block
-        // (i, j) is row 32i + 8(r/4) + r%4 + 4(l/32), column 32j + l%32 of the
-        // wave's quarter: a per-lane base plus a uniform offset, so that the
-        // offsets stay scalar; per store, 32 lanes write 32 consecutive floats
-        const int64_t i0 = static_cast<int64_t>(ti) * kBigM + wr * 128 + 4 * (lane >> 5);
-        const int64_t j0 = static_cast<int64_t>(tj) * kBigN + wc * 128 + (lane & 31);
-        float* const ec = e.c + mb * e.sc + i0 * e.ldc + j0;
-        const float* const ey = e.y ? e.y + mb * e.sy + i0 * e.ldy + j0 : nullptr;
-        // one 32 x 32 block at a time: the empty asm takes the block's 16
-        // sums out of the accumulation registers at that point, so that no
-        // more than one block's worth waits in ordinary registers
-        if (ey) {   // uniform
-            // Y of block b + 1 is loaded before block b is stored (Y is C
-            // itself or apart from it, so every element's Y is read before
-            // its C is written), which keeps 16 loads in flight
-            float yv[2][16];
-            auto load_y = [&](int b, float (&y)[16]) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    y[r] = ey[(32 * (b >> 2) + 8 * (r >> 2) + (r & 3)) * e.ldy + 32 * (b & 3)];
-            };
-            load_y(0, yv[0]);
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                if (b + 1 < 16) load_y(b + 1, yv[(b + 1) & 1]);
+        __syncthreads();   // LDS is free for the next item
+        // accumulator r of block (i, j) is row 32i + 8(r/4) + r%4 + 4(l/32),
+        // column 32j + l%32 of the wave's quarter: a per-lane base plus a
+        // uniform offset.  Blocks leave the accumulation registers one at a
+        // time (the empty asm pins the move there; moved all at once, they
+        // would not fit beside the rest).
+        const int hr = 4 * (lane >> 5), cc = lane & 31;
+        if (slot >= 0) {   // a piece: raw sums, 256 x 256 row-major
+            float* const pp = part + slot * kBigElems + (wr * 128 + hr) * kBigN + wc * 128 + cc;
+            each_block([&](auto bk) {
+                constexpr int b = decltype(bk)::value;
                 f32x16 v = acc[b >> 2][b & 3];
                 asm volatile("" : "+v"(v));
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    ec[(32 * (b >> 2) + 8 * (r >> 2) + (r & 3)) * e.ldc + 32 * (b & 3)] =
-                        e.alpha * v[r] + e.beta * yv[b & 1][r];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x16 v = acc[i][j];
-                    asm volatile("" : "+v"(v));
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        ec[(32 * i + 8 * (r >> 2) + (r & 3)) * e.ldc + 32 * j] = e.alpha * v[r];
-                }
+                    pp[(32 * (b >> 2) + 8 * (r >> 2) + (r & 3)) * kBigN + 32 * (b & 3)] = v[r];
+            });
+            continue;
         }
+        const int64_t i0 = ri + wr * 128 + hr, j0 = rj + wc * 128 + cc;
+        float* const ec = e.c + mb * e.sc + i0 * e.ldc + j0;
+        float* const em = e.c + mb * e.sc + j0 * e.ldc + i0;   // mirror: C[j][i]
+        const float* const ey = e.y ? e.y + mb * e.sy + i0 * e.ldy + j0 : nullptr;
+        // block b of the quarter, at block row 4 wr + b/4 and column 4 wc +
+        // b%4 of the tile: 0 nothing, 1 written, 2 written and mirrored,
+        // 3 a diagonal block of a symmetric result (element-wise)
+        auto mode = [&](int b) {
+            const int bi = 4 * wr + (b >> 2), bj = 4 * wc + (b & 3);
+            if (!wk.sym) return 1;
+            if (ti != tj) return 2;
+            return bi < bj ? 2 : (bi == bj ? 3 : 0);
+        };
+        auto on_diag = [&](int b) { return ti == tj && 4 * wr + (b >> 2) == 4 * wc + (b & 3); };
+        // Y of block b + 1 is loaded before block b is stored (Y is C itself
+        // or apart from it, so every element's Y is read before its C is
+        // written), which keeps 16 loads in flight
+        float yv[2][16];
+        auto load_y = [&](int b, float (&y)[16]) {
+            if (!ey || mode(b) == 0) return;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                y[r] = ey[(32 * (b >> 2) + 8 * (r >> 2) + (r & 3)) * e.ldy + 32 * (b & 3)];
+        };
+        load_y(0, yv[0]);
+        each_block([&](auto bk) {
+            constexpr int b = decltype(bk)::value;
+            if (b + 1 < 16) load_y(b + 1, yv[(b + 1) & 1]);
+            const int md = mode(b);
+            if (md == 0) return;
+            f32x16 v = acc[b >> 2][b & 3];
+            asm volatile("" : "+v"(v));
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                x[r] = e.alpha * v[r];
+                if (ey) x[r] = x[r] + e.beta * yv[b & 1][r];
+            }
+            const int64_t bo = 32 * (b >> 2), bc = 32 * (b & 3);   // block row, column
+            if (on_diag(b)) {
+                // element r sits on row hr + 8(r/4) + r%4 and column cc of
+                // the block: i - j = that row - cc
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int d = hr + 8 * (r >> 2) + (r & 3) - cc;
+                    if (d == 0) x[r] = x[r] + e.diag;
+                    const int64_t o = (bo + 8 * (r >> 2) + (r & 3)) * e.ldc + bc;
+                    if (md != 3 || d <= 0) ec[o] = x[r];
+                    if (md == 3 && d < 0) em[bc * e.ldc + bo + 8 * (r >> 2) + (r & 3)] = x[r];
+                }
+                if (md == 3) return;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    ec[(bo + 8 * (r >> 2) + (r & 3)) * e.ldc + bc] = x[r];
+            }
+            if (md == 2) {   // rows 8g .. 8g + 3 (plus the lane's 4) of column bc: one float4
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 m4 = {x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+                    *reinterpret_cast<f32x4*>(em + bc * e.ldc + bo + 8 * g) = m4;
+                }
+            }
+        });
     }
 }
 
@@ -792,6 +911,58 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__
         return part + (static_cast<int64_t>(r) * wk.tiles + t) * kTileElems;
     };
     reduce_tile_rows(piece, wk.ksplit, t, q, wk, M, N, e);
+}
+
+// The tail tiles of the large-tile kernel: tile dp + tt's ksplit pieces
+// (slots s * tail + tt) summed in K order (piece 0 + piece 1 + ...), then
+// the epilogue, for rows 32q .. 32q + 31 of the tile (workgroup 8 tt + q).
+// Thread t owns columns 4(t%64) .. +3 of rows t/64 + 4p.  A symmetric result
+// is mirrored as in the large-tile kernel, through LDS (rows of 32
+// consecutive i per store).
+__global__ __launch_bounds__(256) void k_reduce_big(const float* __restrict__ part, BigWork wk,
+                                                    Epilogue e) {
+    __shared__ float tr[kBigN][33];
+    const uint32_t tt = blockIdx.x >> 3;
+    const int q = static_cast<int>(blockIdx.x & 7);
+    if (tt >= wk.tail) return;
+    uint32_t mb, ti, tj;
+    big_coords(wk.dp + tt, wk, mb, ti, tj);
+    const int tid = threadIdx.x, lj = 4 * (tid & 63);
+    const bool dtile = wk.sym && ti == tj;
+    float* const c = e.c + mb * e.sc;
+    const float* const y = e.y ? e.y + mb * e.sy : nullptr;
+    const int64_t ri = static_cast<int64_t>(ti) * kBigM, rj = static_cast<int64_t>(tj) * kBigN;
+#pragma unroll 2
+    for (int p = 0; p < 8; ++p) {
+        const int li = 32 * q + (tid >> 6) + 4 * p;   // row within the tile
+        const int64_t off = static_cast<int64_t>(li) * kBigN + lj;
+        f32x4 v = *reinterpret_cast<const f32x4*>(part + tt * kBigElems + off);
+        for (uint32_t s = 1; s < wk.ksplit; ++s) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(
+                part + (static_cast<int64_t>(s) * wk.tail + tt) * kBigElems + off);
+            v = v + x;
+        }
+        const int64_t gi = ri + li;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int64_t gj = rj + lj + x;
+            float o = e.alpha * v[x];
+            if (y) o = o + e.beta * y[gi * e.ldy + gj];
+            if (gi == gj) o = o + e.diag;
+            if (!dtile || gi <= gj) c[gi * e.ldc + gj] = o;
+            if (wk.sym) tr[lj + x][li - 32 * q] = o;
+        }
+    }
+    if (wk.sym) {   // uniform: C[j][i] for the strip's (i, j), 32 consecutive i per row
+        __syncthreads();
+#pragma unroll 4
+        for (int p = 0; p < 32; ++p) {
+            const int idx = p * 256 + tid;
+            const int mr = idx >> 5, mc = idx & 31;
+            const int64_t gi = ri + 32 * q + mc, gj = rj + mr;
+            if (!dtile || gi < gj) c[gj * e.ldc + gi] = tr[mr][mc];
+        }
+    }
 }
 
 // ---- Frobenius norm (two-stage fp64 reduction, fixed order) ---------------
@@ -932,13 +1103,6 @@ void plan_gemm(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch, int64_t
     if (need_bytes) *need_bytes = need;
 }
 
-// Partial-buffer bytes of the preferred split of a batch of products.
-int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch = 1) {
-    Work wk;
-    int64_t need = 0;
-    plan_gemm(M, N, K, sym, batch, INT64_MAX, wk, &need);
-    return need;
-}
 
 // A batch of `batch` products on k_gemm: operand b at A + b*sa and B + b*sb,
 // result and Y at e.c + b*e.sc and e.y + b*e.sy.
@@ -966,52 +1130,127 @@ hipError_t gemm_general(bool tn, const float* A, int64_t lda, int64_t sa, const 
     return hipGetLastError();
 }
 
-// A plain row-major product (NT, not symmetric, no diagonal term) whose
-// 256 x 256 tiles fill the GPU in rounds of at least 90%: its main block on
-// k_gemm_big, the strips past the last whole 256 rows and columns on k_gemm.
-bool big_tiles_pay(bool tn, bool sym, const Epilogue& e, const float* A, int64_t lda, int64_t sa,
-                   const float* B, int64_t ldb, int64_t sb, int64_t M, int64_t N, int64_t K,
-                   int64_t batch) {
-    if (tn || sym || e.diag != 0.0f || K < kBigK || K % kBigK != 0) return false;
+// Whether a product's main block can run on k_gemm_big: K a multiple of 16,
+// 16-byte aligned operand rows (and batch strides) with leading dimensions
+// below 2^24 (32-bit lane offsets); a symmetric result square with M a
+// multiple of 256 (no ragged strips) and 16-byte aligned rows (mirrored
+// float4 stores).
+bool big_fits(bool sym, const Epilogue& e, const float* A, int64_t lda, int64_t sa,
+              const float* B, int64_t ldb, int64_t sb, int64_t M, int64_t N, int64_t K) {
+    if (K < kBigK || K % kBigK != 0 || M < kBigM || N < kBigN) return false;
     if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(B) % 16 ||
         lda % 4 || ldb % 4 || sa % 4 || sb % 4)
         return false;
-    if (lda >= (int64_t{1} << 24) || ldb >= (int64_t{1} << 24)) return false;   // 32-bit lane offsets
-    const int64_t tiles = (M / kBigM) * (N / kBigN) * batch;
-    const int64_t rounds = (tiles + kBigGroups - 1) / kBigGroups;
-    return tiles >= kBigGroups && tiles <= static_cast<int64_t>(UINT32_MAX) &&
-           tiles * 10 >= rounds * kBigGroups * 9;
+    if (lda >= (int64_t{1} << 24) || ldb >= (int64_t{1} << 24)) return false;
+    if (sym && (M != N || M % kBigM != 0 || reinterpret_cast<uintptr_t>(e.c) % 16 ||
+                e.ldc % 4 || e.sc % 4))
+        return false;
+    return true;
+}
+
+// Time model of the large-tile kernel: a tile of K takes 2 * 256^2 * K
+// flops at a 256th of 145 TFLOP/s on its CU; each piece of a split tile adds
+// its partial sums written and read back (512 KiB at 5 TB/s), and the split
+// a reduction launch.
+constexpr double kBigCuFlops = 145e12 / kBigGroups;
+constexpr double kBigPieceSeconds = 2.0 * kBigElems * 4 / 5e12;
+constexpr double kBigReduceSeconds = 10e-6;
+
+// How k_gemm_big spreads a product (main block M/256 x N/256 tiles, or its
+// upper triangle): whole tiles in rounds of 256, and possibly the last
+// round's tiles in pieces along K (one round of pieces at most, each piece
+// 256 KiB of part_bytes), whichever the time model finishes first.  Taken
+// when that time is within 12% of the work spread evenly over all CUs;
+// false otherwise.  need_bytes: the partial-buffer bytes of the choice.
+bool plan_big(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch, int64_t part_bytes,
+              BigWork& wk, int64_t* need_bytes = nullptr) {
+    const int64_t tn = N / kBigN, tm = M / kBigM;
+    const int64_t per = sym ? tn * (tn + 1) / 2 : tm * tn;
+    const int64_t tiles = per * batch, nk = K / kBigK;
+    if (tiles < 1 || nk < 1 || tiles > (int64_t{1} << 30)) return false;
+    const double tile_s = 2.0 * kBigElems * static_cast<double>(K) / kBigCuFlops;
+    double best = static_cast<double>((tiles + kBigGroups - 1) / kBigGroups) * tile_s;
+    int64_t best_s = 1, best_span = nk;
+    const int64_t dp = tiles / kBigGroups * kBigGroups, R = tiles - dp;
+    for (int64_t S = 2; R > 0 && S <= nk && R * S <= kBigGroups; ++S) {
+        const int64_t span = (nk + S - 1) / S, se = (nk + span - 1) / span;
+        const int64_t pieces = R * se;
+        if (pieces * kBigElems * 4 > part_bytes) break;
+        const double t = static_cast<double>(dp / kBigGroups) * tile_s +
+                         tile_s * static_cast<double>(span) / static_cast<double>(nk) +
+                         static_cast<double>(pieces) * kBigPieceSeconds + kBigReduceSeconds;
+        if (t < best) {
+            best = t;
+            best_s = se;
+            best_span = span;
+        }
+    }
+    const double even = static_cast<double>(tiles) * tile_s / kBigGroups;
+    if (best > even * 1.12) return false;
+    wk.tiles_n = static_cast<uint32_t>(tn);
+    wk.tiles_per = static_cast<uint32_t>(per);
+    wk.nk = static_cast<uint32_t>(nk);
+    wk.sym = sym;
+    const bool split = best_s > 1;
+    wk.dp = static_cast<uint32_t>(split ? dp : tiles);
+    wk.tail = static_cast<uint32_t>(split ? R : 0);
+    wk.ksplit = static_cast<uint32_t>(best_s);
+    wk.kspan = static_cast<uint32_t>(best_span);
+    if (need_bytes) *need_bytes = split ? R * best_s * kBigElems * 4 : 0;
+    return true;
+}
+
+// Partial-buffer bytes of the preferred split of a batch of products (on
+// k_gemm, or on k_gemm_big for aligned operands).
+int64_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch = 1) {
+    Work wk;
+    int64_t need = 0;
+    plan_gemm(M, N, K, sym, batch, INT64_MAX, wk, &need);
+    BigWork bw;
+    int64_t big = 0;
+    if (K % kBigK == 0 && M >= kBigM && N >= kBigN && (!sym || (M == N && M % kBigM == 0)) &&
+        plan_big(M, N, K, sym, batch, INT64_MAX, bw, &big) && big > need)
+        need = big;
+    return need;
 }
 
 // A batch of `batch` products: operand b at A + b*sa and B + b*sb, result and
-// Y at e.c + b*e.sc and e.y + b*e.sy.
+// Y at e.c + b*e.sc and e.y + b*e.sy.  The main block on k_gemm_big when it
+// fits and pays, the strips past the last whole 256 rows and columns (not
+// for a symmetric result, whose M is a multiple of 256 there) on k_gemm;
+// otherwise everything on k_gemm.
 hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B, int64_t ldb,
                 int64_t sb, int64_t M, int64_t N, int64_t K, const Epilogue& e, bool sym,
                 int64_t batch, float* part, int64_t part_bytes, hipStream_t s) {
-    if (!big_tiles_pay(tn, sym, e, A, lda, sa, B, ldb, sb, M, N, K, batch))
+    BigWork wk;
+    if (!big_fits(sym, e, A, lda, sa, B, ldb, sb, M, N, K) ||
+        !plan_big(M, N, K, sym, batch, part ? part_bytes : 0, wk))
         return gemm_general(tn, A, lda, sa, B, ldb, sb, M, N, K, e, sym, batch, part, part_bytes,
                             s);
-    const int64_t mm = M / kBigM * kBigM, nm = N / kBigN * kBigN;
-    const uint32_t tiles_m = static_cast<uint32_t>(mm / kBigM);
-    const uint32_t tiles_n = static_cast<uint32_t>(nm / kBigN);
-    hipLaunchKernelGGL(k_gemm_big, dim3(kBigGroups), dim3(kGemmThreads), 0, s, A, lda, sa, B, ldb,
-                       sb, K, tiles_m, tiles_n, static_cast<uint32_t>(tiles_m * tiles_n * batch),
-                       e);
+    if (tn)
+        hipLaunchKernelGGL(k_gemm_big<true>, dim3(kBigGroups), dim3(kGemmThreads), 0, s, A, lda,
+                           sa, B, ldb, sb, wk, e, part);
+    else
+        hipLaunchKernelGGL(k_gemm_big<false>, dim3(kBigGroups), dim3(kGemmThreads), 0, s, A, lda,
+                           sa, B, ldb, sb, wk, e, part);
+    if (wk.tail != 0)
+        hipLaunchKernelGGL(k_reduce_big, dim3(wk.tail * 8), dim3(256), 0, s, part, wk, e);
     if (hipError_t err = hipGetLastError()) return err;
+    const int64_t mm = M / kBigM * kBigM, nm = N / kBigN * kBigN;
     if (mm < M) {   // rows mm .. M-1, every column
         Epilogue eb = e;
         eb.c = e.c + mm * e.ldc;
         eb.y = e.y ? e.y + mm * e.ldy : nullptr;
-        if (hipError_t err = gemm_general(false, A + mm * lda, lda, sa, B, ldb, sb, M - mm, N, K,
-                                          eb, false, batch, part, part_bytes, s))
+        if (hipError_t err = gemm_general(tn, tn ? A + mm : A + mm * lda, lda, sa, B, ldb, sb,
+                                          M - mm, N, K, eb, false, batch, part, part_bytes, s))
             return err;
     }
     if (nm < N) {   // rows 0 .. mm-1, columns nm .. N-1
         Epilogue er = e;
         er.c = e.c + nm;
         er.y = e.y ? e.y + nm : nullptr;
-        if (hipError_t err = gemm_general(false, A, lda, sa, B + nm * ldb, ldb, sb, mm, N - nm, K,
-                                          er, false, batch, part, part_bytes, s))
+        if (hipError_t err = gemm_general(tn, A, lda, sa, tn ? B + nm : B + nm * ldb, ldb, sb, mm,
+                                          N - nm, K, er, false, batch, part, part_bytes, s))
             return err;
     }
     return hipSuccess;
@@ -1168,6 +1407,15 @@ hipError_t polar_iterate(const float* const* src, const float* const* sub, float
 
 int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch) {
     return gemm_partial_bytes(M, N, K, sym, batch);
+}
+
+bool matmul_large_tiles(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch,
+                        int64_t ws_bytes) {
+    if (K % kBigK != 0 || M < kBigM || N < kBigN || (sym && (M != N || M % kBigM != 0)) ||
+        K >= (int64_t{1} << 24))
+        return false;
+    BigWork wk;
+    return plan_big(M, N, K, sym, batch, ws_bytes, wk);
 }
 
 hipError_t matmul(bool tn, const float* A, int64_t lda, int64_t sa, const float* B, int64_t ldb,

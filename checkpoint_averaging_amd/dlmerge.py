@@ -41,7 +41,7 @@ SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer
            "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_workspace_bytes_batch",
            "dl_polar_factor", "dl_outer_orthogonal_step", "dl_outer_orthogonal_step_batch",
            "dl_matmul_workspace_bytes", "dl_matmul_f32",
-           "dl_matmul_workspace_bytes_batch", "dl_matmul_f32_batch",
+           "dl_matmul_workspace_bytes_batch", "dl_matmul_f32_batch", "dl_matmul_large_tiles",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
            "dl_round_end", "dl_strerror")
 DL_MAX_SNAPSHOTS = 16
@@ -78,6 +78,8 @@ _lib.dl_outer_orthogonal_step.argtypes = [_p, _p, _i64, _i64, _f32, _i32, _i32, 
 _lib.dl_matmul_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64)]
 _lib.dl_matmul_workspace_bytes_batch.argtypes = [_i64, _i64, _i64, _i32, _i32,
                                                  ctypes.POINTER(_i64)]
+_lib.dl_matmul_large_tiles.argtypes = [_i64, _i64, _i64, _i32, _i32, _i64,
+                                       ctypes.POINTER(_i32)]
 _lib.dl_matmul_f32_batch.argtypes = [_i32, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _i64, _p,
                                      _i64, _i64, _p, _i64, _f32, _f32, _f32, _i32, _i32, _p, _i64,
                                      _p]
@@ -367,6 +369,15 @@ def dl_matmul_workspace_bytes_batch(m: int, n: int, k: int, symmetric: bool, bat
                                                 int(batch), ctypes.byref(b)),
            "dl_matmul_workspace_bytes_batch")
     return b.value
+
+
+def dl_matmul_large_tiles(m: int, n: int, k: int, symmetric: bool, batch: int,
+                          workspace_bytes: int) -> bool:
+    out = _i32()
+    _check(_lib.dl_matmul_large_tiles(int(m), int(n), int(k), int(bool(symmetric)), int(batch),
+                                      int(workspace_bytes), ctypes.byref(out)),
+           "dl_matmul_large_tiles")
+    return bool(out.value)
 
 
 def dl_matmul_f32_batch(form: int, a: Array, lda: int, stride_a: int, b: Array, ldb: int,

@@ -88,20 +88,14 @@ def batch_sizes(count: int, batch: Optional[int] = None) -> List[int]:
     return [count // n + (1 if i < count % n else 0) for i in range(n)]
 
 
-def product_kernel(form: str, m: int, n: int, k: int, batch: int, symmetric: bool,
-                   diag: float = 0.0) -> str:
-    """The kernel a product's main block runs on (the rule the library's
-    dispatch applies, given aligned operands): plain row-major (NT) products,
-    not symmetric and without a diagonal term, with K a multiple of 16 and at
-    least 256 tiles of 256 x 256 filling their rounds to 90% or more, go to
-    the large-tile kernel (their ragged strips to the general one);
-    everything else to the general kernel of its form."""
-    if form == "NT" and not symmetric and diag == 0.0 and k >= 16 and k % 16 == 0:
-        tiles = (m // 256) * (n // 256) * batch
-        rounds = -(-tiles // 256)
-        if tiles >= 256 and tiles * 10 >= rounds * 256 * 9:
-            return "k_gemm_big"
-    return f"k_gemm<{form}>"
+def product_kernel(form: str, m: int, n: int, k: int, batch: int, symmetric: bool) -> str:
+    """The kernel a product's main block runs on, asked of the library (its
+    rule for aligned, contiguous operands with the workspace the product
+    asks for): "k_gemm_big<TN>" / "k_gemm_big<NT>" for the large-tile
+    kernel, else "k_gemm<TN>" / "k_gemm<NT>"."""
+    ws = dl.dl_matmul_workspace_bytes_batch(m, n, k, symmetric, batch)
+    big = dl.dl_matmul_large_tiles(m, n, k, symmetric, batch, ws)
+    return f"k_gemm_big<{form}>" if big else f"k_gemm<{form}>"
 
 
 class OrthogonalStep:

@@ -122,10 +122,12 @@ def polar_kind(name: str):
         return "gemm_TN"
     if "k_gemm<false>" in name:
         return "gemm_NT"
-    if "k_gemm_big(" in name:
-        return "gemm_big"
-    for k in ("k_reduce_pieces", "k_reduce_splits", "k_sumsq_partial", "k_sumsq_final", "k_scale",
-              "k_step"):
+    if "k_gemm_big<true>" in name:
+        return "gemm_big_TN"
+    if "k_gemm_big<false>" in name:
+        return "gemm_big_NT"
+    for k in ("k_reduce_pieces", "k_reduce_splits", "k_reduce_big", "k_sumsq_partial",
+              "k_sumsq_final", "k_scale", "k_step"):
         if f"::{k}(" in name or name.startswith(k + "("):
             return k[2:]
     return None

@@ -396,7 +396,12 @@ enum dl_matmul_form {
  * workspace (few output tiles over a long K: K cut into ranges, every tile
  * in pieces, summed in K order); a smaller workspace may still hold the
  * stream-K split's pieces; otherwise, or without one, every workgroup
- * computes one whole output tile.  The plans give different (each
+ * computes one whole output tile.  Products large enough to fill the GPU
+ * with 256 x 256 tiles, with K a multiple of 16 and 16-byte aligned operand
+ * rows (and, when symmetric, m a multiple of 256 and 16-byte aligned result
+ * rows), run those tiles on a large-tile kernel instead (the last round's
+ * tiles possibly cut along K and summed in K order through the workspace)
+ * and the ragged rest as above.  The plans give different (each
  * deterministic) summation orders.  m = 0 or n = 0 is a no-op.  Errors:
  * DL_E_INVAL (also: symmetric with m != n), DL_E_ALIGN, DL_E_HIP.
  */
@@ -417,6 +422,17 @@ int dl_matmul_f32(int form, const float *a, int64_t lda, const float *b, int64_t
  */
 int dl_matmul_workspace_bytes_batch(int64_t m, int64_t n, int64_t k, int symmetric, int batch,
                                     int64_t *bytes);
+
+/*
+ * *large = 1 when a batch of such products with 16-byte aligned, contiguous
+ * operands (leading dimension k) and workspace_bytes of workspace runs its
+ * main block on the large-tile kernel, else 0 (either form: the rule does
+ * not depend on it).  For reports and tests; nothing is launched.  Errors:
+ * as dl_matmul_workspace_bytes_batch, and DL_E_INVAL for a negative
+ * workspace_bytes or a NULL large.
+ */
+int dl_matmul_large_tiles(int64_t m, int64_t n, int64_t k, int symmetric, int batch,
+                          int64_t workspace_bytes, int *large);
 int dl_matmul_f32_batch(int form, const float *a, int64_t lda, int64_t stride_a, const float *b,
                         int64_t ldb, int64_t stride_b, int64_t m, int64_t n, int64_t k, float *c,
                         int64_t ldc, int64_t stride_c, const float *y, int64_t stride_y,

@@ -95,15 +95,25 @@ def test_flops_square_and_rectangular():
 
 
 def test_product_kernel_rule():
+    """The library's choice of kernel for the step's products (a host-side
+    query, no GPU): large tiles where 256 x 256 tiles fill the CUs, with the
+    last round's tiles cut along K where that evens them out."""
     from checkpoint_averaging_amd.orthogonalize import product_kernel
-    # the step's next-iterate products (tall: X M as NT) fill their rounds
-    assert product_kernel("NT", 2048, 2048, 2048, 36, False) == "k_gemm_big"   # 2304 tiles
-    assert product_kernel("NT", 5632, 2048, 2048, 36, False) == "k_gemm_big"   # 6336 tiles
-    assert product_kernel("NT", 73760, 2048, 2048, 1, False) == "k_gemm_big"   # 2304 + strip
-    # symmetric, k-major, a diagonal term, too few tiles, a partly filled round, K % 16
-    assert product_kernel("NT", 2048, 2048, 5632, 18, True) == "k_gemm<NT>"
-    assert product_kernel("TN", 2048, 5632, 2048, 18, False) == "k_gemm<TN>"
-    assert product_kernel("NT", 2048, 2048, 2048, 36, False, diag=1.5) == "k_gemm<NT>"
-    assert product_kernel("NT", 2048, 2048, 2048, 3, False) == "k_gemm<NT>"      # 192 tiles
-    assert product_kernel("NT", 2048, 2048, 2048, 5, False) == "k_gemm<NT>"      # 320: 62%
+    # next iterates (tall: X M as NT; wide: M X as TN) fill their rounds
+    assert product_kernel("NT", 2048, 2048, 2048, 36, False) == "k_gemm_big<NT>"   # 2304 tiles
+    assert product_kernel("NT", 5632, 2048, 2048, 36, False) == "k_gemm_big<NT>"   # 6336 tiles
+    assert product_kernel("NT", 73760, 2048, 2048, 1, False) == "k_gemm_big<NT>"   # + a strip
+    assert product_kernel("TN", 2048, 5632, 2048, 18, False) == "k_gemm_big<TN>"   # 3168 tiles
+    # symmetric Gram products and squares: 36 upper tiles per 2048^2 result
+    assert product_kernel("TN", 2048, 2048, 2048, 36, True) == "k_gemm_big<TN>"    # 1296: split
+    assert product_kernel("NT", 2048, 2048, 2048, 36, True) == "k_gemm_big<NT>"
+    assert product_kernel("TN", 2048, 2048, 73760, 1, True) == "k_gemm_big<TN>"   # all in pieces
+    # too few tiles to fill the CUs, or rounds that no split evens out
+    assert product_kernel("NT", 2048, 2048, 2048, 1, True) == "k_gemm<NT>"
+    assert product_kernel("NT", 2048, 2048, 5632, 18, True) == "k_gemm<NT>"       # 648 tiles
+    assert product_kernel("NT", 2048, 2048, 2048, 3, False) == "k_gemm<NT>"       # 192 tiles
+    # K not a multiple of 16; a symmetric result not a multiple of 256
     assert product_kernel("NT", 2048, 2048, 2040, 36, False) == "k_gemm<NT>"
+    assert product_kernel("TN", 2000, 2000, 4096, 36, True) == "k_gemm<TN>"
+    # the small model's matrices never fill large tiles
+    assert product_kernel("TN", 128, 128, 50304, 2, True) == "k_gemm<TN>"

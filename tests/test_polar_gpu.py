@@ -331,6 +331,73 @@ def test_matmul_large_tiles(m, n, k, batch, epi):
         _bound_check(outs[0][i], want, mag, k)
 
 
+@pytest.mark.parametrize("form,m,n,k,batch,sym,epi", [
+    (dl.DL_TN, 2048 + 40, 2048, 96, 4, False, "plain"),        # k-major operands, bottom strip
+    (dl.DL_TN, 2048, 2048 + 72, 128, 4, False, "y_in_place"),  # right strip, theta - s P style
+    (dl.DL_TN, 2048, 2048, 2048, 8, True, "plain"),    # Gram: upper tiles, last round's split
+    (dl.DL_TN, 2048, 2048, 2048, 8, True, "cubic"),    # -0.5 G + 1.5 I
+    (dl.DL_NT, 2048, 2048, 2048, 8, True, "square"),   # c G G + b G + a I, G symmetric
+    (dl.DL_TN, 2048, 2048, 16384, 1, True, "plain"),   # few tiles over a long K: all in pieces
+], ids=["TN-strip-rows", "TN-strip-cols-y", "TN-gram", "TN-gram-cubic", "NT-square",
+        "TN-gram-longK"])
+def test_matmul_large_tiles_forms(form, m, n, k, batch, sym, epi):
+    """The large-tile kernel with k-major operands (transposed on their way to
+    LDS) and with symmetric results (upper tiles only, mirrored; the last
+    round's tiles cut along K and summed in K order by a second kernel):
+    every element within the product bound of fp64 (computed on the GPU in
+    fp64), symmetric results exactly symmetric, the same bits on a second
+    call."""
+    wsb = dl.dl_matmul_workspace_bytes_batch(m, n, k, sym, batch)
+    assert dl.dl_matmul_large_tiles(m, n, k, sym, batch, wsb)
+    rng = np.random.default_rng(m + 3 * n + 7 * k + batch + len(epi))
+    if form == dl.DL_TN:
+        a = rng.standard_normal((batch, k, m)).astype(np.float32)
+        b = a if sym else rng.standard_normal((batch, k, n)).astype(np.float32)
+        lda, ldb = m, n
+    else:
+        a = rng.standard_normal((batch, m, k)).astype(np.float32)
+        if epi == "square":   # a symmetric G (m == k), exactly
+            a = ((a + np.transpose(a, (0, 2, 1))) * np.float32(0.5)).astype(np.float32)
+        b = a if sym else rng.standard_normal((batch, n, k)).astype(np.float32)
+        lda, ldb = k, k
+    c0 = rng.standard_normal((batch, m, n)).astype(np.float32)
+    alpha, beta, diag = {"plain": (1.0, 0.0, 0.0), "y_in_place": (-0.25, 1.0, 0.0),
+                         "cubic": (-0.5, 0.0, 1.5),
+                         "square": (2.0315, -4.7750, 3.4445)}[epi]
+    a_d = gpu(a)
+    b_d = a_d if b is a else gpu(b)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV)
+    outs = []
+    for _ in range(2):
+        c_d = gpu(c0)
+        y_d = {"y_in_place": c_d, "square": a_d}.get(epi)
+        dl.dl_matmul_f32_batch(form, a_d, lda, a[0].size, b_d, ldb, b[0].size, m, n, k, c_d, n,
+                               m * n, batch, y=y_d, stride_y=m * n if y_d is not None else 0,
+                               alpha=alpha, beta=beta, diag=diag, symmetric=sym, workspace=ws)
+        outs.append(host(c_d))
+    assert np.array_equal(outs[0], outs[1])
+    a64, b64 = a_d.double(), b_d.double()
+    for i in range(batch):
+        ai, bi = (a64[i].T, b64[i]) if form == dl.DL_TN else (a64[i], b64[i].T)
+        want = alpha * (ai @ bi)
+        mag = abs(alpha) * (ai.abs() @ bi.abs())
+        if epi == "y_in_place":
+            y64 = torch.from_numpy(c0[i]).to(DEV, torch.float64)
+        elif epi == "square":
+            y64 = a64[i]
+        else:
+            y64 = None
+        if y64 is not None:
+            want = want + beta * y64
+            mag = mag + abs(beta) * y64.abs()
+        if diag:
+            want = want + diag * torch.eye(m, dtype=torch.float64, device=DEV)
+            mag = mag + abs(diag) * torch.eye(m, dtype=torch.float64, device=DEV)
+        _bound_check(outs[0][i], host(want), host(mag), k)
+        if sym:
+            assert np.array_equal(outs[0][i], outs[0][i].T)
+
+
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("sym", [False, True], ids=["general", "symmetric"])
 @pytest.mark.parametrize("ws_mode", ["stream", "none"])
