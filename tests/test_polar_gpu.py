@@ -398,6 +398,64 @@ def test_matmul_large_tiles_forms(form, m, n, k, batch, sym, epi):
             assert np.array_equal(outs[0][i], outs[0][i].T)
 
 
+@pytest.mark.parametrize("form,sym", [(dl.DL_TN, False), (dl.DL_NT, True), (dl.DL_TN, True)],
+                         ids=["TN-general", "NT-symmetric", "TN-symmetric"])
+def test_matmul_large_tiles_strided(form, sym):
+    """The large-tile kernel on a strided batch: padded leading dimensions
+    (still 16-byte aligned), batch strides with gaps, Y at its own stride,
+    a result pitch wider than the result.  Every element within the product
+    bound, symmetric results exactly symmetric, the gaps untouched."""
+    batch, m = 8, 2048
+    k = 2048 if sym else 1024   # enough work per tile for the symmetric split to pay
+    n = m if sym else 2048 + 256
+    lda = (k if form == dl.DL_NT else m) + 4
+    ldb = (k if form == dl.DL_NT else n) + 4
+    rows_a = m if form == dl.DL_NT else k
+    rows_b = n if form == dl.DL_NT else k
+    sa = lda * rows_a + 16
+    sb = sa if sym else ldb * rows_b + 32   # symmetric: B is A
+    ldc = n + 8
+    sc, sy = ldc * m + 64, ldc * m + 128
+    wsb = dl.dl_matmul_workspace_bytes_batch(m, n, k, sym, batch)
+    assert dl.dl_matmul_large_tiles(m, n, k, sym, batch, wsb)
+    rng = np.random.default_rng(4242 + form + 2 * sym)
+    a = rng.standard_normal(sa * batch).astype(np.float32)
+    b = a if sym else rng.standard_normal(sb * batch).astype(np.float32)
+    c0 = rng.standard_normal(sc * batch).astype(np.float32)
+    yv = rng.standard_normal(sy * batch).astype(np.float32)
+    for i in range(batch):   # a symmetric Y for the symmetric case
+        yy = yv[i * sy:i * sy + m * ldc].reshape(m, ldc)
+        if sym:
+            yy[:, :n] = (yy[:, :n] + yy[:, :n].T) * np.float32(0.5)
+    alpha, beta, diag = (0.75, -0.5, 1.25) if sym else (-0.25, 2.0, 0.0)
+    a_d, y_d = gpu(a), gpu(yv)
+    b_d = a_d if sym else gpu(b)
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV)
+    c_d = gpu(c0)
+    dl.dl_matmul_f32_batch(form, a_d, lda, sa, b_d, ldb, sb, m, n, k, c_d, ldc, sc, batch,
+                           y=y_d, stride_y=sy, alpha=alpha, beta=beta, diag=diag,
+                           symmetric=sym, workspace=ws)
+    out = host(c_d)
+    a64, b64 = a_d.double(), b_d.double()
+    y64 = y_d.double()
+    eye = torch.eye(m, n, dtype=torch.float64, device=DEV)
+    for i in range(batch):
+        av = a64[i * sa:i * sa + rows_a * lda].reshape(rows_a, lda)
+        bv = b64[i * sb:i * sb + rows_b * ldb].reshape(rows_b, ldb)
+        ai, bi = (av[:, :m].T, bv[:, :n]) if form == dl.DL_TN else (av[:, :k], bv[:, :k].T)
+        yi = y64[i * sy:i * sy + m * ldc].reshape(m, ldc)[:, :n]
+        want = alpha * (ai @ bi) + beta * yi + diag * eye
+        mag = abs(alpha) * (ai.abs() @ bi.abs()) + abs(beta) * yi.abs() + abs(diag) * eye
+        ci = out[i * sc:i * sc + m * ldc].reshape(m, ldc)
+        _bound_check(ci[:, :n], host(want), host(mag), k)
+        if sym:
+            assert np.array_equal(ci[:, :n], ci[:, :n].T)
+        # the row padding and the gap after the matrix are untouched
+        c0i = c0[i * sc:i * sc + m * ldc].reshape(m, ldc)
+        assert np.array_equal(ci[:, n:], c0i[:, n:])
+        assert np.array_equal(out[i * sc + m * ldc:(i + 1) * sc], c0[i * sc + m * ldc:(i + 1) * sc])
+
+
 @pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
 @pytest.mark.parametrize("sym", [False, True], ids=["general", "symmetric"])
 @pytest.mark.parametrize("ws_mode", ["stream", "none"])
