@@ -327,6 +327,26 @@ def test_matmul_workspace_sizes():
     assert ws >= 2 * 2048 * 2048 * 4 * 2 + full
 
 
+def test_matmul_large_tiles_query():
+    """Which kernel a shape's main block runs on (asked on the host, nothing
+    launched): large tiles need K a multiple of 16, at least one whole row
+    and column of 256 x 256 tiles, enough of them to fill the CUs (the last
+    round's tiles possibly cut along K, within the workspace), and for a
+    symmetric result M a multiple of 256."""
+    full = dl.dl_matmul_workspace_bytes_batch(2048, 2048, 2048, True, 36)
+    assert dl.dl_matmul_large_tiles(2048, 2048, 2048, True, 36, full)
+    assert not dl.dl_matmul_large_tiles(2048, 2048, 2048, True, 36, 0)    # its tail needs pieces
+    assert dl.dl_matmul_large_tiles(2048, 2048, 2048, False, 4, 0)        # 256 whole tiles
+    assert not dl.dl_matmul_large_tiles(2048, 2048, 2040, False, 4, 0)    # K % 16
+    assert not dl.dl_matmul_large_tiles(2048, 2048, 2048, False, 3, 0)    # 192 tiles
+    assert not dl.dl_matmul_large_tiles(2000, 2000, 4096, True, 36, full)
+    assert not dl.dl_matmul_large_tiles(255, 4096, 4096, False, 64, full)
+    assert not dl.dl_matmul_large_tiles(0, 5, 5, False, 1, 0)
+    for bad in ((5, 6, 7, True, 1, 0), (-1, 5, 5, False, 1, 0), (5, 5, 5, False, 0, 0),
+                (5, 5, 5, False, 1, -1)):
+        _expect(dl.DL_E_INVAL, dl.dl_matmul_large_tiles, *bad)
+
+
 def test_participants_capacity():
     lib = dl.raw_lib()
     import ctypes
