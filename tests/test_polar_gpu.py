@@ -427,7 +427,7 @@ def test_matmul_large_tiles_strided(form, sym):
         yy = yv[i * sy:i * sy + m * ldc].reshape(m, ldc)
         if sym:
             yy[:, :n] = (yy[:, :n] + yy[:, :n].T) * np.float32(0.5)
-    alpha, beta, diag = (0.75, -0.5, 1.25) if sym else (-0.25, 2.0, 0.0)
+    alpha, beta, diag = (0.75, -0.5, 1.25) if sym else (-0.25, 2.0, 0.5)
     a_d, y_d = gpu(a), gpu(yv)
     b_d = a_d if sym else gpu(b)
     ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV)
