@@ -785,3 +785,55 @@ def test_polar_full_size_embedding_rows():
     orth = np.max(np.abs(gram - np.eye(cols)))
     print(f"embedding orthonormality: {orth:.3e}", flush=True)
     assert orth <= 2 * bound
+
+
+def test_orthogonal_step_over_diffurefill1b_layout_sampled():
+    """The benchmark's configuration at full size: the whole-model step over
+    the DiffuRefill-1B layout (127 matrices; each shape's matrices together,
+    split evenly into launches of at most 64, so the products run on the
+    large-tile kernel with the last round's tiles cut along K), then sampled
+    matrices against the oracle: the first and the last matrix of each
+    batch (the last one holds the tiles cut along K) and sampled rows of the
+    embedding; every parameter outside the matrices untouched."""
+    from checkpoint_averaging_amd.orthogonalize import OrthogonalStep
+    layout = synth.DIFFUREFILL_1B
+    n = layout.n_params
+    theta = synth.global0(1311, n, device=DEV)
+    avg = synth.worker_checkpoint(1311, 0, 0, theta)
+    step = OrthogonalStep(layout, DEV)
+    mats = step.matrices
+    assert len(mats) == 127
+    # the first and the last matrix of every batch
+    picks = [g[i] for g in step.groups for i in sorted({0, len(g) - 1})]
+    assert len(picks) == 9
+    before = {m.name: (host(theta[m.offset:m.offset + m.rows * m.cols]),
+                       host(avg[m.offset:m.offset + m.rows * m.cols])) for m in picks}
+    outside = torch.ones(n, dtype=torch.bool, device=DEV)
+    for m in mats:
+        outside[m.offset:m.offset + m.rows * m.cols] = False
+    rest = theta[outside].clone()
+    scale = 1e-2
+    step.run(theta, avg, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(theta[outside], rest)
+    for m in picks:
+        t, a = (x.reshape(m.rows, m.cols) for x in before[m.name])
+        got = host(theta[m.offset:m.offset + m.rows * m.cols]).reshape(m.rows, m.cols)
+        upd = t - a
+        if m.rows > 8 * m.cols:   # the embedding: sampled rows, Gram closed form
+            pick = np.random.default_rng(9).choice(m.rows, 64, replace=False)
+            pick = np.concatenate([[0, m.rows - 1], pick])
+            want = opolar.polar_factor_rows(upd, pick)
+            s = np.linalg.svd(upd.T @ upd, compute_uv=False)
+            est = estimate_from(math.sqrt(s[0] / s[-1]), m.cols)
+            t, got = t[pick], got[pick]
+        else:
+            want = opolar.polar_factor(upd)
+            est = polar_estimate(upd)
+        p_got = (t - got) / scale
+        rel = np.linalg.norm(p_got - want) / np.linalg.norm(want)
+        # theta - s P loses |theta| u per element: bound that on top
+        extra = 2 * U32 * np.linalg.norm(t) / scale / np.linalg.norm(want)
+        print(f"1B step {m.name} {m.rows}x{m.cols}: rel_F={rel:.3e} "
+              f"estimate={est:.3e} + {extra:.3e}", flush=True)
+        assert rel <= est + extra, m.name
