@@ -16,20 +16,25 @@
 // within fp32 rounding.  For a wide matrix (rows < cols) the same runs on
 // G = X X^T with X <- M X.
 //
-// Every product is a GEMM of fp32 on MFMA (v_mfma_f32_32x32x2f32):
+// Every product is a GEMM of fp32 on MFMA (v_mfma_f32_32x32x2f32), on one
+// of two kernels.  Products large enough to fill the CUs with 256 x 256
+// tiles run those on k_gemm_big: one workgroup per CU, one wave per SIMD,
+// each wave a 128 x 128 quarter whose sums fill the accumulation registers,
+// K-tiles of 16 double-buffered in LDS.  Everything else (and the ragged
+// strips past the last whole 256 rows and columns) runs on k_gemm:
 // workgroups of 4 wave64 compute 128 x 128 output tiles, each wave a 64 x 64
 // quarter as 2 x 2 MFMA blocks of 32 x 32, over K in tiles of 32 staged
-// through LDS with the next tile's loads in flight.  The work of a product
-// (output tiles x K-tiles; for a batch of equally shaped matrices, all their
-// tiles) goes to as many workgroups as the GPU holds at once: whole tiles in
-// rounds, then the last round or two's worth split stream-K; tiles cut
-// between workgroups are summed in K order by a second kernel, so results
-// are deterministic.  A product with fewer tiles than workgroups over a long
-// K (the Gram matrix of a tall embedding) is split along K instead, its
-// (K range, tile) units dealt range by range so that the workgroups of an
-// XCD read the same operand rows together, and each tile's pieces summed in
-// K order.  Edge tiles take the plain loads with clamped rows where the
-// layout allows it.  The Gram matrix and its square are symmetric: only
+// through LDS with the next tile's loads in flight.  On k_gemm the work of a
+// product (output tiles x K-tiles; for a batch of equally shaped matrices,
+// all their tiles) goes to as many workgroups as the GPU holds at once:
+// whole tiles in rounds, then the last round or two's worth split stream-K;
+// tiles cut between workgroups are summed in K order by a second kernel, so
+// results are deterministic.  A product with fewer tiles than workgroups
+// over a long K is split along K instead, its (K range, tile) units dealt
+// range by range so that the workgroups of an XCD read the same operand
+// rows together, and each tile's pieces summed in K order; k_gemm_big cuts
+// the last round's tiles along K the same way.  Edge tiles take the plain
+// loads with clamped rows where the layout allows it.  The Gram matrix and its square are symmetric: only
 // their upper tiles are computed and the lower ones are written as mirror
 // images.  The epilogue is fused: out = alpha*acc + beta*Y + (i == j ? d :
 // 0), which forms a I + b G + c G^2 in the G^2 product, 1.5 I - 0.5 G in the
