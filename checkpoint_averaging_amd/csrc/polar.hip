@@ -975,13 +975,29 @@ __global__ __launch_bounds__(256) void k_reduce_big(const float* __restrict__ pa
 constexpr int kRedBlocks = 1024;
 constexpr int kRedThreads = 256;
 
-// Stage 1: block b sums the squares of its grid-stride elements in fp64.
-// With `y`, the element is x - y (rounded in fp32) and is also written to d.
-__global__ __launch_bounds__(kRedThreads) void k_sumsq_partial(const float* __restrict__ x,
-                                                               const float* __restrict__ y,
-                                                               float* __restrict__ d, int64_t n,
+// A batch's elementwise passes run as one launch each, matrix blockIdx.y of
+// the batch per grid row; every matrix is split into blocks exactly as it
+// would be alone, so a batch gives each matrix the same bits.
+constexpr int kMaxBatch = 64;   // matrices per launch (the C ABI's limit)
+struct MatPtrs {                // one pointer per matrix, passed by value
+    const float* p[kMaxBatch];
+};
+struct MatPtrsW {
+    float* p[kMaxBatch];
+};
+
+// Stage 1: block b of matrix m sums the squares of its grid-stride elements
+// in fp64 into partial[m * gridDim.x + b].  With ys.p[m], the element is x -
+// y (rounded in fp32) and is also written to d0 + m * sd.
+__global__ __launch_bounds__(kRedThreads) void k_sumsq_partial(MatPtrs xs, MatPtrs ys,
+                                                               float* __restrict__ d0, int64_t sd,
+                                                               int64_t n,
                                                                double* __restrict__ partial) {
     __shared__ double red[kRedThreads];
+    const int m = static_cast<int>(blockIdx.y);
+    const float* __restrict__ x = xs.p[m];
+    const float* __restrict__ y = ys.p[m];
+    float* __restrict__ d = d0 + m * sd;
     double s = 0.0;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * kRedThreads + threadIdx.x; e < n;
          e += static_cast<int64_t>(gridDim.x) * kRedThreads) {
@@ -998,29 +1014,35 @@ __global__ __launch_bounds__(kRedThreads) void k_sumsq_partial(const float* __re
         if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+    if (threadIdx.x == 0) partial[static_cast<int64_t>(m) * gridDim.x + blockIdx.x] = red[0];
 }
 
-// Stage 2 (one block): inv = 1 / sqrt(sum of partials), or 0 for a zero matrix.
+// Stage 2 (block m for matrix m): inv[m] = 1 / sqrt(sum of its partials),
+// or 0 for a zero matrix.
 __global__ __launch_bounds__(kRedThreads) void k_sumsq_final(const double* __restrict__ partial,
                                                              int nparts, float* __restrict__ inv) {
     __shared__ double red[kRedThreads];
+    const double* __restrict__ pm = partial + static_cast<int64_t>(blockIdx.x) * nparts;
     double s = 0.0;
-    for (int p = threadIdx.x; p < nparts; p += kRedThreads) s += partial[p];
+    for (int p = threadIdx.x; p < nparts; p += kRedThreads) s += pm[p];
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = kRedThreads / 2; w > 0; w >>= 1) {
         if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
-    if (threadIdx.x == 0) inv[0] = red[0] > 0.0 ? static_cast<float>(1.0 / sqrt(red[0])) : 0.0f;
+    if (threadIdx.x == 0)
+        inv[blockIdx.x] = red[0] > 0.0 ? static_cast<float>(1.0 / sqrt(red[0])) : 0.0f;
 }
 
-// x[e] = src[e] * inv[0]
-// (x may be src: each element is read and written by the same thread)
-__global__ __launch_bounds__(256) void k_scale(float* x, const float* src,
+// x_m[e] = src_m[e] * inv[m], x_m = x0 + m * sx, src_m = srcs.p[m] or (when
+// null) x_m itself: each element is read and written by the same thread
+__global__ __launch_bounds__(256) void k_scale(float* x0, int64_t sx, MatPtrs srcs,
                                                const float* __restrict__ inv, int64_t n) {
-    const float s = inv[0];
+    const int m = static_cast<int>(blockIdx.y);
+    float* x = x0 + m * sx;
+    const float* src = srcs.p[m] ? srcs.p[m] : x;
+    const float s = inv[m];
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
          e += static_cast<int64_t>(gridDim.x) * 256)
         x[e] = src[e] * s;
@@ -1314,10 +1336,13 @@ PolarSpace polar_space(void* ws, int64_t rows, int64_t cols, int64_t batch) {
     return sp;
 }
 
-// theta = theta - scale * P, the same two roundings as the fused epilogue:
-// fl(fl(-scale * P) + theta).
-__global__ __launch_bounds__(256) void k_step(float* __restrict__ theta, const float* __restrict__ P,
-                                              float scale, int64_t n) {
+// theta_m = theta_m - scale * P_m (matrix blockIdx.y, P_m = P0 + m * sp), the
+// same two roundings as the fused epilogue: fl(fl(-scale * P) + theta).
+__global__ __launch_bounds__(256) void k_step(MatPtrsW thetas, const float* __restrict__ P0,
+                                              int64_t sp, float scale, int64_t n) {
+    const int m = static_cast<int>(blockIdx.y);
+    float* __restrict__ theta = thetas.p[m];
+    const float* __restrict__ P = P0 + m * sp;
     const float ns = -scale;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
          e += static_cast<int64_t>(gridDim.x) * 256)
@@ -1333,25 +1358,27 @@ int64_t polar_workspace_bytes(int64_t rows, int64_t cols, int64_t batch) {
 hipError_t polar_iterate(const float* const* src, const float* const* sub, float* const* out,
                          float* const* theta, float scale, int64_t batch, int64_t rows,
                          int64_t cols, int quintic, int cubic, void* ws, hipStream_t s) {
-    if (batch < 1 || (batch > 1 && (out || !theta))) return hipErrorInvalidValue;
+    if (batch < 1 || batch > kMaxBatch || (batch > 1 && (out || !theta)))
+        return hipErrorInvalidValue;
     const int64_t n = rows * cols;
     const bool tall = rows >= cols;
     const int64_t r = tall ? cols : rows;
     const PolarSpace sp = polar_space(ws, rows, cols, batch);
 
     // X0 = A / ||A||_F per matrix, with A = src (or src - sub, formed in fp32
-    // into the first iterate)
+    // into the first iterate); one launch per pass for the whole batch
+    MatPtrs ps{}, pu{}, pscale{};
     for (int64_t b = 0; b < batch; ++b) {
-        float* xa = sp.xa + b * sp.sx;
-        double* partial = sp.partial + b * kRedBlocks;
-        const float* sb = sub ? sub[b] : nullptr;
-        hipLaunchKernelGGL(k_sumsq_partial, dim3(kRedBlocks), dim3(kRedThreads), 0, s, src[b], sb,
-                           sb ? xa : nullptr, n, partial);
-        hipLaunchKernelGGL(k_sumsq_final, dim3(1), dim3(kRedThreads), 0, s, partial, kRedBlocks,
-                           sp.inv + b);
-        hipLaunchKernelGGL(k_scale, dim3(4096), dim3(256), 0, s, xa, sb ? xa : src[b], sp.inv + b,
-                           n);
+        ps.p[b] = src[b];
+        pu.p[b] = sub ? sub[b] : nullptr;
+        pscale.p[b] = sub ? nullptr : src[b];   // scale the difference in place
     }
+    const unsigned nb = static_cast<unsigned>(batch);
+    hipLaunchKernelGGL(k_sumsq_partial, dim3(kRedBlocks, nb), dim3(kRedThreads), 0, s, ps, pu,
+                       sp.xa, sp.sx, n, sp.partial);
+    hipLaunchKernelGGL(k_sumsq_final, dim3(nb), dim3(kRedThreads), 0, s, sp.partial, kRedBlocks,
+                       sp.inv);
+    hipLaunchKernelGGL(k_scale, dim3(4096, nb), dim3(256), 0, s, sp.xa, sp.sx, pscale, sp.inv, n);
     if (hipError_t err = hipGetLastError()) return err;
 
     // A single matrix writes its result straight from the last product's
@@ -1403,10 +1430,11 @@ hipError_t polar_iterate(const float* const* src, const float* const* sub, float
         x = xn;
         xn = t;
     }
-    if (!direct)   // x holds the batch's polar factors
-        for (int64_t b = 0; b < batch; ++b)
-            hipLaunchKernelGGL(k_step, dim3(4096), dim3(256), 0, s, theta[b], x + b * sp.sx, scale,
-                               n);
+    if (!direct) {   // x holds the batch's polar factors
+        MatPtrsW pt{};
+        for (int64_t b = 0; b < batch; ++b) pt.p[b] = theta[b];
+        hipLaunchKernelGGL(k_step, dim3(4096, nb), dim3(256), 0, s, pt, x, sp.sx, scale, n);
+    }
     return hipGetLastError();
 }
 
