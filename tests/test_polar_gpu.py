@@ -302,6 +302,8 @@ def test_matmul_large_tiles(m, n, k, batch, epi):
     run their main block on the large-tile kernel (one wave per SIMD) and
     the ragged strips on the general one: every element within the product
     bound of fp64, the same bits on a second call."""
+    assert dl.dl_matmul_large_tiles(m, n, k, False, batch,
+                                    dl.dl_matmul_workspace_bytes_batch(m, n, k, False, batch))
     rng = np.random.default_rng(m + n + k + batch)
     a = rng.standard_normal((batch, m, k)).astype(np.float32)
     b = rng.standard_normal((batch, n, k)).astype(np.float32)

@@ -35,6 +35,24 @@ def test_kernel_kind(name, kind):
     assert ps.kernel_kind(name) == kind
 
 
+@pytest.mark.parametrize("name,kind", [
+    ("void dlk::(anonymous namespace)::k_gemm<true>(float const*, long, ...)", "gemm_TN"),
+    ("void dlk::(anonymous namespace)::k_gemm<false>(float const*, long, ...)", "gemm_NT"),
+    ("void dlk::(anonymous namespace)::k_gemm_big<true>(float const*, long, ...)", "gemm_big_TN"),
+    ("void dlk::(anonymous namespace)::k_gemm_big<false>(float const*, long, ...)",
+     "gemm_big_NT"),
+    ("dlk::(anonymous namespace)::k_reduce_big(float const*, dlk::(anonymous namespace)::BigWork, "
+     "dlk::(anonymous namespace)::Epilogue)", "reduce_big"),
+    ("dlk::(anonymous namespace)::k_reduce_splits(float const*, ...)", "reduce_splits"),
+    ("dlk::(anonymous namespace)::k_sumsq_partial(dlk::(anonymous namespace)::MatPtrs, ...)",
+     "sumsq_partial"),
+    ("dlk::(anonymous namespace)::k_step(dlk::(anonymous namespace)::MatPtrsW, ...)", "step"),
+    ("void dlk::(anonymous namespace)::k_stream<...FoldSum<float, true>, true>(...)", None),
+])
+def test_polar_kind(name, kind):
+    assert ps.polar_kind(name) == kind
+
+
 def _write_csv(path, counter, rows):
     with open(path, "w", newline="") as fh:
         w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
