@@ -1161,10 +1161,13 @@ hipError_t gemm_general(bool tn, const float* A, int64_t lda, int64_t sa, const 
 // 16-byte aligned operand rows (and batch strides) with leading dimensions
 // below 2^24 (32-bit lane offsets); a symmetric result square with M a
 // multiple of 256 (no ragged strips) and 16-byte aligned rows (mirrored
-// float4 stores).
+// float4 stores).  A diagonal term needs the result's diagonal inside the
+// main block: a non-symmetric product with one and ragged strips runs
+// wholly on k_gemm (a strip's own diagonal is not the result's).
 bool big_fits(bool sym, const Epilogue& e, const float* A, int64_t lda, int64_t sa,
               const float* B, int64_t ldb, int64_t sb, int64_t M, int64_t N, int64_t K) {
     if (K < kBigK || K % kBigK != 0 || M < kBigM || N < kBigN) return false;
+    if (e.diag != 0.0f && (M % kBigM != 0 || N % kBigN != 0)) return false;
     if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(B) % 16 ||
         lda % 4 || ldb % 4 || sa % 4 || sb % 4)
         return false;

@@ -399,9 +399,9 @@ enum dl_matmul_form {
  * computes one whole output tile.  Products large enough to fill the GPU
  * with 256 x 256 tiles, with K a multiple of 16 and 16-byte aligned operand
  * rows (and, when symmetric, m a multiple of 256 and 16-byte aligned result
- * rows), run those tiles on a large-tile kernel instead (the last round's
- * tiles possibly cut along K and summed in K order through the workspace)
- * and the ragged rest as above.  The plans give different (each
+ * rows; with a nonzero diag, m and n multiples of 256), run those tiles on a
+ * large-tile kernel instead (the last round's tiles possibly cut along K and
+ * summed in K order through the workspace) and the ragged rest as above.  The plans give different (each
  * deterministic) summation orders.  m = 0 or n = 0 is a no-op.  Errors:
  * DL_E_INVAL (also: symmetric with m != n), DL_E_ALIGN, DL_E_HIP.
  */
@@ -425,9 +425,9 @@ int dl_matmul_workspace_bytes_batch(int64_t m, int64_t n, int64_t k, int symmetr
 
 /*
  * *large = 1 when a batch of such products with 16-byte aligned, contiguous
- * operands (leading dimension k) and workspace_bytes of workspace runs its
- * main block on the large-tile kernel, else 0 (either form: the rule does
- * not depend on it).  For reports and tests; nothing is launched.  Errors:
+ * operands (leading dimension k), diag = 0 and workspace_bytes of workspace
+ * runs its main block on the large-tile kernel, else 0 (either form: the
+ * rule does not depend on it).  For reports and tests; nothing is launched.  Errors:
  * as dl_matmul_workspace_bytes_batch, and DL_E_INVAL for a negative
  * workspace_bytes or a NULL large.
  */

@@ -400,6 +400,71 @@ def test_matmul_large_tiles_forms(form, m, n, k, batch, sym, epi):
             assert np.array_equal(outs[0][i], outs[0][i].T)
 
 
+# shapes drawn once from a seeded generator (ragged M and N, K from 112 to
+# 2800, batches from 12 to 38) and kept where the library takes the
+# large-tile path: whole rounds, last rounds cut along K into pieces of
+# unequal length, strips on both sides
+SEEDED_BIG = [
+    (dl.DL_TN, 1316, 1124, 2528, 28, False), (dl.DL_TN, 1540, 1024, 2112, 12, False),
+    (dl.DL_TN, 2048, 2048, 2800, 38, True), (dl.DL_NT, 2308, 1792, 1344, 36, False),
+    (dl.DL_NT, 1280, 1536, 1520, 23, False), (dl.DL_TN, 2308, 2560, 112, 27, False),
+    (dl.DL_NT, 2048, 2048, 1328, 32, True), (dl.DL_TN, 2432, 1636, 1040, 29, False),
+]
+
+
+@pytest.mark.parametrize("form,m,n,k,batch,sym", SEEDED_BIG)
+def test_matmul_large_tiles_seeded_shapes(form, m, n, k, batch, sym):
+    """Seeded shapes on the large-tile path, with Y, and a diagonal term
+    where the result's diagonal lies in the main block: every element
+    within the product bound of fp64 (checked on the GPU), symmetric
+    results exactly symmetric."""
+    _check_big_product(form, m, n, k, batch, sym,
+                       0.75 if sym or (m % 256 == 0 and n % 256 == 0) else 0.0)
+
+
+@pytest.mark.parametrize("form", [dl.DL_TN, dl.DL_NT], ids=["TN", "NT"])
+def test_matmul_diagonal_term_with_ragged_edges(form):
+    """A non-symmetric product with a diagonal term and ragged edges: the
+    diagonal crosses into the strips past the last whole 256 rows and
+    columns, so the whole product runs on the general kernel (a strip's own
+    diagonal is not the result's; adding the term there once put it on the
+    wrong elements)."""
+    _check_big_product(form, 1316, 1124, 2528, 28, False, 0.75, shape_takes_large_tiles=None)
+
+
+def _check_big_product(form, m, n, k, batch, sym, diag, shape_takes_large_tiles=True):
+    wsb = dl.dl_matmul_workspace_bytes_batch(m, n, k, sym, batch)
+    if shape_takes_large_tiles is not None:
+        assert dl.dl_matmul_large_tiles(m, n, k, sym, batch, wsb) == shape_takes_large_tiles
+    g = torch.Generator(device=DEV).manual_seed(m * 7 + n * 3 + k + batch)
+    rows_a, rows_b = (k, k) if form == dl.DL_TN else (m, n)
+    cols_a, cols_b = (m, n) if form == dl.DL_TN else (k, k)
+    a_d = torch.randn(batch, rows_a, cols_a, generator=g, device=DEV)
+    b_d = a_d if sym else torch.randn(batch, rows_b, cols_b, generator=g, device=DEV)
+    y_d = torch.randn(batch, m, n, generator=g, device=DEV)
+    if sym:
+        y_d = (y_d + y_d.transpose(1, 2).contiguous()) * 0.5
+    c_d = torch.full((batch, m, n), float("nan"), device=DEV)
+    alpha, beta = 0.625, -1.5
+    ws = torch.empty(max(wsb, 256) // 4, dtype=torch.float32, device=DEV)
+    dl.dl_matmul_f32_batch(form, a_d, cols_a, rows_a * cols_a, b_d, cols_b, rows_b * cols_b, m,
+                           n, k, c_d, n, m * n, batch, y=y_d, stride_y=m * n, alpha=alpha,
+                           beta=beta, diag=diag, symmetric=sym, workspace=ws)
+    torch.cuda.synchronize()
+    gam = (k + 4) * U32 / (1 - (k + 4) * U32)
+    eye = torch.eye(m, n, dtype=torch.float64, device=DEV)
+    for i in range(batch):
+        a64, b64 = a_d[i].double(), b_d[i].double()
+        ai, bi = (a64.T, b64) if form == dl.DL_TN else (a64, b64.T)
+        y64 = y_d[i].double()
+        want = alpha * (ai @ bi) + beta * y64 + diag * eye
+        mag = abs(alpha) * (ai.abs() @ bi.abs()) + abs(beta) * y64.abs() + abs(diag) * eye
+        err = (c_d[i].double() - want).abs()
+        assert bool((err <= gam * mag + 1e-30).all()), (i, float((err / (mag + 1e-30)).max()))
+        if sym:
+            assert torch.equal(c_d[i], c_d[i].T)
+
+
 @pytest.mark.parametrize("form,sym", [(dl.DL_TN, False), (dl.DL_NT, True), (dl.DL_TN, True)],
                          ids=["TN-general", "NT-symmetric", "TN-symmetric"])
 def test_matmul_large_tiles_strided(form, sym):
