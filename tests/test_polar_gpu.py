@@ -746,6 +746,33 @@ def test_outer_orthogonal_step_batch(m, n, batch):
     assert np.array_equal(host(t1), host(t2))
 
 
+@pytest.mark.parametrize("m,n", [(2560, 1536), (1536, 2560)], ids=["tall", "wide"])
+def test_outer_orthogonal_step_batch_large_tiles(m, n):
+    """A batch of 12 on the large-tile path for every product (the Gram
+    matrix and its square with upper tiles only, the next iterate in both
+    forms, rounds not a whole multiple of the CUs): the first and the last
+    matrix of the batch against the oracle."""
+    batch, r, big = 12, min(m, n), max(m, n)
+    for shape in ((r, r, big, True), (r, r, r, True), (m, n, r, False)):
+        wsb = dl.dl_matmul_workspace_bytes_batch(*shape, batch)
+        assert dl.dl_matmul_large_tiles(*shape, batch, wsb), shape
+    thetas = [synth.global0(1400 + b, m * n, device=DEV) for b in range(batch)]
+    avgs = [synth.worker_checkpoint(1400 + b, 0, 0, t) for b, t in enumerate(thetas)]
+    check = (0, batch - 1)
+    th_h = {b: host(thetas[b]).reshape(m, n) for b in check}
+    av_h = {b: host(avgs[b]).reshape(m, n) for b in check}
+    scale = 0.02
+    ws = torch.empty(dl.dl_polar_workspace_bytes_batch(m, n, batch) // 4 + 1, device=DEV)
+    dl.dl_outer_orthogonal_step_batch(thetas, avgs, m, n, scale, ws)
+    for b in check:
+        want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
+        upd = th_h[b] - av_h[b]
+        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        est = scale * polar_estimate(upd) * math.sqrt(r) + 2 * U32 * np.linalg.norm(want)
+        print(f"large-tile batch {m}x{n} [{b}]: err_F={err:.3e} estimate={est:.3e}", flush=True)
+        assert err <= est
+
+
 def test_outer_orthogonal_step_batch_full_size():
     """Four 2048 x 2048 attention updates in one batch against the SVD (the
     batch's 4 x 64 tiles of 256 x 256 send its next-iterate products to the
