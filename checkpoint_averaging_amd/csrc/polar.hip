@@ -1447,8 +1447,10 @@ int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sym, int64_
 
 bool matmul_large_tiles(int64_t M, int64_t N, int64_t K, bool sym, int64_t batch,
                         int64_t ws_bytes) {
+    // contiguous operands: leading dimension K (row-major) or M and N (k-major)
+    const int64_t kMaxLd = int64_t{1} << 24;
     if (K % kBigK != 0 || M < kBigM || N < kBigN || (sym && (M != N || M % kBigM != 0)) ||
-        K >= (int64_t{1} << 24))
+        K >= kMaxLd || M >= kMaxLd || N >= kMaxLd)
         return false;
     BigWork wk;
     return plan_big(M, N, K, sym, batch, ws_bytes, wk);
