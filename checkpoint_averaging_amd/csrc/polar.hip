@@ -986,6 +986,14 @@ struct MatPtrsW {
     float* p[kMaxBatch];
 };
 
+// Whether a matrix's elementwise pass can take 16-byte packs: n a multiple
+// of 4 and every (non-null) pointer 16-byte aligned.
+__device__ __forceinline__ bool vec4_ok(const void* a, const void* b, const void* c, int64_t n) {
+    const uintptr_t u = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                        reinterpret_cast<uintptr_t>(c);
+    return (n & 3) == 0 && (u & 15) == 0;
+}
+
 // Stage 1: block b of matrix m sums the squares of its grid-stride elements
 // in fp64 into partial[m * gridDim.x + b].  With ys.p[m], the element is x -
 // y (rounded in fp32) and is also written to d0 + m * sd.
@@ -999,14 +1007,27 @@ __global__ __launch_bounds__(kRedThreads) void k_sumsq_partial(MatPtrs xs, MatPt
     const float* __restrict__ y = ys.p[m];
     float* __restrict__ d = d0 + m * sd;
     double s = 0.0;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kRedThreads + threadIdx.x; e < n;
-         e += static_cast<int64_t>(gridDim.x) * kRedThreads) {
-        float v = x[e];
-        if (y) {
-            v = v - y[e];
-            d[e] = v;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kRedThreads + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kRedThreads;
+    if (vec4_ok(x, y, y ? d : nullptr, n)) {   // uniform: 16-byte packs, squares in pack order
+        for (int64_t e = first; e < n / 4; e += stride) {
+            f32x4 v = reinterpret_cast<const f32x4*>(x)[e];
+            if (y) {
+                v = v - reinterpret_cast<const f32x4*>(y)[e];
+                reinterpret_cast<f32x4*>(d)[e] = v;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s += static_cast<double>(v[c]) * static_cast<double>(v[c]);
         }
-        s += static_cast<double>(v) * static_cast<double>(v);
+    } else {
+        for (int64_t e = first; e < n; e += stride) {
+            float v = x[e];
+            if (y) {
+                v = v - y[e];
+                d[e] = v;
+            }
+            s += static_cast<double>(v) * static_cast<double>(v);
+        }
     }
     red[threadIdx.x] = s;
     __syncthreads();
@@ -1043,9 +1064,14 @@ __global__ __launch_bounds__(256) void k_scale(float* x0, int64_t sx, MatPtrs sr
     float* x = x0 + m * sx;
     const float* src = srcs.p[m] ? srcs.p[m] : x;
     const float s = inv[m];
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-         e += static_cast<int64_t>(gridDim.x) * 256)
-        x[e] = src[e] * s;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    if (vec4_ok(x, src, nullptr, n)) {
+        for (int64_t e = first; e < n / 4; e += stride)
+            reinterpret_cast<f32x4*>(x)[e] = reinterpret_cast<const f32x4*>(src)[e] * s;
+    } else {
+        for (int64_t e = first; e < n; e += stride) x[e] = src[e] * s;
+    }
 }
 
 constexpr float kQa = 3.4445f, kQb = -4.7750f, kQc = 2.0315f;
@@ -1347,9 +1373,15 @@ __global__ __launch_bounds__(256) void k_step(MatPtrsW thetas, const float* __re
     float* __restrict__ theta = thetas.p[m];
     const float* __restrict__ P = P0 + m * sp;
     const float ns = -scale;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-         e += static_cast<int64_t>(gridDim.x) * 256)
-        theta[e] = ns * P[e] + theta[e];
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    if (vec4_ok(theta, P, nullptr, n)) {
+        f32x4* t4 = reinterpret_cast<f32x4*>(theta);
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(P);
+        for (int64_t e = first; e < n / 4; e += stride) t4[e] = ns * p4[e] + t4[e];
+    } else {
+        for (int64_t e = first; e < n; e += stride) theta[e] = ns * P[e] + theta[e];
+    }
 }
 
 }  // namespace
