@@ -746,6 +746,30 @@ def test_outer_orthogonal_step_batch(m, n, batch):
     assert np.array_equal(host(t1), host(t2))
 
 
+def test_outer_orthogonal_step_batch_unaligned_views():
+    """Matrices that start one element past a 16-byte boundary (views into
+    a flat buffer): the elementwise passes take their element-by-element
+    path, and every matrix still meets the oracle's bounds."""
+    m, n, batch = 192, 64, 3
+    bufs_t = [synth.global0(1500 + b, m * n + 1, device=DEV) for b in range(batch)]
+    bufs_a = [synth.worker_checkpoint(1500 + b, 0, 0, t) for b, t in enumerate(bufs_t)]
+    thetas = [t[1:] for t in bufs_t]
+    avgs = [a[1:] for a in bufs_a]
+    assert all(t.data_ptr() % 16 == 4 for t in thetas)
+    th_h = [host(t).reshape(m, n) for t in thetas]
+    av_h = [host(a).reshape(m, n) for a in avgs]
+    scale = 0.02
+    ws = torch.empty(dl.dl_polar_workspace_bytes_batch(m, n, batch) // 4 + 1, device=DEV)
+    dl.dl_outer_orthogonal_step_batch(thetas, avgs, m, n, scale, ws)
+    for b in range(batch):
+        want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
+        upd = th_h[b] - av_h[b]
+        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        est = scale * polar_estimate(upd) * math.sqrt(min(m, n)) + 2 * U32 * np.linalg.norm(want)
+        assert err <= est, (b, err, est)
+        assert float(bufs_t[b][0]) == float(synth.global0(1500 + b, 1, device=DEV)[0])
+
+
 @pytest.mark.parametrize("m,n", [(2560, 1536), (1536, 2560)], ids=["tall", "wide"])
 def test_outer_orthogonal_step_batch_large_tiles(m, n):
     """A batch of 12 on the large-tile path for every product (the Gram
