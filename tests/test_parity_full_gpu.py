@@ -166,3 +166,28 @@ def test_full_size_every_element(key):
         say(f"[full] {key}: round {r}")
         res = mc.run_round(w, st, r, fused_last=(r != 1))
         mc.assert_round_equal(res, f"{key} round {r}")
+
+
+def test_full_size_fragment_rounds_on_separate_streams():
+    """The 1.08B fragment merge with each fragment's round on its own stream
+    (arrivals issued round-robin across fragments, as
+    `bench.py --fragment-streams 4` times it), on sampled windows of every
+    fragment against the oracle's one-at-a-time rounds."""
+    key = "diffurefill1b_frag_nesterov_ema"
+    w = synth.WORKLOADS[key]
+    say(f"[full-streams] {key}: allocating and generating")
+    gw = GpuWorkload(w)
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for r in range(ROUNDS):
+        gw.generate_checkpoints(r)
+        say(f"[full-streams] {key}: round {r} on 4 streams, fused_close={r == 0}")
+        gw.run_round(r, tag=200 + r, fused_close=(r == 0), streams=streams)
+    torch.cuda.synchronize()
+    wins = windows(w, 16, seed=w.seed + 1)
+    want = oracle_on_windows(w, wins)
+    for f, fw in enumerate(wins):
+        for k, t in (("theta", gw.theta), ("m", gw.m), ("e", gw.e)):
+            g, o = gather(t, fw), want[f][k]
+            assert mc.bits_equal(g, o), f"frag {f} {k}: {mc.first_mismatch(g, o)}"
+    del gw
+    torch.cuda.empty_cache()
