@@ -91,3 +91,41 @@ def test_adopt_keep_drift_matches_oracle(n, dtype):
     dl.dl_adopt_keep_drift(theta, g, pushed)
     torch.cuda.synchronize()
     assert mc.bits_equal(mc.to_np(theta), want), mc.first_mismatch(mc.to_np(theta), want)
+
+
+def test_side_averages_and_adoption_full_size_sampled():
+    """At the 1.08B size the benchmark times (the streaming kernels' non-
+    temporal paths): the uniform average of 5 globals folded one by one, the
+    average of the same 5 as snapshots, and the keep-local-drift adoption,
+    on sampled windows against the oracle run on inputs regenerated on the
+    CPU for those windows only."""
+    n = synth.DIFFUREFILL_1B.n_params
+    seed, count, win = 1016, 5, 4096
+    th0 = synth.global0(seed, n, device="cuda")
+    gs = [synth.worker_checkpoint(seed, r, 0, th0) for r in range(count)]
+    s = torch.empty(n, device="cuda")
+    for k, g in enumerate(gs):
+        dl.dl_swa_fold(s, g, k)
+    swa = torch.empty(n, device="cuda")
+    dl.dl_swa_average(swa, s, count)
+    del s
+    snap = torch.empty(n, device="cuda")
+    dl.dl_snapshot_average(snap, gs)
+    theta = th0.clone()                       # the worker's weights, it pushed gs[0]
+    dl.dl_adopt_keep_drift(theta, gs[1], gs[0])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    starts = sorted({0, n - win, *(int(x) for x in rng.integers(0, n - win, size=12))})
+    for st in starts:
+        t0 = synth.global0(seed, win, start=st)
+        g_w = [mc.to_np(synth.worker_checkpoint(seed, r, 0, t0, start=st)) for r in range(count)]
+        want_swa = oracle.swa_average(g_w)
+        want_snap = oracle.snapshot_average(g_w)
+        want_th = mc.to_np(t0)
+        oracle.adopt_keep_drift(want_th, g_w[1], g_w[0])
+        for got, want, what in ((swa, want_swa, "swa"), (snap, want_snap, "snapshot"),
+                                (theta, want_th, "adopt")):
+            g = mc.to_np(got[st:st + win])
+            assert mc.bits_equal(g, want), (what, st, mc.first_mismatch(g, want))
+    del gs, swa, snap, theta, th0
+    torch.cuda.empty_cache()
