@@ -746,6 +746,31 @@ def test_outer_orthogonal_step_batch(m, n, batch):
     assert np.array_equal(host(t1), host(t2))
 
 
+def test_outer_orthogonal_step_largest_batch():
+    """The largest batch the library takes (64 matrices: every per-matrix
+    pointer slot of the batched passes in use), and one more is refused."""
+    m, n, batch = 256, 128, dl.DL_MAX_BATCH
+    thetas = [synth.global0(1600 + b, m * n, device=DEV) for b in range(batch)]
+    avgs = [synth.worker_checkpoint(1600 + b, 0, 0, t) for b, t in enumerate(thetas)]
+    check = (0, 31, batch - 1)
+    th_h = {b: host(thetas[b]).reshape(m, n) for b in check}
+    av_h = {b: host(avgs[b]).reshape(m, n) for b in check}
+    scale = 0.02
+    ws = torch.empty(dl.dl_polar_workspace_bytes_batch(m, n, batch) // 4 + 1, device=DEV)
+    dl.dl_outer_orthogonal_step_batch(thetas, avgs, m, n, scale, ws)
+    for b in check:
+        want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
+        upd = th_h[b] - av_h[b]
+        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        est = scale * polar_estimate(upd) * math.sqrt(n) + 2 * U32 * np.linalg.norm(want)
+        assert err <= est, (b, err, est)
+    extra = synth.global0(1700, m * n, device=DEV)
+    with pytest.raises(dl.DLError) as ei:
+        dl.dl_outer_orthogonal_step_batch(thetas + [extra], avgs + [extra.clone()], m, n, scale,
+                                          ws)
+    assert ei.value.status == dl.DL_E_INVAL
+
+
 def test_outer_orthogonal_step_batch_unaligned_views():
     """Matrices that start one element past a 16-byte boundary (views into
     a flat buffer): the elementwise passes take their element-by-element
