@@ -469,6 +469,9 @@ def main():
     ap.add_argument("--separate-close", action="store_true",
                     help="close each fragment in its own pass after the last fold, instead of "
                          "folding the last arrival into the close")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one round into a HIP graph and time its replays (the "
+                         "per-kernel figures still come from event-timed eager rounds)")
     ap.add_argument("--fragment-streams", type=int, default=0,
                     help="run every fragment's round as its own handle on one of this many "
                          "streams (rounds in flight together)")
@@ -565,6 +568,26 @@ def main():
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     log(f"[bench] {args.steps} timed rounds: {ms:.3f} ms/round")
+    graph = None
+    if args.graph:
+        if streams is not None:
+            sys.exit("--graph captures one stream; it does not combine with --fragment-streams")
+        # capture records the round's launches without running them; every
+        # replay then runs the same folds and close on the same buffers
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gw.run_round(0, tag=5000, timer=plain, fused_close=fused)
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"[bench] {args.steps} graph replays: {gms:.3f} ms/round")
+        graph = {"ms_per_round": round(gms, 4), "eager_ms_per_round": round(ms, 4)}
+        ms = gms
     round_ms = None
     if spans:
         per = sorted(a.elapsed_time(b) for a, b in spans)
@@ -640,6 +663,7 @@ def main():
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_time_ms_per_step": (round(total_kernel_ms / args.steps, 4) if kinds else None),
         "round_ms": round_ms,
+        "graph": graph,
         "fragment_streams": args.fragment_streams,
         "kernels": kern,
         "roofline": roofline,
