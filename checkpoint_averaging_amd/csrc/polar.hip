@@ -920,26 +920,29 @@ __global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__
 
 // The tail tiles of the large-tile kernel: tile dp + tt's ksplit pieces
 // (slots s * tail + tt) summed in K order (piece 0 + piece 1 + ...), then
-// the epilogue, for rows 32q .. 32q + 31 of the tile (workgroup 8 tt + q).
-// Thread t owns columns 4(t%64) .. +3 of rows t/64 + 4p.  A symmetric result
-// is mirrored as in the large-tile kernel, through LDS (rows of 32
-// consecutive i per store).
+// the epilogue, for rows 32q .. 32q + 31 and columns 64h .. 64h + 63 of the
+// tile (workgroup 32 tt + 4q + h: 32 per tile, so that a tail of a few
+// tiles still spreads over the CUs).  Thread t owns columns 4(t%16) .. +3
+// of that block's rows t/16 and t/16 + 16.  A symmetric result is mirrored
+// as in the large-tile kernel, through LDS (rows of 32 consecutive i per
+// store).
 __global__ __launch_bounds__(256) void k_reduce_big(const float* __restrict__ part, BigWork wk,
                                                     Epilogue e) {
-    __shared__ float tr[kBigN][33];
-    const uint32_t tt = blockIdx.x >> 3;
-    const int q = static_cast<int>(blockIdx.x & 7);
+    __shared__ float tr[64][33];
+    const uint32_t tt = blockIdx.x >> 5;
+    const int q = static_cast<int>((blockIdx.x >> 2) & 7), h = static_cast<int>(blockIdx.x & 3);
     if (tt >= wk.tail) return;
     uint32_t mb, ti, tj;
     big_coords(wk.dp + tt, wk, mb, ti, tj);
-    const int tid = threadIdx.x, lj = 4 * (tid & 63);
+    const int tid = threadIdx.x, cl = 4 * (tid & 15), lj = 64 * h + cl;
     const bool dtile = wk.sym && ti == tj;
     float* const c = e.c + mb * e.sc;
     const float* const y = e.y ? e.y + mb * e.sy : nullptr;
     const int64_t ri = static_cast<int64_t>(ti) * kBigM, rj = static_cast<int64_t>(tj) * kBigN;
-#pragma unroll 2
-    for (int p = 0; p < 8; ++p) {
-        const int li = 32 * q + (tid >> 6) + 4 * p;   // row within the tile
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int lr = (tid >> 4) + 16 * p;   // row within the block
+        const int li = 32 * q + lr;           // row within the tile
         const int64_t off = static_cast<int64_t>(li) * kBigN + lj;
         f32x4 v = *reinterpret_cast<const f32x4*>(part + tt * kBigElems + off);
         for (uint32_t s = 1; s < wk.ksplit; ++s) {
@@ -955,16 +958,16 @@ __global__ __launch_bounds__(256) void k_reduce_big(const float* __restrict__ pa
             if (y) o = o + e.beta * y[gi * e.ldy + gj];
             if (gi == gj) o = o + e.diag;
             if (!dtile || gi <= gj) c[gi * e.ldc + gj] = o;
-            if (wk.sym) tr[lj + x][li - 32 * q] = o;
+            if (wk.sym) tr[cl + x][lr] = o;
         }
     }
-    if (wk.sym) {   // uniform: C[j][i] for the strip's (i, j), 32 consecutive i per row
+    if (wk.sym) {   // uniform: C[j][i] for the block's (i, j), 32 consecutive i per row
         __syncthreads();
-#pragma unroll 4
-        for (int p = 0; p < 32; ++p) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
             const int idx = p * 256 + tid;
-            const int mr = idx >> 5, mc = idx & 31;
-            const int64_t gi = ri + 32 * q + mc, gj = rj + mr;
+            const int mr = idx >> 5, mc = idx & 31;   // block column, block row
+            const int64_t gi = ri + 32 * q + mc, gj = rj + 64 * h + mr;
             if (!dtile || gi < gj) c[gj * e.ldc + gi] = tr[mr][mc];
         }
     }
@@ -1290,7 +1293,7 @@ hipError_t gemm(bool tn, const float* A, int64_t lda, int64_t sa, const float* B
         hipLaunchKernelGGL(k_gemm_big<false>, dim3(kBigGroups), dim3(kGemmThreads), 0, s, A, lda,
                            sa, B, ldb, sb, wk, e, part);
     if (wk.tail != 0)
-        hipLaunchKernelGGL(k_reduce_big, dim3(wk.tail * 8), dim3(256), 0, s, part, wk, e);
+        hipLaunchKernelGGL(k_reduce_big, dim3(wk.tail * 32), dim3(256), 0, s, part, wk, e);
     if (hipError_t err = hipGetLastError()) return err;
     const int64_t mm = M / kBigM * kBigM, nm = N / kBigN * kBigN;
     if (mm < M) {   // rows mm .. M-1, every column
