@@ -252,3 +252,195 @@ def test_planted_mistake_is_caught(name):
 
 def test_unplanted_oracle_passes_all_checks():
     all_checks(polar)
+
+
+# -- the iteration's exact-arithmetic result (iterated_factor) ---------------------
+
+def spectrum_matrix(rng, m, n, svals):
+    r = min(m, n)
+    q1, q2 = orthonormal(rng, m, r), orthonormal(rng, n, r)
+    return (q1 * np.asarray(svals, dtype=np.float64)) @ q2.T
+
+
+ITERATED_CASES = [
+    # (m, n, smallest s / ||A||_F, quintic, cubic)
+    (60, 20, 1e-3, 12, 6), (20, 60, 1e-3, 12, 6), (30, 30, 1e-4, 12, 6),
+    (60, 20, 2e-8, 12, 6), (30, 30, 3e-8, 12, 6),     # directions left unconverged
+    (40, 16, 1e-2, 1, 0), (16, 40, 1e-2, 3, 2), (25, 25, 1e-3, 12, 0),
+]
+
+
+def check_iterated_matches_newton_schulz(impl, m, n, xmin, q, c):
+    """The plain fp64 matrix iteration (newton_schulz above) and U phi(S) V^T
+    agree: the polynomial steps keep the singular vectors."""
+    rng = np.random.default_rng(m * 13 + n + q)
+    r = min(m, n)
+    x = np.logspace(0, np.log10(xmin), r)
+    s = x * 1.0
+    a = spectrum_matrix(rng, m, n, s)
+    a = a * (1.0 / np.linalg.norm(a))          # ||A||_F = 1, so s/||A||_F = x (approx.)
+    got = impl.iterated_factor(a, q, c)
+    want = newton_schulz(a, q, c)
+    assert np.max(np.abs(got - want)) <= 1e-7, np.max(np.abs(got - want))
+    if xmin >= 2e-7 and q == 12 and c == 6:
+        assert np.max(np.abs(got - impl.polar_factor(a))) <= 1e-11
+
+
+def check_iterated_diagonal(impl):
+    """A diagonal matrix: the factor is diag(phi(d / ||d||)), and phi pins the
+    first steps by hand: one quintic step of x is a x + b x^3 + c x^5."""
+    d = np.array([3.0, 1.0, 0.5, 1e-6, 3e-8])
+    a = np.diag(d)
+    nrm = np.linalg.norm(d)
+    for q, c in ((12, 6), (1, 0), (0, 1), (2, 3)):
+        got = impl.iterated_factor(a, q, c)
+        want = np.diag(polar.iteration_map(d / nrm, q, c))
+        assert np.max(np.abs(got - want)) <= 1e-14
+    x = 0.3
+    assert abs(float(polar.iteration_map(x, 1, 0)) - (3.4445 * x - 4.7750 * x ** 3
+                                                      + 2.0315 * x ** 5)) <= 1e-15
+    assert abs(float(polar.iteration_map(x, 0, 1)) - (1.5 * x - 0.5 * x ** 3)) <= 1e-15
+    assert abs(float(polar.iteration_map(x, 1, 1))
+               - float(polar.iteration_map(polar.iteration_map(x, 1, 0), 0, 1))) <= 1e-15
+
+
+def check_iterated_rows(impl):
+    rng = np.random.default_rng(44)
+    a = spectrum_matrix(rng, 300, 40, np.logspace(0, -2, 40))
+    rows = [0, 3, 150, 299]
+    for q, c in ((12, 6), (2, 1)):
+        got = impl.iterated_factor_rows(a, rows, q, c)
+        want = impl.iterated_factor(a, q, c)[rows]
+        assert np.max(np.abs(got - want)) <= 1e-10
+
+
+def iterated_checks(impl):
+    for case in ITERATED_CASES:
+        check_iterated_matches_newton_schulz(impl, *case)
+    check_iterated_diagonal(impl)
+    check_iterated_rows(impl)
+
+
+def test_iterated_factor_pins():
+    iterated_checks(polar)
+
+
+def _it_spectral_norm(a, q=12, c=6):
+    a = np.asarray(a, dtype=np.float64)
+    u, s, vt = np.linalg.svd(a, full_matrices=False)
+    return (u * polar.iteration_map(s / s[0], q, c)) @ vt
+
+
+def _it_steps_swapped(a, q=12, c=6):
+    a = np.asarray(a, dtype=np.float64)
+    u, s, vt = np.linalg.svd(a, full_matrices=False)
+    x = s / np.linalg.norm(a)
+    x = polar.iteration_map(polar.iteration_map(x, 0, c), q, 0)
+    return (u * x) @ vt
+
+
+def _it_coefficients_swapped(a, q=12, c=6):
+    a = np.asarray(a, dtype=np.float64)
+    u, s, vt = np.linalg.svd(a, full_matrices=False)
+    x = s / np.linalg.norm(a)
+    for _ in range(q):
+        x = 3.4445 * x + 2.0315 * x ** 3 - 4.7750 * x ** 5
+    x = polar.iteration_map(x, 0, c)
+    return (u * x) @ vt
+
+
+def _it_rows_times_s(a, rows, q=12, c=6):
+    a = np.asarray(a, dtype=np.float64)
+    lam, v = np.linalg.eigh(a.T @ a)
+    s = np.sqrt(lam)
+    f = polar.iteration_map(s / np.linalg.norm(a), q, c)
+    return a[np.asarray(rows)] @ ((v * (f * s)) @ v.T)
+
+
+ITERATED_PLANTED = {
+    "normalised_by_largest_singular_value": dict(iterated_factor=_it_spectral_norm),
+    "cubic_steps_first": dict(iterated_factor=_it_steps_swapped),
+    "quintic_coefficients_swapped": dict(iterated_factor=_it_coefficients_swapped),
+    "rows_scaled_by_s_not_one_over_s": dict(iterated_factor_rows=_it_rows_times_s),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ITERATED_PLANTED))
+def test_iterated_planted_mistake_is_caught(name):
+    impl = types.SimpleNamespace(iterated_factor=polar.iterated_factor,
+                                 iterated_factor_rows=polar.iterated_factor_rows,
+                                 polar_factor=polar.polar_factor)
+    for k, v in ITERATED_PLANTED[name].items():
+        setattr(impl, k, v)
+    with pytest.raises(AssertionError):
+        iterated_checks(impl)
+
+
+# -- the per-element tolerance's first-order formula ------------------------------
+
+def check_variance_formula(var_fn, m, n, q, c, samples=600, seed=0):
+    """Monte Carlo of the fp64 oracle: perturb a tall A by eps G (G with
+    independent N(0, 1) entries, so its coefficients in A's singular bases are
+    independent N(0, 1) too) and collect iterated_factor(A + eps G) -
+    iterated_factor(A).  The formula, cross terms dropped, must give the
+    total variance over all elements exactly (the cross terms cancel in the
+    sum because U and V have orthonormal columns), and bound every element's
+    variance within a factor 2 (each pair's cross term is at most its share),
+    up to the Monte Carlo's own scatter."""
+    from tests import polar_tolerance as pt
+    rng = np.random.default_rng(seed + 100 * m + n)
+    a = spectrum_matrix(rng, m, n, np.logspace(0, -1.3, min(m, n)))
+    u, s, vt = np.linalg.svd(a, full_matrices=False)
+    model = var_fn(u, s, vt.T, q, c)
+    base = polar.iterated_factor(a, q, c)
+    eps = 1e-7
+    acc = np.zeros_like(a)
+    for _ in range(samples):
+        d = polar.iterated_factor(a + eps * rng.standard_normal(a.shape), q, c) - base
+        acc += d * d
+    emp = acc / samples / eps ** 2
+    ratio_total = emp.sum() / model.sum()
+    assert abs(ratio_total - 1.0) <= 0.06, ratio_total
+    assert np.all(emp <= 2.0 * model * 1.35), float(np.max(emp / model))
+
+
+VARIANCE_CASES = [(36, 14, 2, 1), (20, 20, 3, 0), (6, 6, 1, 0), (40, 8, 12, 6)]
+
+
+@pytest.mark.parametrize("m,n,q,c", VARIANCE_CASES)
+def test_variance_formula_matches_monte_carlo(m, n, q, c):
+    from tests import polar_tolerance as pt
+    check_variance_formula(pt.backward_variance, m, n, q, c)
+
+
+def _var_mutant(drop):
+    from tests import polar_tolerance as pt
+
+    def fn(U, s, V, q, c):
+        nf = float(np.sqrt(np.sum(s ** 2)))
+        f = polar.iteration_map(s / nf, q, c)
+        fp = pt.iteration_map_derivative(s / nf, q, c) / nf
+        ds = s[:, None] - s[None, :]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            sym = np.where(ds == 0, fp[:, None], (f[:, None] - f[None, :]) / np.where(ds == 0, 1, ds))
+        skw = (f[:, None] + f[None, :]) / (s[:, None] + s[None, :])
+        if drop == "skew_over_difference":
+            skw = (f[:, None] + f[None, :]) / np.where(ds == 0, 1, np.abs(ds))
+        if drop == "symmetric_term":
+            sym = 0 * sym
+        w = 0.5 * (sym ** 2 + skw ** 2)
+        np.fill_diagonal(w, 0 if drop == "diagonal_derivative" else fp ** 2)
+        out = (U ** 2) @ w @ (V ** 2).T
+        if drop != "complement":
+            rest = np.maximum(0.0, 1.0 - np.sum(U ** 2, axis=1))
+            out = out + np.outer(rest, (V ** 2) @ (f ** 2 / s ** 2))
+        return out
+    return fn
+
+
+@pytest.mark.parametrize("drop", ["complement", "diagonal_derivative", "symmetric_term",
+                                  "skew_over_difference"])
+def test_variance_formula_planted_mistake_is_caught(drop):
+    with pytest.raises(AssertionError):
+        for case in VARIANCE_CASES:
+            check_variance_formula(_var_mutant(drop), *case, samples=300)
