@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <new>
+#include <stdexcept>
 #include <vector>
 
 #include "dlmerge.h"
@@ -44,11 +45,28 @@ Span span_of(const void* p, int64_t bytes) {
     return Span{a, a + static_cast<uintptr_t>(bytes)};
 }
 
+// A HIP error left pending on this thread by earlier work (a failed call, or
+// an asynchronous fault the runtime has reported) is the caller's to see:
+// the library neither launches over it nor clears it.  "Not ready" from an
+// event or stream query is a status, not a failure: it is consumed so that
+// the launch status read after this call's own launch is that launch's.
+bool hip_error_pending() {
+    const hipError_t e = hipPeekAtLastError();
+    if (e == hipErrorNotReady) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return e != hipSuccess;
+}
+
 // The span must lie inside one device allocation known to the HIP runtime.
 // A host pointer or a span running past its allocation is rejected here
-// instead of faulting the GPU.
+// instead of faulting the GPU.  Every call reaches this check before its
+// launch, so a pending HIP error is reported here as DL_E_HIP, before the
+// runtime is asked anything.
 int check_device_span(const void* p, int64_t bytes) {
     if (p == nullptr) return DL_E_INVAL;
+    if (hip_error_pending()) return DL_E_HIP;
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
     if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
@@ -113,6 +131,19 @@ int check_arrival(const dl_round* r, int frag, int worker_id, uint64_t ckpt_roun
     *esize = dtype == DL_BF16 ? 2 : 4;
     if (!aligned_to(ckpt, static_cast<uintptr_t>(*esize))) return DL_E_ALIGN;
     if (global != nullptr && !aligned_to(global, alignof(float))) return DL_E_ALIGN;
+    return DL_OK;
+}
+
+// Makes room for one more arrival in the fragment's record before anything is
+// launched, so that recording it after the launch cannot fail.
+int reserve_arrival(Fragment& F) {
+    try {
+        F.arrivals.reserve(F.arrivals.size() + 1);
+    } catch (const std::bad_alloc&) {
+        return DL_E_NOMEM;
+    } catch (const std::length_error&) {
+        return DL_E_NOMEM;
+    }
     return DL_OK;
 }
 
@@ -200,16 +231,21 @@ int dl_round_begin(dl_round** out, uint64_t round_tag, int mode, int64_t n_param
     if (n_params > INT64_MAX / static_cast<int64_t>(sizeof(float))) return DL_E_INVAL;
 
     dl_round* r = new (std::nothrow) dl_round;
-    if (r == nullptr) return DL_E_INVAL;
+    if (r == nullptr) return DL_E_NOMEM;
+    try {
+        r->offsets.assign(frag_offsets, frag_offsets + n_frags + 1);
+        r->frags.resize(static_cast<size_t>(n_frags));
+    } catch (const std::bad_alloc&) {
+        delete r;
+        return DL_E_NOMEM;
+    }
     r->tag = round_tag;
     r->mode = mode;
     r->n_params = n_params;
-    r->offsets.assign(frag_offsets, frag_offsets + n_frags + 1);
     r->quorum = quorum;
     r->max_workers = max_workers;
     r->acc = acc;
     r->stream = static_cast<hipStream_t>(stream);
-    r->frags.resize(static_cast<size_t>(n_frags));
     *out = r;
     return DL_OK;
 }
@@ -236,9 +272,9 @@ int dl_fold_checkpoint(dl_round* r, int frag, int worker_id, uint64_t ckpt_round
     if (int e = check_device_span(acc, n * 4)) return e;
     if (int e = check_device_span(ckpt, n * esize)) return e;
 
+    if (int st = reserve_arrival(F)) return st;
     const bool first = F.arrivals.empty();
     const bool backward = (F.passes & 1) != 0;
-    (void)hipGetLastError();          // launch status below is this call's own
     hipError_t err;
     if (r->mode == DL_MEAN) {
         err = dlk::launch_fold_sum(acc, ckpt, dtype == DL_BF16, n, first, backward, r->stream);
@@ -268,7 +304,6 @@ int dl_finalize_mean(dl_round* r, int frag, float* out_global, float* ema, float
     if (int st = check_mean_close(r, frag, out_global, ema, Span{0, 0}, &out, &e)) return st;
 
     const float count = static_cast<float>(F.arrivals.size());
-    (void)hipGetLastError();
     const hipError_t err =
         dlk::launch_finalize_mean(out, r->acc + r->off(frag), count, e, beta, one_minus(beta),
                                   r->len(frag), (F.passes & 1) != 0, r->stream);
@@ -292,7 +327,6 @@ int dl_outer_nesterov(dl_round* r, int frag, float* global, float* momentum, flo
         return st;
 
     const float total = static_cast<float>(F.tokens);    // exact int64 sum, rounded once
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_nesterov(theta, m, r->acc + r->off(frag), total, lr, mu,
                                                 e, beta, one_minus(beta), r->len(frag),
                                                 (F.passes & 1) != 0, r->stream);
@@ -319,10 +353,10 @@ int dl_fold_and_finalize_mean(dl_round* r, int frag, int worker_id, uint64_t ckp
     float *out = nullptr, *e = nullptr;
     if (int st = check_mean_close(r, frag, out_global, ema, ck_s, &out, &e)) return st;
     if (int st = check_device_span(ckpt, n * esize)) return st;
+    if (int st = reserve_arrival(F)) return st;
 
     const bool first = F.arrivals.empty();
     const float count = static_cast<float>(F.arrivals.size() + 1);
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_fold_finalize_mean(
         out, r->acc + off, ckpt, dtype == DL_BF16, first, count, e, beta, one_minus(beta), n,
         (F.passes & 1) != 0, r->stream);
@@ -351,11 +385,11 @@ int dl_fold_and_outer_nesterov(dl_round* r, int frag, int worker_id, uint64_t ck
     if (int st = check_nesterov_close(r, frag, global, momentum, ema, ck_s, &theta, &m, &e))
         return st;
     if (int st = check_device_span(ckpt, n * esize)) return st;
+    if (int st = reserve_arrival(F)) return st;
 
     const bool first = F.arrivals.empty();
     const float w = static_cast<float>(tokens);               // nearest-even
     const float total = static_cast<float>(F.tokens + tokens);  // exact int64 sum, rounded once
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_fold_nesterov(
         theta, m, r->acc + off, ckpt, dtype == DL_BF16, first, w, total, lr, mu, e, beta,
         one_minus(beta), n, (F.passes & 1) != 0, r->stream);
@@ -377,7 +411,6 @@ int dl_ema_update(float* ema, const float* global, int64_t n, float beta, void* 
     if (span_of(ema, n * 4).overlaps(span_of(global, n * 4))) return DL_E_INVAL;
     if (int st = check_device_span(ema, n * 4)) return st;
     if (int st = check_device_span(global, n * 4)) return st;
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_ema(ema, global, beta, one_minus(beta), n,
                                            static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
@@ -392,7 +425,6 @@ int dl_swa_fold(float* sum, const float* global, int64_t n, int64_t folded_befor
     if (span_of(sum, n * 4).overlaps(span_of(global, n * 4))) return DL_E_INVAL;
     if (int st = check_device_span(sum, n * 4)) return st;
     if (int st = check_device_span(global, n * 4)) return st;
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_fold_sum(sum, global, false, n, folded_before == 0, false,
                                                 static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
@@ -407,7 +439,6 @@ int dl_swa_average(float* out, const float* sum, int64_t n, int64_t count, void*
     if (!out_s.same(sum_s) && out_s.overlaps(sum_s)) return DL_E_INVAL;
     if (int st = check_device_span(out, n * 4)) return st;
     if (int st = check_device_span(sum, n * 4)) return st;
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_finalize_mean(out, sum, static_cast<float>(count), nullptr,
                                                      0.0f, 0.0f, n, false,
                                                      static_cast<hipStream_t>(stream));
@@ -429,7 +460,6 @@ int dl_snapshot_average(float* out, const float* const* snapshots, int k, int64_
     if (int st = check_device_span(out, n * 4)) return st;
     for (int i = 0; i < k; ++i)
         if (int st = check_device_span(snapshots[i], n * 4)) return st;
-    (void)hipGetLastError();
     const hipError_t err =
         dlk::launch_snapshot_mean(out, snapshots, k, n, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? DL_OK : DL_E_HIP;
@@ -452,7 +482,6 @@ int dl_adopt_keep_drift(float* theta, const float* global, const void* pushed, i
     if (int st = check_device_span(theta, n * 4)) return st;
     if (int st = check_device_span(global, n * 4)) return st;
     if (int st = check_device_span(pushed, n * esize)) return st;
-    (void)hipGetLastError();
     const hipError_t err = dlk::launch_adopt_keep_drift(theta, global, pushed,
                                                         pushed_dtype == DL_BF16, n,
                                                         static_cast<hipStream_t>(stream));
@@ -543,7 +572,6 @@ int dl_matmul_f32_batch(int form, const float* a, int64_t lda, int64_t stride_a,
         if (int st = check_device_span(y, y_bytes)) return st;
     if (ws_bytes > 0)
         if (int st = check_device_span(workspace, ws_bytes)) return st;
-    (void)hipGetLastError();
     const hipError_t err = dlk::matmul(tn, a, lda, stride_a, b, ldb, stride_b, m, n, k, c, ldc,
                                        stride_c, y, stride_y, alpha, beta, diag, symmetric != 0,
                                        batch, workspace, ws_bytes,
@@ -602,7 +630,6 @@ int dl_polar_factor(float* out, const float* update, int64_t rows, int64_t cols,
     if (int st = check_device_span(workspace, need)) return st;
     if (int st = check_device_span(out, bytes)) return st;
     if (int st = check_device_span(update, bytes)) return st;
-    (void)hipGetLastError();
     const hipError_t err = dlk::polar_iterate(&update, nullptr, &out, nullptr, 0.0f, 1, rows, cols,
                                               quintic_steps, cubic_steps, workspace,
                                               static_cast<hipStream_t>(stream));
@@ -637,7 +664,6 @@ int dl_outer_orthogonal_step_batch(float* const* theta, const float* const* aver
         if (int st = check_device_span(theta[b], bytes)) return st;
         if (int st = check_device_span(averaged[b], bytes)) return st;
     }
-    (void)hipGetLastError();
     const hipError_t err = dlk::polar_iterate(theta, averaged, nullptr, theta, scale, batch, rows,
                                               cols, quintic_steps, cubic_steps, workspace,
                                               static_cast<hipStream_t>(stream));
@@ -691,8 +717,9 @@ const char* dl_strerror(int status) {
         case DL_E_QUORUM: return "fewer arrivals than the quorum";
         case DL_E_STATE: return "call not allowed in this state";
         case DL_E_ALIGN: return "pointer not aligned to its element type";
-        case DL_E_HIP: return "HIP launch failed; the round is failed";
+        case DL_E_HIP: return "HIP error (pending before the call, or at launch)";
         case DL_E_CAPACITY: return "output array too small";
+        case DL_E_NOMEM: return "host memory exhausted";
         default: return "unknown status";
     }
 }

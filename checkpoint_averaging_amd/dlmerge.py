@@ -34,6 +34,7 @@ DL_E_STATE = -5
 DL_E_ALIGN = -6
 DL_E_HIP = -7
 DL_E_CAPACITY = -8
+DL_E_NOMEM = -9
 
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",

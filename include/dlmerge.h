@@ -54,8 +54,14 @@
  * checks with the HIP runtime before launching.
  *
  * Errors.  Every call returns DL_OK (0) or a negative status.  All checks
- * except DL_E_HIP happen on the host before any launch; a call that fails
- * them launches nothing and leaves the handle unchanged.  Device buffers
+ * happen on the host before any launch; a call that fails them launches
+ * nothing and leaves the handle unchanged.  Among them: a HIP error already
+ * pending on the calling thread (hipPeekAtLastError; e.g. a failed runtime
+ * call or a reported asynchronous fault) is returned as DL_E_HIP and left
+ * pending for the caller, who clears it (hipGetLastError) and may retry.
+ * A launch that fails is also DL_E_HIP, and then the round is failed: only
+ * dl_round_end is allowed, and recovery is a new round that folds the
+ * arrivals again.  A host allocation that fails is DL_E_NOMEM.  Device buffers
  * holding the global, momentum and EMA are written only by the closing calls
  * (dl_finalize_mean, dl_outer_nesterov, dl_fold_and_finalize_mean,
  * dl_fold_and_outer_nesterov, dl_ema_update), so an abandoned round changes
@@ -96,8 +102,11 @@ enum dl_status {
     DL_E_QUORUM = -4,    /* closing a fragment with fewer arrivals than quorum */
     DL_E_STATE = -5,     /* call not allowed in the fragment's/round's state   */
     DL_E_ALIGN = -6,     /* pointer not aligned to its element type            */
-    DL_E_HIP = -7,       /* HIP runtime error at launch; round is now failed   */
-    DL_E_CAPACITY = -8   /* output array too small                             */
+    DL_E_HIP = -7,       /* HIP error pending before the call (nothing launched,
+                            handle unchanged, error left pending), or a failed
+                            launch (the round is then failed)                  */
+    DL_E_CAPACITY = -8,  /* output array too small                             */
+    DL_E_NOMEM = -9      /* host memory for the round's bookkeeping exhausted  */
 };
 
 /*
@@ -131,7 +140,7 @@ enum dl_status {
  *                 (NULL: the null stream).
  *
  * Errors: DL_E_INVAL (bad value or offsets), DL_E_ALIGN (acc not 4-byte
- * aligned).
+ * aligned), DL_E_NOMEM (the handle could not be allocated).
  */
 int dl_round_begin(dl_round **out, uint64_t round_tag, int mode, int64_t n_params,
                    int n_frags, const int64_t *frag_offsets, int quorum, int max_workers,
@@ -157,7 +166,8 @@ int dl_round_begin(dl_round **out, uint64_t round_tag, int mode, int64_t n_param
  *                   ignored.
  *
  * Errors (all before launch): DL_E_STATE (round failed, or fragment already
- * closed), DL_E_INVAL, DL_E_STALE, DL_E_DUP, DL_E_ALIGN; DL_E_HIP after a
+ * closed), DL_E_INVAL, DL_E_STALE, DL_E_DUP, DL_E_ALIGN, DL_E_NOMEM, and
+ * DL_E_HIP for an error already pending (handle unchanged); DL_E_HIP after a
  * launch failure (the round is then failed: only dl_round_end is allowed).
  */
 int dl_fold_checkpoint(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
@@ -211,7 +221,7 @@ int dl_outer_nesterov(dl_round *r, int frag, float *global, float *momentum, flo
  * counts this arrival.  ckpt must not overlap out_global or ema.
  *
  * Errors: those of both calls; nothing is launched and the handle is
- * unchanged on any error but DL_E_HIP.
+ * unchanged on any error but a failed launch (DL_E_HIP, round failed).
  */
 int dl_fold_and_finalize_mean(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
                               const void *ckpt, int dtype, float *out_global, float *ema,
@@ -231,7 +241,7 @@ int dl_fold_and_finalize_mean(dl_round *r, int frag, int worker_id, uint64_t ckp
  * global, momentum or ema.
  *
  * Errors: those of both calls; nothing is launched and the handle is
- * unchanged on any error but DL_E_HIP.
+ * unchanged on any error but a failed launch (DL_E_HIP, round failed).
  */
 int dl_fold_and_outer_nesterov(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
                                const void *ckpt, int dtype, int64_t tokens, float *global,

@@ -149,3 +149,45 @@ def test_streams_are_respected():
     dl.dl_round_end(r)
     s.synchronize()
     assert torch.equal(out, torch.full((n,), 2.5, device=dev))
+
+
+def test_pending_hip_error_is_reported_and_left_pending():
+    """A HIP error left pending on the thread by earlier work is reported as
+    DL_E_HIP before anything is launched: the library does not clear it, the
+    handle is unchanged, and after the caller clears it the same call goes
+    through.  The pending error comes from a harmless failed runtime call
+    (selecting a device ordinal that does not exist); no kernel faults."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    n = 4096
+    dev = torch.device("cuda")
+    acc = torch.full((n,), 7.0, device=dev)
+    ck = torch.ones(n, device=dev)
+    torch.cuda.synchronize()
+    r = dl.dl_round_begin(11, dl.DL_MEAN, n, [0, n], 1, 2, acc)
+    hip.hipGetLastError()                                    # start from a clear state
+    assert hip.hipSetDevice(1 << 20) != 0                    # leaves an error pending
+    assert hip.hipPeekAtLastError() != 0
+    lib = dl.raw_lib()
+    st = lib.dl_fold_checkpoint(r.handle, 0, 0, 11, ck.data_ptr(), dl.DL_F32, None, 0)
+    assert st == dl.DL_E_HIP
+    assert hip.hipPeekAtLastError() != 0                     # still pending: not cleared
+    assert hip.hipGetLastError() != 0                        # the caller clears it
+    assert dl.dl_round_participants(r, 0) == []              # handle unchanged
+    torch.cuda.synchronize()
+    assert torch.all(acc == 7.0)                             # nothing launched
+    assert lib.dl_fold_checkpoint(r.handle, 0, 0, 11, ck.data_ptr(), dl.DL_F32, None, 0) == 0
+    dl.dl_finalize_mean(r, 0, acc)
+    dl.dl_round_end(r)
+    torch.cuda.synchronize()
+    assert torch.all(acc == 1.0)
+    # the stand-alone calls report it the same way
+    e = torch.zeros(n, device=dev)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(1 << 20) != 0
+    assert lib.dl_ema_update(e.data_ptr(), ck.data_ptr(), n, 0.5, None) == dl.DL_E_HIP
+    assert hip.hipGetLastError() != 0
+    assert lib.dl_ema_update(e.data_ptr(), ck.data_ptr(), n, 0.5, None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(e == 0.5)

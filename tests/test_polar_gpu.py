@@ -2,7 +2,14 @@
 technical report, "What we measured", "Optimisers": the averaged outer
 update is replaced by its polar factor).
 
-Tolerances come from the arithmetic:
+Every element of every polar factor and outer step below is compared with
+the oracle's exact-arithmetic iteration result U phi(S/||A||_F) V^T.  That
+result is U V^T wherever the iteration has converged.  The per-element
+tolerance is the first-order propagation of the fp32 iteration's rounding
+errors through the singular bases of A (tests/polar_tolerance.py).
+
+The Frobenius-norm checks stay as a second line.  Their tolerances come
+from the arithmetic:
   * the fp32 MFMA product: any summation order of k products in binary32
     stays within gamma_(k+1) = (k+1) u / (1 - (k+1) u) of the exact sum
     times the sum of magnitudes, plus one rounding per epilogue operation;
@@ -23,6 +30,7 @@ import torch
 from checkpoint_averaging_amd import dlmerge as dl
 from checkpoint_averaging_amd import synth
 from oracle import polar as opolar
+from tests import polar_tolerance as pt
 
 pytestmark = pytest.mark.gpu
 
@@ -591,6 +599,31 @@ def test_matmul_k0_writes_the_epilogue():
     assert np.array_equal(host(c), want.astype(np.float32).astype(np.float64))
 
 
+# -- element-wise parity helpers -------------------------------------------------
+
+def assert_factor_elementwise(got, a64, what, quintic=12, cubic=6):
+    """Every element of a computed factor within the per-element tolerance
+    of the oracle's iterated factor; returns the oracle's figures."""
+    e = pt.expected(a64, quintic, cubic)
+    z = pt.report(got, e, what)
+    assert z <= pt.Z, (what, z)
+    return e
+
+
+def assert_step_elementwise(got_theta, theta, upd, scale, what, e=None):
+    """Every element of theta' = theta - scale * P within |scale| times the
+    factor's tolerance plus the step's two binary32 roundings, about theta -
+    scale * (the oracle's iterated factor of the update)."""
+    if e is None:
+        e = pt.expected(upd)
+    want = theta - scale * e.iterated
+    tol = pt.step_tolerance(theta, got_theta, e, scale)
+    worst = float(np.max(np.abs(got_theta - want) / tol))
+    print(f"{what}: step max |err|/tol = {worst:.3f}", flush=True)
+    assert worst <= 1.0, (what, worst)
+    return e
+
+
 # -- the polar factor -----------------------------------------------------------
 
 @pytest.mark.parametrize("m,n,kappa", [(256, 64, 1), (256, 64, 10), (64, 256, 10),
@@ -605,6 +638,7 @@ def test_polar_factor_constructed(m, n, kappa):
     a_d = gpu(a)
     dl.dl_polar_factor(out, a_d, m, n, workspace(m, n))
     got = host(out)
+    assert_factor_elementwise(got, a64, f"polar {m}x{n} kappa={kappa:g}")
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     bound = polar_bound(a64)
     est = polar_estimate(a64)
@@ -624,6 +658,7 @@ def test_polar_factor_in_place_and_vectors():
         dl.dl_polar_factor(a_d, a_d, m, n, workspace(m, n))       # out == update
         want = opolar.polar_factor(a.astype(np.float64))
         got = host(a_d)
+        assert_factor_elementwise(got, a.astype(np.float64), f"in place {m}x{n}")
         assert np.linalg.norm(got - want) <= polar_bound(a.astype(np.float64)) * np.linalg.norm(want)
 
 
@@ -675,6 +710,7 @@ def test_polar_factor_scale_invariant_and_deterministic():
         outs.append(host(o))
     assert np.array_equal(outs[0], outs[1])
     assert np.array_equal(outs[0], outs[2])
+    assert_factor_elementwise(outs[0], a.astype(np.float64), "scale-invariant 300x100")
 
 
 def test_polar_steps_schedule():
@@ -685,27 +721,35 @@ def test_polar_steps_schedule():
     want = opolar.polar_factor(a.astype(np.float64))
     ws = workspace(256, 128)
     errs = []
-    for q, c in ((1, 0), (12, 0), (12, 6)):
+    for q, c in ((1, 0), (12, 0), (12, 6), (3, 2)):
         o = torch.empty((256, 128), device=DEV)
         dl.dl_polar_factor(o, gpu(a), 256, 128, ws, quintic_steps=q, cubic_steps=c)
-        errs.append(np.linalg.norm(host(o) - want))
+        got = host(o)
+        # each schedule's result, element by element, is that schedule's
+        # exact-arithmetic iterate: the step counts reach the kernel
+        assert_factor_elementwise(got, a.astype(np.float64), f"schedule {q}+{c}", q, c)
+        errs.append(np.linalg.norm(got - want))
+    errs = errs[:3]
     assert errs[0] > errs[1] > errs[2]
     assert errs[2] <= polar_bound(a.astype(np.float64)) * np.linalg.norm(want)
 
 
 # -- the outer step --------------------------------------------------------------
 
-@pytest.mark.parametrize("m,n", [(192, 64), (64, 192), (257, 255)])
-def test_outer_orthogonal_step(m, n):
+@pytest.mark.parametrize("m,n,scale", [(192, 64, 0.02), (64, 192, 1.0), (257, 255, 0.02)])
+def test_outer_orthogonal_step(m, n, scale):
+    """theta - scale * P from the last product's epilogue.  At scale 1 the
+    rounding of theta' is no larger than P's own, so every element of P is
+    resolved to its tolerance."""
     seed = 900 + m
     theta = synth.global0(seed, m * n, device=DEV)
     avg = synth.worker_checkpoint(seed, 0, 0, theta)
     th_h, avg_h = host(theta), host(avg)
-    scale = 0.02
     want = opolar.outer_orthogonal_step(th_h.reshape(m, n), avg_h.reshape(m, n), scale).reshape(-1)
     upd = (th_h - avg_h).reshape(m, n)
     dl.dl_outer_orthogonal_step(theta, avg, m, n, scale, workspace(m, n))
     got = host(theta)
+    assert_step_elementwise(got.reshape(m, n), th_h.reshape(m, n), upd, scale, f"step {m}x{n}")
     p_err = polar_bound(upd) * math.sqrt(min(m, n))            # ||P||_F = sqrt(r)
     err = np.linalg.norm(got - want)
     print(f"step {m}x{n}: err_F={err:.3e} bound={scale * p_err:.3e}", flush=True)
@@ -732,7 +776,9 @@ def test_outer_orthogonal_step_batch(m, n, batch):
     for b in range(batch):
         want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
         upd = th_h[b] - av_h[b]
-        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        got = host(thetas[b]).reshape(m, n)
+        assert_step_elementwise(got, th_h[b], upd, scale, f"batch {m}x{n} [{b}]")
+        err = np.linalg.norm(got - want)
         bound = scale * polar_bound(upd) * math.sqrt(min(m, n)) + 2 * U32 * np.linalg.norm(want)
         est = scale * polar_estimate(upd) * math.sqrt(min(m, n)) + 2 * U32 * np.linalg.norm(want)
         print(f"batch {m}x{n} [{b}]: err_F={err:.3e} estimate={est:.3e}", flush=True)
@@ -761,7 +807,9 @@ def test_outer_orthogonal_step_largest_batch():
     for b in check:
         want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
         upd = th_h[b] - av_h[b]
-        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        got = host(thetas[b]).reshape(m, n)
+        assert_step_elementwise(got, th_h[b], upd, scale, f"largest batch [{b}]")
+        err = np.linalg.norm(got - want)
         est = scale * polar_estimate(upd) * math.sqrt(n) + 2 * U32 * np.linalg.norm(want)
         assert err <= est, (b, err, est)
     extra = synth.global0(1700, m * n, device=DEV)
@@ -789,7 +837,9 @@ def test_outer_orthogonal_step_batch_unaligned_views():
     for b in range(batch):
         want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
         upd = th_h[b] - av_h[b]
-        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        got = host(thetas[b]).reshape(m, n)
+        assert_step_elementwise(got, th_h[b], upd, scale, f"unaligned [{b}]")
+        err = np.linalg.norm(got - want)
         est = scale * polar_estimate(upd) * math.sqrt(min(m, n)) + 2 * U32 * np.linalg.norm(want)
         assert err <= est, (b, err, est)
         assert float(bufs_t[b][0]) == float(synth.global0(1500 + b, 1, device=DEV)[0])
@@ -810,13 +860,15 @@ def test_outer_orthogonal_step_batch_large_tiles(m, n):
     check = (0, batch - 1)
     th_h = {b: host(thetas[b]).reshape(m, n) for b in check}
     av_h = {b: host(avgs[b]).reshape(m, n) for b in check}
-    scale = 0.02
+    scale = 1.0
     ws = torch.empty(dl.dl_polar_workspace_bytes_batch(m, n, batch) // 4 + 1, device=DEV)
     dl.dl_outer_orthogonal_step_batch(thetas, avgs, m, n, scale, ws)
     for b in check:
         want = opolar.outer_orthogonal_step(th_h[b], av_h[b], scale)
         upd = th_h[b] - av_h[b]
-        err = np.linalg.norm(host(thetas[b]).reshape(m, n) - want)
+        got = host(thetas[b]).reshape(m, n)
+        assert_step_elementwise(got, th_h[b], upd, scale, f"large-tile batch {m}x{n} [{b}]")
+        err = np.linalg.norm(got - want)
         est = scale * polar_estimate(upd) * math.sqrt(r) + 2 * U32 * np.linalg.norm(want)
         print(f"large-tile batch {m}x{n} [{b}]: err_F={err:.3e} estimate={est:.3e}", flush=True)
         assert err <= est
@@ -832,13 +884,15 @@ def test_outer_orthogonal_step_batch_full_size():
     avgs = [synth.worker_checkpoint(960 + b, 0, 0, t) for b, t in enumerate(thetas)]
     th_h = [host(t).reshape(rows, cols) for t in thetas]
     av_h = [host(a).reshape(rows, cols) for a in avgs]
-    scale = 1e-3
+    scale = 1.0           # theta' rounds no coarser than P: P's elements are resolved
     ws = torch.empty(dl.dl_polar_workspace_bytes_batch(rows, cols, batch) // 4 + 1, device=DEV)
     dl.dl_outer_orthogonal_step_batch(thetas, avgs, rows, cols, scale, ws)
     for b in range(batch):
         upd = th_h[b] - av_h[b]
-        p_got = (th_h[b] - host(thetas[b]).reshape(rows, cols)) / scale
-        want = opolar.polar_factor(upd)
+        got = host(thetas[b]).reshape(rows, cols)
+        e = assert_step_elementwise(got, th_h[b], upd, scale, f"batch full 2048x2048 [{b}]")
+        p_got = (th_h[b] - got) / scale
+        want = e.svd
         rel = np.linalg.norm(p_got - want) / np.linalg.norm(want)
         # theta - s P loses |theta| u per element: bound that on top
         extra = 2 * U32 * np.linalg.norm(th_h[b]) / scale / np.linalg.norm(want)
@@ -874,6 +928,7 @@ def test_orthogonal_step_over_pythia14m_layout(batch, streams):
         want = opolar.outer_orthogonal_step(t, a, scale)
         upd = t - a
         r = min(m.rows, m.cols)
+        assert_step_elementwise(got[sl].reshape(m.rows, m.cols), t, upd, scale, m.name)
         err = np.linalg.norm(got[sl].reshape(m.rows, m.cols) - want)
         est = scale * polar_estimate(upd) * math.sqrt(r) + 2 * U32 * np.linalg.norm(want)
         assert err <= est, (m.name, err, est)
@@ -893,7 +948,8 @@ def test_polar_full_size_against_svd(rows, cols):
     out = torch.empty(rows * cols, device=DEV)
     dl.dl_polar_factor(out, a32, rows, cols, workspace(rows, cols))
     got = host(out).reshape(rows, cols)
-    want = opolar.polar_factor(upd.reshape(rows, cols))
+    e = assert_factor_elementwise(got, upd.reshape(rows, cols), f"full {rows}x{cols}")
+    want = e.svd
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     bound = polar_bound(upd.reshape(rows, cols))
     est = polar_estimate(upd.reshape(rows, cols))
@@ -903,8 +959,9 @@ def test_polar_full_size_against_svd(rows, cols):
 
 
 def test_polar_full_size_embedding_rows():
-    """The 73760 x 2048 embedding: sampled rows against the Gram closed form,
-    and orthonormal columns over the whole factor."""
+    """The 73760 x 2048 embedding: every element of sampled rows against the
+    oracle (through the eigendecomposition of A^T A), and orthonormal columns
+    over the whole factor."""
     rows, cols = 73760, 2048
     seed = 977
     theta = synth.global0(seed, rows * cols, device=DEV)
@@ -915,11 +972,13 @@ def test_polar_full_size_embedding_rows():
     got = host(out).reshape(rows, cols)
     pick = np.random.default_rng(5).choice(rows, 64, replace=False)
     pick = np.concatenate([[0, rows - 1], pick])
-    want = opolar.polar_factor_rows(upd, pick)
-    s = np.linalg.svd(upd.T @ upd, compute_uv=False)
-    kappa_f = np.linalg.norm(upd) / math.sqrt(s[-1])
+    e = pt.expected_rows(upd, pick)
+    z = pt.report(got[pick], e, "embedding rows")
+    assert z <= pt.Z
+    want = e.svd
+    kappa_f = np.linalg.norm(upd) / e.sigma[-1]
     bound = C_POLAR * math.sqrt(cols) * U32 * kappa_f
-    est = estimate_from(math.sqrt(s[0] / s[-1]), cols)
+    est = estimate_from(e.sigma[0] / e.sigma[-1], cols)
     rel = np.linalg.norm(got[pick] - want) / np.linalg.norm(want)
     print(f"embedding rows: rel_F={rel:.3e} bound={bound:.3e} estimate={est:.3e}", flush=True)
     assert rel <= bound
@@ -928,6 +987,40 @@ def test_polar_full_size_embedding_rows():
     orth = np.max(np.abs(gram - np.eye(cols)))
     print(f"embedding orthonormality: {orth:.3e}", flush=True)
     assert orth <= 2 * bound
+
+
+def test_polar_factor_unconverged_directions():
+    """Directions with s / ||A||_F below about 1.4e-7 are not brought to 1 by
+    12 quintic and 6 cubic steps: the iteration maps such an s to
+    phi(s / ||A||_F) < 1, the oracle's iterated factor.  A 2048 x 1024
+    update with a flat spectrum (so ||A||_F = 32 s_max and such directions
+    are still above fp32 noise) and six small singular values at 1e-8 ..
+    2e-7 ||A||_F: every element within the per-element tolerance about the
+    iterated factor, the factor's gain along the small directions short of 1
+    where phi is and at 1 where phi is, and no direction above 1."""
+    rows, cols = 2048, 1024
+    rng = np.random.default_rng(31)
+    xs = np.array([2e-7, 1e-7, 5e-8, 3e-8, 2e-8, 1e-8])
+    k = xs.size
+    f_norm = math.sqrt(cols - k)
+    sv = np.concatenate([np.ones(cols - k), xs * f_norm])
+    a = ((orthonormal(rng, rows, cols) * sv) @ orthonormal(rng, cols, cols).T).astype(np.float32)
+    a64 = a.astype(np.float64)
+    out = torch.empty((rows, cols), device=DEV)
+    dl.dl_polar_factor(out, gpu(a), rows, cols, workspace(rows, cols))
+    got = host(out)
+    e = assert_factor_elementwise(got, a64, "unconverged directions 2048x1024")
+    _, s, vt = np.linalg.svd(a64, full_matrices=False)
+    x = s[-k:] / np.linalg.norm(a64)
+    gain = np.linalg.norm(got @ vt[-k:].T, axis=0)
+    phi = opolar.iteration_map(x)
+    for xi, g, p in zip(x, gain, phi):
+        print(f"  s/||A||_F = {xi:.2e}: phi = {p:.6f}, gain of the fp32 factor = {g:.6f}", flush=True)
+    assert np.all(gain[x <= 2.5e-8] <= 0.9)
+    assert np.all(gain[x >= 0.9e-7] >= 0.999)
+    assert np.linalg.svd(got, compute_uv=False)[0] <= 1 + 1e-5
+    moved = np.max(np.abs(e.iterated - e.svd))
+    print(f"  largest element gap between U phi V^T and U V^T: {moved:.3e}", flush=True)
 
 
 def test_orthogonal_step_over_diffurefill1b_layout_sampled():
@@ -955,7 +1048,7 @@ def test_orthogonal_step_over_diffurefill1b_layout_sampled():
     for m in mats:
         outside[m.offset:m.offset + m.rows * m.cols] = False
     rest = theta[outside].clone()
-    scale = 1e-2
+    scale = 1.0           # theta' rounds no coarser than P: P's elements are resolved
     step.run(theta, avg, scale)
     torch.cuda.synchronize()
     assert torch.equal(theta[outside], rest)
@@ -963,16 +1056,17 @@ def test_orthogonal_step_over_diffurefill1b_layout_sampled():
         t, a = (x.reshape(m.rows, m.cols) for x in before[m.name])
         got = host(theta[m.offset:m.offset + m.rows * m.cols]).reshape(m.rows, m.cols)
         upd = t - a
-        if m.rows > 8 * m.cols:   # the embedding: sampled rows, Gram closed form
+        if m.rows > 8 * m.cols:   # the embedding: sampled rows, Gram eigendecomposition
             pick = np.random.default_rng(9).choice(m.rows, 64, replace=False)
             pick = np.concatenate([[0, m.rows - 1], pick])
-            want = opolar.polar_factor_rows(upd, pick)
-            s = np.linalg.svd(upd.T @ upd, compute_uv=False)
-            est = estimate_from(math.sqrt(s[0] / s[-1]), m.cols)
+            e = pt.expected_rows(upd, pick)
+            est = estimate_from(e.sigma[0] / e.sigma[-1], m.cols)
             t, got = t[pick], got[pick]
         else:
-            want = opolar.polar_factor(upd)
-            est = polar_estimate(upd)
+            e = pt.expected(upd)
+            est = estimate_from(e.sigma[0] / e.sigma[-1], min(m.rows, m.cols))
+        assert_step_elementwise(got, t, None, scale, f"1B step {m.name}", e=e)
+        want = e.svd
         p_got = (t - got) / scale
         rel = np.linalg.norm(p_got - want) / np.linalg.norm(want)
         # theta - s P loses |theta| u per element: bound that on top
