@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "polar.hip"),
-           os.path.join(CSRC, "api.cpp")]
+           os.path.join(CSRC, "noalloc.hip"), os.path.join(CSRC, "api.cpp")]
 DRIVER = os.path.join(PKG, "dlmerge_driver")
 DRIVER_SOURCES = [os.path.join(CSRC, "merge_driver.hip")]
 POLAR_DRIVER = os.path.join(PKG, "dlpolar_driver")

@@ -677,6 +677,39 @@ int dl_outer_orthogonal_step(float* theta, const float* averaged, int64_t rows, 
                                           cubic_steps, workspace, workspace_bytes, stream);
 }
 
+int dl_outer_orthogonal_step_noalloc(float* theta, const float* averaged, int64_t rows,
+                                     int64_t cols, float scale, int quintic_steps,
+                                     int cubic_steps, void* stream) {
+    int64_t need = 0;
+    if (int st = dl_polar_workspace_bytes_batch(rows, cols, 1, &need)) return st;
+    if (quintic_steps < 0 || cubic_steps < 0 || quintic_steps + cubic_steps < 1 ||
+        quintic_steps > 64 || cubic_steps > 64)
+        return DL_E_INVAL;
+    if (need > dlk::kNoallocScratchBytes) return DL_E_TOO_LARGE;
+    if (theta == nullptr || averaged == nullptr) return DL_E_INVAL;
+    if (!aligned_to(theta, alignof(float)) || !aligned_to(averaged, alignof(float)))
+        return DL_E_ALIGN;
+    const int64_t bytes = rows * cols * 4;
+    if (span_of(theta, bytes).overlaps(span_of(averaged, bytes))) return DL_E_INVAL;
+    if (int st = check_device_span(theta, bytes)) return st;
+    if (int st = check_device_span(averaged, bytes)) return st;
+    // the scratch is looked up on the calling thread's current device, which
+    // must be the stream's
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DL_E_HIP;
+    if (s != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return DL_E_HIP;
+        if (sdev != dev) return DL_E_INVAL;
+    }
+    void* ws = nullptr;
+    if (dlk::noalloc_scratch(dev, &ws) != hipSuccess) return DL_E_HIP;
+    const hipError_t err = dlk::polar_iterate(&theta, &averaged, nullptr, &theta, scale, 1, rows,
+                                              cols, quintic_steps, cubic_steps, ws, s);
+    return err == hipSuccess ? DL_OK : DL_E_HIP;
+}
+
 int dl_frag_range(const dl_round* r, int frag, int64_t* offset, int64_t* length) {
     if (r == nullptr || offset == nullptr || length == nullptr) return DL_E_INVAL;
     if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
@@ -720,6 +753,8 @@ const char* dl_strerror(int status) {
         case DL_E_HIP: return "HIP error (pending before the call, or at launch)";
         case DL_E_CAPACITY: return "output array too small";
         case DL_E_NOMEM: return "host memory exhausted";
+        case DL_E_TOO_LARGE:
+            return "matrix needs more workspace than the allocation-free entry point's scratch";
         default: return "unknown status";
     }
 }

@@ -35,12 +35,15 @@ DL_E_ALIGN = -6
 DL_E_HIP = -7
 DL_E_CAPACITY = -8
 DL_E_NOMEM = -9
+DL_E_TOO_LARGE = -10
+DL_NOALLOC_SCRATCH_BYTES = 192 << 20
 
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
            "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_workspace_bytes_batch",
            "dl_polar_factor", "dl_outer_orthogonal_step", "dl_outer_orthogonal_step_batch",
+           "dl_outer_orthogonal_step_noalloc",
            "dl_matmul_workspace_bytes", "dl_matmul_f32",
            "dl_matmul_workspace_bytes_batch", "dl_matmul_f32_batch", "dl_matmul_large_tiles",
            "dl_frag_range", "dl_round_participants", "dl_round_tokens",
@@ -76,6 +79,7 @@ _lib.dl_polar_factor.argtypes = [_p, _p, _i64, _i64, _i32, _i32, _p, _i64, _p]
 _lib.dl_outer_orthogonal_step_batch.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32,
                                                 _i64, _i64, _f32, _i32, _i32, _p, _i64, _p]
 _lib.dl_outer_orthogonal_step.argtypes = [_p, _p, _i64, _i64, _f32, _i32, _i32, _p, _i64, _p]
+_lib.dl_outer_orthogonal_step_noalloc.argtypes = [_p, _p, _i64, _i64, _f32, _i32, _i32, _p]
 _lib.dl_matmul_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(_i64)]
 _lib.dl_matmul_workspace_bytes_batch.argtypes = [_i64, _i64, _i64, _i32, _i32,
                                                  ctypes.POINTER(_i64)]
@@ -316,6 +320,16 @@ def dl_outer_orthogonal_step(theta: Array, averaged: Array, rows: int, cols: int
                                          int(rows), int(cols), float(scale), int(quintic_steps),
                                          int(cubic_steps), w, wb, _stream(stream)),
            "dl_outer_orthogonal_step")
+
+
+def dl_outer_orthogonal_step_noalloc(theta: Array, averaged: Array, rows: int, cols: int,
+                                     scale: float, quintic_steps: int = 12, cubic_steps: int = 6,
+                                     stream=None) -> None:
+    _check(_lib.dl_outer_orthogonal_step_noalloc(_f32_addr(theta, "theta"),
+                                                 _f32_addr(averaged, "averaged"), int(rows),
+                                                 int(cols), float(scale), int(quintic_steps),
+                                                 int(cubic_steps), _stream(stream)),
+           "dl_outer_orthogonal_step_noalloc")
 
 
 def dl_polar_workspace_bytes_batch(rows: int, cols: int, batch: int) -> int:

@@ -106,7 +106,9 @@ enum dl_status {
                             handle unchanged, error left pending), or a failed
                             launch (the round is then failed)                  */
     DL_E_CAPACITY = -8,  /* output array too small                             */
-    DL_E_NOMEM = -9      /* host memory for the round's bookkeeping exhausted  */
+    DL_E_NOMEM = -9,     /* host memory for the round's bookkeeping exhausted  */
+    DL_E_TOO_LARGE = -10 /* matrix workspace beyond the allocation-free entry
+                            point's scratch (DL_NOALLOC_SCRATCH_BYTES)         */
 };
 
 /*
@@ -365,6 +367,37 @@ int dl_polar_factor(float *out, const float *update, int64_t rows, int64_t cols,
 int dl_outer_orthogonal_step(float *theta, const float *averaged, int64_t rows, int64_t cols,
                              float scale, int quintic_steps, int cubic_steps, void *workspace,
                              int64_t workspace_bytes, void *stream);
+
+/*
+ * dl_outer_orthogonal_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; the library's own scratch is used
+ * instead, and the call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).
+ *
+ * The scratch is a file-scope device array of DL_NOALLOC_SCRATCH_BYTES
+ * (192 MiB) that every GPU the entry point runs on holds until the process
+ * ends.  A matrix fits when dl_polar_workspace_bytes(rows, cols) is at most
+ * that: every weight matrix of DiffuRefill-1B but its 73,760 x 2048
+ * embedding, and every one of Pythia-14M.  No part of the scratch needs to
+ * start at zero; every value is written before it is read within a call.
+ *
+ * Calls on one GPU share its scratch.  Calls whose work overlaps in time on
+ * one GPU (different streams, or host threads without ordering) race and
+ * give undefined results; calls in one stream's order are safe.  The
+ * calling thread's current device must be the stream's device (NULL: the
+ * current device's null stream).
+ *
+ * Same arguments and results as dl_outer_orthogonal_step, bit for bit (same
+ * kernels, same workspace layout).  Errors: DL_E_TOO_LARGE (the matrix's
+ * workspace exceeds the scratch), DL_E_INVAL (sizes, steps, overlapping or
+ * out-of-allocation spans, a stream of another device), DL_E_ALIGN,
+ * DL_E_HIP.
+ */
+#define DL_NOALLOC_SCRATCH_BYTES (192LL << 20)
+int dl_outer_orthogonal_step_noalloc(float *theta, const float *averaged, int64_t rows,
+                                     int64_t cols, float scale, int quintic_steps,
+                                     int cubic_steps, void *stream);
 
 /*
  * The same step for a batch of equally shaped weight matrices (the model's

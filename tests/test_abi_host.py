@@ -26,7 +26,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 26
+    assert len(declared) == 27
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -36,12 +36,13 @@ def test_library_exports_every_declared_function():
 def test_status_codes_match_header():
     text = open(HEADER).read()
     for name in ("DL_OK", "DL_E_INVAL", "DL_E_STALE", "DL_E_DUP", "DL_E_QUORUM", "DL_E_STATE",
-                 "DL_E_ALIGN", "DL_E_HIP", "DL_E_CAPACITY", "DL_E_NOMEM", "DL_MEAN",
+                 "DL_E_ALIGN", "DL_E_HIP", "DL_E_CAPACITY", "DL_E_NOMEM", "DL_E_TOO_LARGE",
+                 "DL_MEAN",
                  "DL_DELTA_NESTEROV",
                  "DL_F32", "DL_BF16"):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert m and int(m.group(1)) == getattr(dl, name), name
-    for s in range(-9, 1):
+    for s in range(-10, 1):
         assert dl.dl_strerror(s) != "unknown status"
     assert dl.dl_strerror(-99) == "unknown status"
 
@@ -423,3 +424,23 @@ def test_orthogonalisation_isa(tmp_path):
     sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm)
     assert sizes and all(int(s) == 0 for s in sizes)
 
+
+def test_noalloc_step_host_rules():
+    """The allocation-free outer step: a matrix whose workspace exceeds the
+    library's scratch is refused before anything else runs; so are bad sizes,
+    steps and overlapping or unaligned matrices."""
+    t, a = FAKE, FAKE + (1 << 34)
+    step = lambda **k: dl.dl_outer_orthogonal_step_noalloc(**{**dict(
+        theta=t, averaged=a, rows=300, cols=200, scale=0.1, stream=0), **k})
+    assert dl.dl_polar_workspace_bytes(73760, 2048) > dl.DL_NOALLOC_SCRATCH_BYTES
+    assert dl.dl_polar_workspace_bytes(5632, 2048) <= dl.DL_NOALLOC_SCRATCH_BYTES
+    assert dl.dl_polar_workspace_bytes(50304, 128) <= dl.DL_NOALLOC_SCRATCH_BYTES
+    _expect(dl.DL_E_TOO_LARGE, step, rows=73760, cols=2048)
+    _expect(dl.DL_E_TOO_LARGE, step, rows=2048, cols=73760)
+    _expect(dl.DL_E_INVAL, step, rows=0)
+    _expect(dl.DL_E_INVAL, step, quintic_steps=0, cubic_steps=0)
+    _expect(dl.DL_E_INVAL, step, cubic_steps=65)
+    _expect(dl.DL_E_INVAL, step, averaged=t + 4 * 1000)            # overlaps theta
+    _expect(dl.DL_E_INVAL, step, theta=0)
+    _expect(dl.DL_E_ALIGN, step, theta=t + 2)
+    assert dl.dl_strerror(dl.DL_E_TOO_LARGE) != "unknown status"
