@@ -626,8 +626,14 @@ def main():
             "traffic": measured_traffic(w.key, dom),
             "algorithmic_bytes_per_launch": dd["bytes"] // dd["launches"],
         }
-    value = ab["per_round"] / (ms / 1e3) / 1e9
+    # value: the HBM bytes the timed schedule moves per round / round time.
+    # The algorithmic bytes of the separate-close schedule (every arrival
+    # folded, then the close) are reported beside it: the fused close moves
+    # fewer bytes for the same round, so dividing those by its time would
+    # credit bytes it never streams.
     moved = ab["per_round_fused"] if fused else ab["per_round"]
+    value = moved / (ms / 1e3) / 1e9
+    algorithmic = ab["per_round"] / (ms / 1e3) / 1e9
     out = {
         "metric": "merge-round throughput: effective HBM GB/s and merged params/s; % of HBM peak",
         "value": round(value, 1),
@@ -655,12 +661,17 @@ def main():
                                if fused else
                                "each arrival folded on its own; the close a separate pass"),
         },
-        "value_basis": ("algorithmic bytes of the round with a separate close (every arrival "
-                        "folded, then every state buffer read and written once) / round time"),
+        "value_basis": ("HBM bytes the timed schedule moves per round (each buffer a pass "
+                        "touches counted once per pass) / round time"),
         "moved_bytes_per_param": moved // w.n_params,
-        "moved_GB_per_s": round(moved / (ms / 1e3) / 1e9, 1),
-        "merged_params_per_s": round(w.n_params / (ms / 1e3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "merged_params_per_s": round(w.n_params / (ms / 1e3), 1),
+        "algorithmic_bytes_per_param": ab["per_param"],
+        "algorithmic_GB_per_s": round(algorithmic, 1),
+        "algorithmic_frac_of_hbm_peak": round(algorithmic / HBM_PEAK_GBS, 4),
+        "algorithmic_basis": ("bytes of the round with a separate close (every arrival folded "
+                              "and written back, then every state buffer read and written "
+                              "once) / round time"),
         "kernel_time_ms_per_step": (round(total_kernel_ms / args.steps, 4) if kinds else None),
         "round_ms": round_ms,
         "graph": graph,

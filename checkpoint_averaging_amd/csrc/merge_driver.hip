@@ -7,13 +7,16 @@
 //   dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
 //                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
-//                  [--streams S] [--side 1]
+//                  [--streams S] [--side 1] [--inplace 0|1]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
 // folded (token-weighted delta in delta mode) and the fragment is closed
 // (mean, or outer Nesterov lr 0.7 / momentum 0.9), with the EMA (beta 0.9)
 // fused in when enabled.  With --fused 1 (default) the last worker is folded
-// in the same pass as the close.  With --streams S > 1 every fragment's round
+// in the same pass as the close.  With --inplace 1 (default) a mean round
+// writes the new global over the running sum and the two buffers swap roles
+// for the next round, as the benchmark does; --inplace 0 writes it to a
+// separate global buffer.  With --streams S > 1 every fragment's round
 // is its own handle on one of S streams (rounds in flight together), the
 // arrivals issued round-robin across fragments.  With --side 1 a round is
 // instead the side averages and the worker adoption over the whole buffer:
@@ -29,6 +32,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "dlmerge.h"
@@ -103,6 +107,7 @@ struct Args {
     bool fused = true;
     int streams = 1;
     bool side = false;
+    bool inplace = true;
 };
 
 [[noreturn]] void usage() {
@@ -110,7 +115,7 @@ struct Args {
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
                  "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n"
-                 "       [--side 0|1]\n");
+                 "       [--side 0|1] [--inplace 0|1]\n");
     std::exit(2);
 }
 
@@ -139,6 +144,7 @@ Args parse(int argc, char** argv) {
         else if (k == "--fused") a.fused = std::atoi(v.c_str()) != 0;
         else if (k == "--streams") a.streams = std::atoi(v.c_str());
         else if (k == "--side") a.side = std::atoi(v.c_str()) != 0;
+        else if (k == "--inplace") a.inplace = std::atoi(v.c_str()) != 0;
         else usage();
     }
     if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0 || a.streams < 1 ||
@@ -235,22 +241,24 @@ int main(int argc, char** argv) {
                 const char* base = static_cast<const char*>(ck[i]) + a.offsets[f] * esz;
                 const int64_t tok = 19660800 + 1000 * int64_t(i);
                 const bool last = i == a.workers - 1;
+                float* out = a.inplace ? acc : theta;   // mean rounds: where the mean lands
                 if (last && a.fused) {
                     if (a.delta)
                         DLCHECK(dl_fold_and_outer_nesterov(h, f, i, tag, base, dt, tok, theta, m,
                                                            0.7f, 0.9f, e, 0.9f));
                     else
-                        DLCHECK(dl_fold_and_finalize_mean(h, f, i, tag, base, dt, theta, e, 0.9f));
+                        DLCHECK(dl_fold_and_finalize_mean(h, f, i, tag, base, dt, out, e, 0.9f));
                     continue;
                 }
                 DLCHECK(dl_fold_checkpoint(h, f, i, tag, base, dt, a.delta ? theta : nullptr, tok));
                 if (last) {
                     if (a.delta) DLCHECK(dl_outer_nesterov(h, f, theta, m, 0.7f, 0.9f, e, 0.9f));
-                    else DLCHECK(dl_finalize_mean(h, f, theta, e, 0.9f));
+                    else DLCHECK(dl_finalize_mean(h, f, out, e, 0.9f));
                 }
             }
         }
         for (auto h : rd) DLCHECK(dl_round_end(h));
+        if (!a.delta && a.inplace) std::swap(theta, acc);   // the sum's buffer holds the new global
         for (int i = 1; i < a.streams; ++i) {
             HIPCHECK(hipEventRecord(joins[i], fs[i]));
             HIPCHECK(hipStreamWaitEvent(s, joins[i], 0));

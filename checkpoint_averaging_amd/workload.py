@@ -9,7 +9,16 @@ round starts (never inside a timed region).
 
 Round structure (all on torch's current stream):
 * plain mean:      for each fragment, fold every worker in its seeded arrival
-                   order, then close the fragment with the mean (+ EMA)
+                   order, then close the fragment with the mean (+ EMA).
+                   The mean is written over the running sum (out == acc),
+                   and after the round the two buffers swap roles: the sum's
+                   buffer is the new global, the old global's the next
+                   round's accumulator.  The mean round never reads the old
+                   global, so this only changes where the result lands.  The
+                   close then writes lines it has just read.  At 1.08B
+                   elements that ran 6-8% faster on MI355X than writing the
+                   mean to a buffer the pass does not read (75% against 70-71%
+                   of 8 TB/s).
 * delta Nesterov:  for each fragment, fold every worker's token-weighted delta
                    in arrival order, then close with the outer Nesterov step
                    (+ EMA)
@@ -27,8 +36,9 @@ _GEN_CHUNK = 1 << 25
 
 
 class GpuWorkload:
-    def __init__(self, w: synth.Workload, device="cuda"):
+    def __init__(self, w: synth.Workload, device="cuda", close_in_place: bool = True):
         self.w = w
+        self.close_in_place = close_in_place
         self.dev = torch.device(device)
         n = w.n_params
         self.delta = w.mode == "delta_nesterov"
@@ -85,6 +95,7 @@ class GpuWorkload:
         run = timer if timer is not None else (lambda kind, n, call: call())
         ema = "_ema" if self.e is not None else ""
         if not self.delta:
+            out = self.acc if self.close_in_place else self.theta
             r = dl.dl_round_begin(tag, dl.DL_MEAN, w.n_params, offs, w.quorum, w.workers,
                                   self.acc)
             try:
@@ -101,12 +112,13 @@ class GpuWorkload:
                         ck = self.ckpts[i][o0:o1]
                         kind = "fold_finalize_mean" + ema + ("_first" if not folds else "")
                         run(kind, o1 - o0, lambda f=f, i=i, ck=ck: dl.dl_fold_and_finalize_mean(
-                            r, f, i, tag, ck, self.theta, self.e, w.beta))
+                            r, f, i, tag, ck, out, self.e, w.beta))
                     else:
                         run("finalize_mean" + ema, o1 - o0,
-                            lambda f=f: dl.dl_finalize_mean(r, f, self.theta, self.e, w.beta))
+                            lambda f=f: dl.dl_finalize_mean(r, f, out, self.e, w.beta))
             finally:
                 dl.dl_round_end(r)
+            self._swap_if_in_place()
         else:
             tok = self.tokens(rnd)
             r = dl.dl_round_begin(tag, dl.DL_DELTA_NESTEROV, w.n_params, offs, w.quorum,
@@ -136,6 +148,12 @@ class GpuWorkload:
                 dl.dl_round_end(r)
 
 
+    def _swap_if_in_place(self) -> None:
+        """After a mean round closed in place, the accumulator holds the new
+        global: the buffers swap roles."""
+        if not self.delta and self.close_in_place:
+            self.theta, self.acc = self.acc, self.theta
+
     def _run_round_streams(self, rnd, tag, timer, fused_close, streams):
         w = self.w
         offs = list(w.frag_offsets)
@@ -147,6 +165,7 @@ class GpuWorkload:
         start = torch.cuda.Event()
         start.record(cur)
         mode = dl.DL_DELTA_NESTEROV if self.delta else dl.DL_MEAN
+        out = self.acc if self.close_in_place else self.theta
         handles = []
         try:
             for f in range(w.n_frags):
@@ -168,14 +187,13 @@ class GpuWorkload:
                             if last and fused_close:
                                 kind = "fold_finalize_mean" + ema + ("_first" if k == 0 else "")
                                 run(kind, o1 - o0, lambda: dl.dl_fold_and_finalize_mean(
-                                    r, f, i, tag, ck, self.theta, self.e, w.beta))
+                                    r, f, i, tag, ck, out, self.e, w.beta))
                             else:
                                 run("fold_first" if k == 0 else "fold", o1 - o0,
                                     lambda: dl.dl_fold_checkpoint(r, f, i, tag, ck))
                                 if last:
                                     run("finalize_mean" + ema, o1 - o0,
-                                        lambda: dl.dl_finalize_mean(r, f, self.theta, self.e,
-                                                                    w.beta))
+                                        lambda: dl.dl_finalize_mean(r, f, out, self.e, w.beta))
                         else:
                             if last and fused_close:
                                 kind = "fold_nesterov" + ema + ("_first" if k == 0 else "")
@@ -197,6 +215,7 @@ class GpuWorkload:
             done = torch.cuda.Event()
             done.record(st)
             cur.wait_event(done)
+        self._swap_if_in_place()
 
 
 def algorithmic_bytes(w: synth.Workload, fused_close: bool = False) -> Dict[str, int]:

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+from checkpoint_averaging_amd import dlmerge as dl
 from checkpoint_averaging_amd import synth
 from checkpoint_averaging_amd.workload import GpuWorkload
 from tests import merge_cases as mc
@@ -189,5 +190,116 @@ def test_full_size_fragment_rounds_on_separate_streams():
         for k, t in (("theta", gw.theta), ("m", gw.m), ("e", gw.e)):
             g, o = gather(t, fw), want[f][k]
             assert mc.bits_equal(g, o), f"frag {f} {k}: {mc.first_mismatch(g, o)}"
+    del gw
+    torch.cuda.empty_cache()
+
+
+def _partial_participants(w, rnd, f, n):
+    """The first n arrivals of a round and fragment that are not among its
+    seeded late workers (the seeded late worker and the worker arriving right
+    after it miss the close)."""
+    order = synth.arrival_order(w, rnd, f)
+    late = synth.late_worker(w, rnd, f)
+    k = order.index(late)
+    missing = {late, order[(k + 1) % len(order)]}
+    return [i for i in order if i not in missing][:n]
+
+
+def _run_partial_round(gw, rnd, tag, parts, quorum, fused):
+    """One round through the C ABI on the workload's full-size buffers (the
+    benchmark's launch configuration), each fragment closed by the given
+    participants in the given order."""
+    w = gw.w
+    offs = list(w.frag_offsets)
+    mode = dl.DL_DELTA_NESTEROV if gw.delta else dl.DL_MEAN
+    tok = synth.token_counts(w, rnd)
+    out = gw.acc if gw.close_in_place else gw.theta
+    r = dl.dl_round_begin(tag, mode, w.n_params, offs, quorum, w.workers, gw.acc)
+    try:
+        for f in range(w.n_frags):
+            o0, o1 = offs[f], offs[f + 1]
+            ps = parts[f]
+            for i in (ps[:-1] if fused else ps):
+                ck = gw.ckpts[i][o0:o1]
+                if gw.delta:
+                    dl.dl_fold_checkpoint(r, f, i, tag, ck, gw.theta, tok[i])
+                else:
+                    dl.dl_fold_checkpoint(r, f, i, tag, ck)
+            if gw.delta:
+                if fused:
+                    dl.dl_fold_and_outer_nesterov(r, f, ps[-1], tag, gw.ckpts[ps[-1]][o0:o1],
+                                                  tok[ps[-1]], gw.theta, gw.m, w.lr, w.mu,
+                                                  gw.e, w.beta)
+                else:
+                    dl.dl_outer_nesterov(r, f, gw.theta, gw.m, w.lr, w.mu, gw.e, w.beta)
+            else:
+                if fused:
+                    dl.dl_fold_and_finalize_mean(r, f, ps[-1], tag, gw.ckpts[ps[-1]][o0:o1], out,
+                                                 gw.e, w.beta)
+                else:
+                    dl.dl_finalize_mean(r, f, out, gw.e, w.beta)
+            assert dl.dl_round_participants(r, f) == list(ps)
+    finally:
+        dl.dl_round_end(r)
+    gw._swap_if_in_place()
+
+
+def _oracle_partial_on_windows(w, wins, parts_of):
+    """The oracle's rounds over the windows, each fragment closed by
+    parts_of(rnd, f) in that order."""
+    orc = oracle.load()
+    res = []
+    for f, fw in enumerate(wins):
+        th0 = np.concatenate([synth.global0(w.seed, L, start=s).numpy() for s, L in fw])
+        theta, m = th0.copy(), np.zeros_like(th0)
+        e = th0.copy() if w.ema else None
+        for r in range(ROUNDS):
+            ps = parts_of(r, f)
+            cks = {i: mc.to_np(torch.cat([synth.worker_checkpoint(
+                w.seed, r, i, synth.global0(w.seed, L, start=s), start=s, dtype=w.ckpt_dtype)
+                for s, L in fw])) for i in ps}
+            if w.mode == "mean":
+                theta = orc.mean_round([cks[i] for i in ps], ema=e, beta=w.beta)
+            else:
+                tok = synth.token_counts(w, r)
+                orc.nesterov_fragment_round(theta, m, [cks[i] for i in ps], [tok[i] for i in ps],
+                                            w.lr, w.mu, e, w.beta)
+        res.append({"theta": theta, "m": m if w.mode != "mean" else None, "e": e})
+    return res
+
+
+@pytest.mark.parametrize("key,n_close", [
+    # every fragment closed by exactly its quorum of 3 of the 5 workers
+    # (GradientMail post, "Completing the run": 10 of 348 rounds closed with 3)
+    ("diffurefill1b_frag_nesterov_ema", 3),
+    # a drain: a single leftover checkpoint closes the round with quorum 1
+    # (technical report, Table 2, row "Recovery")
+    ("diffurefill1b_mean_ema", 1),
+])
+def test_full_size_partial_participation(key, n_close):
+    """Partial participation at full size, on the non-temporal kernels the
+    small parity cases never reach: round 0 closes with the fused last
+    arrival (for the drain: the first arrival folded in the same pass as the
+    close), round 1 with a separate close; sampled windows of every fragment
+    against the oracle, bit for bit."""
+    w = synth.WORKLOADS[key]
+    quorum = min(w.quorum, n_close)
+    parts_of = lambda r, f: _partial_participants(w, r, f, n_close)
+    say(f"[partial] {key}: allocating and generating, {n_close} of {w.workers} close")
+    gw = GpuWorkload(w)
+    for r in range(ROUNDS):
+        gw.generate_checkpoints(r)
+        parts = [parts_of(r, f) for f in range(w.n_frags)]
+        say(f"[partial] {key}: round {r} participants {parts} fused_close={r == 0}")
+        _run_partial_round(gw, r, 300 + r, parts, quorum, fused=(r == 0))
+    torch.cuda.synchronize()
+    wins = windows(w, 16, seed=w.seed + 2)
+    want = _oracle_partial_on_windows(w, wins, parts_of)
+    for f, fw in enumerate(wins):
+        for k, t in (("theta", gw.theta), ("m", gw.m), ("e", gw.e)):
+            if t is None:
+                continue
+            g, o = gather(t, fw), want[f][k]
+            assert mc.bits_equal(g, o), f"{key} frag {f} {k}: {mc.first_mismatch(g, o)}"
     del gw
     torch.cuda.empty_cache()
