@@ -56,6 +56,23 @@ def measured_traffic(workload: str, kind: str):
     return k.get("hbm_bytes_per_launch")
 
 
+def measured_dram_traffic(workload: str, kind: str):
+    """DRAM bytes (read + write) per launch of `kind` from the committed
+    summary of the raw request counters (no copy-kernel scale), if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"dram_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kind)
+    if not k:
+        return None
+    return k["dram_read_bytes_per_launch"] + k["write_bytes_per_launch"]
+
+
 def measured_polar_traffic(kind: str, batching: str):
     """HBM bytes per launch of an orthogonalisation kernel kind from the
     committed counter summary, if it was taken on the current source of the
@@ -485,6 +502,11 @@ def main():
                          "0: all of a shape, split evenly into launches of at most 64)")
     ap.add_argument("--orth-streams", type=int, default=1,
                     help="streams the orthogonalised step's batches are spread over")
+    ap.add_argument("--runtime-fill", action="store_true",
+                    help="fill the inputs with constants through the HIP runtime's memset "
+                         "instead of the seeded generator, so that the process launches no "
+                         "torch kernel (for counter runs under the profiler; timing and "
+                         "traffic do not depend on the values)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB "
                          "(for scaling hardware byte counters)")
@@ -511,7 +533,10 @@ def main():
     ab = algorithmic_bytes(w)
     log(f"[bench] {w.key}: {w.n_params:,} params, {w.workers} {w.ckpt_dtype} workers, "
         f"{w.n_frags} fragment(s), {ab['per_param']} B/param")
-    gw = GpuWorkload(w)
+    if args.runtime_fill and args.copy_calibration_mib:
+        sys.exit("--copy-calibration-mib runs torch kernels; it does not combine with "
+                 "--runtime-fill")
+    gw = GpuWorkload(w, fill="runtime" if args.runtime_fill else "philox")
     gw.generate_checkpoints(0)
     torch.cuda.synchronize()
     log("[bench] inputs resident")
@@ -624,6 +649,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.key, dom),
+            "traffic_raw_dram_counters": measured_dram_traffic(w.key, dom),
             "algorithmic_bytes_per_launch": dd["bytes"] // dd["launches"],
         }
     # value: the HBM bytes the timed schedule moves per round / round time.
@@ -646,7 +672,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded Philox; shapes of the pages' models)",
+        "data": ("synthetic (constants from the HIP runtime's memset; counter run)"
+                 if args.runtime_fill else
+                 "synthetic (seeded Philox; shapes of the pages' models)"),
         "config": {
             "workload": w.key,
             "description": w.description,

@@ -19,6 +19,7 @@
 
 #include "dlmerge.h"
 #include "kernels.h"
+#include "noalloc.h"
 #include "polar.h"
 
 namespace {

@@ -14,7 +14,7 @@
 
 #include <mutex>
 
-#include "polar.h"
+#include "noalloc.h"
 
 namespace {
 

@@ -8,6 +8,11 @@ orthogonalisation kernels.
         -> HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by
            what the same counter reads for the plain copy kernel of known size
 
+    python -m checkpoint_averaging_amd.profile_summary pmc-dram READ_CSV WRITE_CSV \
+        --workload KEY --command-read CMD --command-write CMD [--json OUT]
+        -> DRAM read bytes from the 32-byte-unit request counter and write bytes
+           from the write requests, per dispatch, with no calibration
+
     python -m checkpoint_averaging_amd.profile_summary polar-stats STATS_CSV --command CMD
     python -m checkpoint_averaging_amd.profile_summary polar-pmc RUN_DIR --command CMD \
         --copy-bytes B [--json OUT]
@@ -341,6 +346,113 @@ def pmc_markdown(s: dict, alg_per_elem: dict, frag_elems: dict) -> str:
     return "\n".join(out) + "\n"
 
 
+# Raw request counters of the L2-to-memory interface, which need no
+# copy-kernel scale: a read counted in 32-byte units towards DRAM (a 64-byte
+# request counts 2, a 128-byte one 4), the request counts FETCH_SIZE is
+# built from, and the write requests with their 64-byte share and the part
+# destined for DRAM.
+DRAM_READ_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                      "TCC_BUBBLE_sum")
+DRAM_WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum")
+
+
+def _per_dispatch(path: str, counters):
+    """{dispatch id: (kernel name, {counter: value})} of one --pmc pass."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] not in counters:
+            continue
+        name, vals = out.setdefault(r["Dispatch_Id"], (r["Kernel_Name"], {}))
+        vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def dram_pmc_summary(read_csv: str, write_csv: str, workload: str, cmd_read: str,
+                     cmd_write: str) -> dict:
+    """Per kernel kind and dispatch: DRAM read bytes from the 32-byte-unit
+    counter; the bytes FETCH_SIZE's formula gives from the same pass's
+    request counts (128 B per TCC_BUBBLE, 32 B per 32-byte request, 64 B per
+    other request), unscaled; write bytes from the write requests (64 B per
+    64-byte request, 32 B per other); the share of write requests that go to
+    DRAM."""
+    reads = _per_dispatch(read_csv, DRAM_READ_COUNTERS)
+    writes = _per_dispatch(write_csv, DRAM_WRITE_COUNTERS)
+    per = defaultdict(lambda: defaultdict(float))
+    for name, v in reads.values():
+        kind = kernel_kind(name)
+        if kind is None:
+            continue
+        d = per[kind]
+        d["launches"] += 1
+        d["dram_read"] += 32 * v.get("TCC_EA0_RDREQ_DRAM_32B_sum", 0.0)
+        bubble = v.get("TCC_BUBBLE_sum", 0.0)
+        r32 = v.get("TCC_EA0_RDREQ_32B_sum", 0.0)
+        rall = v.get("TCC_EA0_RDREQ_sum", 0.0)
+        d["fetch_formula"] += 128 * bubble + 64 * (rall - bubble - r32) + 32 * r32
+        d["read_requests"] += rall
+    for name, v in writes.values():
+        kind = kernel_kind(name)
+        if kind is None:
+            continue
+        d = per[kind]
+        d["write_launches"] += 1
+        w64 = v.get("TCC_EA0_WRREQ_64B_sum", 0.0)
+        wall = v.get("TCC_EA0_WRREQ_sum", 0.0)
+        d["write"] += 64 * w64 + 32 * (wall - w64)
+        d["write_requests"] += wall
+        d["write_requests_dram"] += v.get("TCC_EA0_WRREQ_DRAM_sum", 0.0)
+    kernels = {}
+    for kind, d in per.items():
+        n, nw = d["launches"] or 1, d["write_launches"] or 1
+        kernels[kind] = {
+            "launches": int(d["launches"]),
+            "dram_read_bytes_per_launch": round(d["dram_read"] / n),
+            "fetch_formula_bytes_per_launch": round(d["fetch_formula"] / n),
+            "read_bytes_per_request": (round(d["dram_read"] / d["read_requests"], 2)
+                                       if d["read_requests"] else None),
+            "write_bytes_per_launch": round(d["write"] / nw),
+            "write_requests_to_dram": (round(d["write_requests_dram"] / d["write_requests"], 4)
+                                       if d["write_requests"] else None),
+        }
+    return {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+            "command_read": cmd_read, "command_write": cmd_write, "kernels": kernels}
+
+
+def dram_pmc_markdown(s: dict, alg_per_elem: dict, frag_elems: dict) -> str:
+    out = [f"# Merge kernels: DRAM traffic per dispatch from raw request counters "
+           f"({s['workload']})", "",
+           "Two rocprofv3 --pmc passes of the same command, no copy-kernel calibration:",
+           "- reads: TCC_EA0_RDREQ_DRAM_32B (32-byte units, a 128-byte request counted 4) x 32 B,"
+           " beside the FETCH_SIZE formula over the same pass's TCC_EA0_RDREQ, "
+           "TCC_EA0_RDREQ_32B and TCC_BUBBLE (unscaled);",
+           "- writes: 64 B per TCC_EA0_WRREQ_64B + 32 B per other TCC_EA0_WRREQ, and the share "
+           "of write requests counted towards DRAM (TCC_EA0_WRREQ_DRAM).", "",
+           "Commands:", "", "```", s["command_read"], s["command_write"], "```", "",
+           f"Kernel source hash: `{s['kernel_source_hash']}`", "",
+           "| kind | launches | DRAM read / launch (GB) | FETCH_SIZE formula / launch (GB) | "
+           "read bytes per request | write / launch (GB) | writes to DRAM | "
+           "algorithmic / launch (GB) | (read + write) / algorithmic |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for kind, k in sorted(s["kernels"].items()):
+        alg = alg_per_elem.get(kind.replace("_bf16", ""), 0) * frag_elems.get(kind, 0)
+        tot = k["dram_read_bytes_per_launch"] + k["write_bytes_per_launch"]
+        ratio = f"{tot / alg:.4f}" if alg else "n/a"
+        out.append(f"| {kind} | {k['launches']} | {k['dram_read_bytes_per_launch'] / 1e9:.4f} | "
+                   f"{k['fetch_formula_bytes_per_launch'] / 1e9:.4f} | "
+                   f"{k['read_bytes_per_request']} | {k['write_bytes_per_launch'] / 1e9:.4f} | "
+                   f"{k['write_requests_to_dram']} | {alg / 1e9:.4f} | {ratio} |")
+    return "\n".join(out) + "\n"
+
+
+def _workload_bytes(key: str, kinds):
+    from . import synth
+    from .workload import algorithmic_bytes
+    w = synth.WORKLOADS[key]
+    sizes = [w.frag_offsets[f + 1] - w.frag_offsets[f] for f in range(w.n_frags)]
+    avg = sum(sizes) / len(sizes)
+    return algorithmic_bytes(w)["per_elem"], {k: avg for k in kinds}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -365,6 +477,13 @@ def main(argv=None):
     d.add_argument("--command", required=True)
     d.add_argument("--copy-bytes", type=int, required=True)
     d.add_argument("--json")
+    e = sub.add_parser("pmc-dram")
+    e.add_argument("read_csv")
+    e.add_argument("write_csv")
+    e.add_argument("--workload", required=True)
+    e.add_argument("--command-read", required=True)
+    e.add_argument("--command-write", required=True)
+    e.add_argument("--json")
     d.add_argument("--batching", default="even",
                    help="how the run batched equally shaped matrices: 'even' (all of a shape, "
                         "split evenly into launches of at most 64) or the fixed batch size")
@@ -381,6 +500,14 @@ def main(argv=None):
         return
     if args.mode == "stats":
         print(stats_markdown(args.stats_csv, args.command, args.title))
+        return
+    if args.mode == "pmc-dram":
+        s = dram_pmc_summary(args.read_csv, args.write_csv, args.workload, args.command_read,
+                             args.command_write)
+        if args.json:
+            with open(args.json, "w") as fh:
+                json.dump(s, fh, indent=1)
+        sys.stdout.write(dram_pmc_markdown(s, *_workload_bytes(args.workload, s["kernels"])))
         return
     s = pmc_summary(args.fetch_csv, args.write_csv, args.workload, args.command_fetch,
                     args.command_write, args.copy_bytes)

@@ -25,6 +25,8 @@ Round structure (all on torch's current stream):
 """
 from __future__ import annotations
 
+import ctypes
+import struct
 from typing import Callable, Dict, List, Optional
 
 import torch
@@ -33,19 +35,68 @@ from . import dlmerge as dl
 from . import synth
 
 _GEN_CHUNK = 1 << 25
+_HIP = None
+
+
+def _hip():
+    global _HIP
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipMemsetD32Async.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t,
+                                           ctypes.c_void_p]
+        _HIP.hipMemsetD16Async.argtypes = [ctypes.c_void_p, ctypes.c_ushort, ctypes.c_size_t,
+                                           ctypes.c_void_p]
+    return _HIP
+
+
+def _runtime_fill(t: torch.Tensor, value: float) -> None:
+    """Fills t with one constant through the HIP runtime's own memset on
+    torch's current stream: no torch kernel is launched (for runs under a
+    counter-collecting profiler, whose host side crashed on one of torch's
+    kernel launches)."""
+    bits = struct.unpack("<I", struct.pack("<f", value))[0]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if t.dtype == torch.bfloat16:
+        st = _hip().hipMemsetD16Async(t.data_ptr(), bits >> 16, t.numel(), stream)
+    else:
+        st = _hip().hipMemsetD32Async(t.data_ptr(), ctypes.c_int(bits - (1 << 32)
+                                                                  if bits >= 1 << 31 else bits),
+                                      t.numel(), stream)
+    if st != 0:
+        raise RuntimeError(f"hipMemset failed ({st})")
 
 
 class GpuWorkload:
-    def __init__(self, w: synth.Workload, device="cuda", close_in_place: bool = True):
+    """fill="philox": the seeded generator's values (parity tests, the
+    benchmark).  fill="runtime": constants written by the HIP runtime's
+    memset, so that the process launches no torch kernel (counter runs; the
+    merge's timing and traffic do not depend on the values)."""
+
+    def __init__(self, w: synth.Workload, device="cuda", close_in_place: bool = True,
+                 fill: str = "philox"):
+        if fill not in ("philox", "runtime"):
+            raise ValueError(fill)
         self.w = w
         self.close_in_place = close_in_place
+        self.fill = fill
         self.dev = torch.device(device)
         n = w.n_params
         self.delta = w.mode == "delta_nesterov"
-        self.theta = synth.global0(w.seed, n, device=self.dev)
-        self.m = torch.zeros(n, dtype=torch.float32, device=self.dev) if self.delta else None
-        self.e = self.theta.clone() if w.ema else None
-        self.acc = torch.empty(n, dtype=torch.float32, device=self.dev)
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        if fill == "philox":
+            self.theta = synth.global0(w.seed, n, device=self.dev)
+            self.m = torch.zeros(n, **f32) if self.delta else None
+            self.e = self.theta.clone() if w.ema else None
+        else:
+            self.theta = torch.empty(n, **f32)
+            _runtime_fill(self.theta, 0.02)
+            self.m = torch.empty(n, **f32) if self.delta else None
+            if self.m is not None:
+                _runtime_fill(self.m, 0.0)
+            self.e = torch.empty(n, **f32) if w.ema else None
+            if self.e is not None:
+                _runtime_fill(self.e, 0.02)
+        self.acc = torch.empty(n, **f32)
         cdt = torch.bfloat16 if w.ckpt_dtype == "bf16" else torch.float32
         self.ckpts: List[torch.Tensor] = [torch.empty(n, dtype=cdt, device=self.dev)
                                           for _ in range(w.workers)]
@@ -55,6 +106,11 @@ class GpuWorkload:
         """Worker checkpoints of round rnd: global0 + seeded drift (chunked so
         the generator's temporaries stay small)."""
         w, n = self.w, self.w.n_params
+        if self.fill == "runtime":
+            for i, c in enumerate(self.ckpts):
+                _runtime_fill(c, 0.02 + 1e-3 * (i + 1))
+            self.ckpt_round = rnd
+            return
         for s in range(0, n, _GEN_CHUNK):
             c = min(_GEN_CHUNK, n - s)
             th0 = synth.global0(w.seed, c, device=self.dev, start=s)

@@ -116,3 +116,60 @@ def test_source_hash_ignores_comments_only():
     assert strip(src) == strip(same)
     assert strip(src) != strip(code)
     assert '"http://x /* kept */"' in strip(src)      # string literals untouched
+
+
+def test_dram_summary_counts_bytes_from_requests(tmp_path):
+    """Raw request counters: 32 B per 32-byte unit of DRAM reads, the
+    FETCH_SIZE formula over the request counts, 64 B per 64-byte write
+    request and 32 B per other."""
+    fold = ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldSum<float, "
+            "false>, true>(...)")
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(tmp_path / "r.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        for d in ("1", "2"):
+            # 1000 read requests of 128 B, seen as TCC_BUBBLE, plus 10 of 32 B
+            for c, v in (("TCC_EA0_RDREQ_DRAM_32B_sum", 4 * 1000 + 10),
+                         ("TCC_EA0_RDREQ_sum", 1010), ("TCC_EA0_RDREQ_32B_sum", 10),
+                         ("TCC_BUBBLE_sum", 1000)):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": fold, "Counter_Name": c,
+                            "Counter_Value": v})
+        w.writerow({"Dispatch_Id": "3", "Kernel_Name": "other_kernel", "Counter_Name":
+                    "TCC_EA0_RDREQ_DRAM_32B_sum", "Counter_Value": 7})
+    with open(tmp_path / "w.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=fields)
+        w.writeheader()
+        for d in ("1", "2"):
+            for c, v in (("TCC_EA0_WRREQ_sum", 600), ("TCC_EA0_WRREQ_64B_sum", 500),
+                         ("TCC_EA0_WRREQ_DRAM_sum", 600)):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": fold, "Counter_Name": c,
+                            "Counter_Value": v})
+    s = ps.dram_pmc_summary(str(tmp_path / "r.csv"), str(tmp_path / "w.csv"), "x", "cr", "cw")
+    k = s["kernels"]["fold"]
+    assert k["launches"] == 2
+    assert k["dram_read_bytes_per_launch"] == 32 * 4010
+    assert k["fetch_formula_bytes_per_launch"] == 128 * 1000 + 32 * 10
+    assert k["read_bytes_per_request"] == pytest.approx(32 * 4010 / 1010, abs=0.01)
+    assert k["write_bytes_per_launch"] == 64 * 500 + 32 * 100
+    assert k["write_requests_to_dram"] == 1.0
+    md = ps.dram_pmc_markdown(s, {"fold": 12}, {"fold": 10})
+    assert "| fold | 2 |" in md
+
+
+@pytest.mark.parametrize("key", ["diffurefill1b_frag_nesterov_ema", "diffurefill1b_mean_ema"])
+def test_raw_dram_counters_match_algorithmic_bytes(key):
+    """The committed raw-counter summaries: DRAM reads (32-byte units) plus
+    writes equal each kernel's algorithmic bytes with no calibration, and
+    FETCH_SIZE's formula over the same requests reads half (every read is a
+    128-byte request, which it counts as 64 bytes)."""
+    d = _committed(f"dram_traffic_{key}.json")
+    w = synth.WORKLOADS[d["workload"]]
+    per = algorithmic_bytes(w)["per_elem"]
+    avg = w.n_params / w.n_frags
+    for kind, k in d["kernels"].items():
+        total = k["dram_read_bytes_per_launch"] + k["write_bytes_per_launch"]
+        assert total == pytest.approx(per[kind] * avg, rel=5e-3), kind
+        assert k["fetch_formula_bytes_per_launch"] == pytest.approx(
+            k["dram_read_bytes_per_launch"] / 2, rel=1e-3), kind
+        assert k["read_bytes_per_request"] == pytest.approx(128.0, rel=1e-3), kind
