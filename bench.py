@@ -60,7 +60,9 @@ def measured_dram_traffic(workload: str, kind: str):
     """DRAM bytes (read + write) per launch of `kind` from the committed
     summary of the raw request counters (no copy-kernel scale), if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"dram_traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"dram_traffic_{workload}_bench.json")
+    if not os.path.exists(path):       # the benchmark's own process first, else the native driver
+        path = os.path.join(ROOT, "profiles", f"dram_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
