@@ -4,15 +4,15 @@
  * A merge round turns the worker checkpoints pushed after H local steps into
  * the next global model and its EMA.  Two variants are provided:
  *
- *  DL_MEAN            plain replacement averaging: every arriving checkpoint
- *                     is folded into a running fp32 sum in arrival order; the
+ *  DL_MEAN            plain replacement averaging: each checkpoint is added
+ *                     to an fp32 running sum in the order it arrives; the
  *                     new global is that sum divided by the number of
  *                     checkpoints (DiffuRefill-1B technical report, section
  *                     "Training system", Table 2, rows "Merger" and "Outer
  *                     step"; DiffuRefill-1B model card, "How it is trained",
  *                     Merging bullet).
- *  DL_DELTA_NESTEROV  fragment merge: per parameter fragment, a token-weighted
- *                     mean of the participants' deltas feeds an outer
+ *  DL_DELTA_NESTEROV  fragment merge: per parameter fragment, the
+ *                     participants' deltas, averaged with token weights, feed an outer
  *                     Nesterov optimizer (GradientMail post "Pythia-14M on
  *                     four rented GPUs and a bucket", section "Getting
  *                     updates through the bucket").
@@ -124,7 +124,8 @@ enum dl_status {
  *
  *   out           receives the handle (set to NULL on error).
  *   round_tag     the round's tag; checkpoints carrying another tag are
- *                 rejected (a rollback is published under a new round number,
+ *                 rejected (after a rollback the merger publishes under a
+ *                 fresh round number,
  *                 technical report, "Training system", failure rule iii).
  *   mode          DL_MEAN or DL_DELTA_NESTEROV.
  *   n_params      flat parameter count, >= 1.
@@ -262,8 +263,8 @@ int dl_ema_update(float *ema, const float *global, int64_t n, float beta, void *
  * Side averages of the globals (technical report, "Training system", Table 2,
  * row "Side averages": besides the EMA, the merger keeps a uniform average
  * (SWA) of the globals and periodic snapshots in the final stretch; section
- * "Data and schedule": the released weights are the uniform average of the
- * 130 globals merged from step ~181k to 200k; section "The final stretch",
+ * "Data and schedule": the published model is the equal-weight average of
+ * the 130 globals committed between steps ~181k and 200k; section "The final stretch",
  * Table 5: averages of the last 3 and the last 5 snapshots).  These calls
  * keep no state: the caller owns the running sum and its count (so the
  * average survives a restart of the merger) and orders the calls on stream.
@@ -320,8 +321,8 @@ int dl_adopt_keep_drift(float *theta, const float *global, const void *pushed, i
 
 /*
  * Outer orthogonalisation (DiffuRefill-1B technical report, "What we
- * measured", "Optimisers": the averaged outer update is replaced by its
- * polar factor; it helped on a 4-worker stand run).  For one weight matrix
+ * measured", "Optimisers": the polar factor takes the place of the averaged
+ * outer update; it was a gain in a run on the 4-worker stand).  For one weight matrix
  * of rows x cols (row-major fp32) whose averaged update is A = U S V^T (thin
  * SVD), the polar factor is P = U V^T.  It is reached by a Newton-Schulz
  * iteration on fp32 MFMA: X_0 = A / ||A||_F, then `quintic_steps` steps of

@@ -51,10 +51,10 @@ static float oracle_ckpt_value(const void *ckpt, int dtype, int64_t j)
 
 /*
  * Plain replacement averaging, folding step (DiffuRefill-1B model card, "How
- * it is trained", Merging: the round's checkpoints are averaged by a plain
- * mean folded into a running fp32 sum as they arrive; technical report,
- * "Training system", Table 2, Outer step: the new global is the mean of the
- * workers).
+ * it is trained", Merging bullet: each checkpoint is added to an fp32 running
+ * sum in the order it comes in, and the round's result is its average;
+ * technical report, "Training system", Table 2, row "Outer step": the next
+ * global is that average of the workers).
  *
  * One arriving checkpoint c of n elements (fp32 or bf16 widened to fp32) is
  * added to the running sum: sum[j] = c[j] for the first arrival of the round,
@@ -76,7 +76,8 @@ void oracle_fold_mean(float *sum, const void *ckpt, int dtype, int64_t n, int fi
  * Plain replacement averaging, closing step: global = sum / N, N the number of
  * checkpoints folded (same passages as above).  If ema is not NULL the EMA of
  * globals is advanced as well (technical report, Table 2, Side averages; model
- * card, EMA bullet: an exponential average of the globals with beta 0.9):
+ * card, EMA bullet: an exponentially weighted average over the sequence of
+ * globals, beta 0.9):
  *     ema[j] = beta * ema[j] + (1 - beta) * global[j]
  * with 1 - beta formed once in binary32.  out may be the same array as sum.
  */
@@ -96,7 +97,8 @@ void oracle_finalize_mean(float *out, const float *sum, int64_t n, int count,
 
 /*
  * Fragment merge, folding step (GradientMail post, "Getting updates through
- * the bucket": the merge takes a token-weighted mean of the deltas).
+ * the bucket": each participant's delta is weighted by its token count and
+ * the weighted deltas are averaged).
  *
  * For one participant's fragment snapshot c (n elements) taken against the
  * fragment's current global theta, with t tokens:
@@ -124,8 +126,8 @@ void oracle_fold_delta(float *acc, const float *theta, const void *ckpt, int dty
 
 /*
  * Fragment merge, closing step (GradientMail post, "Getting updates through
- * the bucket": an outer Nesterov optimizer with learning rate 0.7 and
- * momentum 0.9 applied to the token-weighted mean of the deltas).
+ * the bucket": the averaged, token-weighted delta drives an outer
+ * Nesterov step, learning rate 0.7, momentum 0.9).
  *
  * With W = fp32(sum of the participants' tokens):
  *     dbar  = acc[j] / W                  token-weighted mean delta
@@ -133,8 +135,8 @@ void oracle_fold_delta(float *acc, const float *theta, const void *ckpt, int dty
  *     u     = dbar + mu * m'              Nesterov look-ahead step
  *     theta'= theta[j] - lr * u
  * and, if ema is not NULL, ema[j] = beta * ema[j] + (1 - beta) * theta'.
- * With mu = 0 and lr = 1 this is theta - dbar, the token-weighted mean of the
- * checkpoints: plain parameter averaging (GradientMail post, "What might
+ * With mu = 0 and lr = 1 this is theta - dbar, the checkpoints averaged with
+ * token weights: plain parameter averaging (GradientMail post, "What might
  * explain the loss difference", second follow-up run).
  */
 void oracle_outer_nesterov(float *theta, float *m, const float *acc, int64_t n,

@@ -153,13 +153,13 @@ class Oracle:
                             lr, mu, ema, beta)
 
     # -- side averages (technical report, "Training system", Table 2, row
-    # "Side averages"; "Data and schedule": the released weights are the
-    # uniform average of the globals merged over the final stretch; "The
-    # final stretch", Table 5: averages of the last 3 and 5 snapshots) -----
+    # "Side averages"; "Data and schedule": the published model is an
+    # equal-weight average of the globals committed in the final stretch;
+    # "The final stretch", Table 5: averages of the last 3 and 5 snapshots) --
 
     def swa_average(self, globals_in_commit_order: Sequence[np.ndarray]) -> np.ndarray:
-        """Uniform average of globals: a plain mean, the globals folded into a
-        running fp32 sum in the order they were committed."""
+        """Uniform average of globals: a plain mean, the globals added to an
+        fp32 running sum in the order they were committed."""
         return self.mean_round(globals_in_commit_order)
 
     def snapshot_average(self, snapshots_oldest_first: Sequence[np.ndarray]) -> np.ndarray:

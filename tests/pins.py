@@ -475,7 +475,7 @@ def pin_delta_sign_and_weights(orc):
 
 
 def pin_uniform_average_of_130_globals(orc):
-    """The released weights are the uniform average of 130 globals (technical
+    """The published model averages 130 globals with equal weights (technical
     report, "Data and schedule").  Dyadic globals with 14 fraction bits keep
     every partial sum of 130 of them exact in binary32, so the average must be
     the correctly rounded rational mean; the last-3 and last-5 snapshot
