@@ -7,7 +7,7 @@
 //   dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
 //                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
-//                  [--streams S] [--side 1] [--inplace 0|1]
+//                  [--streams S] [--side 1] [--inplace 0|1] [--host-timing 1]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
 // folded (token-weighted delta in delta mode) and the fragment is closed
@@ -16,7 +16,11 @@
 // in the same pass as the close.  With --inplace 1 (default) a mean round
 // writes the new global over the running sum and the two buffers swap roles
 // for the next round, as the benchmark does; --inplace 0 writes it to a
-// separate global buffer.  With --streams S > 1 every fragment's round
+// separate global buffer.  With --host-timing 1 the driver also reports the
+// host time each C-ABI call takes to return (validation, the allocation-range
+// checks and the launch; the kernels run asynchronously), averaged per call
+// kind over the timed rounds, and the time of one allocation-range query on
+// its own.  With --streams S > 1 every fragment's round
 // is its own handle on one of S streams (rounds in flight together), the
 // arrivals issued round-robin across fragments.  With --side 1 a round is
 // instead the side averages and the worker adoption over the whole buffer:
@@ -32,6 +36,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <chrono>
+#include <map>
 #include <utility>
 #include <vector>
 
@@ -108,6 +114,7 @@ struct Args {
     int streams = 1;
     bool side = false;
     bool inplace = true;
+    bool host_timing = false;
 };
 
 [[noreturn]] void usage() {
@@ -115,7 +122,7 @@ struct Args {
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
                  "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n"
-                 "       [--side 0|1] [--inplace 0|1]\n");
+                 "       [--side 0|1] [--inplace 0|1] [--host-timing 0|1]\n");
     std::exit(2);
 }
 
@@ -145,6 +152,7 @@ Args parse(int argc, char** argv) {
         else if (k == "--streams") a.streams = std::atoi(v.c_str());
         else if (k == "--side") a.side = std::atoi(v.c_str()) != 0;
         else if (k == "--inplace") a.inplace = std::atoi(v.c_str()) != 0;
+        else if (k == "--host-timing") a.host_timing = std::atoi(v.c_str()) != 0;
         else usage();
     }
     if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0 || a.streams < 1 ||
@@ -210,7 +218,21 @@ int main(int argc, char** argv) {
     for (auto& ev : joins) HIPCHECK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
     const int dt = a.bf16 ? DL_BF16 : DL_F32;
     const int64_t esz = a.bf16 ? 2 : 4;
+    // host time per call kind over the timed rounds (--host-timing)
+    std::map<std::string, std::pair<double, long>> host_us;
+    auto timed = [&](const char* kind, bool on, auto&& call) {
+        if (!a.host_timing || !on) return call();
+        const auto t0 = std::chrono::steady_clock::now();
+        const int st = call();
+        const double us =
+            std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+        auto& h = host_us[kind];
+        h.first += us;
+        h.second += 1;
+        return st;
+    };
     for (int r = 0; r < a.warmup + a.rounds; ++r) {
+        const bool tr = r >= a.warmup;
         if (r == a.warmup) HIPCHECK(hipEventRecord(e0, s));
         if (a.side) {
             const float* snaps[5];
@@ -227,9 +249,11 @@ int main(int argc, char** argv) {
         for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamWaitEvent(fs[i], joins[0], 0));
         std::vector<dl_round*> rd(a.streams > 1 ? n_frags : 1, nullptr);
         for (size_t h = 0; h < rd.size(); ++h)
-            DLCHECK(dl_round_begin(&rd[h], tag, a.delta ? DL_DELTA_NESTEROV : DL_MEAN, a.n, n_frags,
-                                   a.offsets.data(), 1, a.workers, acc,
-                                   fs[h % a.streams]));
+            DLCHECK(timed("round_begin", tr, [&] {
+                return dl_round_begin(&rd[h], tag, a.delta ? DL_DELTA_NESTEROV : DL_MEAN, a.n,
+                                      n_frags, a.offsets.data(), 1, a.workers, acc,
+                                      fs[h % a.streams]);
+            }));
         // One stream: one handle, fragment after fragment (as the benchmark
         // issues a round).  Several streams: one handle per fragment, the
         // arrivals round-robin across fragments.
@@ -244,20 +268,33 @@ int main(int argc, char** argv) {
                 float* out = a.inplace ? acc : theta;   // mean rounds: where the mean lands
                 if (last && a.fused) {
                     if (a.delta)
-                        DLCHECK(dl_fold_and_outer_nesterov(h, f, i, tag, base, dt, tok, theta, m,
-                                                           0.7f, 0.9f, e, 0.9f));
+                        DLCHECK(timed("fold_and_outer_nesterov", tr, [&] {
+                            return dl_fold_and_outer_nesterov(h, f, i, tag, base, dt, tok, theta,
+                                                              m, 0.7f, 0.9f, e, 0.9f);
+                        }));
                     else
-                        DLCHECK(dl_fold_and_finalize_mean(h, f, i, tag, base, dt, out, e, 0.9f));
+                        DLCHECK(timed("fold_and_finalize_mean", tr, [&] {
+                            return dl_fold_and_finalize_mean(h, f, i, tag, base, dt, out, e, 0.9f);
+                        }));
                     continue;
                 }
-                DLCHECK(dl_fold_checkpoint(h, f, i, tag, base, dt, a.delta ? theta : nullptr, tok));
+                DLCHECK(timed("fold_checkpoint", tr, [&] {
+                    return dl_fold_checkpoint(h, f, i, tag, base, dt, a.delta ? theta : nullptr,
+                                              tok);
+                }));
                 if (last) {
-                    if (a.delta) DLCHECK(dl_outer_nesterov(h, f, theta, m, 0.7f, 0.9f, e, 0.9f));
-                    else DLCHECK(dl_finalize_mean(h, f, out, e, 0.9f));
+                    if (a.delta)
+                        DLCHECK(timed("outer_nesterov", tr, [&] {
+                            return dl_outer_nesterov(h, f, theta, m, 0.7f, 0.9f, e, 0.9f);
+                        }));
+                    else
+                        DLCHECK(timed("finalize_mean", tr, [&] {
+                            return dl_finalize_mean(h, f, out, e, 0.9f);
+                        }));
                 }
             }
         }
-        for (auto h : rd) DLCHECK(dl_round_end(h));
+        for (auto h : rd) DLCHECK(timed("round_end", tr, [&] { return dl_round_end(h); }));
         if (!a.delta && a.inplace) std::swap(theta, acc);   // the sum's buffer holds the new global
         for (int i = 1; i < a.streams; ++i) {
             HIPCHECK(hipEventRecord(joins[i], fs[i]));
@@ -270,6 +307,23 @@ int main(int argc, char** argv) {
         float ms = 0.f;
         HIPCHECK(hipEventElapsedTime(&ms, e0, e1));
         std::printf("%d rounds: %.4f ms per round\n", a.rounds, ms / a.rounds);
+    }
+    if (a.host_timing) {
+        for (const auto& kv : host_us)
+            std::printf("host time per call: %-26s %8.2f us (%ld calls)\n", kv.first.c_str(),
+                        kv.second.first / kv.second.second, kv.second.second);
+        // one allocation-range query alone, as the library makes per device span
+        const int reps = 10000;
+        const auto t0 = std::chrono::steady_clock::now();
+        for (int k = 0; k < reps; ++k) {
+            hipDeviceptr_t base = nullptr;
+            size_t size = 0;
+            HIPCHECK(hipMemGetAddressRange(&base, &size, acc + k));
+        }
+        const double us =
+            std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+        std::printf("host time per call: %-26s %8.2f us (%d calls)\n", "hipMemGetAddressRange",
+                    us / reps, reps);
     }
 
     for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamDestroy(fs[i]));
