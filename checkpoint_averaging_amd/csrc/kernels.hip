@@ -15,7 +15,14 @@
 //    deep per-lane unrolling.
 //  * Non-temporal loads and stores for ranges too large to stay in the
 //    256 MB Infinity Cache; ordinary (cached) accesses for small ranges, where
-//    a fragment's accumulator can still be resident at the next fold.
+//    a fragment's accumulator can still be resident at the next fold.  One
+//    stream is always cached: the global theta of the fragment merge, which
+//    every pass over a fragment reads again (each fold and the close).
+//    Leaving the cache to it alone keeps part of theta there from one pass
+//    to the next.  A fragment round took 1.3% (308M elements) and 4.9% (151M)
+//    less time that way on MI355X.  Caching the accumulator or the momentum
+//    and EMA as well was slower, and in the mean merge caching the running
+//    sum was slower.
 //  * Alternating direction: on non-temporal (large) ranges a pass may walk
 //    its tiles from the last to the first, so that consecutive passes over
 //    the same fragment meet where the previous one ended and find part of its
@@ -185,7 +192,7 @@ struct FoldDelta {              // acc = w*(theta - c) (first) or acc + w*(theta
     float w;
     struct Regs { f32x4 a, t, c; };
     template <bool NT> __device__ void load(int64_t p, Regs& r) const {
-        r.t = ld4<NT>(theta, p);
+        r.t = ld4<false>(theta, p);             // cached: every pass reads theta again
         r.c = Ckpt<CT>::template pack<NT>(c, p);
         if constexpr (!FIRST) r.a = ld4<NT>(acc, p);
     }
@@ -239,7 +246,7 @@ struct NesterovClose {          // outer Nesterov from the accumulated weighted 
     struct Regs { f32x4 a, t, m, e; };
     template <bool NT> __device__ void load(int64_t p, Regs& r) const {
         r.a = ld4<NT>(acc, p);
-        r.t = ld4<NT>(theta, p);
+        r.t = ld4<false>(theta, p);             // cached: every pass reads theta again
         r.m = ld4<NT>(m, p);
         if constexpr (EMA) r.e = ld4<NT>(ema, p);
     }
@@ -253,7 +260,7 @@ struct NesterovClose {          // outer Nesterov from the accumulated weighted 
             mm[i] = mi;
             if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
         }
-        st4<NT>(theta, p, t);
+        st4<false>(theta, p, t);
         st4<NT>(m, p, mm);
         if constexpr (EMA) st4<NT>(ema, p, e);
     }
@@ -315,7 +322,7 @@ struct FoldNesterovClose {
     float w, total, lr, mu, beta, omega;
     struct Regs { f32x4 a, t, c, m, e; };
     template <bool NT> __device__ void load(int64_t p, Regs& r) const {
-        r.t = ld4<NT>(theta, p);
+        r.t = ld4<false>(theta, p);             // cached: every pass reads theta again
         r.c = Ckpt<CT>::template pack<NT>(c, p);
         if constexpr (!FIRST) r.a = ld4<NT>(acc, p);
         r.m = ld4<NT>(m, p);
@@ -332,7 +339,7 @@ struct FoldNesterovClose {
             mm[i] = mi;
             if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
         }
-        st4<NT>(theta, p, t);
+        st4<false>(theta, p, t);
         st4<NT>(m, p, mm);
         if constexpr (EMA) st4<NT>(ema, p, e);
     }
