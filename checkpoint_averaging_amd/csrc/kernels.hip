@@ -16,13 +16,16 @@
 //  * Non-temporal loads and stores for ranges too large to stay in the
 //    256 MB Infinity Cache; ordinary (cached) accesses for small ranges, where
 //    a fragment's accumulator can still be resident at the next fold.  One
-//    stream is always cached: the global theta of the fragment merge, which
-//    every pass over a fragment reads again (each fold and the close).
-//    Leaving the cache to it alone keeps part of theta there from one pass
-//    to the next.  A fragment round took 1.3% (308M elements) and 4.9% (151M)
-//    less time that way on MI355X.  Caching the accumulator or the momentum
-//    and EMA as well was slower, and in the mean merge caching the running
-//    sum was slower.
+//    stream is always read through the cache: the global theta of the
+//    fragment merge, which every pass over a fragment reads again (each fold
+//    and the close).  Leaving the cache to it alone keeps part of theta there
+//    from one pass to the next.  On MI355X the 1.08B fragment round took
+//    1.7-3% less time that way (the library's builds alternating in one
+//    process).  The close writes theta non-temporally: the next pass is
+//    another fragment's, so a cached store would only leave dirty lines for
+//    that pass to write back (same round time, measured).  Caching the
+//    accumulator, momentum or EMA as well was slower, and so was caching the
+//    running sum of the mean merge.
 //  * Alternating direction: on non-temporal (large) ranges a pass may walk
 //    its tiles from the last to the first, so that consecutive passes over
 //    the same fragment meet where the previous one ended and find part of its
@@ -260,7 +263,7 @@ struct NesterovClose {          // outer Nesterov from the accumulated weighted 
             mm[i] = mi;
             if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
         }
-        st4<false>(theta, p, t);
+        st4<NT>(theta, p, t);
         st4<NT>(m, p, mm);
         if constexpr (EMA) st4<NT>(ema, p, e);
     }
@@ -339,7 +342,7 @@ struct FoldNesterovClose {
             mm[i] = mi;
             if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
         }
-        st4<false>(theta, p, t);
+        st4<NT>(theta, p, t);
         st4<NT>(m, p, mm);
         if constexpr (EMA) st4<NT>(ema, p, e);
     }

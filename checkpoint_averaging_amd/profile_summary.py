@@ -447,6 +447,9 @@ def dram_pmc_markdown(s: dict, alg_per_elem: dict, frag_elems: dict) -> str:
 def _workload_bytes(key: str, kinds):
     from . import synth
     from .workload import algorithmic_bytes
+    if key == SIDE_WORKLOAD:
+        # every side-average call runs over the whole DiffuRefill-1B buffer
+        return dict(SIDE_BYTES_PER_ELEM), {k: synth.DIFFUREFILL_1B.n_params for k in kinds}
     w = synth.WORKLOADS[key]
     sizes = [w.frag_offsets[f + 1] - w.frag_offsets[f] for f in range(w.n_frags)]
     avg = sum(sizes) / len(sizes)

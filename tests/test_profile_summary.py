@@ -157,19 +157,23 @@ def test_dram_summary_counts_bytes_from_requests(tmp_path):
     assert "| fold | 2 |" in md
 
 
-@pytest.mark.parametrize("key", ["diffurefill1b_frag_nesterov_ema", "diffurefill1b_mean_ema"])
+@pytest.mark.parametrize("key", ["diffurefill1b_frag_nesterov_ema", "diffurefill1b_mean_ema",
+                                 "diffurefill1b_bf16_mean_ema", "diffurefill1b_side_averages",
+                                 "diffurefill1b_frag_nesterov_ema_bench"])
 def test_raw_dram_counters_match_algorithmic_bytes(key):
     """The committed raw-counter summaries: DRAM reads (32-byte units) plus
     writes equal each kernel's algorithmic bytes with no calibration, and
     FETCH_SIZE's formula over the same requests reads half (every read is a
     128-byte request, which it counts as 64 bytes)."""
     d = _committed(f"dram_traffic_{key}.json")
-    w = synth.WORKLOADS[d["workload"]]
-    per = algorithmic_bytes(w)["per_elem"]
-    avg = w.n_params / w.n_frags
+    if d["workload"] == ps.SIDE_WORKLOAD:
+        per, avg = ps.SIDE_BYTES_PER_ELEM, synth.DIFFUREFILL_1B.n_params
+    else:
+        w = synth.WORKLOADS[d["workload"]]
+        per, avg = algorithmic_bytes(w)["per_elem"], w.n_params / w.n_frags
     for kind, k in d["kernels"].items():
         total = k["dram_read_bytes_per_launch"] + k["write_bytes_per_launch"]
-        assert total == pytest.approx(per[kind] * avg, rel=5e-3), kind
+        assert total == pytest.approx(per[kind.replace("_bf16", "")] * avg, rel=5e-3), kind
         assert k["fetch_formula_bytes_per_launch"] == pytest.approx(
             k["dram_read_bytes_per_launch"] / 2, rel=1e-3), kind
         assert k["read_bytes_per_request"] == pytest.approx(128.0, rel=1e-3), kind
