@@ -138,49 +138,67 @@ def test_reconstruction_gives_identical_bits():
         assert mc.bits_equal(ra[k][0], rb[k][0]), k
 
 
-def test_special_values_propagate():
-    """NaN, infinities and subnormals in checkpoints propagate exactly as in
-    the oracle (IEEE semantics, no flush to zero)."""
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_close", "fused_close"])
+@pytest.mark.parametrize("n", [4096 + 3, (1 << 24) + 3], ids=["cached", "non_temporal"])
+def test_special_values_propagate(n, fused):
+    """NaN, infinities and subnormals in checkpoints (and, in the fragment
+    merge, in the global) propagate exactly as in the oracle (IEEE
+    semantics, no flush to zero).  At 2^24 + 3 elements the non-temporal
+    kernels run, passes alternate direction and the fragment merge reads the
+    global through the cache."""
     import oracle
     from checkpoint_averaging_amd import dlmerge as dl
-    n = 4096 + 3
-    rng = np.random.default_rng(3)
+    rng = np.random.default_rng(3 + n)
     base = (0.02 * rng.standard_normal(n)).astype(np.float32)
     specials = np.array([np.nan, np.inf, -np.inf, 1e-40, -1e-42, 2.0 ** -149, -0.0, 3e38],
                         dtype=np.float32)
-    cks = []
-    for i in range(3):
-        c = base.copy()
-        idx = rng.integers(0, n, size=200)
-        c[idx] = specials[rng.integers(0, specials.size, size=200)]
-        cks.append(c)
+    k = max(200, n // 1000)
+
+    def planted(a):
+        a = a.copy()
+        idx = np.concatenate([rng.integers(0, n, size=k), [0, n - 1]])
+        a[idx] = specials[rng.integers(0, specials.size, size=idx.size)]
+        return a
+
+    cks = [planted(base) for _ in range(3)]
     dev = torch.device("cuda")
     acc = torch.empty(n, device=dev)
     out = torch.empty(n, device=dev)
     ema = torch.from_numpy(base.copy()).to(dev)
     e_o = base.copy()
     r = dl.dl_round_begin(1, dl.DL_MEAN, n, [0, n], 1, 3, acc)
-    for i, c in enumerate(cks):
+    for i, c in enumerate(cks[:-1] if fused else cks):
         dl.dl_fold_checkpoint(r, 0, i, 1, torch.from_numpy(c).to(dev))
-    dl.dl_finalize_mean(r, 0, out, ema, 0.9)
+    if fused:
+        dl.dl_fold_and_finalize_mean(r, 0, 2, 1, torch.from_numpy(cks[2]).to(dev), out, ema, 0.9)
+    else:
+        dl.dl_finalize_mean(r, 0, out, ema, 0.9)
     dl.dl_round_end(r)
     g_o = oracle.mean_round(cks, ema=e_o)
     torch.cuda.synchronize()
     assert mc.bits_equal(mc.to_np(out), g_o), mc.first_mismatch(mc.to_np(out), g_o)
-    assert mc.bits_equal(mc.to_np(ema), e_o)
-    # delta mode with the same special values
-    theta = torch.from_numpy(base.copy()).to(dev)
+    assert mc.bits_equal(mc.to_np(ema), e_o), mc.first_mismatch(mc.to_np(ema), e_o)
+    # the fragment merge with the same checkpoints and special values in the
+    # global too, EMA fused into the close
+    th0 = planted(base)
+    theta = torch.from_numpy(th0.copy()).to(dev)
     m = torch.zeros(n, device=dev)
-    th_o, m_o = base.copy(), np.zeros(n, np.float32)
+    ema = torch.from_numpy(th0.copy()).to(dev)
+    th_o, m_o, e_o = th0.copy(), np.zeros(n, np.float32), th0.copy()
+    tok = [1000, 1001, 1002]
     r = dl.dl_round_begin(2, dl.DL_DELTA_NESTEROV, n, [0, n], 1, 3, acc)
-    for i, c in enumerate(cks):
-        dl.dl_fold_checkpoint(r, 0, i, 2, torch.from_numpy(c).to(dev), theta, 1000 + i)
-    dl.dl_outer_nesterov(r, 0, theta, m, 0.7, 0.9)
+    for i, c in enumerate(cks[:-1] if fused else cks):
+        dl.dl_fold_checkpoint(r, 0, i, 2, torch.from_numpy(c).to(dev), theta, tok[i])
+    if fused:
+        dl.dl_fold_and_outer_nesterov(r, 0, 2, 2, torch.from_numpy(cks[2]).to(dev), tok[2], theta,
+                                      m, 0.7, 0.9, ema, 0.9)
+    else:
+        dl.dl_outer_nesterov(r, 0, theta, m, 0.7, 0.9, ema, 0.9)
     dl.dl_round_end(r)
-    oracle.nesterov_fragment_round(th_o, m_o, cks, [1000, 1001, 1002], 0.7, 0.9)
+    oracle.nesterov_fragment_round(th_o, m_o, cks, tok, 0.7, 0.9, e_o, 0.9)
     torch.cuda.synchronize()
-    assert mc.bits_equal(mc.to_np(theta), th_o), mc.first_mismatch(mc.to_np(theta), th_o)
-    assert mc.bits_equal(mc.to_np(m), m_o)
+    for name, g, o in (("theta", theta, th_o), ("m", m, m_o), ("ema", ema, e_o)):
+        assert mc.bits_equal(mc.to_np(g), o), (name, mc.first_mismatch(mc.to_np(g), o))
 
 
 def test_in_place_mean_and_misaligned_checkpoint():
