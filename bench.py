@@ -7,9 +7,11 @@ fragment, then every fragment's close), issued through the C ABI on inputs
 already resident in HBM.  W untimed rounds, then K timed rounds between two
 device synchronisations; every launch is bracketed by HIP events on the
 stream it runs on, giving each kernel's average duration.  Prints one JSON
-line: effective HBM GB/s (algorithmic bytes per round / round time), merged
-params/s, the fraction of the 8 TB/s HBM peak, the roofline of the dominant
-kernel, and the CPU oracle timed on a bounded sample of the same workload.
+line: the HBM bytes the round moves per second, merged params/s, the
+fraction of the 8 TB/s HBM peak, the workload's algorithmic bytes per second,
+the roofline of the dominant kernel, the same round with each fragment's
+arrivals passed in one call (`batched_round`, one pass per fragment), and the
+CPU oracle timed on a bounded sample of the same workload.
 
 Default workload: DiffuRefill-1B (1,075,980,288 fp32 params) in 4 fragments,
 5 fp32 workers, token-weighted delta mean + outer Nesterov (lr 0.7, momentum
@@ -478,6 +480,68 @@ def cpu_baseline_polar(max_seconds: float = 12.0):
                       f"factor, {el:.1f} s on {cpu_model()}"}
 
 
+def batched_round(gw, w, ab, args, torch):
+    """The same round with every fragment's arrivals passed in one
+    several-arrival call that also closes (all checkpoints are resident): one
+    pass per fragment.  Same buffers, same results bit for bit; W untimed and
+    K timed rounds, each launch between events on its stream."""
+    for r in range(args.warmup):
+        gw.run_round(0, tag=7000 + r, batched=True)
+    torch.cuda.synchronize()
+    records, spans = [], []
+
+    def timed(kind, n, call):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        records.append((kind, n, e0, e1))
+
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        r0.record()
+        gw.run_round(0, tag=8000 + r, timer=timed, batched=True)
+        r1.record()
+        spans.append((r0, r1))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"[bench] {args.steps} timed batched rounds: {ms:.3f} ms/round")
+    per = sorted(a.elapsed_time(b) for a, b in spans)
+    kind = records[0][0]
+    launches = len(records)
+    kms = sum(e0.elapsed_time(e1) for _, _, e0, e1 in records)
+    kbytes = sum(ab["per_elem"][k] * n for k, n, _, _ in records)
+    achieved = kbytes / (kms / 1e3) / 1e9
+    moved = ab["per_round_batched"]
+    value = moved / (ms / 1e3) / 1e9
+    return {
+        "round_schedule": ("every arrival of a fragment passed in one call, in arrival order: "
+                           "one pass per fragment folds them all and closes"),
+        "ms_per_step": round(ms, 4),
+        "round_ms_median": round(per[len(per) // 2], 4),
+        "moved_bytes_per_param": ab["per_param_batched"],
+        "moved_GB_per_s": round(value, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "merged_params_per_s": round(w.n_params / (ms / 1e3), 1),
+        "speedup_vs_per_arrival_round": None,
+        "roofline": {
+            "kernel": kind,
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.key, kind),
+            "traffic_raw_dram_counters": measured_dram_traffic(w.key, kind),
+            "algorithmic_bytes_per_launch": kbytes // launches,
+            "avg_ms": round(kms / launches, 4),
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -488,6 +552,9 @@ def main():
     ap.add_argument("--separate-close", action="store_true",
                     help="close each fragment in its own pass after the last fold, instead of "
                          "folding the last arrival into the close")
+    ap.add_argument("--batched", action="store_true",
+                    help="pass each fragment's arrivals to the library in one several-arrival "
+                         "call (every checkpoint resident): one pass per fragment")
     ap.add_argument("--graph", action="store_true",
                     help="capture one round into a HIP graph and time its replays (the "
                          "per-kernel figures still come from event-timed eager rounds)")
@@ -561,7 +628,8 @@ def main():
     streams = ([torch.cuda.Stream() for _ in range(args.fragment_streams)]
                if args.fragment_streams > 0 else None)
     for r in range(args.warmup):
-        gw.run_round(0, tag=r + 1, timer=plain, fused_close=fused, streams=streams)
+        gw.run_round(0, tag=r + 1, timer=plain, fused_close=fused, streams=streams,
+                     batched=args.batched)
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup rounds done")
 
@@ -587,7 +655,7 @@ def main():
             r1 = torch.cuda.Event(enable_timing=True)
             r0.record()
         gw.run_round(0, tag=1000 + r, timer=timed if streams is None else plain,
-                     fused_close=fused, streams=streams)
+                     fused_close=fused, streams=streams, batched=args.batched)
         if streams is None:
             r1.record()
             spans.append((r0, r1))
@@ -603,7 +671,7 @@ def main():
         # replay then runs the same folds and close on the same buffers
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            gw.run_round(0, tag=5000, timer=plain, fused_close=fused)
+            gw.run_round(0, tag=5000, timer=plain, fused_close=fused, batched=args.batched)
         for _ in range(max(args.warmup, 1)):
             g.replay()
         torch.cuda.synchronize()
@@ -659,9 +727,20 @@ def main():
     # folded, then the close) are reported beside it: the fused close moves
     # fewer bytes for the same round, so dividing those by its time would
     # credit bytes it never streams.
-    moved = ab["per_round_fused"] if fused else ab["per_round"]
+    if args.batched:
+        moved = ab["per_round_batched"] if fused else ab["per_round_batched_separate"]
+    else:
+        moved = ab["per_round_fused"] if fused else ab["per_round"]
     value = moved / (ms / 1e3) / 1e9
     algorithmic = ab["per_round"] / (ms / 1e3) / 1e9
+    if args.batched:
+        schedule = ("every arrival of a fragment passed in one call, in arrival order: "
+                    + ("one pass per fragment folds them all and closes" if fused else
+                       "one pass folds them all, the close a separate pass"))
+    else:
+        schedule = ("each arrival folded on its own; the last arrival of each fragment folded "
+                    "in the same pass as the close" if fused else
+                    "each arrival folded on its own; the close a separate pass")
     out = {
         "metric": "merge-round throughput: effective HBM GB/s and merged params/s; % of HBM peak",
         "value": round(value, 1),
@@ -686,10 +765,7 @@ def main():
             "fragments": w.n_frags,
             "algorithmic_bytes_per_param": ab["per_param"],
             "algorithmic_bytes_per_round": ab["per_round"],
-            "round_schedule": ("each arrival folded on its own; the last arrival of each "
-                               "fragment folded in the same pass as the close"
-                               if fused else
-                               "each arrival folded on its own; the close a separate pass"),
+            "round_schedule": schedule,
         },
         "value_basis": ("HBM bytes the timed schedule moves per round (each buffer a pass "
                         "touches counted once per pass) / round time"),
@@ -699,9 +775,10 @@ def main():
         "algorithmic_bytes_per_param": ab["per_param"],
         "algorithmic_GB_per_s": round(algorithmic, 1),
         "algorithmic_frac_of_hbm_peak": round(algorithmic / HBM_PEAK_GBS, 4),
-        "algorithmic_basis": ("bytes of the round with a separate close (every arrival folded "
-                              "and written back, then every state buffer read and written "
-                              "once) / round time"),
+        "algorithmic_basis": ("bytes of the per-arrival round with a separate close (every "
+                              "arrival folded and written back, then every state buffer read "
+                              "and written once) / round time; schedules that fuse passes "
+                              "move fewer bytes (value), so this can exceed what HBM streams"),
         "kernel_time_ms_per_step": (round(total_kernel_ms / args.steps, 4) if kinds else None),
         "round_ms": round_ms,
         "graph": graph,
@@ -710,6 +787,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if not args.batched and streams is None and not args.graph and args.steps > 0:
+        out["batched_round"] = batched_round(gw, w, ab, args, torch)
+        out["batched_round"]["speedup_vs_per_arrival_round"] = round(
+            ms / out["batched_round"]["ms_per_step"], 3)
     if not args.no_cpu_baseline:
         del gw
         torch.cuda.empty_cache()

@@ -108,10 +108,13 @@ namespace {
 
 // Checks shared by every call that folds an arrival: state, indices, tag,
 // duplicate, mode-specific arguments, alignment.  Sets *esize to the
-// checkpoint element size.
+// checkpoint element size.  A call folding several arrivals checks each one
+// after those before it: `tokens_before` is their token sum and `seen` marks
+// every worker already folded into the fragment or earlier in the call.
 int check_arrival(const dl_round* r, int frag, int worker_id, uint64_t ckpt_round_tag,
                   const void* ckpt, int dtype, const float* global, int64_t tokens,
-                  int64_t* esize) {
+                  int64_t* esize, int64_t tokens_before = 0,
+                  const std::vector<char>* seen = nullptr) {
     if (r->failed) return DL_E_STATE;
     if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
     const Fragment& F = r->frags[frag];
@@ -119,13 +122,15 @@ int check_arrival(const dl_round* r, int frag, int worker_id, uint64_t ckpt_roun
     if (worker_id < 0 || worker_id >= r->max_workers) return DL_E_INVAL;
     if (dtype != DL_F32 && dtype != DL_BF16) return DL_E_INVAL;
     if (ckpt_round_tag != r->tag) return DL_E_STALE;
-    if (std::find(F.arrivals.begin(), F.arrivals.end(), worker_id) != F.arrivals.end())
+    if (seen != nullptr ? (*seen)[static_cast<size_t>(worker_id)] != 0
+                        : std::find(F.arrivals.begin(), F.arrivals.end(), worker_id) !=
+                              F.arrivals.end())
         return DL_E_DUP;
     if (r->mode == DL_MEAN) {
         if (global != nullptr) return DL_E_INVAL;
     } else {
         if (global == nullptr || tokens <= 0) return DL_E_INVAL;
-        if (F.tokens > INT64_MAX - tokens) return DL_E_INVAL;
+        if (F.tokens + tokens_before > INT64_MAX - tokens) return DL_E_INVAL;
         if (F.global != nullptr && F.global != global) return DL_E_INVAL;
     }
     if (ckpt == nullptr) return DL_E_INVAL;
@@ -135,11 +140,11 @@ int check_arrival(const dl_round* r, int frag, int worker_id, uint64_t ckpt_roun
     return DL_OK;
 }
 
-// Makes room for one more arrival in the fragment's record before anything is
-// launched, so that recording it after the launch cannot fail.
-int reserve_arrival(Fragment& F) {
+// Makes room for `count` more arrivals in the fragment's record before
+// anything is launched, so that recording them after the launch cannot fail.
+int reserve_arrival(Fragment& F, int count = 1) {
     try {
-        F.arrivals.reserve(F.arrivals.size() + 1);
+        F.arrivals.reserve(F.arrivals.size() + static_cast<size_t>(count));
     } catch (const std::bad_alloc&) {
         return DL_E_NOMEM;
     } catch (const std::length_error&) {
@@ -157,10 +162,17 @@ int after_launch(dl_round* r, hipError_t err) {
     return DL_OK;
 }
 
-// Validates the buffers of a mean close over fragment frag.  `ckpt_s` is the
-// span of an arrival folded in the same pass (empty if none).
-int check_mean_close(dl_round* r, int frag, float* out_global, float* ema, const Span& ckpt_s,
-                     float** out, float** e) {
+// True if s overlaps any of the n spans at ck.
+bool overlaps_any(const Span& s, const Span* ck, size_t n) {
+    for (size_t i = 0; i < n; ++i)
+        if (s.overlaps(ck[i])) return true;
+    return false;
+}
+
+// Validates the buffers of a mean close over fragment frag.  `ck[0..nck)` are
+// the spans of the arrivals folded in the same pass (none for a plain close).
+int check_mean_close(dl_round* r, int frag, float* out_global, float* ema, const Span* ck,
+                     size_t nck, float** out, float** e) {
     if (out_global == nullptr) return DL_E_INVAL;
     if (!aligned_to(out_global, alignof(float)) || (ema && !aligned_to(ema, alignof(float))))
         return DL_E_ALIGN;
@@ -169,21 +181,23 @@ int check_mean_close(dl_round* r, int frag, float* out_global, float* ema, const
     *out = out_global + off;
     const Span acc_s = span_of(acc, n * 4), out_s = span_of(*out, n * 4);
     if (!out_s.same(acc_s) && out_s.overlaps(acc_s)) return DL_E_INVAL;
-    if (out_s.overlaps(ckpt_s)) return DL_E_INVAL;
+    if (overlaps_any(out_s, ck, nck)) return DL_E_INVAL;
     *e = nullptr;
     if (ema != nullptr) {
         *e = ema + off;
         const Span e_s = span_of(*e, n * 4);
-        if (e_s.overlaps(acc_s) || e_s.overlaps(out_s) || e_s.overlaps(ckpt_s)) return DL_E_INVAL;
+        if (e_s.overlaps(acc_s) || e_s.overlaps(out_s) || overlaps_any(e_s, ck, nck))
+            return DL_E_INVAL;
         if (int st = check_device_span(*e, n * 4)) return st;
     }
     if (int st = check_device_span(acc, n * 4)) return st;
     return check_device_span(*out, n * 4);
 }
 
-// Validates the buffers of a Nesterov close over fragment frag.
+// Validates the buffers of a Nesterov close over fragment frag (arrival spans
+// as in check_mean_close).
 int check_nesterov_close(dl_round* r, int frag, float* global, float* momentum, float* ema,
-                         const Span& ckpt_s, float** theta, float** m, float** e) {
+                         const Span* ck, size_t nck, float** theta, float** m, float** e) {
     if (global == nullptr || momentum == nullptr) return DL_E_INVAL;
     if (!aligned_to(global, alignof(float)) || !aligned_to(momentum, alignof(float)) ||
         (ema && !aligned_to(ema, alignof(float))))
@@ -195,19 +209,144 @@ int check_nesterov_close(dl_round* r, int frag, float* global, float* momentum, 
     const Span acc_s = span_of(acc, n * 4), th_s = span_of(*theta, n * 4),
                m_s = span_of(*m, n * 4);
     if (th_s.overlaps(acc_s) || m_s.overlaps(acc_s) || m_s.overlaps(th_s)) return DL_E_INVAL;
-    if (th_s.overlaps(ckpt_s) || m_s.overlaps(ckpt_s)) return DL_E_INVAL;
+    if (overlaps_any(th_s, ck, nck) || overlaps_any(m_s, ck, nck)) return DL_E_INVAL;
     *e = nullptr;
     if (ema != nullptr) {
         *e = ema + off;
         const Span e_s = span_of(*e, n * 4);
         if (e_s.overlaps(acc_s) || e_s.overlaps(th_s) || e_s.overlaps(m_s) ||
-            e_s.overlaps(ckpt_s))
+            overlaps_any(e_s, ck, nck))
             return DL_E_INVAL;
         if (int st = check_device_span(*e, n * 4)) return st;
     }
     if (int st = check_device_span(acc, n * 4)) return st;
     if (int st = check_device_span(*theta, n * 4)) return st;
     return check_device_span(*m, n * 4);
+}
+
+// The arrivals of one call that folds several, validated.
+struct Arrivals {
+    int64_t esize = 0;
+    int64_t tokens = 0;                  // exact sum of the call's token counts
+    std::vector<float> w;                // each count rounded once (DL_DELTA_NESTEROV)
+    std::vector<Span> spans;             // checkpoint spans
+};
+
+// Validates `count` arrivals for fragment frag as that many dl_fold_checkpoint
+// calls in array order would (duplicates within the call included), without
+// recording anything.  Host rules only; check_arrival_spans does the rest.
+int check_arrivals(const dl_round* r, int frag, int count, const int* worker_ids,
+                   const uint64_t* ckpt_round_tags, const void* const* ckpts, int dtype,
+                   const float* global, const int64_t* tokens, Arrivals* a) {
+    if (r->failed) return DL_E_STATE;
+    if (frag < 0 || frag >= r->n_frags()) return DL_E_INVAL;
+    const Fragment& F = r->frags[frag];
+    if (F.closed) return DL_E_STATE;
+    if (count < 1 || count > r->max_workers) return DL_E_INVAL;
+    if (worker_ids == nullptr || ckpt_round_tags == nullptr || ckpts == nullptr)
+        return DL_E_INVAL;
+    if (r->mode == DL_DELTA_NESTEROV && tokens == nullptr) return DL_E_INVAL;
+    std::vector<char> seen;
+    try {
+        seen.assign(static_cast<size_t>(r->max_workers), 0);
+        a->w.reserve(static_cast<size_t>(count));
+        a->spans.reserve(static_cast<size_t>(count));
+    } catch (const std::bad_alloc&) {
+        return DL_E_NOMEM;
+    }
+    for (int wk : F.arrivals) seen[static_cast<size_t>(wk)] = 1;
+    const int64_t off = r->off(frag), n = r->len(frag);
+    const Span acc_s = span_of(r->acc + off, n * 4);
+    const Span th_s = global != nullptr ? span_of(global + off, n * 4) : Span{0, 0};
+    for (int i = 0; i < count; ++i) {
+        const int64_t t = r->mode == DL_DELTA_NESTEROV ? tokens[i] : 0;
+        if (int st = check_arrival(r, frag, worker_ids[i], ckpt_round_tags[i], ckpts[i], dtype,
+                                   global, t, &a->esize, a->tokens, &seen))
+            return st;
+        const Span ck_s = span_of(ckpts[i], n * a->esize);
+        if (ck_s.overlaps(acc_s) || ck_s.overlaps(th_s)) return DL_E_INVAL;
+        seen[static_cast<size_t>(worker_ids[i])] = 1;
+        a->tokens += t;
+        a->w.push_back(static_cast<float>(t));    // nearest-even
+        a->spans.push_back(ck_s);
+    }
+    return DL_OK;
+}
+
+// The device-side checks of a validated call's buffers (after every host rule,
+// as in the one-arrival calls).
+int check_arrival_spans(const dl_round* r, int frag, const void* const* ckpts,
+                        const float* global, const Arrivals& a) {
+    const int64_t off = r->off(frag), n = r->len(frag);
+    if (global != nullptr)
+        if (int st = check_device_span(global + off, n * 4)) return st;
+    if (int st = check_device_span(r->acc + off, n * 4)) return st;
+    for (size_t i = 0; i < a.spans.size(); ++i)
+        if (int st = check_device_span(ckpts[i], n * a.esize)) return st;
+    return DL_OK;
+}
+
+// Launches the folds of a validated call in passes of at most
+// dlk::max_arrivals_per_pass() arrivals, in order; with `close_mean` or
+// `close_nesterov` the last pass also closes the fragment.  Records the
+// arrivals once every pass is launched.
+struct CloseArgs {
+    float* out = nullptr;                // mean: new global (offset to the fragment)
+    float* theta = nullptr;              // Nesterov: global, momentum (offset)
+    float* m = nullptr;
+    float* ema = nullptr;
+    float lr = 0, mu = 0, beta = 0;
+};
+
+int fold_passes(dl_round* r, int frag, int count, const int* worker_ids,
+                const void* const* ckpts, int dtype, const float* global, const Arrivals& a,
+                const CloseArgs* close) {
+    Fragment& F = r->frags[frag];
+    const int64_t off = r->off(frag), n = r->len(frag);
+    float* acc = r->acc + off;
+    const bool bf16 = dtype == DL_BF16;
+    const int kmax = dlk::max_arrivals_per_pass();
+    for (int i = 0; i < count; i += kmax) {
+        const int k = std::min(kmax, count - i);
+        const bool first = i == 0 && F.arrivals.empty();
+        const bool backward = (F.passes & 1) != 0;
+        const bool closing = close != nullptr && i + k == count;
+        hipError_t err;
+        if (r->mode == DL_MEAN) {
+            if (closing) {
+                const float cnt = static_cast<float>(F.arrivals.size() + count);
+                err = dlk::launch_fold_many_finalize_mean(close->out, acc, ckpts + i, k, bf16,
+                                                          first, cnt, close->ema, close->beta,
+                                                          one_minus(close->beta), n, backward,
+                                                          r->stream);
+            } else {
+                err = dlk::launch_fold_sum_many(acc, ckpts + i, k, bf16, n, first, backward,
+                                                r->stream);
+            }
+        } else {
+            const float* theta = global + off;
+            if (closing) {
+                const float total = static_cast<float>(F.tokens + a.tokens);   // exact sum, rounded once
+                err = dlk::launch_fold_many_nesterov(close->theta, close->m, acc, ckpts + i,
+                                                     a.w.data() + i, k, bf16, first, total,
+                                                     close->lr, close->mu, close->ema,
+                                                     close->beta, one_minus(close->beta), n,
+                                                     backward, r->stream);
+            } else {
+                err = dlk::launch_fold_delta_many(acc, theta, ckpts + i, a.w.data() + i, k, bf16,
+                                                  n, first, backward, r->stream);
+            }
+        }
+        if (int st = after_launch(r, err)) return st;
+        F.passes += 1;
+    }
+    F.arrivals.insert(F.arrivals.end(), worker_ids, worker_ids + count);   // reserved
+    if (r->mode == DL_DELTA_NESTEROV) {
+        F.tokens += a.tokens;
+        F.global = global;
+    }
+    if (close != nullptr) F.closed = true;
+    return DL_OK;
 }
 
 }  // namespace
@@ -302,7 +441,7 @@ int dl_finalize_mean(dl_round* r, int frag, float* out_global, float* ema, float
     if (F.closed) return DL_E_STATE;
     if (static_cast<int>(F.arrivals.size()) < r->quorum) return DL_E_QUORUM;
     float *out = nullptr, *e = nullptr;
-    if (int st = check_mean_close(r, frag, out_global, ema, Span{0, 0}, &out, &e)) return st;
+    if (int st = check_mean_close(r, frag, out_global, ema, nullptr, 0, &out, &e)) return st;
 
     const float count = static_cast<float>(F.arrivals.size());
     const hipError_t err =
@@ -324,7 +463,7 @@ int dl_outer_nesterov(dl_round* r, int frag, float* global, float* momentum, flo
     if (static_cast<int>(F.arrivals.size()) < r->quorum) return DL_E_QUORUM;
     if (global == nullptr || global != F.global) return DL_E_INVAL;
     float *theta = nullptr, *m = nullptr, *e = nullptr;
-    if (int st = check_nesterov_close(r, frag, global, momentum, ema, Span{0, 0}, &theta, &m, &e))
+    if (int st = check_nesterov_close(r, frag, global, momentum, ema, nullptr, 0, &theta, &m, &e))
         return st;
 
     const float total = static_cast<float>(F.tokens);    // exact int64 sum, rounded once
@@ -352,7 +491,7 @@ int dl_fold_and_finalize_mean(dl_round* r, int frag, int worker_id, uint64_t ckp
     const Span ck_s = span_of(ckpt, n * esize);
     if (span_of(r->acc + off, n * 4).overlaps(ck_s)) return DL_E_INVAL;
     float *out = nullptr, *e = nullptr;
-    if (int st = check_mean_close(r, frag, out_global, ema, ck_s, &out, &e)) return st;
+    if (int st = check_mean_close(r, frag, out_global, ema, &ck_s, 1, &out, &e)) return st;
     if (int st = check_device_span(ckpt, n * esize)) return st;
     if (int st = reserve_arrival(F)) return st;
 
@@ -383,7 +522,7 @@ int dl_fold_and_outer_nesterov(dl_round* r, int frag, int worker_id, uint64_t ck
     const Span ck_s = span_of(ckpt, n * esize);
     if (span_of(r->acc + off, n * 4).overlaps(ck_s)) return DL_E_INVAL;
     float *theta = nullptr, *m = nullptr, *e = nullptr;
-    if (int st = check_nesterov_close(r, frag, global, momentum, ema, ck_s, &theta, &m, &e))
+    if (int st = check_nesterov_close(r, frag, global, momentum, ema, &ck_s, 1, &theta, &m, &e))
         return st;
     if (int st = check_device_span(ckpt, n * esize)) return st;
     if (int st = reserve_arrival(F)) return st;
@@ -401,6 +540,67 @@ int dl_fold_and_outer_nesterov(dl_round* r, int frag, int worker_id, uint64_t ck
     F.passes += 1;
     F.closed = true;
     return DL_OK;
+}
+
+int dl_fold_checkpoints(dl_round* r, int frag, int count, const int* worker_ids,
+                        const uint64_t* ckpt_round_tags, const void* const* ckpts, int dtype,
+                        const float* global, const int64_t* tokens) {
+    if (r == nullptr) return DL_E_INVAL;
+    Arrivals a;
+    if (int st = check_arrivals(r, frag, count, worker_ids, ckpt_round_tags, ckpts, dtype, global,
+                                tokens, &a))
+        return st;
+    if (int st = check_arrival_spans(r, frag, ckpts, global, a)) return st;
+    if (int st = reserve_arrival(r->frags[frag], count)) return st;
+    return fold_passes(r, frag, count, worker_ids, ckpts, dtype, global, a, nullptr);
+}
+
+int dl_fold_checkpoints_and_finalize_mean(dl_round* r, int frag, int count,
+                                          const int* worker_ids, const uint64_t* ckpt_round_tags,
+                                          const void* const* ckpts, int dtype, float* out_global,
+                                          float* ema, float beta) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->mode != DL_MEAN) return DL_E_STATE;
+    Arrivals a;
+    if (int st = check_arrivals(r, frag, count, worker_ids, ckpt_round_tags, ckpts, dtype,
+                                nullptr, nullptr, &a))
+        return st;
+    Fragment& F = r->frags[frag];
+    if (static_cast<int64_t>(F.arrivals.size()) + count < r->quorum) return DL_E_QUORUM;
+    CloseArgs c;
+    if (int st = check_mean_close(r, frag, out_global, ema, a.spans.data(), a.spans.size(),
+                                  &c.out, &c.ema))
+        return st;
+    if (int st = check_arrival_spans(r, frag, ckpts, nullptr, a)) return st;
+    if (int st = reserve_arrival(F, count)) return st;
+    c.beta = beta;
+    return fold_passes(r, frag, count, worker_ids, ckpts, dtype, nullptr, a, &c);
+}
+
+int dl_fold_checkpoints_and_outer_nesterov(dl_round* r, int frag, int count,
+                                           const int* worker_ids,
+                                           const uint64_t* ckpt_round_tags,
+                                           const void* const* ckpts, int dtype,
+                                           const int64_t* tokens, float* global, float* momentum,
+                                           float lr, float mu, float* ema, float beta) {
+    if (r == nullptr) return DL_E_INVAL;
+    if (r->mode != DL_DELTA_NESTEROV) return DL_E_STATE;
+    Arrivals a;
+    if (int st = check_arrivals(r, frag, count, worker_ids, ckpt_round_tags, ckpts, dtype, global,
+                                tokens, &a))
+        return st;
+    Fragment& F = r->frags[frag];
+    if (static_cast<int64_t>(F.arrivals.size()) + count < r->quorum) return DL_E_QUORUM;
+    CloseArgs c;
+    if (int st = check_nesterov_close(r, frag, global, momentum, ema, a.spans.data(),
+                                      a.spans.size(), &c.theta, &c.m, &c.ema))
+        return st;
+    if (int st = check_arrival_spans(r, frag, ckpts, global, a)) return st;
+    if (int st = reserve_arrival(F, count)) return st;
+    c.lr = lr;
+    c.mu = mu;
+    c.beta = beta;
+    return fold_passes(r, frag, count, worker_ids, ckpts, dtype, global, a, &c);
 }
 
 int dl_ema_update(float* ema, const float* global, int64_t n, float beta, void* stream) {

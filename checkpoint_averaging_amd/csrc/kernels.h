@@ -45,6 +45,29 @@ hipError_t launch_fold_nesterov(float* theta, float* m, const float* acc, const 
                                 float* ema, float beta, float omega, int64_t n, bool backward,
                                 hipStream_t s);
 
+// The passes above for k arrivals at once, 1 <= k <= max_arrivals_per_pass():
+// ckpts[0..k) are the arrivals in arrival order (all fp32, or all bf16), w[i]
+// the token weight of arrival i.  Each gives the bits of k one-arrival passes
+// in that order (the closing ones: k - 1 folds, then the fold and close),
+// with the accumulator read and written once.  `first`: acc holds no earlier
+// arrival of the fragment (it is not read).  k out of range:
+// hipErrorInvalidValue, nothing launched.
+int max_arrivals_per_pass();
+hipError_t launch_fold_sum_many(float* acc, const void* const* ckpts, int k, bool bf16,
+                                int64_t n, bool first, bool backward, hipStream_t s);
+hipError_t launch_fold_delta_many(float* acc, const float* theta, const void* const* ckpts,
+                                  const float* w, int k, bool bf16, int64_t n, bool first,
+                                  bool backward, hipStream_t s);
+hipError_t launch_fold_many_finalize_mean(float* out, const float* sum, const void* const* ckpts,
+                                          int k, bool bf16, bool first, float count, float* ema,
+                                          float beta, float omega, int64_t n, bool backward,
+                                          hipStream_t s);
+hipError_t launch_fold_many_nesterov(float* theta, float* m, const float* acc,
+                                     const void* const* ckpts, const float* w, int k, bool bf16,
+                                     bool first, float total, float lr, float mu, float* ema,
+                                     float beta, float omega, int64_t n, bool backward,
+                                     hipStream_t s);
+
 // out[j] = (((s_0[j] + s_1[j]) + ...) + s_{k-1}[j]) / k, 1 <= k <= 16, in one pass.
 // out must not overlap any snapshot.
 hipError_t launch_snapshot_mean(float* out, const float* const* snaps, int k, int64_t n,

@@ -356,6 +356,182 @@ struct FoldNesterovClose {
     }
 };
 
+// ---- several arrivals in one pass ----------------------------------------------
+//
+// A merger that already holds several arrivals of a fragment (they came in
+// while it waited for its quorum, or a restarted merger finds them waiting)
+// folds them in one pass.  Every arrival's pack is loaded, then the
+// operations of the one-arrival passes run in registers, in arrival order, so
+// the results are those passes' bit for bit; the accumulator (and, when the
+// pass also closes, the global, momentum and EMA) is read and written once
+// instead of once per arrival.  k is a kernel argument: the unrolled loops
+// test it with a uniform branch, so a pass loads only its k checkpoints.
+constexpr int kMaxArrivals = 8;
+
+template <typename CT>
+struct Arrivals {
+    const CT* c[kMaxArrivals];   // fragment-length checkpoints, in arrival order
+    float w[kMaxArrivals];       // token weights (delta folds only)
+    int k;                       // 1 <= k <= kMaxArrivals
+
+    template <bool NT> __device__ void load(int64_t p, f32x4 (&v)[kMaxArrivals]) const {
+#pragma unroll
+        for (int i = 0; i < kMaxArrivals; ++i)
+            if (i < k) v[i] = Ckpt<CT>::template pack<NT>(c[i], p);
+    }
+    // S = c_0 (first) or S + c_0, then S + c_i for each later arrival
+    __device__ f32x4 sum(f32x4 s, const f32x4 (&v)[kMaxArrivals], bool first) const {
+#pragma unroll
+        for (int e = 0; e < kPack; ++e) s[e] = fold_sum(s[e], v[0][e], first);
+#pragma unroll
+        for (int i = 1; i < kMaxArrivals; ++i)
+            if (i < k) {
+#pragma unroll
+                for (int e = 0; e < kPack; ++e) s[e] = fold_sum(s[e], v[i][e], false);
+            }
+        return s;
+    }
+    // A = w_0*(theta - c_0) (first) or A + w_0*(theta - c_0), then A + w_i*(theta - c_i)
+    __device__ f32x4 delta(f32x4 a, f32x4 t, const f32x4 (&v)[kMaxArrivals], bool first) const {
+#pragma unroll
+        for (int e = 0; e < kPack; ++e) a[e] = fold_delta(a[e], t[e], v[0][e], w[0], first);
+#pragma unroll
+        for (int i = 1; i < kMaxArrivals; ++i)
+            if (i < k) {
+#pragma unroll
+                for (int e = 0; e < kPack; ++e) a[e] = fold_delta(a[e], t[e], v[i][e], w[i], false);
+            }
+        return a;
+    }
+    __device__ float sum_one(float s, int64_t j, bool first) const {
+        s = fold_sum(s, Ckpt<CT>::one(c[0], j), first);
+#pragma unroll
+        for (int i = 1; i < kMaxArrivals; ++i)
+            if (i < k) s = fold_sum(s, Ckpt<CT>::one(c[i], j), false);
+        return s;
+    }
+    __device__ float delta_one(float a, float t, int64_t j, bool first) const {
+        a = fold_delta(a, t, Ckpt<CT>::one(c[0], j), w[0], first);
+#pragma unroll
+        for (int i = 1; i < kMaxArrivals; ++i)
+            if (i < k) a = fold_delta(a, t, Ckpt<CT>::one(c[i], j), w[i], false);
+        return a;
+    }
+};
+
+template <typename CT, bool FIRST>
+struct FoldSumMany {            // FoldSum of each arrival in turn
+    float* acc;
+    Arrivals<CT> in;
+    struct Regs { f32x4 s; f32x4 c[kMaxArrivals]; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        in.template load<NT>(p, r.c);
+        if constexpr (!FIRST) r.s = ld4<NT>(acc, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        st4<NT>(acc, p, in.sum(FIRST ? f32x4{} : r.s, r.c, FIRST));
+    }
+    __device__ void scalar(int64_t j) const {
+        acc[j] = in.sum_one(FIRST ? 0.0f : acc[j], j, FIRST);
+    }
+};
+
+template <typename CT, bool FIRST>
+struct FoldDeltaMany {          // FoldDelta of each arrival in turn
+    float* acc;
+    const float* theta;
+    Arrivals<CT> in;
+    struct Regs { f32x4 a, t; f32x4 c[kMaxArrivals]; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.t = ld4<false>(theta, p);             // cached: later passes read theta again
+        in.template load<NT>(p, r.c);
+        if constexpr (!FIRST) r.a = ld4<NT>(acc, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        st4<NT>(acc, p, in.delta(FIRST ? f32x4{} : r.a, r.t, r.c, FIRST));
+    }
+    __device__ void scalar(int64_t j) const {
+        acc[j] = in.delta_one(FIRST ? 0.0f : acc[j], theta[j], j, FIRST);
+    }
+};
+
+// The fragment's remaining arrivals folded and the fragment closed with the
+// mean (+ EMA) in one pass: FoldSumMany followed by MeanClose.  out may be sum.
+template <typename CT, bool FIRST, bool EMA>
+struct FoldManyMeanClose {
+    float* out;
+    const float* sum;
+    Arrivals<CT> in;
+    float* ema;
+    float count, beta, omega;
+    struct Regs { f32x4 s, e; f32x4 c[kMaxArrivals]; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        in.template load<NT>(p, r.c);
+        if constexpr (!FIRST) r.s = ld4<NT>(sum, p);
+        if constexpr (EMA) r.e = ld4<NT>(ema, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        const f32x4 s = in.sum(FIRST ? f32x4{} : r.s, r.c, FIRST);
+        f32x4 g, e;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            g[i] = s[i] / count;
+            if constexpr (EMA) e[i] = ema_step(r.e[i], g[i], beta, omega);
+        }
+        st4<NT>(out, p, g);
+        if constexpr (EMA) st4<NT>(ema, p, e);
+    }
+    __device__ void scalar(int64_t j) const {
+        const float g = in.sum_one(FIRST ? 0.0f : sum[j], j, FIRST) / count;
+        out[j] = g;
+        if constexpr (EMA) ema[j] = ema_step(ema[j], g, beta, omega);
+    }
+};
+
+// The fragment's remaining arrivals folded (token-weighted deltas) and the
+// outer Nesterov step (+ EMA) taken in one pass: FoldDeltaMany followed by
+// NesterovClose.  Theta is read once for every delta and the update.
+template <typename CT, bool FIRST, bool EMA>
+struct FoldManyNesterovClose {
+    float* theta;
+    float* m;
+    const float* acc;
+    Arrivals<CT> in;
+    float* ema;
+    float total, lr, mu, beta, omega;
+    struct Regs { f32x4 a, t, m, e; f32x4 c[kMaxArrivals]; };
+    template <bool NT> __device__ void load(int64_t p, Regs& r) const {
+        r.t = ld4<false>(theta, p);             // cached, as in the one-arrival close
+        in.template load<NT>(p, r.c);
+        if constexpr (!FIRST) r.a = ld4<NT>(acc, p);
+        r.m = ld4<NT>(m, p);
+        if constexpr (EMA) r.e = ld4<NT>(ema, p);
+    }
+    template <bool NT> __device__ void store(int64_t p, const Regs& r) const {
+        const f32x4 a = in.delta(FIRST ? f32x4{} : r.a, r.t, r.c, FIRST);
+        f32x4 t = r.t, mm = r.m, e;
+#pragma unroll
+        for (int i = 0; i < kPack; ++i) {
+            float ti = t[i], mi = mm[i];
+            nesterov_step(a[i], total, lr, mu, ti, mi);
+            t[i] = ti;
+            mm[i] = mi;
+            if constexpr (EMA) e[i] = ema_step(r.e[i], ti, beta, omega);
+        }
+        st4<NT>(theta, p, t);
+        st4<NT>(m, p, mm);
+        if constexpr (EMA) st4<NT>(ema, p, e);
+    }
+    __device__ void scalar(int64_t j) const {
+        float t = theta[j], mj = m[j];
+        const float a = in.delta_one(FIRST ? 0.0f : acc[j], t, j, FIRST);
+        nesterov_step(a, total, lr, mu, t, mj);
+        theta[j] = t;
+        m[j] = mj;
+        if constexpr (EMA) ema[j] = ema_step(ema[j], t, beta, omega);
+    }
+};
+
 // Keep-local-drift adoption on a worker: theta = theta + (g - pushed), the
 // difference rounded first.
 template <typename CT>
@@ -606,6 +782,106 @@ hipError_t launch_fold_nesterov(float* theta, float* m, const float* acc, const 
     if (ema) DLK_FNC(float, false, true);
     DLK_FNC(float, false, false);
 #undef DLK_FNC
+}
+
+namespace {
+
+bool valid_arrivals(int k) { return k >= 1 && k <= kMaxArrivals; }
+
+// The arrivals of one pass; *vec4 is cleared if a checkpoint is not aligned
+// for the 128-bit path.  Slots past k stay null and are never read.
+template <typename CT>
+Arrivals<CT> arrivals(const void* const* ckpts, const float* w, int k, bool* vec4) {
+    Arrivals<CT> in{};
+    in.k = k;
+    for (int i = 0; i < k; ++i) {
+        in.c[i] = static_cast<const CT*>(ckpts[i]);
+        in.w[i] = w != nullptr ? w[i] : 0.0f;
+        *vec4 = *vec4 && ckpt_aligned(ckpts[i], sizeof(CT) == 2);
+    }
+    return in;
+}
+
+}  // namespace
+
+int max_arrivals_per_pass() { return kMaxArrivals; }
+
+hipError_t launch_fold_sum_many(float* acc, const void* const* ckpts, int k, bool bf16,
+                                int64_t n, bool first, bool backward, hipStream_t s) {
+    if (!valid_arrivals(k)) return hipErrorInvalidValue;
+    bool vec4 = aligned16(acc);
+#define DLK_FSM(CT)                                                                         \
+    {                                                                                        \
+        const Arrivals<CT> in = arrivals<CT>(ckpts, nullptr, k, &vec4);                      \
+        if (first) return launch(FoldSumMany<CT, true>{acc, in}, n, vec4, backward, s);      \
+        return launch(FoldSumMany<CT, false>{acc, in}, n, vec4, backward, s);                \
+    }
+    if (bf16) DLK_FSM(uint16_t);
+    DLK_FSM(float);
+#undef DLK_FSM
+}
+
+hipError_t launch_fold_delta_many(float* acc, const float* theta, const void* const* ckpts,
+                                  const float* w, int k, bool bf16, int64_t n, bool first,
+                                  bool backward, hipStream_t s) {
+    if (!valid_arrivals(k)) return hipErrorInvalidValue;
+    bool vec4 = aligned16(acc) && aligned16(theta);
+#define DLK_FDM(CT)                                                                          \
+    {                                                                                         \
+        const Arrivals<CT> in = arrivals<CT>(ckpts, w, k, &vec4);                             \
+        if (first) return launch(FoldDeltaMany<CT, true>{acc, theta, in}, n, vec4, backward, s); \
+        return launch(FoldDeltaMany<CT, false>{acc, theta, in}, n, vec4, backward, s);        \
+    }
+    if (bf16) DLK_FDM(uint16_t);
+    DLK_FDM(float);
+#undef DLK_FDM
+}
+
+hipError_t launch_fold_many_finalize_mean(float* out, const float* sum, const void* const* ckpts,
+                                          int k, bool bf16, bool first, float count, float* ema,
+                                          float beta, float omega, int64_t n, bool backward,
+                                          hipStream_t s) {
+    if (!valid_arrivals(k)) return hipErrorInvalidValue;
+    bool vec4 = aligned16(out) && aligned16(sum) && (ema == nullptr || aligned16(ema));
+#define DLK_FMMC(CT, FIRST, EMA)                                                             \
+    return launch(FoldManyMeanClose<CT, FIRST, EMA>{out, sum, in, ema, count, beta, omega}, n, \
+                  vec4, backward, s)
+#define DLK_FMMC_CT(CT)                                                                      \
+    {                                                                                         \
+        const Arrivals<CT> in = arrivals<CT>(ckpts, nullptr, k, &vec4);                       \
+        if (first) { if (ema) DLK_FMMC(CT, true, true); else DLK_FMMC(CT, true, false); }     \
+        if (ema) DLK_FMMC(CT, false, true);                                                   \
+        DLK_FMMC(CT, false, false);                                                           \
+    }
+    if (bf16) DLK_FMMC_CT(uint16_t);
+    DLK_FMMC_CT(float);
+#undef DLK_FMMC_CT
+#undef DLK_FMMC
+}
+
+hipError_t launch_fold_many_nesterov(float* theta, float* m, const float* acc,
+                                     const void* const* ckpts, const float* w, int k, bool bf16,
+                                     bool first, float total, float lr, float mu, float* ema,
+                                     float beta, float omega, int64_t n, bool backward,
+                                     hipStream_t s) {
+    if (!valid_arrivals(k)) return hipErrorInvalidValue;
+    bool vec4 = aligned16(theta) && aligned16(m) && aligned16(acc) &&
+                (ema == nullptr || aligned16(ema));
+#define DLK_FMNC(CT, FIRST, EMA)                                                             \
+    return launch(FoldManyNesterovClose<CT, FIRST, EMA>{theta, m, acc, in, ema, total, lr, mu, \
+                                                        beta, omega},                        \
+                  n, vec4, backward, s)
+#define DLK_FMNC_CT(CT)                                                                      \
+    {                                                                                         \
+        const Arrivals<CT> in = arrivals<CT>(ckpts, w, k, &vec4);                             \
+        if (first) { if (ema) DLK_FMNC(CT, true, true); else DLK_FMNC(CT, true, false); }     \
+        if (ema) DLK_FMNC(CT, false, true);                                                   \
+        DLK_FMNC(CT, false, false);                                                           \
+    }
+    if (bf16) DLK_FMNC_CT(uint16_t);
+    DLK_FMNC_CT(float);
+#undef DLK_FMNC_CT
+#undef DLK_FMNC
 }
 
 namespace {

@@ -8,6 +8,7 @@
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
 //                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
 //                  [--streams S] [--side 1] [--inplace 0|1] [--host-timing 1]
+//                  [--batched 0|1]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
 // folded (token-weighted delta in delta mode) and the fragment is closed
@@ -20,7 +21,9 @@
 // host time each C-ABI call takes to return (validation, the allocation-range
 // checks and the launch; the kernels run asynchronously), averaged per call
 // kind over the timed rounds, and the time of one allocation-range query on
-// its own.  With --streams S > 1 every fragment's round
+// its own.  With --batched 1 each fragment's arrivals go to the library in
+// one several-arrival call (with --fused 1 the call also closes: one pass
+// per fragment).  With --streams S > 1 every fragment's round
 // is its own handle on one of S streams (rounds in flight together), the
 // arrivals issued round-robin across fragments.  With --side 1 a round is
 // instead the side averages and the worker adoption over the whole buffer:
@@ -115,6 +118,7 @@ struct Args {
     bool side = false;
     bool inplace = true;
     bool host_timing = false;
+    bool batched = false;
 };
 
 [[noreturn]] void usage() {
@@ -122,7 +126,7 @@ struct Args {
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
                  "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n"
-                 "       [--side 0|1] [--inplace 0|1] [--host-timing 0|1]\n");
+                 "       [--side 0|1] [--inplace 0|1] [--host-timing 0|1] [--batched 0|1]\n");
     std::exit(2);
 }
 
@@ -153,10 +157,12 @@ Args parse(int argc, char** argv) {
         else if (k == "--side") a.side = std::atoi(v.c_str()) != 0;
         else if (k == "--inplace") a.inplace = std::atoi(v.c_str()) != 0;
         else if (k == "--host-timing") a.host_timing = std::atoi(v.c_str()) != 0;
+        else if (k == "--batched") a.batched = std::atoi(v.c_str()) != 0;
         else usage();
     }
     if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0 || a.streams < 1 ||
-        a.streams > 16 || (a.side && (a.workers < 5 || a.bf16 || !a.ema)))
+        a.streams > 16 || (a.side && (a.workers < 5 || a.bf16 || !a.ema)) ||
+        (a.batched && (a.streams > 1 || a.side)))
         usage();
     if (a.offsets.empty()) a.offsets = {0, a.n};
     return a;
@@ -254,10 +260,52 @@ int main(int argc, char** argv) {
                                       n_frags, a.offsets.data(), 1, a.workers, acc,
                                       fs[h % a.streams]);
             }));
+        // Batched: one several-arrival call per fragment (plus the close
+        // when it is not fused).
+        for (int f = 0; a.batched && f < n_frags; ++f) {
+            dl_round* h = rd[0];
+            std::vector<int> ids(a.workers);
+            std::vector<uint64_t> tags(a.workers, tag);
+            std::vector<int64_t> toks(a.workers);
+            std::vector<const void*> bases(a.workers);
+            for (int i = 0; i < a.workers; ++i) {
+                ids[i] = i;
+                toks[i] = 19660800 + 1000 * int64_t(i);
+                bases[i] = static_cast<const char*>(ck[i]) + a.offsets[f] * esz;
+            }
+            float* out = a.inplace ? acc : theta;
+            if (a.fused && a.delta)
+                DLCHECK(timed("fold_checkpoints_and_outer_nesterov", tr, [&] {
+                    return dl_fold_checkpoints_and_outer_nesterov(
+                        h, f, a.workers, ids.data(), tags.data(), bases.data(), dt, toks.data(),
+                        theta, m, 0.7f, 0.9f, e, 0.9f);
+                }));
+            else if (a.fused)
+                DLCHECK(timed("fold_checkpoints_and_finalize_mean", tr, [&] {
+                    return dl_fold_checkpoints_and_finalize_mean(h, f, a.workers, ids.data(),
+                                                                 tags.data(), bases.data(), dt,
+                                                                 out, e, 0.9f);
+                }));
+            else {
+                DLCHECK(timed("fold_checkpoints", tr, [&] {
+                    return dl_fold_checkpoints(h, f, a.workers, ids.data(), tags.data(),
+                                               bases.data(), dt, a.delta ? theta : nullptr,
+                                               toks.data());
+                }));
+                if (a.delta)
+                    DLCHECK(timed("outer_nesterov", tr, [&] {
+                        return dl_outer_nesterov(h, f, theta, m, 0.7f, 0.9f, e, 0.9f);
+                    }));
+                else
+                    DLCHECK(timed("finalize_mean", tr, [&] {
+                        return dl_finalize_mean(h, f, out, e, 0.9f);
+                    }));
+            }
+        }
         // One stream: one handle, fragment after fragment (as the benchmark
         // issues a round).  Several streams: one handle per fragment, the
         // arrivals round-robin across fragments.
-        for (int step = 0; step < a.workers * n_frags; ++step) {
+        for (int step = 0; !a.batched && step < a.workers * n_frags; ++step) {
             const int f = a.streams > 1 ? step % n_frags : step / a.workers;
             const int i = a.streams > 1 ? step / n_frags : step % a.workers;
             {

@@ -40,6 +40,8 @@ DL_NOALLOC_SCRATCH_BYTES = 192 << 20
 
 SYMBOLS = ("dl_round_begin", "dl_fold_checkpoint", "dl_finalize_mean", "dl_outer_nesterov",
            "dl_fold_and_finalize_mean", "dl_fold_and_outer_nesterov",
+           "dl_fold_checkpoints", "dl_fold_checkpoints_and_finalize_mean",
+           "dl_fold_checkpoints_and_outer_nesterov",
            "dl_ema_update", "dl_swa_fold", "dl_swa_average", "dl_snapshot_average",
            "dl_adopt_keep_drift", "dl_polar_workspace_bytes", "dl_polar_workspace_bytes_batch",
            "dl_polar_factor", "dl_outer_orthogonal_step", "dl_outer_orthogonal_step_batch",
@@ -68,6 +70,15 @@ _lib.dl_outer_nesterov.argtypes = [_p, _i32, _p, _p, _f32, _f32, _p, _f32]
 _lib.dl_fold_and_finalize_mean.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _p, _p, _f32]
 _lib.dl_fold_and_outer_nesterov.argtypes = [_p, _i32, _i32, _u64, _p, _i32, _i64, _p, _p, _f32,
                                             _f32, _p, _f32]
+_lib.dl_fold_checkpoints.argtypes = [_p, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_u64),
+                                     ctypes.POINTER(_p), _i32, _p, ctypes.POINTER(_i64)]
+_lib.dl_fold_checkpoints_and_finalize_mean.argtypes = [_p, _i32, _i32, ctypes.POINTER(_i32),
+                                                       ctypes.POINTER(_u64), ctypes.POINTER(_p),
+                                                       _i32, _p, _p, _f32]
+_lib.dl_fold_checkpoints_and_outer_nesterov.argtypes = [_p, _i32, _i32, ctypes.POINTER(_i32),
+                                                        ctypes.POINTER(_u64), ctypes.POINTER(_p),
+                                                        _i32, ctypes.POINTER(_i64), _p, _p, _f32,
+                                                        _f32, _p, _f32]
 _lib.dl_ema_update.argtypes = [_p, _p, _i64, _f32, _p]
 _lib.dl_swa_fold.argtypes = [_p, _p, _i64, _i64, _p]
 _lib.dl_swa_average.argtypes = [_p, _p, _i64, _i64, _p]
@@ -234,6 +245,70 @@ def dl_fold_and_outer_nesterov(r: Round, frag: int, worker_id: int, ckpt_round_t
                                            _f32_addr(momentum, "momentum"), float(lr),
                                            float(mu), _f32_addr(ema, "ema"), float(beta)),
            "dl_fold_and_outer_nesterov")
+
+
+def _arrivals(worker_ids: Sequence[int], ckpt_round_tags, ckpts: Sequence[Array],
+              tokens: Optional[Sequence[int]], dtype: Optional[int]):
+    """Host arrays of a several-arrival call.  An int tag applies to every
+    arrival; the dtype comes from the first checkpoint tensor unless given."""
+    count = len(worker_ids)
+    if isinstance(ckpt_round_tags, int):
+        ckpt_round_tags = [ckpt_round_tags] * count
+    if len(ckpt_round_tags) != count or len(ckpts) != count or \
+            (tokens is not None and len(tokens) != count):
+        raise ValueError("worker_ids, tags, checkpoints and tokens differ in length")
+    if dtype is None:
+        if count == 0:
+            dtype = DL_F32
+        else:
+            dtype = _ckpt_dtype(ckpts[0], None)
+            for c in ckpts[1:]:
+                if isinstance(c, torch.Tensor) and _ckpt_dtype(c, None) != dtype:
+                    raise TypeError("checkpoints of one call share one dtype")
+    n = max(1, count)
+    ids = (_i32 * n)(*[int(x) for x in worker_ids])
+    tags = (_u64 * n)(*[int(x) for x in ckpt_round_tags])
+    ptrs = (_p * n)(*[_addr(c) for c in ckpts])
+    tok = None if tokens is None else (_i64 * n)(*[int(x) for x in tokens])
+    return count, ids, tags, ptrs, tok, int(dtype)
+
+
+def dl_fold_checkpoints(r: Round, frag: int, worker_ids: Sequence[int], ckpt_round_tags,
+                        ckpts: Sequence[Array], global_: Array = None,
+                        tokens: Optional[Sequence[int]] = None,
+                        dtype: Optional[int] = None) -> None:
+    count, ids, tags, ptrs, tok, dtype = _arrivals(worker_ids, ckpt_round_tags, ckpts, tokens,
+                                                   dtype)
+    _check(_lib.dl_fold_checkpoints(r.handle, int(frag), count, ids, tags, ptrs, dtype,
+                                    _f32_addr(global_, "global"), tok),
+           "dl_fold_checkpoints")
+
+
+def dl_fold_checkpoints_and_finalize_mean(r: Round, frag: int, worker_ids: Sequence[int],
+                                          ckpt_round_tags, ckpts: Sequence[Array],
+                                          out_global: Array, ema: Array = None,
+                                          beta: float = 0.9,
+                                          dtype: Optional[int] = None) -> None:
+    count, ids, tags, ptrs, _, dtype = _arrivals(worker_ids, ckpt_round_tags, ckpts, None, dtype)
+    _check(_lib.dl_fold_checkpoints_and_finalize_mean(r.handle, int(frag), count, ids, tags, ptrs,
+                                                      dtype, _f32_addr(out_global, "out_global"),
+                                                      _f32_addr(ema, "ema"), float(beta)),
+           "dl_fold_checkpoints_and_finalize_mean")
+
+
+def dl_fold_checkpoints_and_outer_nesterov(r: Round, frag: int, worker_ids: Sequence[int],
+                                           ckpt_round_tags, ckpts: Sequence[Array],
+                                           tokens: Sequence[int], global_: Array,
+                                           momentum: Array, lr: float = 0.7, mu: float = 0.9,
+                                           ema: Array = None, beta: float = 0.9,
+                                           dtype: Optional[int] = None) -> None:
+    count, ids, tags, ptrs, tok, dtype = _arrivals(worker_ids, ckpt_round_tags, ckpts, tokens,
+                                                   dtype)
+    _check(_lib.dl_fold_checkpoints_and_outer_nesterov(
+        r.handle, int(frag), count, ids, tags, ptrs, dtype, tok, _f32_addr(global_, "global"),
+        _f32_addr(momentum, "momentum"), float(lr), float(mu), _f32_addr(ema, "ema"),
+        float(beta)),
+        "dl_fold_checkpoints_and_outer_nesterov")
 
 
 def dl_ema_update(ema: Array, global_: Array, beta: float = 0.9, n: Optional[int] = None,

@@ -23,7 +23,10 @@ orthogonalisation kernels.
 Kernel kinds follow the names the benchmark uses (fold, fold_first,
 fold_delta, fold_delta_first, finalize_mean[_ema], nesterov[_ema],
 fold_finalize_mean[_ema][_first], fold_nesterov[_ema][_first], ema,
-snapshot_mean_K, adopt_keep_drift; _bf16 for bf16 checkpoints).
+snapshot_mean_K, adopt_keep_drift; for several arrivals in one pass
+fold_all, fold_delta_all, fold_all_finalize_mean[_ema],
+fold_all_nesterov[_ema], with _more when earlier folds came first; _bf16 for
+bf16 checkpoints).
 """
 from __future__ import annotations
 
@@ -44,7 +47,8 @@ def kernel_kind(name: str):
 
     Kernels are k_stream<Op, NT> (128-bit path) or k_stream_scalar<Op>; the
     kind comes from the operation and its template arguments."""
-    m = re.search(r"::(FoldMeanClose|FoldNesterovClose|FoldSum|FoldDelta|MeanClose|"
+    m = re.search(r"::(FoldManyMeanClose|FoldManyNesterovClose|FoldSumMany|FoldDeltaMany|"
+                  r"FoldMeanClose|FoldNesterovClose|FoldSum|FoldDelta|MeanClose|"
                   r"NesterovClose|Ema|SnapshotMean|AdoptKeepDrift)\b(?:<([^>]*)>)?", name)
     if not m or "k_stream" not in name:
         return None
@@ -55,6 +59,16 @@ def kernel_kind(name: str):
     if op == "AdoptKeepDrift":
         return "adopt_keep_drift" + ("_bf16" if "short" in targs[0] else "")
     bf16 = "_bf16" if targs and "short" in targs[0] else ""
+    # several arrivals in one pass: the kinds of a call holding every arrival
+    # of the fragment (nothing folded before it); "_more" after earlier folds
+    more = "" if len(targs) > 1 and targs[1] == "true" else "_more"
+    if op == "FoldSumMany":
+        return "fold_all" + more + bf16
+    if op == "FoldDeltaMany":
+        return "fold_delta_all" + more + bf16
+    if op in ("FoldManyMeanClose", "FoldManyNesterovClose"):
+        base = "fold_all_finalize_mean" if op == "FoldManyMeanClose" else "fold_all_nesterov"
+        return base + ("_ema" if targs[2] == "true" else "") + more + bf16
     if op == "FoldSum":
         return ("fold_first" if targs[1] == "true" else "fold") + bf16
     if op == "FoldDelta":

@@ -22,6 +22,10 @@ Round structure (all on torch's current stream):
 * delta Nesterov:  for each fragment, fold every worker's token-weighted delta
                    in arrival order, then close with the outer Nesterov step
                    (+ EMA)
+* batched:         every checkpoint of the round is already resident, so each
+                   fragment's arrivals go to the library in one call (still in
+                   arrival order) and the fragment's whole merge is one pass
+                   that reads each buffer once
 """
 from __future__ import annotations
 
@@ -129,7 +133,8 @@ class GpuWorkload:
     def run_round(self, rnd: int, tag: int,
                   timer: Optional[Callable[[str, int, Callable[[], None]], None]] = None,
                   fused_close: bool = True,
-                  streams: Optional[List[torch.cuda.Stream]] = None) -> None:
+                  streams: Optional[List[torch.cuda.Stream]] = None,
+                  batched: bool = False) -> None:
         """Issue one merge round.  `timer(kind, elements, call)` (if given)
         wraps every kernel-launching call, e.g. to record events around it.
 
@@ -141,9 +146,19 @@ class GpuWorkload:
         stream (fragment f on streams[f % len(streams)]), so the fragments'
         rounds are in flight together; they touch disjoint element ranges.
         The streams wait for the caller's stream first and the caller's
-        stream waits for all of them at the end."""
+        stream waits for all of them at the end.
+
+        With `batched`, each fragment's arrivals are passed in one
+        several-arrival call (dl_fold_checkpoints_and_*, or
+        dl_fold_checkpoints and a separate close): same results, bit for bit,
+        in one pass per fragment."""
         if streams:
+            if batched:
+                raise ValueError("batched rounds run on one stream")
             self._run_round_streams(rnd, tag, timer, fused_close, streams)
+            return
+        if batched:
+            self._run_round_batched(rnd, tag, timer, fused_close)
             return
         w = self.w
         offs = list(w.frag_offsets)
@@ -203,6 +218,49 @@ class GpuWorkload:
             finally:
                 dl.dl_round_end(r)
 
+
+    def _run_round_batched(self, rnd, tag, timer, fused_close):
+        w = self.w
+        offs = list(w.frag_offsets)
+        orders = self.orders(rnd)
+        run = timer if timer is not None else (lambda kind, n, call: call())
+        ema = "_ema" if self.e is not None else ""
+        mode = dl.DL_DELTA_NESTEROV if self.delta else dl.DL_MEAN
+        out = self.acc if self.close_in_place else self.theta
+        tok = self.tokens(rnd) if self.delta else None
+        r = dl.dl_round_begin(tag, mode, w.n_params, offs, w.quorum, w.workers, self.acc)
+        try:
+            for f in range(w.n_frags):
+                o0, o1 = offs[f], offs[f + 1]
+                ids = list(orders[f])
+                cks = [self.ckpts[i][o0:o1] for i in ids]
+                if not self.delta:
+                    if fused_close:
+                        run("fold_all_finalize_mean" + ema, o1 - o0,
+                            lambda f=f, ids=ids, cks=cks: dl.dl_fold_checkpoints_and_finalize_mean(
+                                r, f, ids, tag, cks, out, self.e, w.beta))
+                    else:
+                        run("fold_all", o1 - o0, lambda f=f, ids=ids, cks=cks:
+                            dl.dl_fold_checkpoints(r, f, ids, tag, cks))
+                        run("finalize_mean" + ema, o1 - o0,
+                            lambda f=f: dl.dl_finalize_mean(r, f, out, self.e, w.beta))
+                else:
+                    t = [tok[i] for i in ids]
+                    if fused_close:
+                        run("fold_all_nesterov" + ema, o1 - o0,
+                            lambda f=f, ids=ids, cks=cks, t=t:
+                            dl.dl_fold_checkpoints_and_outer_nesterov(
+                                r, f, ids, tag, cks, t, self.theta, self.m, w.lr, w.mu, self.e,
+                                w.beta))
+                    else:
+                        run("fold_delta_all", o1 - o0, lambda f=f, ids=ids, cks=cks, t=t:
+                            dl.dl_fold_checkpoints(r, f, ids, tag, cks, self.theta, t))
+                        run("nesterov" + ema, o1 - o0,
+                            lambda f=f: dl.dl_outer_nesterov(r, f, self.theta, self.m, w.lr,
+                                                             w.mu, self.e, w.beta))
+        finally:
+            dl.dl_round_end(r)
+        self._swap_if_in_place()
 
     def _swap_if_in_place(self) -> None:
         """After a mean round closed in place, the accumulator holds the new
@@ -296,6 +354,15 @@ def algorithmic_bytes(w: synth.Workload, fused_close: bool = False) -> Dict[str,
         "fold_nesterov_first": cb + 16, "fold_nesterov_ema_first": cb + 24,
         "ema": 12,
     }
+    # every arrival of the fragment in one call (k = all workers): each
+    # checkpoint read once, the accumulator written once (not at all when the
+    # same pass closes), the state buffers read and written once
+    k = w.workers
+    per_elem.update({
+        "fold_all": k * cb + 4, "fold_delta_all": k * cb + 8,
+        "fold_all_finalize_mean": k * cb + 4, "fold_all_finalize_mean_ema": k * cb + 12,
+        "fold_all_nesterov": k * cb + 16, "fold_all_nesterov_ema": k * cb + 24,
+    })
     ema = "_ema" if w.ema else ""
     if w.mode == "mean":
         first, fold, close, fused = "fold_first", "fold", "finalize_mean", "fold_finalize_mean"
@@ -308,6 +375,14 @@ def algorithmic_bytes(w: synth.Workload, fused_close: bool = False) -> Dict[str,
                            + per_elem[fused + ema])
     else:
         per_param_fused = per_elem[fused + ema + "_first"]
+    batched = "fold_all_finalize_mean" if w.mode == "mean" else "fold_all_nesterov"
+    per_param_batched = per_elem[batched + ema]
+    fold_all = "fold_all" if w.mode == "mean" else "fold_delta_all"
+    per_param_batched_separate = per_elem[fold_all] + per_elem[close + ema]
     return {"per_elem": per_elem, "per_param": per_param, "per_round": per_param * w.n_params,
             "per_param_fused": per_param_fused,
-            "per_round_fused": per_param_fused * w.n_params}
+            "per_round_fused": per_param_fused * w.n_params,
+            "per_param_batched": per_param_batched,
+            "per_round_batched": per_param_batched * w.n_params,
+            "per_param_batched_separate": per_param_batched_separate,
+            "per_round_batched_separate": per_param_batched_separate * w.n_params}

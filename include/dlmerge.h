@@ -64,8 +64,8 @@
  * arrivals again.  A host allocation that fails is DL_E_NOMEM.  Device buffers
  * holding the global, momentum and EMA are written only by the closing calls
  * (dl_finalize_mean, dl_outer_nesterov, dl_fold_and_finalize_mean,
- * dl_fold_and_outer_nesterov, dl_ema_update), so an abandoned round changes
- * none of them.
+ * dl_fold_and_outer_nesterov, their several-arrival forms, dl_ema_update),
+ * so an abandoned round changes none of them.
  *
  * Threads.  A handle is used by one host thread at a time.  Several handles
  * may be open at once (two rounds in flight, GradientMail post, "Getting
@@ -249,6 +249,76 @@ int dl_fold_and_finalize_mean(dl_round *r, int frag, int worker_id, uint64_t ckp
 int dl_fold_and_outer_nesterov(dl_round *r, int frag, int worker_id, uint64_t ckpt_round_tag,
                                const void *ckpt, int dtype, int64_t tokens, float *global,
                                float *momentum, float lr, float mu, float *ema, float beta);
+
+/*
+ * Fold several arrivals of fragment frag in one pass.  A merger that holds
+ * more than one checkpoint of the fragment at once (they came in while it
+ * waited for the quorum or the grace timer, or a restarted merger finds the
+ * leftovers of the round, technical report, Table 2, rows "Merger" and
+ * "Recovery") reads the accumulator and the global once for all of them
+ * instead of once per arrival.  Results are identical, bit for bit, to
+ * `count` dl_fold_checkpoint calls in array order, which is taken as the
+ * arrival order (model card, "How it is trained", Merging bullet).
+ *
+ *   count            number of arrivals, 1 <= count <= max_workers.
+ *   worker_ids       host array of count worker ids (distinct, and not yet
+ *                    folded into the fragment).
+ *   ckpt_round_tags  host array of count tags, each equal to the round's.
+ *   ckpts            host array of count device pointers, each a
+ *                    fragment-length array of dtype (one dtype for all).
+ *                    Checkpoints may overlap one another (they are only
+ *                    read), not acc or global.
+ *   global, dtype    as in dl_fold_checkpoint.
+ *   tokens           DL_DELTA_NESTEROV: host array of count token counts,
+ *                    each > 0.  DL_MEAN: ignored (may be NULL).
+ *
+ * The host arrays are read during the call only.  The kernels take at most 8
+ * arrivals per pass; a larger count runs ceil(count / 8) passes, each
+ * arrival still folded in order.  Every arrival is checked as the single
+ * call would check it, after those before it; on any error nothing is
+ * launched and the handle is unchanged (first failing arrival's status).
+ *
+ * Errors: those of dl_fold_checkpoint, and DL_E_INVAL for count out of range
+ * or a NULL array.
+ */
+int dl_fold_checkpoints(dl_round *r, int frag, int count, const int *worker_ids,
+                        const uint64_t *ckpt_round_tags, const void *const *ckpts, int dtype,
+                        const float *global, const int64_t *tokens);
+
+/*
+ * dl_fold_checkpoints followed by dl_finalize_mean, the last pass folding and
+ * closing at once (one pass for up to 8 arrivals): the round's whole merge of
+ * a fragment when every checkpoint is already in.  Bit-identical to the
+ * separate calls; acc's fragment range is unspecified afterwards, as in
+ * dl_fold_and_finalize_mean.  The quorum check counts this call's arrivals.
+ * No checkpoint may overlap out_global or ema.
+ *
+ * Errors: those of dl_fold_checkpoints and dl_finalize_mean; nothing is
+ * launched and the handle is unchanged on any error but a failed launch.
+ */
+int dl_fold_checkpoints_and_finalize_mean(dl_round *r, int frag, int count,
+                                          const int *worker_ids, const uint64_t *ckpt_round_tags,
+                                          const void *const *ckpts, int dtype, float *out_global,
+                                          float *ema, float beta);
+
+/*
+ * dl_fold_checkpoints followed by dl_outer_nesterov, the last pass folding
+ * and taking the outer step (+ EMA) at once: with every arrival of a
+ * fragment in hand, each buffer (global, momentum, EMA and the checkpoints)
+ * is read once and global, momentum and EMA written once per round.
+ * Bit-identical to the separate calls; the token total is the exact sum over
+ * the fragment's arrivals including this call's.  No checkpoint may overlap
+ * global, momentum or ema.
+ *
+ * Errors: those of dl_fold_checkpoints and dl_outer_nesterov; nothing is
+ * launched and the handle is unchanged on any error but a failed launch.
+ */
+int dl_fold_checkpoints_and_outer_nesterov(dl_round *r, int frag, int count,
+                                           const int *worker_ids,
+                                           const uint64_t *ckpt_round_tags,
+                                           const void *const *ckpts, int dtype,
+                                           const int64_t *tokens, float *global, float *momentum,
+                                           float lr, float mu, float *ema, float beta);
 
 /*
  * Stand-alone EMA of globals: ema[j] = beta*ema[j] + (1-beta)*global[j] for

@@ -91,15 +91,43 @@ def participants(w: synth.Workload, rnd: int, frag: int, exactly_quorum: bool) -
     return order
 
 
+def _calls(order: Sequence[int], fused_last: bool, batch: Optional[int], single_first: int):
+    """How the GPU side issues a fragment's arrivals: a list of (kind, ids)
+    with kind "one" (dl_fold_checkpoint), "many" (dl_fold_checkpoints),
+    "one_close" / "many_close" (the folding-and-closing calls) or "close"."""
+    order = list(order)
+    if batch is None:
+        calls = [("one", [i]) for i in order]
+        if fused_last:
+            calls[-1] = ("one_close", calls[-1][1])
+        else:
+            calls.append(("close", []))
+        return calls
+    calls = [("one", [i]) for i in order[:single_first]]
+    rest = order[single_first:]
+    chunks = [rest[k:k + batch] for k in range(0, len(rest), batch)]
+    calls += [("many", c) for c in chunks]
+    if fused_last:
+        kind, ids = calls[-1]
+        calls[-1] = ("many_close" if kind == "many" else "one_close", ids)
+    else:
+        calls.append(("close", []))
+    return calls
+
+
 def run_round(w: synth.Workload, st: State, rnd: int, exactly_quorum: bool = False,
               orders: Optional[Sequence[Sequence[int]]] = None, stream=None,
-              fused_last: bool = False) -> dict:
+              fused_last: bool = False, batch: Optional[int] = None,
+              single_first: int = 0) -> dict:
     """One round on both sides.  Returns the GPU and oracle results (numpy).
 
     With `fused_last` the GPU folds each fragment's last arrival and closes
     the fragment in one call (dl_fold_and_*); the oracle always folds and
     closes in separate steps, so the comparison also checks that the fused
-    pass gives the same bits."""
+    pass gives the same bits.  With `batch`, the GPU folds the arrivals after
+    the first `single_first` in calls of up to `batch` arrivals each
+    (dl_fold_checkpoints, and with `fused_last` the last call also closes);
+    the oracle still folds one arrival at a time."""
     cks_gpu = worker_inputs(w, rnd, st.theta, st.g_theta.device)
     cks_np = {i: to_np(c) for i, c in cks_gpu.items()}
     offs = list(w.frag_offsets)
@@ -115,15 +143,20 @@ def run_round(w: synth.Workload, st: State, rnd: int, exactly_quorum: bool = Fal
         try:
             for f in range(w.n_frags):
                 o0, o1 = offs[f], offs[f + 1]
-                folds = list(orders[f][:-1]) if fused_last else list(orders[f])
-                for i in folds:
-                    dl.dl_fold_checkpoint(r, f, i, tag, cks_gpu[i][o0:o1])
-                if fused_last:
-                    i = orders[f][-1]
-                    dl.dl_fold_and_finalize_mean(r, f, i, tag, cks_gpu[i][o0:o1], st.g_theta,
-                                                 st.g_e, w.beta)
-                else:
-                    dl.dl_finalize_mean(r, f, st.g_theta, st.g_e, w.beta)
+                for kind, ids in _calls(orders[f], fused_last, batch, single_first):
+                    cks = [cks_gpu[i][o0:o1] for i in ids]
+                    if kind == "one":
+                        dl.dl_fold_checkpoint(r, f, ids[0], tag, cks[0])
+                    elif kind == "many":
+                        dl.dl_fold_checkpoints(r, f, ids, tag, cks)
+                    elif kind == "one_close":
+                        dl.dl_fold_and_finalize_mean(r, f, ids[0], tag, cks[0], st.g_theta,
+                                                     st.g_e, w.beta)
+                    elif kind == "many_close":
+                        dl.dl_fold_checkpoints_and_finalize_mean(r, f, ids, tag, cks, st.g_theta,
+                                                                 st.g_e, w.beta)
+                    else:
+                        dl.dl_finalize_mean(r, f, st.g_theta, st.g_e, w.beta)
             parts = [dl.dl_round_participants(r, f) for f in range(w.n_frags)]
         finally:
             dl.dl_round_end(r)
@@ -140,15 +173,23 @@ def run_round(w: synth.Workload, st: State, rnd: int, exactly_quorum: bool = Fal
         try:
             for f in range(w.n_frags):
                 o0, o1 = offs[f], offs[f + 1]
-                folds = list(orders[f][:-1]) if fused_last else list(orders[f])
-                for i in folds:
-                    dl.dl_fold_checkpoint(r, f, i, tag, cks_gpu[i][o0:o1], st.g_theta, tokens[i])
-                if fused_last:
-                    i = orders[f][-1]
-                    dl.dl_fold_and_outer_nesterov(r, f, i, tag, cks_gpu[i][o0:o1], tokens[i],
-                                                  st.g_theta, st.g_m, w.lr, w.mu, st.g_e, w.beta)
-                else:
-                    dl.dl_outer_nesterov(r, f, st.g_theta, st.g_m, w.lr, w.mu, st.g_e, w.beta)
+                for kind, ids in _calls(orders[f], fused_last, batch, single_first):
+                    cks = [cks_gpu[i][o0:o1] for i in ids]
+                    tok = [tokens[i] for i in ids]
+                    if kind == "one":
+                        dl.dl_fold_checkpoint(r, f, ids[0], tag, cks[0], st.g_theta, tok[0])
+                    elif kind == "many":
+                        dl.dl_fold_checkpoints(r, f, ids, tag, cks, st.g_theta, tok)
+                    elif kind == "one_close":
+                        dl.dl_fold_and_outer_nesterov(r, f, ids[0], tag, cks[0], tok[0],
+                                                      st.g_theta, st.g_m, w.lr, w.mu, st.g_e,
+                                                      w.beta)
+                    elif kind == "many_close":
+                        dl.dl_fold_checkpoints_and_outer_nesterov(r, f, ids, tag, cks, tok,
+                                                                  st.g_theta, st.g_m, w.lr, w.mu,
+                                                                  st.g_e, w.beta)
+                    else:
+                        dl.dl_outer_nesterov(r, f, st.g_theta, st.g_m, w.lr, w.mu, st.g_e, w.beta)
                 assert dl.dl_round_tokens(r, f) == sum(tokens[i] for i in orders[f])
             parts = [dl.dl_round_participants(r, f) for f in range(w.n_frags)]
         finally:

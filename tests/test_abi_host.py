@@ -26,7 +26,7 @@ def header_functions():
 
 def test_library_exports_every_declared_function():
     declared = header_functions()
-    assert len(declared) == 27
+    assert len(declared) == 30
     assert sorted(dl.SYMBOLS) == declared
     lib = dl.raw_lib()
     for name in declared:
@@ -157,6 +157,62 @@ def test_host_rules_fused_close():
                 g + (1 << 20), dtype=dl.DL_F32)                      # snapshot overlaps global
         _expect(dl.DL_E_STALE, dl.dl_fold_and_outer_nesterov, r, 0, 1, 9, ck, 5, g,
                 g + (1 << 20), dtype=dl.DL_F32)
+    finally:
+        dl.dl_round_end(r)
+
+
+def test_host_rules_several_arrivals():
+    """The several-arrival calls check every arrival as the one-arrival call
+    would, after those before it, and record nothing on any error."""
+    g = FAKE + (1 << 24)
+    ck = [FAKE + (1 << 22) + i * 4096 for i in range(4)]
+    r = dl.dl_round_begin(3, dl.DL_MEAN, 1000, OFFS4, 3, 4, FAKE, stream=0)
+    try:
+        fold = lambda ids, tags, cks, **k: dl.dl_fold_checkpoints(r, 0, ids, tags, cks,
+                                                                  dtype=dl.DL_F32, **k)
+        _expect(dl.DL_E_INVAL, fold, [], 3, [])                               # count 0
+        _expect(dl.DL_E_INVAL, fold, [0, 1, 2, 3, 0], 3, ck + [ck[0]])        # count > workers
+        _expect(dl.DL_E_DUP, fold, [0, 1, 0], 3, ck[:3])                      # within the call
+        _expect(dl.DL_E_STALE, fold, [0, 1], [3, 4], ck[:2])                  # second tag
+        _expect(dl.DL_E_INVAL, fold, [0, 4], 3, ck[:2])                       # worker range
+        _expect(dl.DL_E_INVAL, fold, [0, 1], 3, [ck[0], 0])                   # NULL checkpoint
+        _expect(dl.DL_E_ALIGN, fold, [0, 1], 3, [ck[0], ck[1] + 2])
+        _expect(dl.DL_E_INVAL, fold, [0, 1], 3, [ck[0], FAKE + 4 * 90])       # overlaps acc
+        _expect(dl.DL_E_INVAL, fold, [0, 1], 3, ck[:2], global_=g)            # global in MEAN
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoints, r, 4, [0], 3, ck[:1], dtype=dl.DL_F32)
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoints, r, 0, [0], 3, ck[:1], dtype=2)
+        close = lambda ids, cks, out, **k: dl.dl_fold_checkpoints_and_finalize_mean(
+            r, 0, ids, 3, cks, out, dtype=dl.DL_F32, **k)
+        _expect(dl.DL_E_QUORUM, close, [0, 1], ck[:2], g)                     # 2 < quorum 3
+        _expect(dl.DL_E_INVAL, close, [0, 1, 2], ck[:3], ck[2] - 8)           # out over a ckpt
+        _expect(dl.DL_E_INVAL, close, [0, 1, 2], ck[:3], g, ema=ck[1] + 4)    # ema over a ckpt
+        _expect(dl.DL_E_STATE, dl.dl_fold_checkpoints_and_outer_nesterov, r, 0, [0, 1, 2], 3,
+                ck[:3], [5, 5, 5], g, g + (1 << 20), dtype=dl.DL_F32)
+        assert dl.dl_round_participants(r, 0) == []
+        # a duplicate of an arrival recorded before the call
+        with pytest.raises(ValueError):
+            fold([0, 1], 3, ck[:3])                                           # lengths differ
+    finally:
+        dl.dl_round_end(r)
+    r = dl.dl_round_begin(3, dl.DL_DELTA_NESTEROV, 1000, OFFS4, 1, 4, FAKE, stream=0)
+    try:
+        fold = lambda ids, cks, tokens, **k: dl.dl_fold_checkpoints(
+            r, 0, ids, 3, cks, global_=g, tokens=tokens, dtype=dl.DL_F32, **k)
+        _expect(dl.DL_E_INVAL, fold, [0, 1], ck[:2], None)                    # no tokens
+        _expect(dl.DL_E_INVAL, fold, [0, 1], ck[:2], [5, 0])
+        _expect(dl.DL_E_INVAL, fold, [0, 1], ck[:2], [(1 << 62), (1 << 62)])  # sum overflows
+        _expect(dl.DL_E_INVAL, fold, [0, 1], [ck[0], g + 8], [5, 5])          # ckpt over global
+        _expect(dl.DL_E_INVAL, dl.dl_fold_checkpoints, r, 0, [0], 3, ck[:1], dtype=dl.DL_F32,
+                tokens=[5])                                                   # no global
+        nest = lambda ids, cks, tokens, mom, **k: dl.dl_fold_checkpoints_and_outer_nesterov(
+            r, 0, ids, 3, cks, tokens, g, mom, dtype=dl.DL_F32, **k)
+        _expect(dl.DL_E_INVAL, nest, [0, 1], ck[:2], [5, 5], ck[1])           # momentum = ckpt
+        _expect(dl.DL_E_INVAL, nest, [0, 1], ck[:2], [5, 5], g + (1 << 20), ema=ck[0])
+        _expect(dl.DL_E_INVAL, nest, [0, 1], ck[:2], [5, 5], g + 4)           # momentum over global
+        _expect(dl.DL_E_STATE, dl.dl_fold_checkpoints_and_finalize_mean, r, 0, [0], 3, ck[:1],
+                g, dtype=dl.DL_F32)
+        assert dl.dl_round_participants(r, 0) == []
+        assert dl.dl_round_tokens(r, 0) == 0
     finally:
         dl.dl_round_end(r)
 

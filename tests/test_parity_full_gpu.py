@@ -83,9 +83,12 @@ def gather(t, fw):
     return np.concatenate([mc.to_np(t[s:s + L]) for s, L in fw])
 
 
+@pytest.mark.parametrize("batched", [False, True], ids=["per_arrival", "batched"])
 @pytest.mark.parametrize("key", ["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
                                  "diffurefill1b_frag_nesterov_ema"])
-def test_full_size_sampled(key):
+def test_full_size_sampled(key, batched):
+    """batched: each fragment's arrivals in one several-arrival call (one
+    pass per fragment when it also closes)."""
     w = synth.WORKLOADS[key]
     say(f"[full] {key}: allocating and generating {w.n_params} params x {w.workers} workers")
     gw = GpuWorkload(w)
@@ -93,8 +96,8 @@ def test_full_size_sampled(key):
         gw.generate_checkpoints(r)
         # round 0 closes with the fused last arrival (the benchmark's round),
         # round 1 with a separate close
-        say(f"[full] {key}: round {r} fused_close={r == 0}")
-        gw.run_round(r, tag=100 + r, fused_close=(r == 0))
+        say(f"[full] {key}: round {r} fused_close={r == 0} batched={batched}")
+        gw.run_round(r, tag=100 + r, fused_close=(r == 0), batched=batched)
     torch.cuda.synchronize()
     wins = windows(w, 24, seed=w.seed)
     say(f"[full] {key}: oracle on {sum(L for fw in wins for _, L in fw)} sampled elements")
@@ -127,12 +130,19 @@ def _oracle_full_round(w, r, cks, theta, m, e):
                                         w.lr, w.mu, None if e is None else e[o0:o1], w.beta)
 
 
-@pytest.mark.parametrize("key", ["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
-                                 "diffurefill1b_frag_nesterov_ema"])
-def test_full_size_1b_every_element(key):
+@pytest.mark.parametrize("key,batched", [
+    ("diffurefill1b_mean_ema", False), ("diffurefill1b_bf16_mean_ema", False),
+    ("diffurefill1b_frag_nesterov_ema", False),
+    ("diffurefill1b_bf16_mean_ema", True), ("diffurefill1b_frag_nesterov_ema", True)],
+    ids=["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
+         "diffurefill1b_frag_nesterov_ema", "diffurefill1b_bf16_mean_ema-batched",
+         "diffurefill1b_frag_nesterov_ema-batched"])
+def test_full_size_1b_every_element(key, batched):
     """Every element of the 1.08B rounds, in the benchmark's launch
     configuration: the inputs the generator made on the GPU are copied to
-    host memory and the oracle runs the same rounds over whole arrays."""
+    host memory and the oracle runs the same rounds over whole arrays, one
+    arrival at a time.  batched: the GPU takes each fragment's arrivals in
+    one several-arrival call."""
     w = synth.WORKLOADS[key]
     say(f"[full-all] {key}: allocating and generating")
     gw = GpuWorkload(w)
@@ -141,8 +151,8 @@ def test_full_size_1b_every_element(key):
     e = theta.copy() if gw.e is not None else None
     for r in range(ROUNDS):
         gw.generate_checkpoints(r)
-        say(f"[full-all] {key}: round {r} fused_close={r == 0}")
-        gw.run_round(r, tag=200 + r, fused_close=(r == 0))
+        say(f"[full-all] {key}: round {r} fused_close={r == 0} batched={batched}")
+        gw.run_round(r, tag=200 + r, fused_close=(r == 0), batched=batched)
         cks = [mc.to_np(c) for c in gw.ckpts]
         say(f"[full-all] {key}: oracle round {r}")
         _oracle_full_round(w, r, cks, theta, m, e)
@@ -205,10 +215,11 @@ def _partial_participants(w, rnd, f, n):
     return [i for i in order if i not in missing][:n]
 
 
-def _run_partial_round(gw, rnd, tag, parts, quorum, fused):
+def _run_partial_round(gw, rnd, tag, parts, quorum, fused, batched=False):
     """One round through the C ABI on the workload's full-size buffers (the
     benchmark's launch configuration), each fragment closed by the given
-    participants in the given order."""
+    participants in the given order (with `batched`: all of them in one
+    several-arrival call that also closes)."""
     w = gw.w
     offs = list(w.frag_offsets)
     mode = dl.DL_DELTA_NESTEROV if gw.delta else dl.DL_MEAN
@@ -219,6 +230,17 @@ def _run_partial_round(gw, rnd, tag, parts, quorum, fused):
         for f in range(w.n_frags):
             o0, o1 = offs[f], offs[f + 1]
             ps = parts[f]
+            if batched:
+                cks = [gw.ckpts[i][o0:o1] for i in ps]
+                if gw.delta:
+                    dl.dl_fold_checkpoints_and_outer_nesterov(
+                        r, f, ps, tag, cks, [tok[i] for i in ps], gw.theta, gw.m, w.lr, w.mu,
+                        gw.e, w.beta)
+                else:
+                    dl.dl_fold_checkpoints_and_finalize_mean(r, f, ps, tag, cks, out, gw.e,
+                                                             w.beta)
+                assert dl.dl_round_participants(r, f) == list(ps)
+                continue
             for i in (ps[:-1] if fused else ps):
                 ck = gw.ckpts[i][o0:o1]
                 if gw.delta:
@@ -268,20 +290,23 @@ def _oracle_partial_on_windows(w, wins, parts_of):
     return res
 
 
-@pytest.mark.parametrize("key,n_close", [
+@pytest.mark.parametrize("key,n_close,batched", [
     # every fragment closed by exactly its quorum of 3 of the 5 workers
     # (GradientMail post, "Completing the run": 10 of 348 rounds closed with 3)
-    ("diffurefill1b_frag_nesterov_ema", 3),
+    ("diffurefill1b_frag_nesterov_ema", 3, False),
+    ("diffurefill1b_frag_nesterov_ema", 3, True),
     # a drain: a single leftover checkpoint closes the round with quorum 1
     # (technical report, Table 2, row "Recovery")
-    ("diffurefill1b_mean_ema", 1),
+    ("diffurefill1b_mean_ema", 1, False),
+    ("diffurefill1b_mean_ema", 1, True),
 ])
-def test_full_size_partial_participation(key, n_close):
+def test_full_size_partial_participation(key, n_close, batched):
     """Partial participation at full size, on the non-temporal kernels the
     small parity cases never reach: round 0 closes with the fused last
     arrival (for the drain: the first arrival folded in the same pass as the
-    close), round 1 with a separate close; sampled windows of every fragment
-    against the oracle, bit for bit."""
+    close), round 1 with a separate close; with `batched` both rounds pass
+    the participants in one call that also closes.  Sampled windows of every
+    fragment against the oracle, bit for bit."""
     w = synth.WORKLOADS[key]
     quorum = min(w.quorum, n_close)
     parts_of = lambda r, f: _partial_participants(w, r, f, n_close)
@@ -290,8 +315,9 @@ def test_full_size_partial_participation(key, n_close):
     for r in range(ROUNDS):
         gw.generate_checkpoints(r)
         parts = [parts_of(r, f) for f in range(w.n_frags)]
-        say(f"[partial] {key}: round {r} participants {parts} fused_close={r == 0}")
-        _run_partial_round(gw, r, 300 + r, parts, quorum, fused=(r == 0))
+        say(f"[partial] {key}: round {r} participants {parts} fused_close={r == 0}"
+            f" batched={batched}")
+        _run_partial_round(gw, r, 300 + r, parts, quorum, fused=(r == 0), batched=batched)
     torch.cuda.synchronize()
     wins = windows(w, 16, seed=w.seed + 2)
     want = _oracle_partial_on_windows(w, wins, parts_of)

@@ -29,6 +29,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
      "snapshot_mean_5"),
     ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::AdoptKeepDrift<float>, "
      "true>(...)", "adopt_keep_drift"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldManyNesterovClose<"
+     "float, true, true>, true>(...)", "fold_all_nesterov_ema"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldManyMeanClose<"
+     "unsigned short, true, true>, true>(...)", "fold_all_finalize_mean_ema_bf16"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldDeltaMany<float, "
+     "false>, true>(...)", "fold_delta_all_more"),
+    ("void dlk::(anonymous namespace)::k_stream<dlk::(anonymous namespace)::FoldSumMany<float, "
+     "true>, false>(...)", "fold_all"),
     ("void at::native::vectorized_elementwise_kernel<4, ...>(...)", None),
 ])
 def test_kernel_kind(name, kind):
