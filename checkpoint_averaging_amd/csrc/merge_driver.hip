@@ -8,7 +8,7 @@
 //                  [--workers W] [--dtype f32|bf16] [--ema 0|1]
 //                  [--rounds R] [--warmup R0] [--copy-mib M] [--fused 0|1]
 //                  [--streams S] [--side 1] [--inplace 0|1] [--host-timing 1]
-//                  [--batched 0|1]
+//                  [--batched 0|1|2]
 //
 // Round structure matches the benchmark: for each fragment, every worker is
 // folded (token-weighted delta in delta mode) and the fragment is closed
@@ -23,7 +23,8 @@
 // kind over the timed rounds, and the time of one allocation-range query on
 // its own.  With --batched 1 each fragment's arrivals go to the library in
 // one several-arrival call (with --fused 1 the call also closes: one pass
-// per fragment).  With --streams S > 1 every fragment's round
+// per fragment); --batched 2 alternates the two schedules round by round
+// (odd rounds batched), so one counter run covers both.  With --streams S > 1 every fragment's round
 // is its own handle on one of S streams (rounds in flight together), the
 // arrivals issued round-robin across fragments.  With --side 1 a round is
 // instead the side averages and the worker adoption over the whole buffer:
@@ -118,7 +119,7 @@ struct Args {
     bool side = false;
     bool inplace = true;
     bool host_timing = false;
-    bool batched = false;
+    int batched = 0;
 };
 
 [[noreturn]] void usage() {
@@ -126,7 +127,7 @@ struct Args {
                  "usage: dlmerge_driver --n N [--offsets 0,o1,...,N] [--mode mean|delta]\n"
                  "       [--workers W] [--dtype f32|bf16] [--ema 0|1] [--rounds R]\n"
                  "       [--warmup R0] [--copy-mib M] [--fused 0|1] [--streams S]\n"
-                 "       [--side 0|1] [--inplace 0|1] [--host-timing 0|1] [--batched 0|1]\n");
+                 "       [--side 0|1] [--inplace 0|1] [--host-timing 0|1] [--batched 0|1|2]\n");
     std::exit(2);
 }
 
@@ -157,12 +158,12 @@ Args parse(int argc, char** argv) {
         else if (k == "--side") a.side = std::atoi(v.c_str()) != 0;
         else if (k == "--inplace") a.inplace = std::atoi(v.c_str()) != 0;
         else if (k == "--host-timing") a.host_timing = std::atoi(v.c_str()) != 0;
-        else if (k == "--batched") a.batched = std::atoi(v.c_str()) != 0;
+        else if (k == "--batched") a.batched = std::atoi(v.c_str());
         else usage();
     }
     if (a.n <= 0 || a.workers < 1 || a.rounds < 0 || a.warmup < 0 || a.streams < 1 ||
         a.streams > 16 || (a.side && (a.workers < 5 || a.bf16 || !a.ema)) ||
-        (a.batched && (a.streams > 1 || a.side)))
+        a.batched < 0 || a.batched > 2 || (a.batched && (a.streams > 1 || a.side)))
         usage();
     if (a.offsets.empty()) a.offsets = {0, a.n};
     return a;
@@ -251,6 +252,7 @@ int main(int argc, char** argv) {
             continue;
         }
         const uint64_t tag = uint64_t(r) + 1;
+        const bool batched = a.batched == 1 || (a.batched == 2 && (r & 1));
         HIPCHECK(hipEventRecord(joins[0], s));
         for (int i = 1; i < a.streams; ++i) HIPCHECK(hipStreamWaitEvent(fs[i], joins[0], 0));
         std::vector<dl_round*> rd(a.streams > 1 ? n_frags : 1, nullptr);
@@ -262,7 +264,7 @@ int main(int argc, char** argv) {
             }));
         // Batched: one several-arrival call per fragment (plus the close
         // when it is not fused).
-        for (int f = 0; a.batched && f < n_frags; ++f) {
+        for (int f = 0; batched && f < n_frags; ++f) {
             dl_round* h = rd[0];
             std::vector<int> ids(a.workers);
             std::vector<uint64_t> tags(a.workers, tag);
@@ -305,7 +307,7 @@ int main(int argc, char** argv) {
         // One stream: one handle, fragment after fragment (as the benchmark
         // issues a round).  Several streams: one handle per fragment, the
         // arrivals round-robin across fragments.
-        for (int step = 0; !a.batched && step < a.workers * n_frags; ++step) {
+        for (int step = 0; !batched && step < a.workers * n_frags; ++step) {
             const int f = a.streams > 1 ? step % n_frags : step / a.workers;
             const int i = a.streams > 1 ? step / n_frags : step % a.workers;
             {
