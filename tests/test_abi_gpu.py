@@ -191,3 +191,35 @@ def test_pending_hip_error_is_reported_and_left_pending():
     assert lib.dl_ema_update(e.data_ptr(), ck.data_ptr(), n, 0.5, None) == 0
     torch.cuda.synchronize()
     assert torch.all(e == 0.5)
+
+
+def test_several_arrival_rules_on_device_buffers():
+    """The several-arrival calls: a rejected call (a checkpoint past its
+    allocation, a duplicate, a checkpoint under an output) folds nothing, and
+    the arrivals a later call folds are recorded in array order, after the
+    one-arrival folds before it."""
+    n = 4096
+    dev = torch.device("cuda")
+    acc = torch.empty(n, device=dev)
+    out = torch.empty(n, device=dev)
+    c = [torch.randn(n, device=dev) for _ in range(4)]
+    raw = RawAlloc(1 << 20)
+    try:
+        r = dl.dl_round_begin(6, dl.DL_MEAN, n, [0, n], 3, 4, acc)
+        dl.dl_fold_checkpoint(r, 0, 2, 6, c[2])
+        expect(dl.DL_E_INVAL, dl.dl_fold_checkpoints, r, 0, [0, 1], 6,
+               [c[0], raw.end - 4 * 100], dtype=dl.DL_F32)            # past its allocation
+        expect(dl.DL_E_DUP, dl.dl_fold_checkpoints, r, 0, [0, 2], 6, [c[0], c[2]])
+        expect(dl.DL_E_INVAL, dl.dl_fold_checkpoints_and_finalize_mean, r, 0, [0, 1], 6,
+               [c[0], c[1]], c[1])                                    # output over a checkpoint
+        assert dl.dl_round_participants(r, 0) == [2]
+        dl.dl_fold_checkpoints_and_finalize_mean(r, 0, [3, 0], 6, [c[3], c[0]], out)
+        assert dl.dl_round_participants(r, 0) == [2, 3, 0]
+        expect(dl.DL_E_STATE, dl.dl_fold_checkpoints, r, 0, [1], 6, [c[1]])
+        dl.dl_round_end(r)
+        torch.cuda.synchronize()
+        h = [x.cpu().numpy() for x in c]
+        want = ((h[2] + h[3]) + h[0]) / np.float32(3)         # binary32, IEEE division
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    finally:
+        raw.free()

@@ -4,7 +4,8 @@ the close without running them, and every replay runs one more round on
 the same buffers.  Replays are checked, bit for bit, against the same rounds
 run eagerly on a second copy of the state, with eager work and
 synchronisations between the replays, and the state after the last replay
-against the CPU oracle's same four rounds."""
+against the CPU oracle's same four rounds.  Rounds are issued one call
+per arrival, or with each fragment's arrivals in one several-arrival call."""
 import numpy as np
 import pytest
 import torch
@@ -17,28 +18,30 @@ from tests import merge_cases as mc
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate_close", "fused_close"])
+@pytest.mark.parametrize("fused,batched", [(False, False), (True, False), (True, True),
+                                          (False, True)],
+                         ids=["separate_close", "fused_close", "one_pass", "one_pass_then_close"])
 @pytest.mark.parametrize("key,n,offs", [
     ("pythia14m_mean", 300_005, [0, 300_005]),
     ("pythia14m_frag_nesterov", 400_003, [0, 150_000, 200_004, 250_000, 400_003]),
     ("diffurefill1b_bf16_mean_ema", 200_001, [0, 200_001]),
 ])
-def test_captured_round_replays_match_eager_rounds(key, n, offs, fused):
+def test_captured_round_replays_match_eager_rounds(key, n, offs, fused, batched):
     w = synth.scaled(synth.WORKLOADS[key], n, offs)
     eager = GpuWorkload(w)
     graphed = GpuWorkload(w)
     eager.generate_checkpoints(0)
     graphed.generate_checkpoints(0)
-    eager.run_round(0, tag=1, fused_close=fused)        # also loads the kernels before capture
+    eager.run_round(0, tag=1, fused_close=fused, batched=batched)   # loads the kernels
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        graphed.run_round(0, tag=1, fused_close=fused)
+        graphed.run_round(0, tag=1, fused_close=fused, batched=batched)
     torch.cuda.synchronize()
     for k in range(4):
         g.replay()
         if k:
-            eager.run_round(0, tag=2 + k, fused_close=fused)
+            eager.run_round(0, tag=2 + k, fused_close=fused, batched=batched)
         torch.cuda.synchronize()
         for name in ("theta", "m", "e"):
             a, b = getattr(graphed, name), getattr(eager, name)
