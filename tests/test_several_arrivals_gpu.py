@@ -126,3 +126,90 @@ def test_several_arrivals_at_nontemporal_size():
                      [0, 4, (1 << 24) + 7])
     rounds(w, fused_last=True, batch=8)
     rounds(w, n_rounds=1, fused_last=False, batch=2, single_first=1)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_close", "fused_close"])
+@pytest.mark.parametrize("n", [4096 + 3, (1 << 24) + 3], ids=["cached", "non_temporal"])
+def test_several_arrivals_special_values(n, fused):
+    """NaN, infinities, subnormals and -0 in the checkpoints and the global
+    go through the several-arrival passes as through the oracle's one-arrival
+    folds (IEEE semantics, no flush to zero), on the cached and the
+    non-temporal kernels."""
+    rng = np.random.default_rng(11 + n)
+    base = (0.02 * rng.standard_normal(n)).astype(np.float32)
+    specials = np.array([np.nan, np.inf, -np.inf, 1e-40, -1e-42, 2.0 ** -149, -0.0, 3e38],
+                        dtype=np.float32)
+    k = max(200, n // 1000)
+
+    def planted(a):
+        a = a.copy()
+        idx = np.concatenate([rng.integers(0, n, size=k), [0, n - 1]])
+        a[idx] = specials[rng.integers(0, specials.size, size=idx.size)]
+        return a
+
+    cks = [planted(base) for _ in range(3)]
+    dev = torch.device("cuda")
+    g_cks = [torch.from_numpy(c).to(dev) for c in cks]
+    acc = torch.empty(n, device=dev)
+    out = torch.empty(n, device=dev)
+    ema = torch.from_numpy(base.copy()).to(dev)
+    e_o = base.copy()
+    r = dl.dl_round_begin(1, dl.DL_MEAN, n, [0, n], 1, 3, acc)
+    if fused:
+        dl.dl_fold_checkpoints_and_finalize_mean(r, 0, [0, 1, 2], 1, g_cks, out, ema, 0.9)
+    else:
+        dl.dl_fold_checkpoints(r, 0, [0, 1, 2], 1, g_cks)
+        dl.dl_finalize_mean(r, 0, out, ema, 0.9)
+    dl.dl_round_end(r)
+    g_o = oracle.mean_round(cks, ema=e_o)
+    torch.cuda.synchronize()
+    assert mc.bits_equal(mc.to_np(out), g_o), mc.first_mismatch(mc.to_np(out), g_o)
+    assert mc.bits_equal(mc.to_np(ema), e_o), mc.first_mismatch(mc.to_np(ema), e_o)
+    th0 = planted(base)
+    theta = torch.from_numpy(th0.copy()).to(dev)
+    m = torch.zeros(n, device=dev)
+    ema = torch.from_numpy(th0.copy()).to(dev)
+    th_o, m_o, e_o = th0.copy(), np.zeros(n, np.float32), th0.copy()
+    tok = [1000, 1001, 1002]
+    r = dl.dl_round_begin(2, dl.DL_DELTA_NESTEROV, n, [0, n], 1, 3, acc)
+    if fused:
+        dl.dl_fold_checkpoints_and_outer_nesterov(r, 0, [0, 1, 2], 2, g_cks, tok, theta, m, 0.7,
+                                                  0.9, ema, 0.9)
+    else:
+        dl.dl_fold_checkpoints(r, 0, [0, 1, 2], 2, g_cks, theta, tok)
+        dl.dl_outer_nesterov(r, 0, theta, m, 0.7, 0.9, ema, 0.9)
+    dl.dl_round_end(r)
+    oracle.nesterov_fragment_round(th_o, m_o, cks, tok, 0.7, 0.9, e_o, 0.9)
+    torch.cuda.synchronize()
+    for name, g, o in (("theta", theta, th_o), ("m", m, m_o), ("ema", ema, e_o)):
+        assert mc.bits_equal(mc.to_np(g), o), (name, mc.first_mismatch(mc.to_np(g), o))
+
+
+@pytest.mark.parametrize("ckdtype", ["f32", "bf16"])
+def test_several_arrivals_misaligned_checkpoint(ckdtype):
+    """One checkpoint of the call one element off a 16-byte boundary (8 for
+    bf16): the whole pass takes the element-by-element path, same bits."""
+    w = dataclasses.replace(synth.scaled(W["diffurefill1b_frag_nesterov_ema"], 50_003, [0, 50_003]),
+                            ckpt_dtype=ckdtype)
+    n = w.n_params
+    dev = torch.device("cuda")
+    theta0 = synth.global0(w.seed, n)
+    cks = [synth.worker_checkpoint(w.seed, 0, i, theta0.to(dev), dtype=ckdtype) for i in range(3)]
+    shifted = torch.empty(n + 1, dtype=cks[1].dtype, device=dev)
+    shifted[1:] = cks[1]
+    g_cks = [cks[0], shifted[1:], cks[2]]
+    assert g_cks[1].data_ptr() % (16 if ckdtype == "f32" else 8) != 0
+    theta, m = theta0.to(dev), torch.zeros(n, device=dev)
+    ema = theta0.to(dev)
+    acc = torch.empty(n, device=dev)
+    tok = [200_000, 210_000, 190_000]
+    r = dl.dl_round_begin(3, dl.DL_DELTA_NESTEROV, n, [0, n], 3, 3, acc)
+    dl.dl_fold_checkpoints_and_outer_nesterov(r, 0, [0, 1, 2], 3, g_cks, tok, theta, m, w.lr,
+                                              w.mu, ema, w.beta)
+    dl.dl_round_end(r)
+    th_o, m_o, e_o = theta0.numpy().copy(), np.zeros(n, np.float32), theta0.numpy().copy()
+    oracle.nesterov_fragment_round(th_o, m_o, [mc.to_np(c) for c in cks], tok, w.lr, w.mu, e_o,
+                                   w.beta)
+    torch.cuda.synchronize()
+    for name, g, o in (("theta", theta, th_o), ("m", m, m_o), ("ema", ema, e_o)):
+        assert mc.bits_equal(mc.to_np(g), o), (name, mc.first_mismatch(mc.to_np(g), o))
