@@ -10,7 +10,8 @@ stream it runs on, giving each kernel's average duration.  Prints one JSON
 line: the HBM bytes the round moves per second, merged params/s, the
 fraction of the 8 TB/s HBM peak, the workload's algorithmic bytes per second,
 the roofline of the dominant kernel, the same round with each fragment's
-arrivals passed in one call (`batched_round`, one pass per fragment), and the
+arrivals passed in one call (`batched_round`, one pass per fragment), a plain
+device-to-device copy as the box's reference point (`copy_ceiling`), and the
 CPU oracle timed on a bounded sample of the same workload.
 
 Default workload: DiffuRefill-1B (1,075,980,288 fp32 params) in 4 fragments,
@@ -480,6 +481,44 @@ def cpu_baseline_polar(max_seconds: float = 12.0):
                       f"factor, {el:.1f} s on {cpu_model()}"}
 
 
+def copy_ceiling(torch, nbytes: int = 4 << 30, reps: int = 5):
+    """Plain device-to-device copies of nbytes, timed with events (read +
+    write bytes per second), as the box's reference point for the streaming
+    kernels: the library's own engine copying (dl_swa_fold with nothing
+    folded before is sum = global, one pack per lane, non-temporal), and
+    torch's copy_."""
+    from checkpoint_averaging_amd import dlmerge as dl
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+
+    def median_ms(call):
+        call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]
+
+    eng = median_ms(lambda: dl.dl_swa_fold(dst, src, 0))
+    tch = median_ms(lambda: dst.copy_(src))
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = lambda ms: 2 * nbytes / (ms / 1e3) / 1e9
+    return {"engine_copy_GB_per_s": round(gbs(eng), 1),
+            "engine_copy_frac_of_hbm_peak": round(gbs(eng) / HBM_PEAK_GBS, 4),
+            "torch_copy_GB_per_s": round(gbs(tch), 1),
+            "bytes_each_way": nbytes,
+            "method": ("median of %d copies each: the library's streaming engine "
+                       "(dl_swa_fold with nothing folded before), and torch copy_" % reps)}
+
+
 def batched_round(gw, w, ab, args, torch):
     """The same round with every fragment's arrivals passed in one
     several-arrival call that also closes (all checkpoints are resident): one
@@ -786,11 +825,16 @@ def main():
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": None,
+        "copy_ceiling": None,
     }
     if not args.batched and streams is None and not args.graph and args.steps > 0:
         out["batched_round"] = batched_round(gw, w, ab, args, torch)
         out["batched_round"]["speedup_vs_per_arrival_round"] = round(
             ms / out["batched_round"]["ms_per_step"], 3)
+    if not args.runtime_fill and w.n_params >= (1 << 28):
+        out["copy_ceiling"] = copy_ceiling(torch)
+        log(f"[bench] plain copy: {out['copy_ceiling']['engine_copy_GB_per_s']} GB/s "
+            f"(library engine), {out['copy_ceiling']['torch_copy_GB_per_s']} GB/s (torch)")
     if not args.no_cpu_baseline:
         del gw
         torch.cuda.empty_cache()
