@@ -286,18 +286,19 @@ int check_arrival_spans(const dl_round* r, int frag, const void* const* ckpts,
     return DL_OK;
 }
 
-// Launches the folds of a validated call in passes of at most
-// dlk::max_arrivals_per_pass() arrivals, in order; with `close_mean` or
-// `close_nesterov` the last pass also closes the fragment.  Records the
-// arrivals once every pass is launched.
+// The buffers and parameters of a close taken in the same pass as the last
+// arrivals (pointers already offset to the fragment).
 struct CloseArgs {
-    float* out = nullptr;                // mean: new global (offset to the fragment)
-    float* theta = nullptr;              // Nesterov: global, momentum (offset)
+    float* out = nullptr;                // mean: new global
+    float* theta = nullptr;              // Nesterov: global, momentum
     float* m = nullptr;
     float* ema = nullptr;
     float lr = 0, mu = 0, beta = 0;
 };
 
+// Launches the folds of a validated call in passes of at most
+// dlk::max_arrivals_per_pass() arrivals, in order; with `close` the last pass
+// also closes the fragment.  Records the arrivals once every pass is launched.
 int fold_passes(dl_round* r, int frag, int count, const int* worker_ids,
                 const void* const* ckpts, int dtype, const float* global, const Arrivals& a,
                 const CloseArgs* close) {
