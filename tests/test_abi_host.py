@@ -189,9 +189,9 @@ def test_host_rules_several_arrivals():
         _expect(dl.DL_E_STATE, dl.dl_fold_checkpoints_and_outer_nesterov, r, 0, [0, 1, 2], 3,
                 ck[:3], [5, 5, 5], g, g + (1 << 20), dtype=dl.DL_F32)
         assert dl.dl_round_participants(r, 0) == []
-        # a duplicate of an arrival recorded before the call
+        # the binding checks that the per-arrival arrays agree in length
         with pytest.raises(ValueError):
-            fold([0, 1], 3, ck[:3])                                           # lengths differ
+            fold([0, 1], 3, ck[:3])
     finally:
         dl.dl_round_end(r)
     r = dl.dl_round_begin(3, dl.DL_DELTA_NESTEROV, 1000, OFFS4, 1, 4, FAKE, stream=0)
