@@ -118,13 +118,16 @@ def test_one_buffer_for_two_workers():
         assert mc.bits_equal(g, o), f"{name}: {mc.first_mismatch(g, o)}"
 
 
-def test_several_arrivals_at_nontemporal_size():
+@pytest.mark.parametrize("key", ["diffurefill1b_frag_nesterov_ema", "diffurefill1b_mean_ema",
+                                 "diffurefill1b_bf16_mean_ema"])
+def test_several_arrivals_at_nontemporal_size(key):
     """A fragment of 2^24 + 3 elements (the non-temporal kernels, both pass
-    directions, a ragged tail): the several-arrival round against the
-    oracle's one-at-a-time round."""
-    w = synth.scaled(W["diffurefill1b_frag_nesterov_ema"], (1 << 24) + 7,
-                     [0, 4, (1 << 24) + 7])
+    directions, a ragged tail): several-arrival rounds against the oracle's
+    one-at-a-time rounds, with the closing pass both the fragment's first
+    (all arrivals in one call) and after earlier folds."""
+    w = synth.scaled(W[key], (1 << 24) + 7, [0, 4, (1 << 24) + 7])
     rounds(w, fused_last=True, batch=8)
+    rounds(w, n_rounds=1, fused_last=True, batch=2, single_first=1)
     rounds(w, n_rounds=1, fused_last=False, batch=2, single_first=1)
 
 
