@@ -43,6 +43,8 @@ CASES = [
     ("diffurefill1b_mean_ema", 3 * 4096 * 4 + 3, None),
     ("diffurefill1b_bf16_mean_ema", (1 << 20) + 5, None),
     ("diffurefill1b_frag_nesterov_ema", (1 << 20) + 7, [0, 140_000, 428_000, 716_000, (1 << 20) + 7]),
+    ("diffurefill1b_mean_ema", 300_001, [0, 100_001, 300_001]),                   # unaligned
+    ("diffurefill1b_bf16_mean_ema", 200_003, [0, 66_667, 200_003]),               # unaligned
 ]
 SCHEDULES = [
     dict(batch=8),                      # all arrivals of a fragment in one call
