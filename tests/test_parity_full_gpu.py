@@ -132,11 +132,11 @@ def _oracle_full_round(w, r, cks, theta, m, e):
 
 @pytest.mark.parametrize("key,batched", [
     ("diffurefill1b_mean_ema", False), ("diffurefill1b_bf16_mean_ema", False),
-    ("diffurefill1b_frag_nesterov_ema", False),
+    ("diffurefill1b_frag_nesterov_ema", False), ("diffurefill1b_mean_ema", True),
     ("diffurefill1b_bf16_mean_ema", True), ("diffurefill1b_frag_nesterov_ema", True)],
     ids=["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
-         "diffurefill1b_frag_nesterov_ema", "diffurefill1b_bf16_mean_ema-batched",
-         "diffurefill1b_frag_nesterov_ema-batched"])
+         "diffurefill1b_frag_nesterov_ema", "diffurefill1b_mean_ema-batched",
+         "diffurefill1b_bf16_mean_ema-batched", "diffurefill1b_frag_nesterov_ema-batched"])
 def test_full_size_1b_every_element(key, batched):
     """Every element of the 1.08B rounds, in the benchmark's launch
     configuration: the inputs the generator made on the GPU are copied to
