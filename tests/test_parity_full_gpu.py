@@ -83,35 +83,39 @@ def gather(t, fw):
     return np.concatenate([mc.to_np(t[s:s + L]) for s, L in fw])
 
 
-@pytest.mark.parametrize("batched", [False, True], ids=["per_arrival", "batched"])
 @pytest.mark.parametrize("key", ["diffurefill1b_mean_ema", "diffurefill1b_bf16_mean_ema",
                                  "diffurefill1b_frag_nesterov_ema"])
-def test_full_size_sampled(key, batched):
-    """batched: each fragment's arrivals in one several-arrival call (one
-    pass per fragment when it also closes)."""
+def test_full_size_sampled(key):
+    """Two GPU states on the same checkpoints, one folding each arrival with
+    its own call, the other taking each fragment's arrivals in one
+    several-arrival call (one pass per fragment when it also closes);
+    sampled windows of both against the oracle on CPU-regenerated inputs."""
     w = synth.WORKLOADS[key]
     say(f"[full] {key}: allocating and generating {w.n_params} params x {w.workers} workers")
-    gw = GpuWorkload(w)
+    per_arrival = GpuWorkload(w)
+    batched = GpuWorkload(w)
+    batched.ckpts = per_arrival.ckpts              # the same checkpoint buffers
+    torch.cuda.empty_cache()
     for r in range(ROUNDS):
-        gw.generate_checkpoints(r)
+        per_arrival.generate_checkpoints(r)
         # round 0 closes with the fused last arrival (the benchmark's round),
         # round 1 with a separate close
-        say(f"[full] {key}: round {r} fused_close={r == 0} batched={batched}")
-        gw.run_round(r, tag=100 + r, fused_close=(r == 0), batched=batched)
+        say(f"[full] {key}: round {r} fused_close={r == 0}, per arrival and batched")
+        per_arrival.run_round(r, tag=100 + r, fused_close=(r == 0))
+        batched.run_round(r, tag=100 + r, fused_close=(r == 0), batched=True)
     torch.cuda.synchronize()
     wins = windows(w, 24, seed=w.seed)
     say(f"[full] {key}: oracle on {sum(L for fw in wins for _, L in fw)} sampled elements")
     want = oracle_on_windows(w, wins)
-    for f, fw in enumerate(wins):
-        got = {"theta": gather(gw.theta, fw)}
-        if gw.m is not None:
-            got["m"] = gather(gw.m, fw)
-        if gw.e is not None:
-            got["e"] = gather(gw.e, fw)
-        for k, g in got.items():
-            o = want[f][k]
-            assert mc.bits_equal(g, o), f"{key} frag {f} {k}: {mc.first_mismatch(g, o)}"
-    del gw
+    for gw, how in ((per_arrival, "per arrival"), (batched, "batched")):
+        for f, fw in enumerate(wins):
+            for k in ("theta", "m", "e"):
+                t = getattr(gw, k)
+                if t is None:
+                    continue
+                g, o = gather(t, fw), want[f][k]
+                assert mc.bits_equal(g, o), f"{key} {how} frag {f} {k}: {mc.first_mismatch(g, o)}"
+    del per_arrival, batched
     torch.cuda.empty_cache()
 
 
