@@ -146,16 +146,15 @@ class GpuWorkload:
         stream (fragment f on streams[f % len(streams)]), so the fragments'
         rounds are in flight together; they touch disjoint element ranges.
         The streams wait for the caller's stream first and the caller's
-        stream waits for all of them at the end.
+        stream waits for all of them at the end.  With `batched` too, each
+        fragment's arrivals go in one call on the fragment's stream.
 
         With `batched`, each fragment's arrivals are passed in one
         several-arrival call (dl_fold_checkpoints_and_*, or
         dl_fold_checkpoints and a separate close): same results, bit for bit,
         in one pass per fragment."""
         if streams:
-            if batched:
-                raise ValueError("batched rounds run on one stream")
-            self._run_round_streams(rnd, tag, timer, fused_close, streams)
+            self._run_round_streams(rnd, tag, timer, fused_close, streams, batched)
             return
         if batched:
             self._run_round_batched(rnd, tag, timer, fused_close)
@@ -219,45 +218,48 @@ class GpuWorkload:
                 dl.dl_round_end(r)
 
 
+    def _fragment_batched(self, r, f, tag, order, tok, out, run, ema, fused_close):
+        """Fragment f's arrivals in one several-arrival call on torch's
+        current stream (and the close, when it is not fused)."""
+        w = self.w
+        o0, o1 = w.frag_offsets[f], w.frag_offsets[f + 1]
+        ids = list(order)
+        cks = [self.ckpts[i][o0:o1] for i in ids]
+        if not self.delta:
+            if fused_close:
+                run("fold_all_finalize_mean" + ema, o1 - o0,
+                    lambda: dl.dl_fold_checkpoints_and_finalize_mean(r, f, ids, tag, cks, out,
+                                                                     self.e, w.beta))
+            else:
+                run("fold_all", o1 - o0, lambda: dl.dl_fold_checkpoints(r, f, ids, tag, cks))
+                run("finalize_mean" + ema, o1 - o0,
+                    lambda: dl.dl_finalize_mean(r, f, out, self.e, w.beta))
+        else:
+            t = [tok[i] for i in ids]
+            if fused_close:
+                run("fold_all_nesterov" + ema, o1 - o0,
+                    lambda: dl.dl_fold_checkpoints_and_outer_nesterov(
+                        r, f, ids, tag, cks, t, self.theta, self.m, w.lr, w.mu, self.e, w.beta))
+            else:
+                run("fold_delta_all", o1 - o0,
+                    lambda: dl.dl_fold_checkpoints(r, f, ids, tag, cks, self.theta, t))
+                run("nesterov" + ema, o1 - o0,
+                    lambda: dl.dl_outer_nesterov(r, f, self.theta, self.m, w.lr, w.mu, self.e,
+                                                 w.beta))
+
     def _run_round_batched(self, rnd, tag, timer, fused_close):
         w = self.w
-        offs = list(w.frag_offsets)
         orders = self.orders(rnd)
         run = timer if timer is not None else (lambda kind, n, call: call())
         ema = "_ema" if self.e is not None else ""
         mode = dl.DL_DELTA_NESTEROV if self.delta else dl.DL_MEAN
         out = self.acc if self.close_in_place else self.theta
         tok = self.tokens(rnd) if self.delta else None
-        r = dl.dl_round_begin(tag, mode, w.n_params, offs, w.quorum, w.workers, self.acc)
+        r = dl.dl_round_begin(tag, mode, w.n_params, list(w.frag_offsets), w.quorum, w.workers,
+                              self.acc)
         try:
             for f in range(w.n_frags):
-                o0, o1 = offs[f], offs[f + 1]
-                ids = list(orders[f])
-                cks = [self.ckpts[i][o0:o1] for i in ids]
-                if not self.delta:
-                    if fused_close:
-                        run("fold_all_finalize_mean" + ema, o1 - o0,
-                            lambda f=f, ids=ids, cks=cks: dl.dl_fold_checkpoints_and_finalize_mean(
-                                r, f, ids, tag, cks, out, self.e, w.beta))
-                    else:
-                        run("fold_all", o1 - o0, lambda f=f, ids=ids, cks=cks:
-                            dl.dl_fold_checkpoints(r, f, ids, tag, cks))
-                        run("finalize_mean" + ema, o1 - o0,
-                            lambda f=f: dl.dl_finalize_mean(r, f, out, self.e, w.beta))
-                else:
-                    t = [tok[i] for i in ids]
-                    if fused_close:
-                        run("fold_all_nesterov" + ema, o1 - o0,
-                            lambda f=f, ids=ids, cks=cks, t=t:
-                            dl.dl_fold_checkpoints_and_outer_nesterov(
-                                r, f, ids, tag, cks, t, self.theta, self.m, w.lr, w.mu, self.e,
-                                w.beta))
-                    else:
-                        run("fold_delta_all", o1 - o0, lambda f=f, ids=ids, cks=cks, t=t:
-                            dl.dl_fold_checkpoints(r, f, ids, tag, cks, self.theta, t))
-                        run("nesterov" + ema, o1 - o0,
-                            lambda f=f: dl.dl_outer_nesterov(r, f, self.theta, self.m, w.lr,
-                                                             w.mu, self.e, w.beta))
+                self._fragment_batched(r, f, tag, orders[f], tok, out, run, ema, fused_close)
         finally:
             dl.dl_round_end(r)
         self._swap_if_in_place()
@@ -268,7 +270,7 @@ class GpuWorkload:
         if not self.delta and self.close_in_place:
             self.theta, self.acc = self.acc, self.theta
 
-    def _run_round_streams(self, rnd, tag, timer, fused_close, streams):
+    def _run_round_streams(self, rnd, tag, timer, fused_close, streams, batched=False):
         w = self.w
         offs = list(w.frag_offsets)
         orders = self.orders(rnd)
@@ -287,8 +289,13 @@ class GpuWorkload:
                 st.wait_event(start)
                 handles.append(dl.dl_round_begin(tag, mode, w.n_params, offs, w.quorum,
                                                  w.workers, self.acc, stream=st))
+            if batched:
+                for f in range(w.n_frags):
+                    with torch.cuda.stream(streams[f % len(streams)]):
+                        self._fragment_batched(handles[f], f, tag, orders[f], tok, out, run, ema,
+                                               fused_close)
             # issue arrivals round-robin across fragments, as they would come
-            for k in range(w.workers):
+            for k in range(0 if batched else w.workers):
                 for f in range(w.n_frags):
                     st = streams[f % len(streams)]
                     r = handles[f]

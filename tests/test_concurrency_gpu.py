@@ -16,16 +16,18 @@ from tests import merge_cases as mc
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("batched", [False, True], ids=["per_arrival", "one_call"])
 @pytest.mark.parametrize("fused", [False, True], ids=["separate_close", "fused_close"])
 @pytest.mark.parametrize("key,n,offs", [
     ("pythia14m_frag_nesterov", 400_003, [0, 150_000, 200_004, 250_000, 400_003]),
     ("diffurefill1b_frag_nesterov_ema", 600_001, [0, 84_000, 256_004, 428_000, 600_001]),
     ("diffurefill1b_bf16_mean_ema", 300_005, [0, 300_005]),
 ])
-def test_fragment_rounds_on_separate_streams(key, n, offs, fused):
+def test_fragment_rounds_on_separate_streams(key, n, offs, fused, batched):
     """Every fragment's round is its own handle on its own stream, arrivals
     issued round-robin across fragments (workload.GpuWorkload with
-    `streams`)."""
+    `streams`), or each fragment's arrivals in one several-arrival call on
+    its stream."""
     w = synth.scaled(synth.WORKLOADS[key], n, offs)
     gw = GpuWorkload(w)
     streams = [torch.cuda.Stream() for _ in range(4)]
@@ -35,7 +37,7 @@ def test_fragment_rounds_on_separate_streams(key, n, offs, fused):
     e = theta.copy() if w.ema else None
     for r in range(3):
         gw.generate_checkpoints(r)
-        gw.run_round(r, tag=10 + r, fused_close=fused, streams=streams)
+        gw.run_round(r, tag=10 + r, fused_close=fused, streams=streams, batched=batched)
         cks = [mc.to_np(c) for c in gw.ckpts]
         tok = synth.token_counts(w, r)
         for f in range(w.n_frags):
